@@ -1,0 +1,270 @@
+"""TEST INFRASTRUCTURE ONLY: Python face of the fp64 CPU oracle.
+
+Only tests, the smoke check and the benchmark's CPU-baseline leg import this
+module.  It wraps the plain C routines of svdq_oracle.c (ctypes) and adds the
+one step that calls a library primitive: the top-r SVD of the smoothed
+weight, done with numpy.linalg.svd (LAPACK) in float64.
+
+Method source: "Bringing Nunchaku 4-bit Diffusion Inference to Diffusers"
+(Hugging Face blog), section "Background: SVDQuant and Nunchaku" (smoothing
+moves activation outliers into the weights, a small 16-bit low-rank branch
+takes the hardest part of each weight matrix, the residual goes to 4 bits;
+the low-rank down projection is fused with the quantization and the up
+projection with the 4-bit product), and section "Native loading in
+Diffusers" (rank 32, bfloat16 compute dtype, 4-bit weight groups).
+The formulas, with the readings that fix what the prose leaves open, are at
+the top of svdq_oracle.c.
+
+Parity unpinned: the exact bits of the low-rank factors (several results are
+correct: signs of singular-vector pairs, rotations inside repeated singular
+values, last-bit differences between SVD algorithms); they are checked by
+Eckart-Young instead.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(HERE, "liboracle.so")
+
+INT4 = 0
+MXFP4 = 1
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            from oracle.build import build as _build
+            _build()
+        L = ctypes.CDLL(_LIB_PATH)
+        P = ctypes.c_void_p
+        I = ctypes.c_int
+        L.oracle_quant_group_int4.restype = ctypes.c_float
+        L.oracle_quant_group_int4.argtypes = [P, I, P]
+        L.oracle_quant_block_mxfp4.restype = ctypes.c_uint8
+        L.oracle_quant_block_mxfp4.argtypes = [P, I, P]
+        L.oracle_e2m1_value.restype = ctypes.c_double
+        L.oracle_e2m1_value.argtypes = [ctypes.c_uint8]
+        L.oracle_e8m0_value.restype = ctypes.c_double
+        L.oracle_e8m0_value.argtypes = [ctypes.c_uint8]
+        L.oracle_pack_nibbles.argtypes = [P, I, P]
+        L.oracle_smooth.argtypes = [P, P, I, I, P]
+        L.oracle_residual.argtypes = [P, P, P, P, I, I, I, I, P, P, P]
+        L.oracle_quant_act.argtypes = [P, I, I, P, P, I, I, P, P, P]
+        L.oracle_linear.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, P, I, P, P, P]
+        L.oracle_gelu_tanh.restype = ctypes.c_double
+        L.oracle_gelu_tanh.argtypes = [ctypes.c_double]
+        L.oracle_num_threads.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _p(a: Optional[np.ndarray]):
+    return None if a is None else ctypes.c_void_p(a.ctypes.data)
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(np.asarray(a, dtype=dtype))
+
+
+def group_of(prec: int) -> int:
+    return 64 if prec == INT4 else 32
+
+
+# ------------------------------------------------------------ group quantizers
+
+def quant_group_int4(v) -> tuple[np.ndarray, np.float32]:
+    v = _c(v, np.float32)
+    q = np.zeros(v.size, np.int8)
+    sc = lib().oracle_quant_group_int4(_p(v), v.size, _p(q))
+    return q, np.float32(sc)
+
+
+def quant_block_mxfp4(v) -> tuple[np.ndarray, int]:
+    v = _c(v, np.float32)
+    c = np.zeros(v.size, np.uint8)
+    e = lib().oracle_quant_block_mxfp4(_p(v), v.size, _p(c))
+    return c, int(e)
+
+
+def pack_nibbles(q) -> np.ndarray:
+    q = _c(q, np.int8)
+    out = np.zeros(q.size // 2, np.uint8)
+    lib().oracle_pack_nibbles(_p(q), q.size, _p(out))
+    return out
+
+
+def e2m1_value(code: int) -> float:
+    return lib().oracle_e2m1_value(code)
+
+
+def e8m0_value(e: int) -> float:
+    return lib().oracle_e8m0_value(e)
+
+
+def gelu_tanh(y: float) -> float:
+    return lib().oracle_gelu_tanh(y)
+
+
+def num_threads() -> int:
+    return lib().oracle_num_threads()
+
+
+# ------------------------------------------------------------------ bf16 (own)
+
+def _bf16_bits_from_f64(a: np.ndarray) -> np.ndarray:
+    """Round float64 to bf16 bits: nearest-even on the float64 value, done as
+    float64 -> float32 (RNE) -> bf16 (RNE on the upper 16 bits)."""
+    f = np.asarray(a, np.float64).astype(np.float32)
+    u = f.view(np.uint32).astype(np.int64)
+    keep = u >> 16
+    rem = u & 0xFFFF
+    up = (rem > 0x8000) | ((rem == 0x8000) & ((keep & 1) == 1))
+    return (keep + up.astype(np.int64)).astype(np.uint16)
+
+
+def bf16_to_f64(b: np.ndarray) -> np.ndarray:
+    return (np.asarray(b, np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+# ------------------------------------------------------------------ pack steps
+
+def smooth(W: np.ndarray, act_absmax: np.ndarray) -> np.ndarray:
+    W = _c(W, np.uint16)
+    a = _c(act_absmax, np.float32)
+    N, K = W.shape
+    s = np.zeros(K, np.float32)
+    lib().oracle_smooth(_p(W), _p(a), N, K, _p(s))
+    return s
+
+
+def lowrank(W: np.ndarray, s: np.ndarray, r: int):
+    """Top-r SVD of What_kn = W_nk / s_k (float64, numpy/LAPACK).
+
+    Returns (down_bits [r][K], up_bits [N][r], sigma (all singular values),
+    L1 = U_r S_r [K][r] float64, L2 = V_r^T [r][N] float64).  Components beyond
+    the matrix rank are zero.
+    """
+    Wd = bf16_to_f64(W)                              # [N][K]
+    What = (Wd / np.asarray(s, np.float64)[None, :]).T  # [K][N]
+    U, S, Vt = np.linalg.svd(What, full_matrices=False)
+    K, N = What.shape
+    rr = min(r, S.size)
+    L1 = np.zeros((K, r))
+    L2 = np.zeros((r, N))
+    L1[:, :rr] = U[:, :rr] * S[None, :rr]
+    L2[:rr, :] = Vt[:rr, :]
+    # sign convention (reproducibility only): largest-|.| entry of v_j positive
+    for j in range(rr):
+        i = int(np.argmax(np.abs(L2[j])))
+        if L2[j, i] < 0:
+            L2[j] = -L2[j]
+            L1[:, j] = -L1[:, j]
+    down = _bf16_bits_from_f64((np.asarray(s, np.float64)[:, None] * L1).T)  # [r][K]
+    up = _bf16_bits_from_f64(L2.T)                                         # [N][r]
+    return down, up, S, L1, L2
+
+
+def residual(W, s, down, up, prec: int, want_R: bool = False):
+    W = _c(W, np.uint16)
+    s = _c(s, np.float32)
+    down = _c(down, np.uint16)
+    up = _c(up, np.uint16)
+    N, K = W.shape
+    r = down.shape[0]
+    G = K // group_of(prec)
+    wq = np.zeros((N, K // 2), np.uint8)
+    wscale = np.zeros((N, G), np.float32 if prec == INT4 else np.uint8)
+    R = np.zeros((N, K), np.float32) if want_R else None
+    lib().oracle_residual(_p(W), _p(s), _p(down), _p(up), N, K, r, prec, _p(wq), _p(wscale), _p(R))
+    return (wq, wscale, R) if want_R else (wq, wscale)
+
+
+def pack_weights(W, act_absmax, r: int = 32, prec: int = INT4):
+    """The whole packing step with the oracle's own SVD."""
+    s = smooth(W, act_absmax)
+    down, up, _, _, _ = lowrank(W, s, r)
+    wq, wscale = residual(W, s, down, up, prec)
+    return dict(smooth=s, down=down, up=up, wq=wq, wscale=wscale)
+
+
+# ---------------------------------------------------------------- runtime steps
+
+def quant_act(X, s, down, prec: int):
+    X = _c(X, np.uint16)
+    s = _c(s, np.float32)
+    down = _c(down, np.uint16)
+    M, K = X.shape
+    r = down.shape[0]
+    G = K // group_of(prec)
+    xq = np.zeros((M, K // 2), np.uint8)
+    xscale = np.zeros((M, G), np.float32 if prec == INT4 else np.uint8)
+    h = np.zeros((M, r), np.float64)
+    lib().oracle_quant_act(_p(X), M, K, _p(s), _p(down), r, prec, _p(xq), _p(xscale), _p(h))
+    return xq, xscale, h
+
+
+def linear(xq, xscale, h, wq, wscale, up, bias, prec: int, gelu: bool = False,
+           rows=None, parts: bool = False):
+    """fp64 output for the given rows (all rows by default)."""
+    xq = _c(xq, np.uint8)
+    wq = _c(wq, np.uint8)
+    h = _c(h, np.float64)
+    up = _c(up, np.uint16)
+    sdt = np.float32 if prec == INT4 else np.uint8
+    xscale = _c(xscale, sdt)
+    wscale = _c(wscale, sdt)
+    bias = None if bias is None else _c(bias, np.uint16)
+    M = xq.shape[0]
+    N = wq.shape[0]
+    K = xq.shape[1] * 2
+    r = up.shape[1]
+    if rows is None:
+        rows_a = None
+        nrows = M
+    else:
+        rows_a = _c(rows, np.int32)
+        nrows = rows_a.size
+    y = np.zeros((nrows, N), np.float64)
+    yq = np.zeros((nrows, N), np.float64) if parts else None
+    ylr = np.zeros((nrows, N), np.float64) if parts else None
+    lib().oracle_linear(_p(xq), _p(xscale), _p(h), _p(wq), _p(wscale), _p(up), _p(bias),
+                        M, N, K, r, prec, int(bool(gelu)), _p(rows_a), nrows, _p(y), _p(yq), _p(ylr))
+    return (y, yq, ylr) if parts else y
+
+
+def forward(X, packed: dict, bias, prec: int, gelu: bool = False, rows=None):
+    """Quantize activations, then the linear, with the given packed weights."""
+    xq, xscale, h = quant_act(X, packed["smooth"], packed["down"], prec)
+    y = linear(xq, xscale, h, packed["wq"], packed["wscale"], packed["up"], bias, prec,
+               gelu=gelu, rows=rows)
+    return y, (xq, xscale, h)
+
+
+# ----------------------------------------------------------------- decoding
+
+def unpack_int4(codes: np.ndarray) -> np.ndarray:
+    """Nibble-packed two's-complement INT4 -> int8 (element 2i in the low nibble)."""
+    c = np.asarray(codes, np.uint8)
+    lo = (c & 0x0F).astype(np.int16)
+    hi = (c >> 4).astype(np.int16)
+    out = np.empty(c.shape[:-1] + (c.shape[-1] * 2,), np.int16)
+    out[..., 0::2] = lo
+    out[..., 1::2] = hi
+    out[out >= 8] -= 16
+    return out.astype(np.int8)
+
+
+def unpack_nibbles(codes: np.ndarray) -> np.ndarray:
+    c = np.asarray(codes, np.uint8)
+    out = np.empty(c.shape[:-1] + (c.shape[-1] * 2,), np.uint8)
+    out[..., 0::2] = c & 0x0F
+    out[..., 1::2] = c >> 4
+    return out

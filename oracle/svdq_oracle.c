@@ -1,0 +1,346 @@
+/*
+ * svdq_oracle.c -- TEST INFRASTRUCTURE ONLY.
+ *
+ * A plain, slow, fp64 CPU oracle for the SVDQuant W4A4 linear layer.  Only
+ * the tests, the smoke check and the benchmark's CPU-baseline leg may load
+ * it; the library never links or calls it, and it shares no code, header or
+ * table with the library.  Built with gcc -O2 -ffp-contract=off -fopenmp
+ * (OpenMP only distributes independent output rows).
+ *
+ * What the method computes, from "Bringing Nunchaku 4-bit Diffusion
+ * Inference to Diffusers" (Hugging Face blog), section "Background: SVDQuant
+ * and Nunchaku": activation outliers are moved into the weights by a
+ * per-channel smoothing, the hardest part of each weight matrix is kept in a
+ * small 16-bit low-rank branch, and the remaining residual is quantized to
+ * 4 bits; both weights and activations are 4-bit (W4A4).  Section "Native
+ * loading in Diffusers" fixes rank 32 and a bfloat16 compute dtype.  The
+ * exact formulas below are readings of that prose (listed with their
+ * justification in the design notes of the repository):
+ *
+ *   smoothing   lambda_k = sqrt(max|X_k| / max_n |W_nk|)   (1 if either is 0)
+ *               s_k      = fl32(1 / lambda_k)
+ *   low rank    What_kn = W_nk / s_k;  top-r SVD What ~ U S V^T
+ *               down[j][k] = bf16(s_k * (U S)_kj)   (r x K, smoothing folded)
+ *               up[n][j]   = bf16(V_nj)             (N x r)
+ *   residual    R_kn = (W_nk - sum_j down[j][k]*up[n][j]) / s_k   (fp64)
+ *               quantized from fl32(R) per (n, 64-group along k)
+ *   activation  xhat_mk = fl32(X_mk * s_k), quantized per (m, 64-group)
+ *               h_mj    = sum_k X_mk * down[j][k]
+ *   output      y_mn = sum_g sx_mg sw_ng sum_{k in g} qx_mk qw_nk
+ *                      + sum_j h_mj up[n][j] + b_n     [optionally GELU-tanh]
+ *
+ * INT4 group quantizer (symmetric, 64 wide): a = max|v|; scale = fl32(a/7)
+ * (0 if a == 0; rounded upward instead of to nearest when a/7 is below the
+ * smallest normal fp32); q = round-half-even of the exact real quotient
+ * v/scale, clamped to [-7, 7] (the clamp never acts).  Nibbles: byte i = (q[2i] & 15) | (q[2i+1] & 15) << 4.
+ *
+ * MXFP4 block quantizer (OCP Microscaling v1.0 conversion; 32 wide):
+ * X = floor(log2 a) - 2, clamped to [-127, 127], stored as E8M0 X + 127;
+ * t = v * 2^-X rounded to the E2M1 grid {0, .5, 1, 1.5, 2, 3, 4, 6}, ties to
+ * the even grid index, |t| > 6 saturating to 6; code = sign << 3 | index,
+ * the sign kept for zero.
+ *
+ * Every routine is the definition written out; none is blocked or reordered.
+ */
+#include <float.h>
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#ifndef M_PI
+#define M_PI 3.14159265358979323846
+#endif
+
+#define ORACLE_INT4 0
+#define ORACLE_MXFP4 1
+
+/* ------------------------------------------------------------------ dtypes */
+
+static double bf16_val(uint16_t b)
+{
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+/* ----------------------------------------------------------- INT4 groups */
+
+/* One symmetric INT4 group: returns scale, writes codes in [-7, 7]. */
+float oracle_quant_group_int4(const float *v, int n, int8_t *q)
+{
+    float a = 0.0f;
+    for (int i = 0; i < n; ++i) {
+        float t = fabsf(v[i]);
+        if (t > a) a = t;
+    }
+    if (a == 0.0f) {
+        for (int i = 0; i < n; ++i) q[i] = 0;
+        return 0.0f;
+    }
+    /* fl32(a / 7): the fp64 quotient rounded to fp32 is the correctly rounded
+     * fp32 quotient (53 >= 2*24 + 2, so double rounding cannot bite). */
+    float scale = (float)((double)a / 7.0);
+    /* Below the normal range the quotient is rounded upward instead, so that
+     * a <= 7 * scale holds for every group and no code is ever clamped. */
+    if (scale < FLT_MIN && (double)scale * 7.0 < (double)a)
+        scale = nextafterf(scale, INFINITY);
+    double S = (double)scale;
+    for (int i = 0; i < n; ++i) {
+        double x = (double)v[i];
+        double ax = fabs(x);
+        /* |x| against the tie points (j + 1/2) * S, each exact in fp64. */
+        int m = 8;
+        for (int j = 0; j < 8; ++j) {
+            double tie = ((double)j + 0.5) * S;
+            if (ax < tie) { m = j; break; }
+            if (ax == tie) { m = (j % 2 == 0) ? j : j + 1; break; }
+        }
+        if (m > 7) m = 7;
+        q[i] = (int8_t)(x < 0 ? -m : m);
+    }
+    return scale;
+}
+
+/* ---------------------------------------------------------- MXFP4 blocks */
+
+static const double E2M1_GRID[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+
+/* One MXFP4 block: returns the E8M0 byte, writes E2M1 codes (one per byte). */
+uint8_t oracle_quant_block_mxfp4(const float *v, int n, uint8_t *code)
+{
+    float a = 0.0f;
+    for (int i = 0; i < n; ++i) {
+        float t = fabsf(v[i]);
+        if (t > a) a = t;
+    }
+    int X;
+    if (a == 0.0f) {
+        X = -127;
+    } else {
+        int e;
+        frexp((double)a, &e);          /* a = f * 2^e, f in [0.5, 1) */
+        X = (e - 1) - 2;               /* floor(log2 a) - emax(E2M1) */
+    }
+    if (X < -127) X = -127;
+    if (X > 127) X = 127;
+    for (int i = 0; i < n; ++i) {
+        double t = ldexp((double)v[i], -X);     /* exact */
+        double at = fabs(t);
+        int idx;
+        if (at >= 6.0) {
+            idx = 7;
+        } else {
+            idx = 0;
+            for (int j = 0; j < 7; ++j) {
+                double mid = 0.5 * (E2M1_GRID[j] + E2M1_GRID[j + 1]);
+                if (at < mid) { idx = j; break; }
+                if (at == mid) { idx = (j % 2 == 0) ? j : j + 1; break; }
+                idx = j + 1;
+            }
+        }
+        int sign = signbit(v[i]) ? 1 : 0;
+        code[i] = (uint8_t)((sign << 3) | idx);
+    }
+    return (uint8_t)(X + 127);
+}
+
+double oracle_e2m1_value(uint8_t code)
+{
+    double m = E2M1_GRID[code & 7];
+    return (code & 8) ? -m : m;
+}
+
+double oracle_e8m0_value(uint8_t e)
+{
+    if (e == 0xFF) return NAN;
+    return ldexp(1.0, (int)e - 127);
+}
+
+/* --------------------------------------------------------------- nibbles */
+
+void oracle_pack_nibbles(const int8_t *q, int n, uint8_t *out)
+{
+    for (int i = 0; i < n / 2; ++i)
+        out[i] = (uint8_t)(((uint8_t)q[2 * i] & 0x0F) | (((uint8_t)q[2 * i + 1] & 0x0F) << 4));
+}
+
+static int int4_of_nibble(int nib) { return nib >= 8 ? nib - 16 : nib; }
+
+static int nibble_at(const uint8_t *row, int k)
+{
+    uint8_t b = row[k >> 1];
+    return (k & 1) ? (b >> 4) : (b & 0x0F);
+}
+
+/* Quantize one row of `K` values into codes (K/2 bytes) and scales. */
+static void quant_row(const float *v, int K, int prec, uint8_t *codes, void *scales)
+{
+    if (prec == ORACLE_INT4) {
+        int8_t q[64];
+        float *sc = (float *)scales;
+        for (int g = 0; g < K / 64; ++g) {
+            sc[g] = oracle_quant_group_int4(v + 64 * g, 64, q);
+            oracle_pack_nibbles(q, 64, codes + 32 * g);
+        }
+    } else {
+        uint8_t c[32];
+        uint8_t *sc = (uint8_t *)scales;
+        for (int b = 0; b < K / 32; ++b) {
+            sc[b] = oracle_quant_block_mxfp4(v + 32 * b, 32, c);
+            for (int i = 0; i < 16; ++i)
+                codes[16 * b + i] = (uint8_t)((c[2 * i] & 0x0F) | ((c[2 * i + 1] & 0x0F) << 4));
+        }
+    }
+}
+
+/* -------------------------------------------------------------- smoothing */
+
+/* s_k = fl32(1 / sqrt(max|X_k| / max_n|W_nk|)), 1 when either max is 0. */
+void oracle_smooth(const uint16_t *W, const float *act_absmax, int N, int K, float *s)
+{
+    for (int k = 0; k < K; ++k) {
+        double mw = 0.0;
+        for (int n = 0; n < N; ++n) {
+            double w = fabs(bf16_val(W[(size_t)n * K + k]));
+            if (w > mw) mw = w;
+        }
+        double mx = (double)act_absmax[k];
+        if (mx == 0.0 || mw == 0.0) {
+            s[k] = 1.0f;
+        } else {
+            double lambda = sqrt(mx / mw);
+            s[k] = (float)(1.0 / lambda);
+        }
+    }
+}
+
+/* --------------------------------------------------------------- residual */
+
+/* R_kn = (W_nk - sum_j down[j][k] up[n][j]) / s_k  (fp64, j ascending),
+ * then fl32(R) quantized per (n, group along k). */
+void oracle_residual(const uint16_t *W, const float *s, const uint16_t *down,
+                     const uint16_t *up, int N, int K, int r, int prec,
+                     uint8_t *wq, void *wscale, float *R_out /* may be NULL */)
+{
+    int G = (prec == ORACLE_INT4) ? K / 64 : K / 32;
+#pragma omp parallel for schedule(static)
+    for (int n = 0; n < N; ++n) {
+        float *row = (float *)malloc(sizeof(float) * (size_t)K);
+        for (int k = 0; k < K; ++k) {
+            double acc = 0.0;
+            for (int j = 0; j < r; ++j)
+                acc += bf16_val(down[(size_t)j * K + k]) * bf16_val(up[(size_t)n * r + j]);
+            double R = (bf16_val(W[(size_t)n * K + k]) - acc) / (double)s[k];
+            row[k] = (float)R;
+        }
+        if (R_out) memcpy(R_out + (size_t)n * K, row, sizeof(float) * (size_t)K);
+        if (prec == ORACLE_INT4)
+            quant_row(row, K, prec, wq + (size_t)n * (K / 2), (float *)wscale + (size_t)n * G);
+        else
+            quant_row(row, K, prec, wq + (size_t)n * (K / 2), (uint8_t *)wscale + (size_t)n * G);
+        free(row);
+    }
+}
+
+/* ------------------------------------------------------------- activation */
+
+/* xhat = fl32(X * s) quantized per row/group; h = X . down^T in fp64. */
+void oracle_quant_act(const uint16_t *X, int M, int K, const float *s, const uint16_t *down,
+                      int r, int prec, uint8_t *xq, void *xscale, double *h)
+{
+    int G = (prec == ORACLE_INT4) ? K / 64 : K / 32;
+#pragma omp parallel for schedule(static)
+    for (int m = 0; m < M; ++m) {
+        float *row = (float *)malloc(sizeof(float) * (size_t)K);
+        for (int k = 0; k < K; ++k)
+            row[k] = (float)(bf16_val(X[(size_t)m * K + k]) * (double)s[k]);
+        if (prec == ORACLE_INT4)
+            quant_row(row, K, prec, xq + (size_t)m * (K / 2), (float *)xscale + (size_t)m * G);
+        else
+            quant_row(row, K, prec, xq + (size_t)m * (K / 2), (uint8_t *)xscale + (size_t)m * G);
+        for (int j = 0; j < r; ++j) {
+            double acc = 0.0;
+            for (int k = 0; k < K; ++k)
+                acc += bf16_val(X[(size_t)m * K + k]) * bf16_val(down[(size_t)j * K + k]);
+            h[(size_t)m * r + j] = acc;
+        }
+        free(row);
+    }
+}
+
+/* ----------------------------------------------------------------- output */
+
+static double gelu_tanh(double y)
+{
+    const double c = sqrt(2.0 / M_PI);
+    return 0.5 * y * (1.0 + tanh(c * (y + 0.044715 * y * y * y)));
+}
+
+double oracle_gelu_tanh(double y) { return gelu_tanh(y); }
+
+/* y for the listed rows (all rows when rows == NULL, nrows == M).
+ * The 4-bit term, the low-rank term and the bias are also returned separately
+ * when the matching pointer is non-NULL (each [nrows][N]). */
+void oracle_linear(const uint8_t *xq, const void *xscale, const double *h,
+                   const uint8_t *wq, const void *wscale, const uint16_t *up,
+                   const uint16_t *bias, int M, int N, int K, int r, int prec, int gelu,
+                   const int *rows, int nrows, double *y, double *y_q4, double *y_lr)
+{
+    (void)M;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int i = 0; i < nrows; ++i) {
+        int m = rows ? rows[i] : i;
+        const uint8_t *xr = xq + (size_t)m * (K / 2);
+        for (int n = 0; n < N; ++n) {
+            const uint8_t *wr = wq + (size_t)n * (K / 2);
+            double q4 = 0.0;
+            if (prec == ORACLE_INT4) {
+                const float *sx = (const float *)xscale + (size_t)m * (K / 64);
+                const float *sw = (const float *)wscale + (size_t)n * (K / 64);
+                for (int g = 0; g < K / 64; ++g) {
+                    long long P = 0;
+                    for (int k = 64 * g; k < 64 * g + 64; ++k)
+                        P += (long long)int4_of_nibble(nibble_at(xr, k)) *
+                             (long long)int4_of_nibble(nibble_at(wr, k));
+                    q4 += (double)sx[g] * (double)sw[g] * (double)P;
+                }
+            } else {
+                const uint8_t *ex = (const uint8_t *)xscale + (size_t)m * (K / 32);
+                const uint8_t *ew = (const uint8_t *)wscale + (size_t)n * (K / 32);
+                for (int b = 0; b < K / 32; ++b) {
+                    double P = 0.0;
+                    for (int k = 32 * b; k < 32 * b + 32; ++k)
+                        P += oracle_e2m1_value((uint8_t)nibble_at(xr, k)) *
+                             oracle_e2m1_value((uint8_t)nibble_at(wr, k));
+                    q4 += oracle_e8m0_value(ex[b]) * oracle_e8m0_value(ew[b]) * P;
+                }
+            }
+            double lr = 0.0;
+            for (int j = 0; j < r; ++j)
+                lr += h[(size_t)m * r + j] * bf16_val(up[(size_t)n * r + j]);
+            double v = q4 + lr + (bias ? bf16_val(bias[n]) : 0.0);
+            if (gelu) v = gelu_tanh(v);
+            y[(size_t)i * N + n] = v;
+            if (y_q4) y_q4[(size_t)i * N + n] = q4;
+            if (y_lr) y_lr[(size_t)i * N + n] = lr;
+        }
+    }
+}
+
+int oracle_num_threads(void)
+{
+    int t = 1;
+#ifdef _OPENMP
+#pragma omp parallel
+    {
+#pragma omp single
+        t = omp_get_num_threads();
+    }
+#endif
+    return t;
+}

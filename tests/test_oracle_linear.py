@@ -1,0 +1,145 @@
+"""Pins of the oracle's output routine (4-bit product + low-rank branch + bias
+[+ GELU-tanh]): exact rational brute force on tiny shapes, reductions to
+integer / fp64 matmuls, and the invariants "low-rank factor zero => 4-bit
+product alone" and "residual zero => low-rank product alone"."""
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle as O
+from tests import _exact as E
+from w4a4_rank_corrected_quantize_amd.synth import f32_to_bf16_bits, bf16_bits_to_f32
+
+
+def _rand_codes(rng, rows, K):
+    q = rng.integers(-7, 8, (rows, K)).astype(np.int8)
+    return q, np.stack([O.pack_nibbles(r) for r in q])
+
+
+def _rand_mx_codes(rng, rows, K):
+    c = rng.integers(0, 16, (rows, K)).astype(np.uint8)
+    return c, ((c[:, 0::2] & 15) | (c[:, 1::2] << 4)).astype(np.uint8)
+
+
+def _bf16(rng, shape, std):
+    return f32_to_bf16_bits(rng.normal(0, std, shape).astype(np.float32))
+
+
+@pytest.mark.parametrize("K", [64, 128])
+@pytest.mark.parametrize("gelu", [False, True])
+def test_int4_linear_exact_bruteforce(K, gelu):
+    rng = np.random.default_rng(100 + K + gelu)
+    M, N, r = 3, 4, 32
+    qx, xq = _rand_codes(rng, M, K)
+    qw, wq = _rand_codes(rng, N, K)
+    sx = np.abs(rng.standard_normal((M, K // 64))).astype(np.float32)
+    sw = np.abs(rng.standard_normal((N, K // 64))).astype(np.float32) * 0.01
+    h = rng.standard_normal((M, r))
+    up = _bf16(rng, (N, r), 0.3)
+    bias = _bf16(rng, (N,), 0.1)
+    y, yq, ylr = O.linear(xq, sx, h, wq, sw, up, bias, O.INT4, gelu=gelu, parts=True)
+    upf = bf16_bits_to_f32(up)
+    bf = bf16_bits_to_f32(bias)
+    for m in range(M):
+        for n in range(N):
+            q4 = Fraction(0)
+            for g in range(K // 64):
+                P = sum(int(qx[m, k]) * int(qw[n, k]) for k in range(64 * g, 64 * g + 64))
+                q4 += Fraction(float(sx[m, g])) * Fraction(float(sw[n, g])) * P
+            lr = sum(Fraction(float(h[m, j])) * Fraction(float(upf[n, j])) for j in range(r))
+            tot = q4 + lr + Fraction(float(bf[n]))
+            assert abs(yq[m, n] - float(q4)) <= 1e-12 * max(1.0, abs(float(q4)))
+            assert abs(ylr[m, n] - float(lr)) <= 1e-12 * max(1.0, abs(float(lr)))
+            want = float(tot)
+            if gelu:
+                want = torch.nn.functional.gelu(torch.tensor(want, dtype=torch.float64),
+                                                approximate="tanh").item()
+            assert abs(y[m, n] - want) <= 1e-12 * max(1.0, abs(want))
+
+
+def test_mxfp4_linear_exact_bruteforce():
+    rng = np.random.default_rng(7)
+    M, N, K, r = 2, 3, 96, 32
+    cx, xq = _rand_mx_codes(rng, M, K)
+    cw, wq = _rand_mx_codes(rng, N, K)
+    ex = rng.integers(100, 140, (M, K // 32)).astype(np.uint8)
+    ew = rng.integers(100, 140, (N, K // 32)).astype(np.uint8)
+    h = np.zeros((M, r))
+    up = np.zeros((N, r), np.uint16)
+    y = O.linear(xq, ex, h, wq, ew, up, None, O.MXFP4)
+
+    def val(c):
+        m = E.E2M1[int(c) & 7]
+        return -m if c & 8 else m
+
+    for m in range(M):
+        for n in range(N):
+            tot = Fraction(0)
+            for b in range(K // 32):
+                P = sum(val(cx[m, k]) * val(cw[n, k]) for k in range(32 * b, 32 * b + 32))
+                tot += P * Fraction(2) ** (int(ex[m, b]) + int(ew[n, b]) - 254)
+            # each block term is exact in fp64; only the cross-block sum rounds
+            assert abs(y[m, n] - float(tot)) <= 4 * 2.0 ** -53 * float(sum(
+                abs(sum(val(cx[m, k]) * val(cw[n, k]) for k in range(32 * b, 32 * b + 32))) *
+                Fraction(2) ** (int(ex[m, b]) + int(ew[n, b]) - 254) for b in range(K // 32)))
+
+
+def test_int4_unit_scales_reduce_to_integer_matmul():
+    rng = np.random.default_rng(8)
+    M, N, K = 5, 7, 256
+    qx, xq = _rand_codes(rng, M, K)
+    qw, wq = _rand_codes(rng, N, K)
+    y = O.linear(xq, np.ones((M, K // 64), np.float32), np.zeros((M, 32)), wq,
+                 np.ones((N, K // 64), np.float32), np.zeros((N, 32), np.uint16), None, O.INT4)
+    ref = qx.astype(np.int64) @ qw.astype(np.int64).T
+    assert np.array_equal(y, ref.astype(np.float64))
+
+
+def test_lowrank_term_is_fp64_matmul_and_zero_up_gives_q4_alone():
+    rng = np.random.default_rng(9)
+    M, N, K, r = 6, 16, 128, 32
+    _, xq = _rand_codes(rng, M, K)
+    _, wq = _rand_codes(rng, N, K)
+    sx = np.abs(rng.standard_normal((M, 2))).astype(np.float32)
+    sw = np.abs(rng.standard_normal((N, 2))).astype(np.float32)
+    h = rng.standard_normal((M, r))
+    up = _bf16(rng, (N, r), 0.2)
+    y, yq, ylr = O.linear(xq, sx, h, wq, sw, up, None, O.INT4, parts=True)
+    np.testing.assert_allclose(ylr, h @ bf16_bits_to_f32(up).astype(np.float64).T, rtol=1e-13,
+                               atol=1e-13)
+    # zero up-projection => the output is the 4-bit product alone
+    y0 = O.linear(xq, sx, h, wq, sw, np.zeros_like(up), None, O.INT4)
+    assert np.array_equal(y0, yq)
+    # zero down-projection output (h = 0) => the same
+    y1 = O.linear(xq, sx, np.zeros_like(h), wq, sw, up, None, O.INT4)
+    assert np.array_equal(y1, yq)
+    # zero residual codes => the low-rank product alone (+ bias)
+    bias = _bf16(rng, (N,), 0.1)
+    y2 = O.linear(xq, sx, h, np.zeros_like(wq), sw, up, bias, O.INT4)
+    np.testing.assert_allclose(y2, ylr + bf16_bits_to_f32(bias)[None, :], rtol=1e-14, atol=1e-14)
+
+
+def test_row_subset_matches_full():
+    rng = np.random.default_rng(10)
+    M, N, K = 9, 16, 128
+    _, xq = _rand_codes(rng, M, K)
+    _, wq = _rand_codes(rng, N, K)
+    sx = np.abs(rng.standard_normal((M, 2))).astype(np.float32)
+    sw = np.abs(rng.standard_normal((N, 2))).astype(np.float32)
+    h = rng.standard_normal((M, 32))
+    up = _bf16(rng, (N, 32), 0.2)
+    full = O.linear(xq, sx, h, wq, sw, up, None, O.INT4)
+    rows = [8, 0, 3]
+    sub = O.linear(xq, sx, h, wq, sw, up, None, O.INT4, rows=rows)
+    assert np.array_equal(sub, full[rows])
+
+
+def test_gelu_tanh_reduces_to_library_routine():
+    ys = np.concatenate([np.linspace(-12, 12, 97), [0.0, 1e-30, -1e-30, 40.0, -40.0]])
+    ref = torch.nn.functional.gelu(torch.tensor(ys, dtype=torch.float64), approximate="tanh")
+    got = np.array([O.gelu_tanh(float(v)) for v in ys])
+    np.testing.assert_allclose(got, ref.numpy(), rtol=1e-14, atol=1e-300)
+    assert O.gelu_tanh(0.0) == 0.0
+    assert O.gelu_tanh(40.0) == 40.0 and O.gelu_tanh(-40.0) == 0.0

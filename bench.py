@@ -1,0 +1,183 @@
+#!/usr/bin/env python3
+"""Benchmark of the SVDQuant W4A4 linear on one MI355X.
+
+Workload (one "step" = the whole hot path of one layer over one batch):
+the FLUX-like MLP fc1 linear, 4608 tokens x 3072 -> 12288, rank 32, INT4
+group 64, GELU-tanh epilogue, bias:  svdq_quantize_act (smoothing + INT4
+quantization + rank-32 down projection) followed by svdq_w4a4_linear (4-bit
+product + low-rank up projection + bias + GELU + bf16 store).  Inputs are
+seeded synthetic tensors already resident in HBM; the weights are packed once
+on the host before timing.  Several input/output buffer sets (> 256 MB in all)
+rotate so the 256 MB last-level cache cannot hold a step's working set.
+
+value = 2 M N K / (time per step), in TOPS (tera integer ops of the 4-bit
+product per second).  The JSON line also carries the roofline of the dominant
+kernel (svdq_w4a4_linear vs the dense int8 matrix peak), the activation
+kernel's HBM rate, and the fp64 CPU oracle timed on a bounded row sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+PEAK_INT8_TOPS = 5000.0     # MI355X dense int8 matrix peak, 5.0 POP/s
+PEAK_FP4_TFLOPS = 10100.0   # MI355X dense MXFP4 matrix peak, 10.1 PFLOP/s
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, 8 TB/s
+
+
+def k1_bytes(M, K, r, prec):
+    scales = (M * K // 64) * 4 if prec == 0 else M * K // 32
+    return 2 * M * K + M * K // 2 + scales + 4 * M * r + 4 * K + 2 * r * K
+
+
+def k2_bytes(M, N, K, r, prec, bias=True):
+    scales = lambda rows: (rows * K // 64) * 4 if prec == 0 else rows * K // 32  # noqa: E731
+    return (M * K // 2 + scales(M) + 4 * M * r + N * K // 2 + scales(N) + 2 * N * r
+            + (2 * N if bias else 0) + 2 * M * N)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--prec", choices=["int4", "mxfp4"], default="int4")
+    ap.add_argument("--sets", type=int, default=3, help="rotating buffer sets")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle sample time")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build runs the layer on a single MI355X "
+              "and has no multi-GPU path (see the sharding note in DESIGN.md).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import w4a4_rank_corrected_quantize_amd as svdq
+    from w4a4_rank_corrected_quantize_amd import synth
+
+    torch.cuda.set_device(0)
+    svdq.check_device()
+    prec = svdq.INT4 if args.prec == "int4" else svdq.MXFP4
+    spec = synth.SPECS["fc1" if prec == svdq.INT4 else "mx_fc1"]
+    M, K, N, r = spec.M, spec.K, spec.N, svdq.RANK
+    print(f"[bench] generating {spec.name} {M}x{K}->{N} and packing on the host", file=sys.stderr,
+          flush=True)
+    L = synth.make_layer(spec)
+    t0 = time.time()
+    p = svdq.pack_weights(L["W"], L["act_absmax"], prec=prec)
+    pack_s = time.time() - t0
+    g = svdq.group_of(prec)
+    sdt = torch.float32 if prec == svdq.INT4 else torch.uint8
+
+    sets = []
+    for i in range(args.sets):
+        d = svdq.to_device(p)
+        sets.append(dict(
+            X=svdq.bf16_tensor(L["X"]), smooth=d["smooth"], down=d["down"], up=d["up"], wq=d["wq"],
+            wscale=d["wscale"], bias=svdq.bf16_tensor(L["bias"]),
+            xq=torch.empty((M, K // 2), dtype=torch.uint8, device="cuda"),
+            xscale=torch.empty((M, K // g), dtype=sdt, device="cuda"),
+            h=torch.empty((M, r), dtype=torch.float32, device="cuda"),
+            Y=torch.empty((M, N), dtype=torch.bfloat16, device="cuda")))
+    ws_mb = sum(t.numel() * t.element_size() for t in sets[0].values()) / 1e6
+
+    def step(b, ev=None):
+        if ev is not None:
+            ev[0].record()
+        svdq.quantize_act(b["X"], b["smooth"], b["down"], prec, xq=b["xq"], xscale=b["xscale"], h=b["h"])
+        if ev is not None:
+            ev[1].record()
+        svdq.w4a4_linear(b["xq"], b["xscale"], b["h"], b["wq"], b["wscale"], b["up"], b["bias"], prec,
+                         svdq.EPI_GELU_TANH, Y=b["Y"])
+        if ev is not None:
+            ev[2].record()
+
+    for i in range(args.warmup):
+        step(sets[i % len(sets)])
+    torch.cuda.synchronize()
+    print(f"[bench] warmup done ({args.warmup} steps); timing {args.steps} steps", file=sys.stderr,
+          flush=True)
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(args.steps):
+        step(sets[i % len(sets)], evs[i])
+    stop.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(stop)
+    ms_per_step = total_ms / args.steps
+    k1_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    k2_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    ops = 2.0 * M * N * K
+    value = ops / (ms_per_step * 1e-3) / 1e12
+    k2_tops = ops / (k2_ms * 1e-3) / 1e12
+    peak = PEAK_INT8_TOPS if prec == svdq.INT4 else PEAK_FP4_TFLOPS
+    k1_gbs = k1_bytes(M, K, r, prec) / (k1_ms * 1e-3) / 1e9
+    k2_gbs = k2_bytes(M, N, K, r, prec) / (k2_ms * 1e-3) / 1e9
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle import oracle as O
+        print("[bench] timing the CPU oracle on a row sample", file=sys.stderr, flush=True)
+        rows = 8
+        t0 = time.time()
+        xq, xs, h = O.quant_act(L["X"][:rows], p["smooth"], p["down"], prec)
+        O.linear(xq, xs, h, p["wq"], p["wscale"], p["up"], L["bias"], prec, gelu=True)
+        probe = max(time.time() - t0, 1e-3)
+        rows = int(min(M, max(8, rows * args.cpu_seconds / probe)))
+        t0 = time.time()
+        xq, xs, h = O.quant_act(L["X"][:rows], p["smooth"], p["down"], prec)
+        O.linear(xq, xs, h, p["wq"], p["wscale"], p["up"], L["bias"], prec, gelu=True)
+        t_cpu = time.time() - t0
+        cpu = {"value": round(2.0 * rows * N * K / t_cpu / 1e12, 6), "unit": "TOPS", "cores": O.num_threads(),
+               "kind": "oracle",
+               "sample": f"{rows} of {M} token rows of the same layer (activation step + linear), "
+                         f"{t_cpu:.1f} s"}
+
+    line = {
+        "metric": "W4A4 linear TOPS & % int8-MFMA peak at M=4608,K=3072,N=12288 (r=32)",
+        "value": round(value, 2),
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int4 codes on int8 matrix cores, int32 partials, fp32 rescale" if prec == svdq.INT4
+        else "mxfp4 (e2m1 x e2m1, e8m0 scales) on the scaled fp4 matrix cores, fp32 accumulation",
+        "data": "synthetic (seeded Student-t activations with outlier channels, N(0,0.02^2) weights)",
+        "config": {"workload": f"{spec.name}: {M} tokens x {K} -> {N}, rank {r}, "
+                               f"{'INT4 g64' if prec == svdq.INT4 else 'MXFP4 g32'}, bias, GELU-tanh; "
+                               "step = svdq_quantize_act + svdq_w4a4_linear",
+                   "M": M, "K": K, "N": N, "rank": r, "buffer_sets": len(sets),
+                   "working_set_MB_per_set": round(ws_mb, 1)},
+        "roofline": {"bound": "mfma", "kernel": "svdq_w4a4_linear",
+                     "achieved": round(k2_tops, 2), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(k2_tops / peak, 4), "traffic": None,
+                     "avg_ms": round(k2_ms, 5)},
+        "activation_kernel": {"kernel": "svdq_quantize_act", "bound": "hbm", "avg_ms": round(k1_ms, 5),
+                              "achieved_GBs": round(k1_gbs, 1), "peak_GBs": PEAK_HBM_GBS,
+                              "frac": round(k1_gbs / PEAK_HBM_GBS, 4),
+                              "algorithmic_bytes": k1_bytes(M, K, r, prec)},
+        "linear_kernel_GBs": round(k2_gbs, 1),
+        "host_pack_s": round(pack_s, 2),
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

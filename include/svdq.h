@@ -1,0 +1,188 @@
+/*
+ * svdq.h -- C ABI of libsvdq, an MI355X (gfx950) implementation of the
+ * SVDQuant W4A4 linear layer.
+ *
+ * The layer ("Bringing Nunchaku 4-bit Diffusion Inference to Diffusers",
+ * Hugging Face blog, section "Background: SVDQuant and Nunchaku"): a
+ * per-channel smoothing moves activation outliers into the weights, the
+ * hardest part of each smoothed weight matrix is kept in a small 16-bit
+ * low-rank branch, and the residual runs as a 4-bit-weight x 4-bit-activation
+ * product.  The low-rank down projection is fused with the activation
+ * quantization, and the up projection with the 4-bit product (same section,
+ * figure caption).  Section "Native loading in Diffusers" fixes rank 32 and a
+ * bfloat16 compute dtype.
+ *
+ * Notation.  X is bf16 [M][K] (M tokens), W is bf16 [N][K] (nn.Linear
+ * layout, out x in), y = X W^T + b.  r = rank = 32.  The 4-bit codes come in
+ * groups along K: INT4 (symmetric, 64 wide, fp32 scale) or MXFP4 (E2M1
+ * elements, one E8M0 scale per 32).
+ *
+ * Arithmetic (every step below is what the functions compute):
+ *   s_k      = fl32(1 / sqrt(max|X_k| / max_n|W_nk|)), 1 when either max is 0
+ *   What_kn  = W_nk / s_k ~ U S V^T (top r)
+ *   down     = bf16(s_k (U S)_kj)   stored [r][K]  (K contiguous)
+ *   up       = bf16(V_nj)           stored [N][r]  (r contiguous)
+ *   residual R_kn = (W_nk - sum_j down[j][k] up[n][j]) / s_k, quantized from
+ *            fl32(R) per (n, group)
+ *   xhat     = fl32(X_mk s_k), quantized per (m, group);  h = X down^T (fp32)
+ *   y        = sum_g sx_mg sw_ng (qx . qw)_g + h up^T + b   [GELU-tanh]  -> bf16
+ * INT4 group: a = max|v|, scale = fl32(a / 7) (rounded upward instead of to
+ * nearest below the normal fp32 range), code = round-half-even of the exact
+ * quotient v / scale (always within [-7, 7]).  MXFP4 block: X = floor(log2 a)
+ * - 2 clamped to [-127, 127], E8M0 = X + 127, element = v 2^-X rounded to the
+ * E2M1 grid (ties to the even index, saturating at 6, sign kept for zero).
+ * Codes are nibble-packed, element 2i in the low nibble of byte i; INT4 codes
+ * are two's complement, E2M1 codes are sign << 3 | index.
+ *
+ * Conventions.
+ *   - Ownership: the caller allocates and frees every buffer.  No call
+ *     allocates device memory or keeps a pointer after it returns.
+ *   - Device calls (svdq_quantize_act, svdq_w4a4_linear) take device
+ *     pointers and a hipStream_t (as void*, NULL = the null stream); they
+ *     validate everything first, enqueue kernels on `stream` and return
+ *     without synchronizing.  On any error nothing has been enqueued or
+ *     written.  The current HIP device must be a gfx950; otherwise
+ *     SVDQ_ERR_UNSUPPORTED_DEVICE is returned and nothing runs.
+ *   - Host calls (svdq_pack_weights, svdq_pack_residual) take host pointers,
+ *     run synchronously on the CPU and need no GPU.
+ *   - Device pointers must be 16-byte aligned (SVDQ_ERR_MISALIGNED).
+ *   - Inputs are expected finite; the device calls do not check the values
+ *     of X (non-finite X gives unspecified codes).
+ *   - Every function is thread-safe.  Calls that overlap on one stream are
+ *     ordered by the stream; calls on different streams that share output
+ *     buffers race, as with any kernel.
+ */
+#ifndef SVDQ_H
+#define SVDQ_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum svdq_status {
+    SVDQ_OK = 0,
+    SVDQ_ERR_INVALID_ARG = -1,        /* NULL pointer, bad enum value, negative size */
+    SVDQ_ERR_SHAPE = -2,              /* K not a multiple of the group, N not a multiple of 8, ... */
+    SVDQ_ERR_MISALIGNED = -3,         /* a device pointer not 16-byte aligned */
+    SVDQ_ERR_UNSUPPORTED = -4,        /* rank other than 32 */
+    SVDQ_ERR_UNSUPPORTED_DEVICE = -5, /* no HIP device, or the current device is not gfx950 */
+    SVDQ_ERR_NONFINITE = -6,          /* non-finite weight or calibration statistic (pack) */
+    SVDQ_ERR_HIP = -7                 /* a HIP runtime or launch failure */
+} svdq_status;
+
+typedef enum svdq_precision {
+    SVDQ_INT4 = 0,   /* symmetric INT4, 64-wide groups, fp32 scales  [rows][K/64] */
+    SVDQ_MXFP4 = 1   /* E2M1, 32-wide blocks, E8M0 scales (uint8)    [rows][K/32] */
+} svdq_precision;
+
+typedef enum svdq_epilogue {
+    SVDQ_EPI_NONE = 0,
+    SVDQ_EPI_GELU_TANH = 1  /* 0.5 y (1 + tanh(sqrt(2/pi) (y + 0.044715 y^3))) after the bias */
+} svdq_epilogue;
+
+#define SVDQ_RANK 32
+
+/* Human-readable text of a status code (static storage, never NULL). */
+const char *svdq_status_string(svdq_status status);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int svdq_version(void);
+
+/* SVDQ_OK when the current HIP device is a gfx950, else
+ * SVDQ_ERR_UNSUPPORTED_DEVICE.  Mirrors the capability check the pages
+ * describe ("Hardware support": the quantizer validates the GPU at load time
+ * and raises a clear error instead of producing incorrect outputs). */
+svdq_status svdq_check_device(void);
+
+/*
+ * svdq_pack_weights -- host-side packing of one linear layer
+ * ("Background: SVDQuant and Nunchaku": smoothing, low-rank branch,
+ * 4-bit residual; "Native loading in Diffusers": rank 32).
+ *
+ *   W          [N][K] bf16 bits (nn.Linear weight, out x in), host
+ *   act_absmax [K] fp32, per-channel max |X| from calibration (>= 0), host
+ *   N, K       N >= 1; K >= group and K % group == 0 (group 64 INT4, 32 MXFP4)
+ *   rank       must be 32
+ *   prec       SVDQ_INT4 or SVDQ_MXFP4
+ * Outputs (host, caller-allocated):
+ *   smooth     [K] fp32                       s_k
+ *   down       [rank][K] bf16 bits            bf16(s_k (U S)_kj)
+ *   up         [N][rank] bf16 bits            bf16(V_nj)
+ *   wq         [N][K/2] uint8                 packed residual codes
+ *   wscale     INT4: [N][K/64] fp32; MXFP4: [N][K/32] uint8 (E8M0)
+ * The top-r SVD is a randomized subspace iteration in fp64 with a
+ * Rayleigh-Ritz step (not bit-reproducible against other SVD codes; signs:
+ * the largest-|.| entry of each right singular vector is positive).  Columns
+ * beyond the rank of the smoothed weight come out as zero.  Errors:
+ * SVDQ_ERR_INVALID_ARG, SVDQ_ERR_SHAPE, SVDQ_ERR_UNSUPPORTED, SVDQ_ERR_NONFINITE
+ * (any non-finite W, or a negative / non-finite act_absmax).  Uses all host
+ * cores (std::thread); outputs are deterministic.
+ */
+svdq_status svdq_pack_weights(const uint16_t *W, const float *act_absmax, int N, int K, int rank,
+                              svdq_precision prec, float *smooth, uint16_t *down, uint16_t *up,
+                              uint8_t *wq, void *wscale);
+
+/*
+ * svdq_pack_residual -- the residual step of svdq_pack_weights alone, for
+ * caller-supplied smoothing and low-rank factors (same layouts as above):
+ * R_kn = (W_nk - sum_j down[j][k] up[n][j]) / smooth_k in fp64, j ascending,
+ * then fl32(R) quantized per (n, group).  Host, synchronous.  Errors as for
+ * svdq_pack_weights (smooth must be finite and non-zero).
+ */
+svdq_status svdq_pack_residual(const uint16_t *W, const float *smooth, const uint16_t *down,
+                               const uint16_t *up, int N, int K, int rank, svdq_precision prec,
+                               uint8_t *wq, void *wscale);
+
+/*
+ * svdq_quantize_act -- fused activation step: smoothing, per-group absmax,
+ * 4-bit quantization with nibble packing, and the rank-32 down projection
+ * h = X down^T in the same pass over X ("Background: SVDQuant and Nunchaku":
+ * the low-rank down projection is fused with the quantization kernel).
+ *
+ *   X        [M][K] bf16 bits, device          M >= 0 (M == 0: no-op)
+ *   smooth   [K] fp32, device
+ *   down     [rank][K] bf16 bits, device
+ *   xq       [M][K/2] uint8, device (out)
+ *   xscale   INT4: [M][K/64] fp32; MXFP4: [M][K/32] uint8, device (out)
+ *   h        [M][rank] fp32, device (out)      fp32 accumulation of bf16 products
+ *   stream   hipStream_t or NULL
+ * Codes and scales are bit-exact with the definition above.  One kernel
+ * launch.  Errors: SVDQ_ERR_INVALID_ARG, SVDQ_ERR_SHAPE (K % group),
+ * SVDQ_ERR_UNSUPPORTED (rank), SVDQ_ERR_MISALIGNED, SVDQ_ERR_UNSUPPORTED_DEVICE,
+ * SVDQ_ERR_HIP.
+ */
+svdq_status svdq_quantize_act(const uint16_t *X, int M, int K, const float *smooth,
+                              const uint16_t *down, int rank, svdq_precision prec, uint8_t *xq,
+                              void *xscale, float *h, void *stream);
+
+/*
+ * svdq_w4a4_linear -- the 4-bit product with the fused low-rank up
+ * projection, bias, optional GELU-tanh and bf16 store ("Background: SVDQuant
+ * and Nunchaku": the up projection is fused with the 4-bit compute kernel;
+ * "Introducing Nunchaku Lite": fused GELU/MLP paths).
+ *
+ *   xq, xscale, h   as written by svdq_quantize_act (device)
+ *   wq, wscale      as written by svdq_pack_weights (device copies)
+ *   up              [N][rank] bf16 bits (device)
+ *   bias            [N] bf16 bits (device) or NULL
+ *   M, N, K         M >= 0, N >= 0 (either 0: no-op), N % 8 == 0, K % group == 0
+ *   epi             SVDQ_EPI_NONE or SVDQ_EPI_GELU_TANH
+ *   Y               [M][N] bf16 bits (device, out), round-to-nearest-even
+ * INT4: per 64-group exact int32 partial products from the int8 matrix
+ * cores, rescaled by sx * sw in fp32; MXFP4: the scaled f8f6f4 matrix
+ * instruction applies both E8M0 scales.  The low-rank term uses h split
+ * into a bf16 high and low part.  One kernel launch.  Errors as for
+ * svdq_quantize_act.
+ */
+svdq_status svdq_w4a4_linear(const uint8_t *xq, const void *xscale, const float *h,
+                             const uint8_t *wq, const void *wscale, const uint16_t *up,
+                             const uint16_t *bias, int M, int N, int K, int rank,
+                             svdq_precision prec, svdq_epilogue epi, uint16_t *Y, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SVDQ_H */

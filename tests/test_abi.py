@@ -1,0 +1,78 @@
+"""The C ABI: every function declared in include/svdq.h is exported, status
+strings exist, and the device entry points validate their arguments (and the
+device) before anything runs.  No GPU compute here."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import w4a4_rank_corrected_quantize_amd as svdq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "svdq.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(svdq_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = _declared()
+    assert set(names) == set(svdq.EXPORTS)
+    L = ctypes.CDLL(svdq.LIB_PATH)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings_and_version():
+    for code in svdq.STATUS:
+        s = svdq.status_string(code)
+        assert isinstance(s, str) and s
+    assert svdq.status_string(12345) == "unknown status"
+    assert svdq.version() >= 100
+
+
+def _host(nbytes, offset=0):
+    buf = np.zeros(nbytes + 64, np.uint8)
+    base = (-buf.ctypes.data) % 16
+    return buf, ctypes.c_void_p(buf.ctypes.data + base + offset)
+
+
+def test_device_call_validation_order():
+    """Shape / enum / rank / NULL / alignment errors come before the device check."""
+    L = svdq.lib()
+    _, p = _host(1 << 16)
+    _, q = _host(1 << 16, offset=4)
+    M, K = 16, 128
+    assert L.svdq_quantize_act(p, M, 96, p, p, 32, svdq.INT4, p, p, p, None) == -2
+    assert L.svdq_quantize_act(p, M, K, p, p, 16, svdq.INT4, p, p, p, None) == -4
+    assert L.svdq_quantize_act(p, M, K, p, p, 32, 7, p, p, p, None) == -1
+    assert L.svdq_quantize_act(None, M, K, p, p, 32, svdq.INT4, p, p, p, None) == -1
+    assert L.svdq_quantize_act(p, -1, K, p, p, 32, svdq.INT4, p, p, p, None) == -1
+    assert L.svdq_quantize_act(q, M, K, p, p, 32, svdq.INT4, p, p, p, None) == -3
+    assert L.svdq_w4a4_linear(p, p, p, p, p, p, None, M, 12, K, 32, svdq.INT4, 0, p, None) == -2
+    assert L.svdq_w4a4_linear(p, p, p, p, p, p, None, M, 16, K, 32, svdq.INT4, 5, p, None) == -1
+    assert L.svdq_w4a4_linear(p, p, p, p, p, p, q, M, 16, K, 32, svdq.INT4, 0, p, None) == -3
+    assert L.svdq_w4a4_linear(p, p, p, p, p, p, None, M, 16, 96, 32, svdq.MXFP4, 0, None, None) == -1
+
+
+def _has_gpu():
+    try:
+        import torch
+        return torch.cuda.is_available()
+    except Exception:
+        return False
+
+
+@pytest.mark.skipif(_has_gpu(), reason="checks the no-GPU path")
+def test_no_gpu_means_unsupported_device():
+    L = svdq.lib()
+    _, p = _host(1 << 16)
+    assert L.svdq_check_device() == -5
+    assert L.svdq_quantize_act(p, 16, 128, p, p, 32, svdq.INT4, p, p, p, None) == -5
+    assert L.svdq_w4a4_linear(p, p, p, p, p, p, None, 16, 16, 128, 32, svdq.INT4, 0, p, None) == -5
+    with pytest.raises(svdq.SvdqError):
+        svdq.check_device()

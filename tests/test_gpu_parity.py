@@ -1,0 +1,264 @@
+"""HIP path vs the fp64 oracle on the GPU, through the C ABI.
+
+Bar: codes and scales bit-exact; h within the blocked fp32-summation bound;
+the bf16 output within |y - y_ref| <= 8e-3 |y_ref| + 1e-3 rms(y_ref), where
+y_ref is the oracle's fp64 output on the same codes (those are bit-exact, so
+both sides take every integer decision in the same precision).
+"""
+import os
+import sys
+
+import numpy as np
+import pytest
+
+import w4a4_rank_corrected_quantize_amd as svdq
+from oracle import oracle as O
+from w4a4_rank_corrected_quantize_amd import synth
+from w4a4_rank_corrected_quantize_amd.synth import bf16_bits_to_f32
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+REL, ABS_RMS = 8e-3, 1e-3
+
+
+def _say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    svdq.check_device()
+
+
+def _t(a):
+    """numpy -> device tensor (uint16 arrays become bf16)."""
+    if a is None:
+        return None
+    if a.dtype == np.uint16:
+        return svdq.bf16_tensor(a)
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def _np(t):
+    if t.dtype == torch.bfloat16:
+        return svdq.bf16_bits(t)
+    return t.cpu().numpy()
+
+
+def _h_bound(X, down):
+    """(K/16 + 64) 2^-24 sum_k |X_mk down_jk|: fp32 accumulation of exact bf16
+    products in chunks of at most 16 partial sums plus the wave reduction."""
+    K = X.shape[1]
+    a = np.abs(bf16_bits_to_f32(X).astype(np.float64)) @ np.abs(bf16_bits_to_f32(down).astype(np.float64)).T
+    return (K / 16 + 64) * 2.0 ** -24 * a + 1e-30
+
+
+def _quant_act_check(X, s, down, prec):
+    xq, xs, h = svdq.quantize_act(_t(X), _t(s), _t(down), prec)
+    torch.cuda.synchronize()
+    oq, os_, oh = O.quant_act(X, s, down, prec)
+    gq, gs, gh = _np(xq), _np(xs), _np(h)
+    assert np.array_equal(gq, oq), f"codes differ at {np.argwhere(gq != oq)[:5]}"
+    assert np.array_equal(gs.view(np.uint8), os_.view(np.uint8)), \
+        f"scales differ at {np.argwhere(gs.view(np.uint8).reshape(gs.shape[0], -1) != os_.view(np.uint8).reshape(os_.shape[0], -1))[:5]}"
+    assert np.all(np.abs(gh.astype(np.float64) - oh) <= _h_bound(X, down))
+    return xq, xs, h, oh
+
+
+def _y_check(Y, y_ref, what=""):
+    y = bf16_bits_to_f32(_np(Y)).astype(np.float64)
+    rms = np.sqrt(np.mean(y_ref ** 2)) if y_ref.size else 0.0
+    bad = np.abs(y - y_ref) > REL * np.abs(y_ref) + ABS_RMS * rms
+    assert not bad.any(), (f"{what}: {bad.sum()} of {bad.size} outside tolerance; worst "
+                           f"{np.max(np.abs(y - y_ref) / (REL * np.abs(y_ref) + ABS_RMS * rms)):.3f}")
+
+
+def _layer(spec_name, M, K, N, prec, bias=True):
+    spec = synth.SPECS[spec_name]
+    if spec.x_dist == "external":
+        spec = synth.SPECS["qkv"]
+    L = synth.make_layer(spec, M=M, K=K, N=N)
+    if not bias:
+        L["bias"] = None
+    p = svdq.pack_weights(L["W"], L["act_absmax"], prec=prec)
+    return L, p
+
+
+# ------------------------------------------------------------ activation step
+
+PRECS = [svdq.INT4, svdq.MXFP4]
+
+
+@pytest.mark.parametrize("prec", PRECS)
+@pytest.mark.parametrize("M,K", [(128, 256), (1, 64), (15, 128), (17, 320), (100, 3072), (33, 12288)])
+def test_quantize_act_synthetic(prec, M, K):
+    if prec == svdq.INT4 and K % 64:
+        pytest.skip("INT4 needs K % 64 == 0")
+    _say(f"quantize_act prec={prec} M={M} K={K}")
+    L, p = _layer("qkv", M, K, 64, prec)
+    _quant_act_check(L["X"], p["smooth"], p["down"], prec)
+
+
+@pytest.mark.parametrize("prec", PRECS)
+def test_quantize_act_mx_half_step(prec):
+    """K = 32 * odd: the MXFP4 kernel ends on half a 64-channel step."""
+    if prec == svdq.INT4:
+        pytest.skip("INT4 needs K % 64 == 0")
+    _say("quantize_act mx K=96/160")
+    for M, K in [(20, 96), (3, 160)]:
+        L, p = _layer("qkv", M, K, 16, prec)
+        _quant_act_check(L["X"], p["smooth"], p["down"], prec)
+
+
+@pytest.mark.parametrize("prec", PRECS)
+def test_quantize_act_near_ties(prec):
+    """X = +-1 and s = the target values: xhat = s exactly, so every element can
+    sit on or next to a rounding boundary of its group."""
+    _say(f"quantize_act near ties prec={prec}")
+    rng = np.random.default_rng(77 + prec)
+    M, K = 64, 1024
+    g = 64 if prec == svdq.INT4 else 32
+    t = np.zeros(K, np.float32)
+    for b in range(K // g):
+        a = np.float32(rng.uniform(0.5, 2.0) * 2.0 ** rng.integers(-20, 20))
+        if prec == svdq.INT4:
+            sc = np.float32(np.float64(a) / 7)
+            v = ((rng.integers(0, 7, g) + 0.5) * np.float64(sc)).astype(np.float32)
+        else:
+            mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0])
+            v = (mids[rng.integers(0, 8, g)] * 2.0 ** (np.floor(np.log2(a)) - 2)).astype(np.float32)
+        nudge = rng.integers(-1, 2, g)
+        v = np.where(nudge < 0, np.nextafter(v, np.float32(0)), np.where(nudge > 0, np.nextafter(v, np.float32(np.inf)), v))
+        v[0] = a
+        t[b * g:(b + 1) * g] = v
+    X = np.where(rng.random((M, K)) < 0.5, 0x3F80, 0xBF80).astype(np.uint16)
+    down = synth.f64_to_bf16_bits(rng.normal(0, 0.1, (32, K)))
+    _quant_act_check(X, t, down, prec)
+
+
+@pytest.mark.parametrize("prec", PRECS)
+def test_quantize_act_subnormal_and_zero_groups(prec):
+    _say(f"quantize_act subnormal prec={prec}")
+    rng = np.random.default_rng(91)
+    M, K = 32, 512
+    t = (rng.standard_normal(K) * 2.0 ** rng.integers(-149, -110, K).astype(np.float64)).astype(np.float32)
+    t[:64] = 0.0                                   # an all-zero group
+    t[64:128] = np.float32(2.0 ** -149) * rng.integers(-12, 13, 64).astype(np.float32)
+    X = np.where(rng.random((M, K)) < 0.5, 0x3F80, 0xBF80).astype(np.uint16)
+    X[5] = 0                                       # an all-zero row
+    down = synth.f64_to_bf16_bits(rng.normal(0, 0.1, (32, K)))
+    _quant_act_check(X, t, down, prec)
+
+
+def test_quantize_act_deterministic_and_empty():
+    _say("quantize_act determinism")
+    L, p = _layer("qkv", 200, 1024, 16, svdq.INT4)
+    X, s, d = _t(L["X"]), _t(p["smooth"]), _t(p["down"])
+    a = [svdq.quantize_act(X, s, d) for _ in range(3)]
+    torch.cuda.synchronize()
+    for r in a[1:]:
+        for u, v in zip(a[0], r):
+            assert torch.equal(u, v)
+    e = svdq.quantize_act(X[:0], s, d)
+    assert e[0].shape == (0, 512)
+
+
+# ------------------------------------------------------------------- linear
+
+@pytest.mark.parametrize("prec", PRECS)
+@pytest.mark.parametrize("M,K,N,bias,gelu", [
+    (128, 256, 256, False, False),       # the small configuration
+    (1, 64, 8, True, False),
+    (37, 192, 24, True, True),
+    (130, 320, 136, True, False),
+    (257, 512, 264, False, True),
+    (300, 1024, 512, True, True),
+])
+def test_linear_synthetic(prec, M, K, N, bias, gelu):
+    if prec == svdq.INT4 and K % 64:
+        pytest.skip("INT4 needs K % 64 == 0")
+    _say(f"linear prec={prec} M={M} K={K} N={N} bias={bias} gelu={gelu}")
+    spec = "small" if (M, K, N) == (128, 256, 256) else "qkv"
+    L, p = _layer(spec, M, K, N, prec, bias=bias)
+    xq, xs, h, oh = _quant_act_check(L["X"], p["smooth"], p["down"], prec)
+    Y = svdq.w4a4_linear(xq, xs, h, _t(p["wq"]), _t(p["wscale"]), _t(p["up"]), _t(L["bias"]), prec,
+                         svdq.EPI_GELU_TANH if gelu else svdq.EPI_NONE)
+    torch.cuda.synchronize()
+    y_ref = O.linear(_np(xq), _np(xs), oh, p["wq"], p["wscale"], p["up"], L["bias"], prec, gelu=gelu)
+    _y_check(Y, y_ref, f"M={M} K={K} N={N}")
+
+
+@pytest.mark.parametrize("prec", PRECS)
+def test_linear_invariants(prec):
+    """up = 0 => the 4-bit product alone; residual codes 0 => the low-rank
+    product alone (+ bias)."""
+    _say(f"linear invariants prec={prec}")
+    M, K, N = 96, 512, 128
+    L, p = _layer("qkv", M, K, N, prec)
+    xq, xs, h, oh = _quant_act_check(L["X"], p["smooth"], p["down"], prec)
+    y_ref, yq, ylr = O.linear(_np(xq), _np(xs), oh, p["wq"], p["wscale"], p["up"], L["bias"], prec,
+                              parts=True)
+    zero_up = np.zeros_like(p["up"])
+    Y = svdq.w4a4_linear(xq, xs, h, _t(p["wq"]), _t(p["wscale"]), _t(zero_up), None, prec)
+    _y_check(Y, yq, "up = 0")
+    Y2 = svdq.w4a4_linear(xq, xs, h, _t(np.zeros_like(p["wq"])), _t(p["wscale"]), _t(p["up"]),
+                          _t(L["bias"]), prec)
+    _y_check(Y2, ylr + bf16_bits_to_f32(L["bias"]).astype(np.float64)[None, :], "residual = 0")
+    torch.cuda.synchronize()
+
+
+def test_linear_deterministic_and_empty():
+    _say("linear determinism")
+    L, p = _layer("qkv", 160, 512, 256, svdq.INT4)
+    xq, xs, h = svdq.quantize_act(_t(L["X"]), _t(p["smooth"]), _t(p["down"]))
+    args = (xq, xs, h, _t(p["wq"]), _t(p["wscale"]), _t(p["up"]), _t(L["bias"]))
+    Ys = [svdq.w4a4_linear(*args, svdq.INT4, svdq.EPI_GELU_TANH) for _ in range(3)]
+    torch.cuda.synchronize()
+    assert all(torch.equal(Ys[0], y) for y in Ys[1:])
+    e = svdq.w4a4_linear(xq[:0], xs[:0], h[:0], *args[3:], svdq.INT4)
+    assert e.shape == (0, 256)
+
+
+# ------------------------------------------------- full sizes, bench launches
+
+def _rows(M, n, seed=7):
+    rng = np.random.default_rng(seed)
+    return np.unique(np.concatenate([[0, M - 1], rng.choice(M, n, replace=False)])).astype(np.int32)
+
+
+@pytest.mark.parametrize("prec", PRECS)
+def test_full_size_dit_block(prec):
+    """QKV and the fc1 -> fc2 MLP pair at 4608 tokens, hidden 3072: codes,
+    scales and h of every row bit-exact / bounded; outputs on sampled rows."""
+    _say(f"full-size DiT block prec={prec}")
+    names = ("qkv", "fc1", "fc2") if prec == svdq.INT4 else ("mx_qkv", "mx_fc1", "mx_fc2")
+    q = synth.make_layer(synth.SPECS[names[0]])
+    pq = svdq.pack_weights(q["W"], q["act_absmax"], prec=prec)
+    xq, xs, h, oh = _quant_act_check(q["X"], pq["smooth"], pq["down"], prec)
+    rows = _rows(q["M"], 48)
+    Y = svdq.w4a4_linear(xq, xs, h, _t(pq["wq"]), _t(pq["wscale"]), _t(pq["up"]), _t(q["bias"]), prec)
+    torch.cuda.synchronize()
+    y_ref = O.linear(_np(xq), _np(xs), oh, pq["wq"], pq["wscale"], pq["up"], q["bias"], prec, rows=rows)
+    _y_check(Y[torch.from_numpy(rows).long().cuda()], y_ref, names[0])
+    _say("  fc1")
+    f1 = synth.make_layer(synth.SPECS[names[1]])
+    p1 = svdq.pack_weights(f1["W"], f1["act_absmax"], prec=prec)
+    xq, xs, h, oh = _quant_act_check(f1["X"], p1["smooth"], p1["down"], prec)
+    Y1 = svdq.w4a4_linear(xq, xs, h, _t(p1["wq"]), _t(p1["wscale"]), _t(p1["up"]), _t(f1["bias"]), prec,
+                          svdq.EPI_GELU_TANH)
+    torch.cuda.synchronize()
+    y_ref = O.linear(_np(xq), _np(xs), oh, p1["wq"], p1["wscale"], p1["up"], f1["bias"], prec, gelu=True,
+                     rows=rows)
+    _y_check(Y1[torch.from_numpy(rows).long().cuda()], y_ref, names[1])
+    _say("  fc2 (fc1 output re-quantized)")
+    Y1b = _np(Y1)
+    f2 = synth.make_layer(synth.SPECS[names[2]], X_bits=Y1b)
+    p2 = svdq.pack_weights(f2["W"], f2["act_absmax"], prec=prec)
+    xq, xs, h, oh = _quant_act_check(Y1b, p2["smooth"], p2["down"], prec)
+    Y2 = svdq.w4a4_linear(xq, xs, h, _t(p2["wq"]), _t(p2["wscale"]), _t(p2["up"]), _t(f2["bias"]), prec)
+    torch.cuda.synchronize()
+    y_ref = O.linear(_np(xq), _np(xs), oh, p2["wq"], p2["wscale"], p2["up"], f2["bias"], prec, rows=rows)
+    _y_check(Y2[torch.from_numpy(rows).long().cuda()], y_ref, names[2])

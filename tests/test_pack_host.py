@@ -1,0 +1,154 @@
+"""libsvdq's host packing step against the oracle (CPU only).
+
+Bit-exact: smoothing factors, and residual codes + scales given the
+library's own low-rank factors.  The factors themselves are held to
+Eckart-Young against numpy's SVD.
+"""
+import numpy as np
+import pytest
+
+import w4a4_rank_corrected_quantize_amd as svdq
+from oracle import oracle as O
+from w4a4_rank_corrected_quantize_amd import synth
+from w4a4_rank_corrected_quantize_amd.synth import f32_to_bf16_bits, bf16_bits_to_f32
+
+PRECS = [svdq.INT4, svdq.MXFP4]
+
+
+def _layer(M, K, N, seed, t_dist=True, n_out=8, out_scale=50.0):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_t(4, (M, K)) if t_dist else rng.standard_normal((M, K))
+    ch = rng.choice(K, n_out, replace=False)
+    x[:, ch] *= out_scale
+    X = synth.f64_to_bf16_bits(x)
+    W = synth.f64_to_bf16_bits(rng.normal(0, 0.02, (N, K)))
+    return X, W, synth.calibration_absmax(X)
+
+
+def _energy(W, s, down, up):
+    What = (bf16_bits_to_f32(W).astype(np.float64) / s.astype(np.float64)[None, :]).T
+    lr = (bf16_bits_to_f32(down).astype(np.float64).T / s.astype(np.float64)[:, None]) @ \
+        bf16_bits_to_f32(up).astype(np.float64).T
+    return np.sum((What - lr) ** 2), What
+
+
+@pytest.mark.parametrize("prec", PRECS)
+@pytest.mark.parametrize("shape", [(64, 256, 96), (48, 192, 40), (32, 128, 256)])
+def test_pack_weights_matches_oracle(prec, shape):
+    M, K, N = shape
+    X, W, absmax = _layer(M, K, N, seed=K + N + prec)
+    p = svdq.pack_weights(W, absmax, prec=prec)
+    # smoothing: bit-exact
+    assert np.array_equal(p["smooth"].view(np.uint32), O.smooth(W, absmax).view(np.uint32))
+    # residual codes/scales: bit-exact given the library's factors
+    wq, ws = O.residual(W, p["smooth"], p["down"], p["up"], prec)
+    assert np.array_equal(p["wq"], wq)
+    assert np.array_equal(p["wscale"].view(np.uint8), ws.view(np.uint8))
+    # low rank: Eckart-Young against numpy's SVD (both rounded to bf16 the same way)
+    e_lib, What = _energy(W, p["smooth"], p["down"], p["up"])
+    d_np, u_np, S, _, _ = O.lowrank(W, p["smooth"], 32)
+    e_np, _ = _energy(W, p["smooth"], d_np, u_np)
+    e_opt = np.sum(S[32:] ** 2)
+    assert e_lib >= e_opt * (1 - 1e-9)
+    assert e_lib <= e_np * (1 + 1e-3) + 1e-12 * np.sum(S ** 2)
+
+
+def test_pack_weights_rank_deficient_and_narrow():
+    """N < rank: the factors beyond the matrix rank are zero and the residual
+    is at bf16-rounding level."""
+    rng = np.random.default_rng(5)
+    N, K = 16, 128
+    W = f32_to_bf16_bits(rng.normal(0, 0.02, (N, K)).astype(np.float32))
+    absmax = np.ones(K, np.float32)
+    p = svdq.pack_weights(W, absmax, prec=svdq.INT4)
+    assert not p["up"][:, N:].any() and not p["down"][N:, :].any()
+    wq, ws = O.residual(W, p["smooth"], p["down"], p["up"], svdq.INT4)
+    assert np.array_equal(p["wq"], wq) and np.array_equal(p["wscale"], ws)
+    e_lib, What = _energy(W, p["smooth"], p["down"], p["up"])
+    assert e_lib <= (2.0 ** -7) ** 2 * np.sum(What ** 2)
+
+
+def test_pack_weights_zero_weight():
+    N, K = 32, 64
+    W = np.zeros((N, K), np.uint16)
+    p = svdq.pack_weights(W, np.ones(K, np.float32))
+    assert np.all(p["smooth"] == 1.0)
+    assert not p["down"].any() and not p["up"].any() and not p["wq"].any() and not p["wscale"].any()
+
+
+@pytest.mark.parametrize("prec", PRECS)
+def test_pack_residual_near_ties(prec):
+    """R_kn = W_nk / s_k with W = +-1 and s_k = fl32(1 / t_k): every value lands
+    within an ulp or two of a rounding boundary of its group, which is where a
+    shortcut quantizer goes wrong."""
+    rng = np.random.default_rng(21 + prec)
+    N, K = 64, 512
+    g = 64 if prec == svdq.INT4 else 32
+    t = np.zeros(K, np.float64)
+    for b in range(K // g):
+        a = rng.uniform(0.5, 2.0) * 2.0 ** rng.integers(-12, 12)
+        if prec == svdq.INT4:
+            scale = np.float64(np.float32(a / 7))
+            k = rng.integers(0, 7, g)
+            vals = (k + 0.5) * scale
+        else:
+            X = np.floor(np.log2(a)) - 2
+            mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0])
+            vals = mids[rng.integers(0, mids.size, g)] * 2.0 ** X
+        vals[0] = a
+        t[b * g:(b + 1) * g] = vals
+    with np.errstate(over="ignore"):
+        s = (1.0 / t).astype(np.float32)
+    W = np.where(rng.random((N, K)) < 0.5, 0x3F80, 0xBF80).astype(np.uint16)   # +-1.0
+    down = np.zeros((32, K), np.uint16)
+    up = np.zeros((N, 32), np.uint16)
+    wq, ws = svdq.pack_residual(W, s, down, up, prec)
+    oq, os_ = O.residual(W, s, down, up, prec)
+    assert np.array_equal(wq, oq)
+    assert np.array_equal(ws.view(np.uint8), os_.view(np.uint8))
+
+
+@pytest.mark.parametrize("prec", PRECS)
+def test_pack_residual_subnormal_groups(prec):
+    rng = np.random.default_rng(31)
+    N, K = 8, 256
+    t = rng.standard_normal(K) * 2.0 ** rng.integers(-149, -120, K).astype(np.float64)
+    t[t == 0] = 2.0 ** -149
+    with np.errstate(over="ignore"):
+        s = (1.0 / t).astype(np.float32)
+    s[~np.isfinite(s)] = np.float32(3.0e38)
+    W = np.where(rng.random((N, K)) < 0.5, 0x3F80, 0xBF80).astype(np.uint16)
+    z_d = np.zeros((32, K), np.uint16)
+    z_u = np.zeros((N, 32), np.uint16)
+    wq, ws = svdq.pack_residual(W, s, z_d, z_u, prec)
+    oq, os_ = O.residual(W, s, z_d, z_u, prec)
+    assert np.array_equal(wq, oq)
+    assert np.array_equal(ws.view(np.uint8), os_.view(np.uint8))
+
+
+def test_pack_errors():
+    W = np.zeros((16, 128), np.uint16)
+    a = np.ones(128, np.float32)
+    with pytest.raises(svdq.SvdqError) as e:
+        svdq.pack_weights(W, a, rank=16)
+    assert e.value.status == -4
+    with pytest.raises(svdq.SvdqError) as e:
+        svdq.pack_weights(np.zeros((16, 96), np.uint16), np.ones(96, np.float32), prec=svdq.INT4)
+    assert e.value.status == -2
+    Wn = W.copy()
+    Wn[3, 5] = 0x7FC0                        # NaN
+    with pytest.raises(svdq.SvdqError) as e:
+        svdq.pack_weights(Wn, a)
+    assert e.value.status == -6
+    bad = a.copy()
+    bad[7] = -1.0
+    with pytest.raises(svdq.SvdqError) as e:
+        svdq.pack_weights(W, bad)
+    assert e.value.status == -6
+    with pytest.raises(svdq.SvdqError) as e:
+        svdq.pack_residual(W, np.zeros(128, np.float32), np.zeros((32, 128), np.uint16),
+                           np.zeros((16, 32), np.uint16))
+    assert e.value.status == -6
+    # MXFP4 accepts K % 32 == 0
+    p = svdq.pack_weights(np.zeros((16, 96), np.uint16), np.ones(96, np.float32), prec=svdq.MXFP4)
+    assert p["wscale"].shape == (16, 3)

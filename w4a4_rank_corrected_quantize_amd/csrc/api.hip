@@ -1,0 +1,112 @@
+// api.hip -- the C-ABI entry points of libsvdq that run on the GPU, plus the
+// status helpers.  Each device call validates its arguments and the current
+// device before enqueuing anything ("Bringing Nunchaku 4-bit Diffusion
+// Inference to Diffusers", section "Hardware support": the GPU is validated
+// and a clear error is raised instead of producing incorrect outputs).
+#include <atomic>
+#include <cstring>
+
+#include "svdq.h"
+#include "svdq_internal.h"
+
+namespace svdq {
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_device_state[kMaxDevices];   // 0 unknown, 1 gfx950, 2 other
+
+svdq_status current_device_ok()
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+        (void)hipGetLastError();
+        return SVDQ_ERR_UNSUPPORTED_DEVICE;
+    }
+    if (dev >= kMaxDevices) return SVDQ_ERR_UNSUPPORTED_DEVICE;
+    int st = g_device_state[dev].load(std::memory_order_acquire);
+    if (st == 0) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+            (void)hipGetLastError();
+            return SVDQ_ERR_UNSUPPORTED_DEVICE;
+        }
+        st = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+        g_device_state[dev].store(st, std::memory_order_release);
+    }
+    return st == 1 ? SVDQ_OK : SVDQ_ERR_UNSUPPORTED_DEVICE;
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+svdq_status check_common(int M, int K, int rank, svdq_precision prec)
+{
+    if (prec != SVDQ_INT4 && prec != SVDQ_MXFP4) return SVDQ_ERR_INVALID_ARG;
+    if (M < 0 || K < 0) return SVDQ_ERR_INVALID_ARG;
+    if (rank != SVDQ_RANK) return SVDQ_ERR_UNSUPPORTED;
+    const int g = group_size(prec);
+    if (K < g || K % g != 0) return SVDQ_ERR_SHAPE;
+    return SVDQ_OK;
+}
+
+}  // namespace
+}  // namespace svdq
+
+using namespace svdq;
+
+extern "C" const char *svdq_status_string(svdq_status status)
+{
+    switch (status) {
+    case SVDQ_OK: return "ok";
+    case SVDQ_ERR_INVALID_ARG: return "invalid argument (NULL pointer, bad enum or negative size)";
+    case SVDQ_ERR_SHAPE: return "unsupported shape (K must be a multiple of the group size, N of 8)";
+    case SVDQ_ERR_MISALIGNED: return "device pointer not 16-byte aligned";
+    case SVDQ_ERR_UNSUPPORTED: return "unsupported configuration (rank must be 32)";
+    case SVDQ_ERR_UNSUPPORTED_DEVICE: return "no HIP device, or the current device is not a gfx950 (MI355X)";
+    case SVDQ_ERR_NONFINITE: return "non-finite weight, calibration statistic or smoothing factor";
+    case SVDQ_ERR_HIP: return "HIP runtime or kernel launch failure";
+    }
+    return "unknown status";
+}
+
+extern "C" int svdq_version(void) { return 100; }
+
+extern "C" svdq_status svdq_check_device(void) { return current_device_ok(); }
+
+extern "C" svdq_status svdq_quantize_act(const uint16_t *X, int M, int K, const float *smooth,
+                                         const uint16_t *down, int rank, svdq_precision prec, uint8_t *xq,
+                                         void *xscale, float *h, void *stream)
+{
+    svdq_status st = check_common(M, K, rank, prec);
+    if (st != SVDQ_OK) return st;
+    if (!X || !smooth || !down || !xq || !xscale || !h) return SVDQ_ERR_INVALID_ARG;
+    if (!aligned16(X) || !aligned16(smooth) || !aligned16(down) || !aligned16(xq) || !aligned16(xscale) ||
+        !aligned16(h))
+        return SVDQ_ERR_MISALIGNED;
+    st = current_device_ok();
+    if (st != SVDQ_OK) return st;
+    if (M == 0) return SVDQ_OK;
+    hipError_t e = launch_quant_act(X, M, K, smooth, down, prec, xq, xscale, h, (hipStream_t)stream);
+    return e == hipSuccess ? SVDQ_OK : SVDQ_ERR_HIP;
+}
+
+extern "C" svdq_status svdq_w4a4_linear(const uint8_t *xq, const void *xscale, const float *h,
+                                        const uint8_t *wq, const void *wscale, const uint16_t *up,
+                                        const uint16_t *bias, int M, int N, int K, int rank,
+                                        svdq_precision prec, svdq_epilogue epi, uint16_t *Y, void *stream)
+{
+    svdq_status st = check_common(M, K, rank, prec);
+    if (st != SVDQ_OK) return st;
+    if (N < 0) return SVDQ_ERR_INVALID_ARG;
+    if (epi != SVDQ_EPI_NONE && epi != SVDQ_EPI_GELU_TANH) return SVDQ_ERR_INVALID_ARG;
+    if (N % 8 != 0) return SVDQ_ERR_SHAPE;
+    if (!xq || !xscale || !h || !wq || !wscale || !up || !Y) return SVDQ_ERR_INVALID_ARG;
+    if (!aligned16(xq) || !aligned16(xscale) || !aligned16(h) || !aligned16(wq) || !aligned16(wscale) ||
+        !aligned16(up) || !aligned16(Y) || (bias && !aligned16(bias)))
+        return SVDQ_ERR_MISALIGNED;
+    st = current_device_ok();
+    if (st != SVDQ_OK) return st;
+    if (M == 0 || N == 0) return SVDQ_OK;
+    hipError_t e = launch_w4a4_linear(xq, xscale, h, wq, wscale, up, bias, M, N, K, prec, epi, Y,
+                                      (hipStream_t)stream);
+    return e == hipSuccess ? SVDQ_OK : SVDQ_ERR_HIP;
+}

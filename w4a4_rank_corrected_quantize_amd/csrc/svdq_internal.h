@@ -1,0 +1,24 @@
+// svdq_internal.h -- declarations shared between the C-ABI layer and the
+// kernel translation units of libsvdq (not part of the public ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "svdq.h"
+
+namespace svdq {
+
+int group_size(svdq_precision prec);
+
+// Kernel launchers; arguments are already validated.  They return the HIP
+// status of the launch.
+hipError_t launch_quant_act(const uint16_t *X, int M, int K, const float *smooth, const uint16_t *down,
+                            svdq_precision prec, uint8_t *xq, void *xscale, float *h, hipStream_t stream);
+
+hipError_t launch_w4a4_linear(const uint8_t *xq, const void *xscale, const float *h, const uint8_t *wq,
+                              const void *wscale, const uint16_t *up, const uint16_t *bias, int M, int N,
+                              int K, svdq_precision prec, svdq_epilogue epi, uint16_t *Y,
+                              hipStream_t stream);
+
+}  // namespace svdq

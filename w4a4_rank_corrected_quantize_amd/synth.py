@@ -88,7 +88,7 @@ SPECS = {
     "mx_qkv": LayerSpec("mx_qkv", 4, 4608, 3072, 9216, "student_t4", 16, 50.0, mx=True),
     "mx_fc1": LayerSpec("mx_fc1", 4, 4608, 3072, 12288, "student_t4", 16, 50.0,
                         gelu=True, mx=True, w_stream=5, bias_stream=6),
-    "mx_fc2": LayerSpec("mx_fc2", 4, 4608, 12288, 3072, "student_t4", 16, 50.0,
+    "mx_fc2": LayerSpec("mx_fc2", 4, 4608, 12288, 3072, "external", 0, 1.0,
                         mx=True, w_stream=7, bias_stream=8),
 }
 

@@ -31,8 +31,9 @@
  * quotient v / scale (always within [-7, 7]).  MXFP4 block: X = floor(log2 a)
  * - 2 clamped to [-127, 127], E8M0 = X + 127, element = v 2^-X rounded to the
  * E2M1 grid (ties to the even index, saturating at 6, sign kept for zero).
- * Codes are nibble-packed, element 2i in the low nibble of byte i; INT4 codes
- * are two's complement, E2M1 codes are sign << 3 | index.
+ * Codes are nibble-packed, element 2i in the low nibble of byte i.  Both code
+ * formats are sign-magnitude with the sign of the input in bit 3 (kept for
+ * zero): INT4 code = sign << 3 | |q|, E2M1 code = sign << 3 | grid index.
  *
  * Conventions.
  *   - Ownership: the caller allocates and frees every buffer.  No call
@@ -45,7 +46,8 @@
  *     SVDQ_ERR_UNSUPPORTED_DEVICE is returned and nothing runs.
  *   - Host calls (svdq_pack_weights, svdq_pack_residual) take host pointers,
  *     run synchronously on the CPU and need no GPU.
- *   - Device pointers must be 16-byte aligned (SVDQ_ERR_MISALIGNED).
+ *   - Device pointers must be 16-byte aligned (SVDQ_ERR_MISALIGNED).  A
+ *     buffer whose size is zero (M == 0 or N == 0) may be NULL.
  *   - Inputs are expected finite; the device calls do not check the values
  *     of X (non-finite X gives unspecified codes).
  *   - Every function is thread-safe.  Calls that overlap on one stream are

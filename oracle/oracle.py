@@ -47,7 +47,9 @@ def lib():
         P = ctypes.c_void_p
         I = ctypes.c_int
         L.oracle_quant_group_int4.restype = ctypes.c_float
-        L.oracle_quant_group_int4.argtypes = [P, I, P]
+        L.oracle_quant_group_int4.argtypes = [P, I, P, P]
+        L.oracle_int4_value.restype = I
+        L.oracle_int4_value.argtypes = [ctypes.c_uint8]
         L.oracle_quant_block_mxfp4.restype = ctypes.c_uint8
         L.oracle_quant_block_mxfp4.argtypes = [P, I, P]
         L.oracle_e2m1_value.restype = ctypes.c_double
@@ -80,11 +82,18 @@ def group_of(prec: int) -> int:
 
 # ------------------------------------------------------------ group quantizers
 
-def quant_group_int4(v) -> tuple[np.ndarray, np.float32]:
+def quant_group_int4(v, codes: bool = False):
+    """(q, scale) of one INT4 group, or (q, scale, codes) with the
+    sign-magnitude 4-bit codes (sign of v kept for zero)."""
     v = _c(v, np.float32)
     q = np.zeros(v.size, np.int8)
-    sc = lib().oracle_quant_group_int4(_p(v), v.size, _p(q))
-    return q, np.float32(sc)
+    c = np.zeros(v.size, np.uint8)
+    sc = lib().oracle_quant_group_int4(_p(v), v.size, _p(q), _p(c))
+    return (q, np.float32(sc), c) if codes else (q, np.float32(sc))
+
+
+def int4_value(code: int) -> int:
+    return lib().oracle_int4_value(code)
 
 
 def quant_block_mxfp4(v) -> tuple[np.ndarray, int]:
@@ -94,10 +103,11 @@ def quant_block_mxfp4(v) -> tuple[np.ndarray, int]:
     return c, int(e)
 
 
-def pack_nibbles(q) -> np.ndarray:
-    q = _c(q, np.int8)
-    out = np.zeros(q.size // 2, np.uint8)
-    lib().oracle_pack_nibbles(_p(q), q.size, _p(out))
+def pack_nibbles(codes) -> np.ndarray:
+    """4-bit codes (one per byte) -> packed bytes, element 2i in the low nibble."""
+    c = _c(codes, np.uint8)
+    out = np.zeros(c.size // 2, np.uint8)
+    lib().oracle_pack_nibbles(_p(c), c.size, _p(out))
     return out
 
 
@@ -251,14 +261,9 @@ def forward(X, packed: dict, bias, prec: int, gelu: bool = False, rows=None):
 # ----------------------------------------------------------------- decoding
 
 def unpack_int4(codes: np.ndarray) -> np.ndarray:
-    """Nibble-packed two's-complement INT4 -> int8 (element 2i in the low nibble)."""
-    c = np.asarray(codes, np.uint8)
-    lo = (c & 0x0F).astype(np.int16)
-    hi = (c >> 4).astype(np.int16)
-    out = np.empty(c.shape[:-1] + (c.shape[-1] * 2,), np.int16)
-    out[..., 0::2] = lo
-    out[..., 1::2] = hi
-    out[out >= 8] -= 16
+    """Nibble-packed sign-magnitude INT4 -> int8 (element 2i in the low nibble)."""
+    n = unpack_nibbles(codes).astype(np.int16)
+    out = np.where(n & 8, -(n & 7), n & 7)
     return out.astype(np.int8)
 
 

@@ -32,7 +32,9 @@
  * INT4 group quantizer (symmetric, 64 wide): a = max|v|; scale = fl32(a/7)
  * (0 if a == 0; rounded upward instead of to nearest when a/7 is below the
  * smallest normal fp32); q = round-half-even of the exact real quotient
- * v/scale, clamped to [-7, 7] (the clamp never acts).  Nibbles: byte i = (q[2i] & 15) | (q[2i+1] & 15) << 4.
+ * v/scale, clamped to [-7, 7] (the clamp never acts).  The 4-bit code is
+ * sign-magnitude, the same layout as an E2M1 code: bit 3 = sign of v (kept
+ * for zero), bits 0-2 = |q|.  Nibbles: byte i = code[2i] | code[2i+1] << 4.
  *
  * MXFP4 block quantizer (OCP Microscaling v1.0 conversion; 32 wide):
  * X = floor(log2 a) - 2, clamped to [-127, 127], stored as E8M0 X + 127;
@@ -70,8 +72,9 @@ static double bf16_val(uint16_t b)
 
 /* ----------------------------------------------------------- INT4 groups */
 
-/* One symmetric INT4 group: returns scale, writes codes in [-7, 7]. */
-float oracle_quant_group_int4(const float *v, int n, int8_t *q)
+/* One symmetric INT4 group: returns scale, writes the integers q in [-7, 7]
+ * and (when `code` is not NULL) their sign-magnitude 4-bit codes. */
+float oracle_quant_group_int4(const float *v, int n, int8_t *q, uint8_t *code)
 {
     float a = 0.0f;
     for (int i = 0; i < n; ++i) {
@@ -79,7 +82,10 @@ float oracle_quant_group_int4(const float *v, int n, int8_t *q)
         if (t > a) a = t;
     }
     if (a == 0.0f) {
-        for (int i = 0; i < n; ++i) q[i] = 0;
+        for (int i = 0; i < n; ++i) {
+            q[i] = 0;
+            if (code) code[i] = (uint8_t)(signbit(v[i]) ? 8 : 0);
+        }
         return 0.0f;
     }
     /* fl32(a / 7): the fp64 quotient rounded to fp32 is the correctly rounded
@@ -102,6 +108,7 @@ float oracle_quant_group_int4(const float *v, int n, int8_t *q)
         }
         if (m > 7) m = 7;
         q[i] = (int8_t)(x < 0 ? -m : m);
+        if (code) code[i] = (uint8_t)((signbit(v[i]) ? 8 : 0) | m);
     }
     return scale;
 }
@@ -163,13 +170,17 @@ double oracle_e8m0_value(uint8_t e)
 
 /* --------------------------------------------------------------- nibbles */
 
-void oracle_pack_nibbles(const int8_t *q, int n, uint8_t *out)
+/* Two 4-bit codes per byte, element 2i in the low nibble. */
+void oracle_pack_nibbles(const uint8_t *code, int n, uint8_t *out)
 {
     for (int i = 0; i < n / 2; ++i)
-        out[i] = (uint8_t)(((uint8_t)q[2 * i] & 0x0F) | (((uint8_t)q[2 * i + 1] & 0x0F) << 4));
+        out[i] = (uint8_t)((code[2 * i] & 0x0F) | ((code[2 * i + 1] & 0x0F) << 4));
 }
 
-static int int4_of_nibble(int nib) { return nib >= 8 ? nib - 16 : nib; }
+/* Sign-magnitude INT4 code -> integer. */
+static int int4_of_nibble(int nib) { return (nib & 8) ? -(nib & 7) : (nib & 7); }
+
+int oracle_int4_value(uint8_t code) { return int4_of_nibble(code & 15); }
 
 static int nibble_at(const uint8_t *row, int k)
 {
@@ -182,18 +193,18 @@ static void quant_row(const float *v, int K, int prec, uint8_t *codes, void *sca
 {
     if (prec == ORACLE_INT4) {
         int8_t q[64];
+        uint8_t c[64];
         float *sc = (float *)scales;
         for (int g = 0; g < K / 64; ++g) {
-            sc[g] = oracle_quant_group_int4(v + 64 * g, 64, q);
-            oracle_pack_nibbles(q, 64, codes + 32 * g);
+            sc[g] = oracle_quant_group_int4(v + 64 * g, 64, q, c);
+            oracle_pack_nibbles(c, 64, codes + 32 * g);
         }
     } else {
         uint8_t c[32];
         uint8_t *sc = (uint8_t *)scales;
         for (int b = 0; b < K / 32; ++b) {
             sc[b] = oracle_quant_block_mxfp4(v + 32 * b, 32, c);
-            for (int i = 0; i < 16; ++i)
-                codes[16 * b + i] = (uint8_t)((c[2 * i] & 0x0F) | ((c[2 * i + 1] & 0x0F) << 4));
+            oracle_pack_nibbles(c, 32, codes + 16 * b);
         }
     }
 }

@@ -85,4 +85,5 @@ def quant_block_mxfp4_exact(v):
 
 
 def int4_code(nib: int) -> int:
-    return nib - 16 if nib >= 8 else nib
+    """Sign-magnitude nibble -> integer."""
+    return -(nib & 7) if nib & 8 else nib & 7

@@ -57,6 +57,7 @@ def test_device_call_validation_order():
     assert L.svdq_w4a4_linear(p, p, p, p, p, p, None, M, 16, K, 32, svdq.INT4, 5, p, None) == -1
     assert L.svdq_w4a4_linear(p, p, p, p, p, p, q, M, 16, K, 32, svdq.INT4, 0, p, None) == -3
     assert L.svdq_w4a4_linear(p, p, p, p, p, p, None, M, 16, 96, 32, svdq.MXFP4, 0, None, None) == -1
+    assert L.svdq_quantize_act(None, 0, K, None, p, 32, svdq.INT4, p, p, p, None) == -1   # smooth needed
 
 
 def _has_gpu():

@@ -14,8 +14,11 @@ from w4a4_rank_corrected_quantize_amd.synth import f32_to_bf16_bits, bf16_bits_t
 
 
 def _rand_codes(rng, rows, K):
+    """Random INT4 values and their sign-magnitude nibbles (a random sign on zeros)."""
     q = rng.integers(-7, 8, (rows, K)).astype(np.int8)
-    return q, np.stack([O.pack_nibbles(r) for r in q])
+    neg = (q < 0) | ((q == 0) & (rng.random((rows, K)) < 0.5))
+    c = (np.abs(q) | (neg.astype(np.uint8) << 3)).astype(np.uint8)
+    return q, np.stack([O.pack_nibbles(r) for r in c])
 
 
 def _rand_mx_codes(rng, rows, K):

@@ -121,9 +121,9 @@ def test_quant_act_reassembly(prec):
         for b in range(X.shape[1] // g):
             v = xhat[m, g * b:g * b + g]
             if prec == O.INT4:
-                q, sc = O.quant_group_int4(v)
+                q, sc, c = O.quant_group_int4(v, codes=True)
                 assert xscale[m, b] == sc
-                assert np.array_equal(xq[m, g * b // 2:(g * b + g) // 2], O.pack_nibbles(q))
+                assert np.array_equal(xq[m, g * b // 2:(g * b + g) // 2], O.pack_nibbles(c))
             else:
                 c, e = O.quant_block_mxfp4(v)
                 assert xscale[m, b] == e

@@ -34,12 +34,13 @@ def _group(entry, width):
                          ids=lambda e: e["id"])
 def test_int4_golden(entry):
     v = _group(entry, 64)
-    q, scale = O.quant_group_int4(v)
+    q, scale, c = O.quant_group_int4(v, codes=True)
     assert int(np.float32(scale).view(np.uint32)) == int(entry["scale_hex"], 16)
     n = len(entry["codes"])
     assert q[:n].tolist() == entry["codes"]
-    assert not q[n:].any()
-    packed = O.pack_nibbles(q)
+    assert c[:n].tolist() == entry["nibbles"]
+    assert not q[n:].any() and not c[n:].any()
+    packed = O.pack_nibbles(c)
     want = bytes.fromhex(entry["bytes_hex"])
     assert packed[: len(want)].tobytes() == want
     assert not packed[len(want):].any()
@@ -90,10 +91,11 @@ def _near_tie_groups(rng, count):
 
 
 def _check_int4(v):
-    q, scale = O.quant_group_int4(v)
+    q, scale, c = O.quant_group_int4(v, codes=True)
     qe, se = E.quant_group_int4_exact(v)
     assert Fraction(float(scale)) == se
     assert q.tolist() == qe
+    assert c.tolist() == [(8 if np.signbit(x) else 0) | abs(k) for x, k in zip(v, qe)]
     # invariant: dequantization error at most scale/2, exactly
     for x, c in zip(v, q):
         assert abs(Fraction(float(x)) - c * se) <= se / 2
@@ -140,10 +142,13 @@ def test_int4_tie_trap_is_not_reciprocal_multiply():
 
 def test_nibble_round_trip():
     rng = np.random.default_rng(14)
-    q = rng.integers(-7, 8, 4096).astype(np.int8)
-    packed = O.pack_nibbles(q)
-    assert np.array_equal(O.unpack_int4(packed), q)
-    assert packed[0] == ((int(q[0]) & 15) | ((int(q[1]) & 15) << 4))
+    c = rng.integers(0, 16, 4096).astype(np.uint8)
+    packed = O.pack_nibbles(c)
+    assert packed[0] == (int(c[0]) | (int(c[1]) << 4))
+    assert np.array_equal(O.unpack_nibbles(packed), c)
+    want = np.array([E.int4_code(int(x)) for x in c], np.int8)
+    assert np.array_equal(O.unpack_int4(packed), want)
+    assert [O.int4_value(x) for x in range(16)] == [0, 1, 2, 3, 4, 5, 6, 7, 0, -1, -2, -3, -4, -5, -6, -7]
 
 
 # ------------------------------------------------- exact brute force, MXFP4

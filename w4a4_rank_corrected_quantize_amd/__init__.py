@@ -148,7 +148,7 @@ def _torch():
 
 def _dev(t, dtypes, name):
     torch = _torch()
-    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
         raise TypeError(f"{name} must be a device tensor")
     if t.dtype not in dtypes:
         raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")

@@ -30,7 +30,7 @@ SOURCES = {
     "api.hip": [],
     "pack_host.hip": ["-ffp-contract=off", "-Xarch_host", "-mavx2", "-Xarch_host", "-mfma"],
     "quant_act.hip": ["-ffp-contract=off"],
-    "w4a4_gemm.hip": [],
+    "w4a4_gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 

@@ -78,7 +78,8 @@ extern "C" svdq_status svdq_quantize_act(const uint16_t *X, int M, int K, const 
 {
     svdq_status st = check_common(M, K, rank, prec);
     if (st != SVDQ_OK) return st;
-    if (!X || !smooth || !down || !xq || !xscale || !h) return SVDQ_ERR_INVALID_ARG;
+    // buffers of zero size may be NULL (empty tensors have no storage)
+    if (!smooth || !down || (M > 0 && (!X || !xq || !xscale || !h))) return SVDQ_ERR_INVALID_ARG;
     if (!aligned16(X) || !aligned16(smooth) || !aligned16(down) || !aligned16(xq) || !aligned16(xscale) ||
         !aligned16(h))
         return SVDQ_ERR_MISALIGNED;
@@ -99,7 +100,10 @@ extern "C" svdq_status svdq_w4a4_linear(const uint8_t *xq, const void *xscale, c
     if (N < 0) return SVDQ_ERR_INVALID_ARG;
     if (epi != SVDQ_EPI_NONE && epi != SVDQ_EPI_GELU_TANH) return SVDQ_ERR_INVALID_ARG;
     if (N % 8 != 0) return SVDQ_ERR_SHAPE;
-    if (!xq || !xscale || !h || !wq || !wscale || !up || !Y) return SVDQ_ERR_INVALID_ARG;
+    // buffers of zero size may be NULL (empty tensors have no storage)
+    if ((M > 0 && (!xq || !xscale || !h)) || (N > 0 && (!wq || !wscale || !up)) ||
+        (M > 0 && N > 0 && !Y))
+        return SVDQ_ERR_INVALID_ARG;
     if (!aligned16(xq) || !aligned16(xscale) || !aligned16(h) || !aligned16(wq) || !aligned16(wscale) ||
         !aligned16(up) || !aligned16(Y) || (bias && !aligned16(bias)))
         return SVDQ_ERR_MISALIGNED;

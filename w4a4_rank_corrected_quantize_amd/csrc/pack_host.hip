@@ -290,10 +290,8 @@ static void quantize_row(const float *v, int K, svdq_precision prec, uint8_t *co
             for (int i = 0; i < 64; ++i) a = std::max(a, std::fabs(x[i]));
             float scale = int4_group_scale(a);
             Int4Group G = int4_group_prepare(scale);
-            for (int i = 0; i < 32; ++i) {
-                int q0 = int4_code(x[2 * i], G), q1 = int4_code(x[2 * i + 1], G);
-                codes[32 * g + i] = (uint8_t)((q0 & 15) | ((q1 & 15) << 4));
-            }
+            for (int i = 0; i < 32; ++i)
+                codes[32 * g + i] = (uint8_t)(int4_nibble(x[2 * i], G) | (int4_nibble(x[2 * i + 1], G) << 4));
             sc[g] = scale;
         }
     } else {

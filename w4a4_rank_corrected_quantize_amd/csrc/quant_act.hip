@@ -48,6 +48,13 @@ __device__ __forceinline__ void smooth16(uint4 xa, uint4 xb, const float4 *s, fl
     }
 }
 
+struct K1Load {
+    uint4 xa, xb;          // 16 channels of X (bf16)
+    uint4 d0a, d0b;        // down[rl][16 channels]
+    uint4 d1a, d1b;        // down[rl + 16][16 channels]
+    float4 s[4];           // smoothing factors of the 16 channels
+};
+
 template <bool MX>
 __global__ __launch_bounds__(64 * K1_WAVES) void quant_act_kernel(
     const uint16_t *__restrict__ X, int M, int K, const float *__restrict__ smooth,
@@ -65,69 +72,107 @@ __global__ __launch_bounds__(64 * K1_WAVES) void quant_act_kernel(
     const size_t rowK = (size_t)(rv ? row : 0) * (size_t)K;
     const uint4 z4 = {0u, 0u, 0u, 0u};
 
+    // Loads are unconditional (addresses clamped into the buffers) so that the
+    // number of loads in flight is the same on every path and the next
+    // group's loads can stay in flight while the current group is processed.
+    // Rows >= M read row 0 and are never stored; channels past K (a trailing
+    // half step of MXFP4) are masked out of the down projection at use.
+    auto fetch = [&](int g, K1Load &L) {
+        const int k0 = min(g * 64 + c * 16, K - 16);
+        L.xa = *reinterpret_cast<const uint4 *>(X + rowK + k0);
+        L.xb = *reinterpret_cast<const uint4 *>(X + rowK + k0 + 8);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) L.s[i] = *reinterpret_cast<const float4 *>(smooth + k0 + 4 * i);
+        L.d0a = *reinterpret_cast<const uint4 *>(down + (size_t)rl * K + k0);
+        L.d0b = *reinterpret_cast<const uint4 *>(down + (size_t)rl * K + k0 + 8);
+        L.d1a = *reinterpret_cast<const uint4 *>(down + (size_t)(rl + 16) * K + k0);
+        L.d1b = *reinterpret_cast<const uint4 *>(down + (size_t)(rl + 16) * K + k0 + 8);
+    };
+
     f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-    for (int g = wave; g < steps; g += K1_WAVES) {
-        const int k0 = g * 64 + c * 16;
-        const bool kv = k0 < K;                 // false only in a trailing half step
-        uint4 xa = z4, xb = z4, d0a = z4, d0b = z4, d1a = z4, d1b = z4;
-        float4 s[4] = {};
-        if (kv) {
-            if (rv) {
-                xa = *reinterpret_cast<const uint4 *>(X + rowK + k0);
-                xb = *reinterpret_cast<const uint4 *>(X + rowK + k0 + 8);
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) s[i] = *reinterpret_cast<const float4 *>(smooth + k0 + 4 * i);
-            d0a = *reinterpret_cast<const uint4 *>(down + (size_t)rl * K + k0);
-            d0b = *reinterpret_cast<const uint4 *>(down + (size_t)rl * K + k0 + 8);
-            d1a = *reinterpret_cast<const uint4 *>(down + (size_t)(rl + 16) * K + k0);
-            d1b = *reinterpret_cast<const uint4 *>(down + (size_t)(rl + 16) * K + k0 + 8);
-        }
+    auto process = [&](int g, const K1Load &L) {
+            const int k0 = g * 64 + c * 16;
+            const bool kv = k0 < K;                 // false only in a trailing half step
 
-        // down projection: D[m][j] += sum_k X[m][k] down[j][k]
-        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xa), as_bf16x8(d0a), acc0, 0, 0, 0);
-        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xb), as_bf16x8(d0b), acc0, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xa), as_bf16x8(d1a), acc1, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xb), as_bf16x8(d1b), acc1, 0, 0, 0);
+            // down projection: D[m][j] += sum_k X[m][k] down[j][k]
+            uint4 d0a = L.d0a, d0b = L.d0b, d1a = L.d1a, d1b = L.d1b;
+            if (MX && !kv) d0a = d0b = d1a = d1b = z4;
+            acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(L.xa), as_bf16x8(d0a), acc0, 0, 0, 0);
+            acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(L.xb), as_bf16x8(d0b), acc0, 0, 0, 0);
+            acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(L.xa), as_bf16x8(d1a), acc1, 0, 0, 0);
+            acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(L.xb), as_bf16x8(d1b), acc1, 0, 0, 0);
 
-        float v[16];
-        smooth16(xa, xb, s, v);
-        float a = 0.0f;
+            float v[16];
+            smooth16(L.xa, L.xb, L.s, v);
+            float a = 0.0f;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) a = __builtin_fmaxf(a, __builtin_fabsf(v[i]));
-        uint32_t p0 = 0, p1 = 0;
-        if constexpr (!MX) {
-            a = __builtin_fmaxf(a, __shfl_xor(a, 16));
-            a = __builtin_fmaxf(a, __shfl_xor(a, 32));
-            const float scale = int4_group_scale(a);
-            const Int4Group gq = int4_group_prepare(scale);
+            for (int i = 0; i < 16; ++i) a = __builtin_fmaxf(a, __builtin_fabsf(v[i]));
+            // sign bits of the 16 codes (bit 3 of each nibble), from the fp32 values
+            uint32_t sg0 = 0, sg1 = 0;
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-                const uint32_t nib = (uint32_t)(int4_code(v[i], gq) & 15) << (4 * i);
-                p0 |= nib;
+                sg0 |= (f32_bits(v[i]) >> 31) << (4 * i + 3);
+                sg1 |= (f32_bits(v[8 + i]) >> 31) << (4 * i + 3);
             }
+            uint32_t p0 = 0, p1 = 0;
+            if constexpr (!MX) {
+                a = __builtin_fmaxf(a, __shfl_xor(a, 16));
+                a = __builtin_fmaxf(a, __shfl_xor(a, 32));
+                const float scale = int4_group_scale(a);
+                const bool lifted = scale < 7.88860905e-31f;      // 2^-100: exact path only
+                const float inv = scale == 0.0f ? 0.0f : __builtin_amdgcn_rcpf(scale);
+                bool near = lifted;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const uint32_t nib = (uint32_t)(int4_code(v[8 + i], gq) & 15) << (4 * i);
-                p1 |= nib;
+                for (int i = 0; i < 16; ++i) {
+                    const float t = __builtin_fabsf(v[i]) * inv;
+                    const float q = __builtin_rintf(t);
+                    near |= __builtin_fabsf(t - q) >= kNearTie;
+                    const uint32_t m = (uint32_t)q;
+                    if (i < 8) p0 |= m << (4 * i);
+                    else p1 |= m << (4 * (i - 8));
+                }
+                if (near) {                                       // rare: exact remainder test
+                    const Int4Group gq = int4_group_prepare(scale);
+                    p0 = p1 = 0;
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        p0 |= int4_mag(__builtin_fabsf(v[i]), gq) << (4 * i);
+                        p1 |= int4_mag(__builtin_fabsf(v[8 + i]), gq) << (4 * i);
+                    }
+                }
+                p0 |= sg0;
+                p1 |= sg1;
+                if (rv && c == 0) reinterpret_cast<float *>(xscale)[(size_t)row * G + g] = scale;
+            } else {
+                // two 32-wide blocks per step: lanes c = 0,1 -> block 2g, c = 2,3 -> block 2g+1
+                a = __builtin_fmaxf(a, __shfl_xor(a, 16));
+                const uint32_t e = mx_block_e8m0(a);
+                const float inv = mx_inv_scale(e);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) p0 |= e2m1_code(v[i], inv) << (4 * i);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) p1 |= e2m1_code(v[8 + i], inv) << (4 * i);
+                if (rv && kv && (c & 1) == 0)
+                    reinterpret_cast<uint8_t *>(xscale)[(size_t)row * (K >> 5) + 2 * g + (c >> 1)] = (uint8_t)e;
             }
-            if (rv && c == 0) reinterpret_cast<float *>(xscale)[(size_t)row * G + g] = scale;
-        } else {
-            // two 32-wide blocks per step: lanes c = 0,1 -> block 2g, c = 2,3 -> block 2g+1
-            a = __builtin_fmaxf(a, __shfl_xor(a, 16));
-            const uint32_t e = mx_block_e8m0(a);
-            const float inv = mx_inv_scale(e);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) p0 |= e2m1_code(v[i], inv) << (4 * i);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) p1 |= e2m1_code(v[8 + i], inv) << (4 * i);
-            if (rv && kv && (c & 1) == 0)
-                reinterpret_cast<uint8_t *>(xscale)[(size_t)row * (K >> 5) + 2 * g + (c >> 1)] = (uint8_t)e;
-        }
-        if (rv && kv) {
-            uint2 pk = {p0, p1};
-            *reinterpret_cast<uint2 *>(xq + (size_t)row * (K >> 1) + (k0 >> 1)) = pk;
-        }
+            if (rv && kv) {
+                uint2 pk = {p0, p1};
+                *reinterpret_cast<uint2 *>(xq + (size_t)row * (K >> 1) + (k0 >> 1)) = pk;
+            }
+    };
+
+    // ping-pong register buffers: the loads of the next group are in flight
+    // while the current one is processed
+    K1Load bufA, bufB;
+    int g = wave;
+    if (g < steps) fetch(g, bufA);
+    for (; g < steps; g += 2 * K1_WAVES) {
+        const int g1 = g + K1_WAVES;
+        fetch(min(g1, steps - 1), bufB);
+        process(g, bufA);
+        if (g1 >= steps) break;
+        fetch(min(g1 + K1_WAVES, steps - 1), bufA);
+        process(g1, bufB);
     }
 
     // fixed-order reduction of the per-wave partial h tiles

@@ -57,20 +57,32 @@ SVDQ_HD Int4Group int4_group_prepare(float scale)
     return g;
 }
 
-// Code in [-7, 7] of one element; `v` is the unlifted value.
-SVDQ_HD int int4_code(float v, const Int4Group &g)
+// Exact magnitude code |q| in [0, 7] for av = |v| (unlifted value).
+SVDQ_HD uint32_t int4_mag(float av, const Int4Group &g)
 {
-    float x = v * g.lift;
-    float q0 = __builtin_rintf(x * g.inv);
-    float e = __builtin_fmaf(-q0, g.scale, x);
-    float ae = __builtin_fabsf(e);
-    // q0 odd <=> q0 - 2*rint(q0/2) != 0 (q0 is a small integer, all exact)
-    bool odd = (q0 - 2.0f * __builtin_rintf(0.5f * q0)) != 0.0f;
-    bool move = (ae > g.half) || (ae == g.half && odd);
-    float q = move ? q0 + __builtin_copysignf(1.0f, e) : q0;
-    q = __builtin_fminf(__builtin_fmaxf(q, -7.0f), 7.0f);
-    return (int)q;
+    const float x = av * g.lift;
+    const float q0 = __builtin_rintf(x * g.inv);
+    const float e = __builtin_fmaf(-q0, g.scale, x);      // exact remainder
+    const float d = __builtin_fabsf(e) - g.half;          // sign and zero are exact
+    const int qi = (int)q0;
+    const bool move = d > 0.0f || (d == 0.0f && (qi & 1));
+    int q = qi + (move ? (e < 0.0f ? -1 : 1) : 0);
+    q = q < 0 ? 0 : (q > 7 ? 7 : q);
+    return (uint32_t)q;
 }
+
+// Sign-magnitude 4-bit code: bit 3 = sign of v (kept for zero), bits 0-2 = |q|.
+SVDQ_HD uint32_t int4_nibble(float v, const Int4Group &g)
+{
+    return ((f32_bits(v) >> 28) & 8u) | int4_mag(__builtin_fabsf(v), g);
+}
+
+// Fast path used by the activation kernel: |q| = rint(|v| * inv) is exact
+// unless |v|/scale lies within 2^-20 of a half-integer (the product carries a
+// relative error below 2^-23 on a quotient below 7.5); such elements are
+// flagged (`near`) and redone with int4_mag.  Groups that need the 2^64 lift
+// are always redone.
+constexpr float kNearTie = 0.49999809265136719f;          // 0.5 - 2^-19
 
 // ----------------------------------------------------------------- MXFP4
 

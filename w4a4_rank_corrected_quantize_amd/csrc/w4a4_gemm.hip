@@ -7,29 +7,28 @@
 //
 //   y_mn = sum_g sx_mg sw_ng P_mng + sum_j h_mj up[n][j] + b_n   [GELU-tanh]
 //
-// INT4: P_mng = sum_{k in g} qx_mk qw_nk is an exact int32 from
-// v_mfma_i32_16x16x64_i8 (one instruction = one 64-wide group for a 16x16
-// tile).  The nibbles are widened to int8 in registers with two masks and a
-// shift, which yields 16 q instead of q (no sign extension needed), so the
-// instruction returns 256 P; the 2^-8 is applied once at the end (exact).  The
-// rescale acc += fl(P) * (sx * sw) is fp32 VALU work (convert, multiply, fma
-// per element and group), which is what bounds this kernel on gfx950.
+// INT4: the codes are sign-magnitude nibbles (sign << 3 | |q|).  Widened to a
+// byte as sign << 7 | |q| they are exact E4M3 values q * 2^-9 (E4M3
+// subnormals), so v_mfma_f32_32x32x64_f8f6f4 in fp8 mode returns the exact
+// per-group integer dot product P_mng * 2^-18 in fp32 (|P| <= 3136): one
+// instruction covers exactly one 64-wide group of a 32x32 tile.  The nibbles
+// are widened once per block while staging them into LDS (three bit
+// operations per four codes).  The rescale acc += P * (sx * sw) costs one
+// multiply and one fma per element and group on the fp32 VALU, which is what
+// bounds this kernel on gfx950 (the 2^18 is folded into the staged sw).
 //
 // MXFP4: the E2M1 nibbles are the native fp4 operand format of
 // v_mfma_scale_f32_16x16x128_f8f6f4 and the E8M0 block scales are its scale
 // operands, so the matrix core applies 2^(ex + ew) itself and accumulates
 // across blocks; no per-block VALU work remains.
 //
-// Tiling: a 256-thread block owns a BM x BN tile (m: tokens, n: output
-// channels); 4 waves in a 2 x 2 arrangement each own (BM/2) x (BN/2).  Codes
-// are staged through LDS, double buffered, one barrier per K step.  The matrix
-// instruction's A operand is the weight tile (rows n) and B the activation tile
-// (columns m), so each lane ends with 4 consecutive output channels n of one
-// token m, i.e. one 8-byte bf16 store per 16x16 tile.
+// Operand roles: the matrix instruction's A operand is the weight tile (rows
+// n) and B the activation tile (columns m), so every lane ends up holding
+// runs of 4 consecutive output channels n of one token m (8-byte bf16 stores).
 //
 // Low-rank epilogue: h (fp32) is split into bf16 hi = bf16(h) and lo =
-// bf16(h - hi); two v_mfma_f32_16x16x32_bf16 per tile with `up` as the other
-// operand give h . up to ~16 bits, well inside the output tolerance.
+// bf16(h - hi); the bf16 matrix instruction with `up` as the other operand
+// gives h . up to ~16 bits, well inside the output tolerance.
 #include "svdq_internal.h"
 #include "svdq_quant.h"
 
@@ -39,12 +38,8 @@ namespace {
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-
-constexpr int BM = 128, BN = 128;          // block tile (m, n)
-constexpr int WM = 64, WN = 64;            // wave tile
-constexpr int TM = WM / 16, TN = WN / 16;  // 16x16 tiles per wave
-constexpr int NTHREADS = 256;
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t b) { return bits_f32(b << 16); }
 
@@ -60,198 +55,299 @@ __device__ __forceinline__ float gelu_tanh(float y)
     return 0.5f * y * (1.0f + tanhf(k0 * (y + 0.044715f * y * y * y)));
 }
 
-// 16 INT4 codes (8 bytes) -> 16 int8 holding 16 q each.  Byte order inside
-// the result is a fixed permutation of the k order, identical for both
-// operands, so the dot products are unchanged.
-__device__ __forceinline__ i32x4 widen16(uint2 p)
+// 8 fp32 values of h -> bf16 hi and lo parts (hi = bf16(h), lo = bf16(h - hi)).
+__device__ __forceinline__ void split_h(const float *hv, bf16x8 &hi8, bf16x8 &lo8)
 {
-    i32x4 r;
-    r[0] = (int)((p.x << 4) & 0xF0F0F0F0u);
-    r[1] = (int)(p.x & 0xF0F0F0F0u);
-    r[2] = (int)((p.y << 4) & 0xF0F0F0F0u);
-    r[3] = (int)(p.y & 0xF0F0F0F0u);
-    return r;
+    uint32_t hi[4], lo[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t h0 = f32_to_bf16_rne(hv[2 * i]), h1 = f32_to_bf16_rne(hv[2 * i + 1]);
+        const uint32_t l0 = f32_to_bf16_rne(hv[2 * i] - bf16_to_f32(h0));
+        const uint32_t l1 = f32_to_bf16_rne(hv[2 * i + 1] - bf16_to_f32(h1));
+        hi[i] = h0 | (h1 << 16);
+        lo[i] = l0 | (l1 << 16);
+    }
+    hi8 = __builtin_bit_cast(bf16x8, (uint4){hi[0], hi[1], hi[2], hi[3]});
+    lo8 = __builtin_bit_cast(bf16x8, (uint4){lo[0], lo[1], lo[2], lo[3]});
 }
 
-// Low-rank term + bias (+ GELU) + bf16 store for one wave's (WN x WM) tile.
-// acc[tn][tm][i] holds the 4-bit product of token m = mb + tm*16 + (lane&15)
-// and channel n = nb + tn*16 + 4*(lane>>4) + i.
-__device__ __forceinline__ void epilogue(f32x4 (&acc)[TN][TM], float acc_scale, const float *__restrict__ h,
-                                         const uint16_t *__restrict__ up, const uint16_t *__restrict__ bias,
-                                         int M, int N, int gelu, uint16_t *__restrict__ Y, int mb, int nb,
-                                         int lane)
+__device__ __forceinline__ void load_h8(const float *__restrict__ h, int m, int M, int k, float *hv)
 {
-    const int l16 = lane & 15, c = lane >> 4;
-    bf16x8 hhi[TM], hlo[TM];
+    if (m < M) {
+        const float4 a = *reinterpret_cast<const float4 *>(h + (size_t)m * 32 + k);
+        const float4 b = *reinterpret_cast<const float4 *>(h + (size_t)m * 32 + k + 4);
+        hv[0] = a.x; hv[1] = a.y; hv[2] = a.z; hv[3] = a.w;
+        hv[4] = b.x; hv[5] = b.y; hv[6] = b.z; hv[7] = b.w;
+    } else {
 #pragma unroll
-    for (int tm = 0; tm < TM; ++tm) {
-        const int m = mb + tm * 16 + l16;
-        float hv[8];
-        if (m < M) {
-            const float4 a = *reinterpret_cast<const float4 *>(h + (size_t)m * 32 + 8 * c);
-            const float4 b = *reinterpret_cast<const float4 *>(h + (size_t)m * 32 + 8 * c + 4);
-            hv[0] = a.x; hv[1] = a.y; hv[2] = a.z; hv[3] = a.w;
-            hv[4] = b.x; hv[5] = b.y; hv[6] = b.z; hv[7] = b.w;
-        } else {
-#pragma unroll
-            for (int i = 0; i < 8; ++i) hv[i] = 0.0f;
-        }
-        uint32_t hi[4], lo[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const uint32_t h0 = f32_to_bf16_rne(hv[2 * i]), h1 = f32_to_bf16_rne(hv[2 * i + 1]);
-            const uint32_t l0 = f32_to_bf16_rne(hv[2 * i] - bf16_to_f32(h0));
-            const uint32_t l1 = f32_to_bf16_rne(hv[2 * i + 1] - bf16_to_f32(h1));
-            hi[i] = h0 | (h1 << 16);
-            lo[i] = l0 | (l1 << 16);
-        }
-        hhi[tm] = __builtin_bit_cast(bf16x8, (uint4){hi[0], hi[1], hi[2], hi[3]});
-        hlo[tm] = __builtin_bit_cast(bf16x8, (uint4){lo[0], lo[1], lo[2], lo[3]});
-    }
-#pragma unroll
-    for (int tn = 0; tn < TN; ++tn) {
-        const int nrow = nb + tn * 16 + l16;       // A-operand row of `up`
-        uint4 uv = {0u, 0u, 0u, 0u};
-        if (nrow < N) uv = *reinterpret_cast<const uint4 *>(up + (size_t)nrow * 32 + 8 * c);
-        const bf16x8 ua = __builtin_bit_cast(bf16x8, uv);
-        const int n = nb + tn * 16 + 4 * c;        // this lane's 4 output channels
-        float bv[4] = {0.f, 0.f, 0.f, 0.f};
-        if (bias && n < N) {
-            const uint2 b2 = *reinterpret_cast<const uint2 *>(bias + n);
-            bv[0] = bf16_to_f32(b2.x & 0xFFFFu); bv[1] = bf16_to_f32(b2.x >> 16);
-            bv[2] = bf16_to_f32(b2.y & 0xFFFFu); bv[3] = bf16_to_f32(b2.y >> 16);
-        }
-#pragma unroll
-        for (int tm = 0; tm < TM; ++tm) {
-            f32x4 lr = {0.f, 0.f, 0.f, 0.f};
-            lr = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ua, hhi[tm], lr, 0, 0, 0);
-            lr = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ua, hlo[tm], lr, 0, 0, 0);
-            const int m = mb + tm * 16 + l16;
-            uint32_t o[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                float y = acc[tn][tm][i] * acc_scale + lr[i] + bv[i];
-                if (gelu) y = gelu_tanh(y);
-                o[i] = f32_to_bf16_rne(y);
-            }
-            if (m < M && n < N) {
-                const uint2 st = {o[0] | (o[1] << 16), o[2] | (o[3] << 16)};
-                *reinterpret_cast<uint2 *>(Y + (size_t)m * N + n) = st;
-            }
-        }
+        for (int i = 0; i < 8; ++i) hv[i] = 0.0f;
     }
 }
 
-// ----------------------------------------------------------------- INT4
+// y = acc * acc_scale + lr + b (+ GELU) for 4 consecutive channels n..n+3 of
+// token m, stored as bf16.
+__device__ __forceinline__ void finish4(const float *acc, float acc_scale, const float *lr,
+                                        const uint16_t *__restrict__ bias, int gelu, uint16_t *__restrict__ Y,
+                                        int m, int n, int M, int N)
+{
+    if (m >= M || n >= N) return;
+    float bv[4] = {0.f, 0.f, 0.f, 0.f};
+    if (bias) {
+        const uint2 b2 = *reinterpret_cast<const uint2 *>(bias + n);
+        bv[0] = bf16_to_f32(b2.x & 0xFFFFu); bv[1] = bf16_to_f32(b2.x >> 16);
+        bv[2] = bf16_to_f32(b2.y & 0xFFFFu); bv[3] = bf16_to_f32(b2.y >> 16);
+    }
+    uint32_t o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        float y = acc[i] * acc_scale + lr[i] + bv[i];
+        if (gelu) y = gelu_tanh(y);
+        o[i] = f32_to_bf16_rne(y);
+    }
+    const uint2 st = {o[0] | (o[1] << 16), o[2] | (o[3] << 16)};
+    *reinterpret_cast<uint2 *>(Y + (size_t)m * N + n) = st;
+}
 
-constexpr int I4_STRIDE = 48;   // LDS bytes per row: 32 code bytes + 16 pad
+// Tile order: with 8 XCDs, consecutive workgroup ids land on different XCDs;
+// give each XCD a contiguous range of tiles (n fastest) so the activation tile
+// of a row of tiles stays in that XCD's L2.
+__device__ __forceinline__ int xcd_tile(int b, int T)
+{
+    if (T % 8 != 0) return b;
+    return (b & 7) * (T >> 3) + (b >> 3);
+}
 
-__global__ __launch_bounds__(NTHREADS) void w4a4_int4_kernel(
+// ================================================================ INT4 (fp8 path)
+
+constexpr int I4_BN = 256, I4_BM = 128;          // block tile (n, m)
+constexpr int I4_WAVES_N = 4, I4_WAVES_M = 2;    // 8 waves
+constexpr int I4_WN = I4_BN / I4_WAVES_N, I4_WM = I4_BM / I4_WAVES_M;   // 64 x 64
+constexpr int I4_TN = I4_WN / 32, I4_TM = I4_WM / 32;                   // 2 x 2 tiles of 32x32
+constexpr int I4_THREADS = 64 * I4_WAVES_N * I4_WAVES_M;
+constexpr int I4_KSTEP = 128;                    // channels per pipeline step (two groups)
+constexpr int I4_ROWB = I4_KSTEP + 16;           // LDS bytes per row: 128 fp8 + 16 pad
+constexpr float kTwo18 = 262144.0f;
+
+// 16 nibble bytes (32 sign-magnitude codes) -> 32 E4M3 bytes (q * 2^-9).
+// Dword j of the input gives E (codes 8j, 8j+2, 8j+4, 8j+6) and O (the odd
+// ones); the resulting k order is a fixed permutation, the same for both
+// operands, so every dot product is unchanged.
+__device__ __forceinline__ void widen_fp8(uint4 p, uint4 &lo, uint4 &hi)
+{
+    const uint32_t w[4] = {p.x, p.y, p.z, p.w};
+    uint32_t o[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        o[2 * j] = (w[j] & 0x07070707u) | ((w[j] & 0x08080808u) << 4);
+        o[2 * j + 1] = ((w[j] >> 4) & 0x07070707u) | (w[j] & 0x80808080u);
+    }
+    lo = (uint4){o[0], o[1], o[2], o[3]};
+    hi = (uint4){o[4], o[5], o[6], o[7]};
+}
+
+struct __attribute__((aligned(16))) I4Smem {
+    uint8_t w[2][I4_BN * I4_ROWB];
+    uint8_t x[2][I4_BM * I4_ROWB];
+    float sw[2][2][I4_BN];     // [buf][group in step][n], times 2^18
+    float sx[2][2][I4_BM];     // [buf][group in step][m]
+};
+
+__global__ __launch_bounds__(I4_THREADS) void w4a4_int4_kernel(
     const uint8_t *__restrict__ xq, const float *__restrict__ xscale, const float *__restrict__ h,
     const uint8_t *__restrict__ wq, const float *__restrict__ wscale, const uint16_t *__restrict__ up,
     const uint16_t *__restrict__ bias, int M, int N, int K, int gelu, uint16_t *__restrict__ Y)
 {
-    __shared__ __attribute__((aligned(16))) uint8_t sW[2][BN * I4_STRIDE];
-    __shared__ __attribute__((aligned(16))) uint8_t sX[2][BM * I4_STRIDE];
-    __shared__ float sSw[2][BN];
-    __shared__ float sSx[2][BM];
-
+    __shared__ I4Smem sm;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wn = wave & 1, wm = wave >> 1;
-    const int m0 = blockIdx.x * BM, n0 = blockIdx.y * BN;
+    const int wn = wave % I4_WAVES_N, wm = wave / I4_WAVES_N;
+    const int tiles_n = (N + I4_BN - 1) / I4_BN;
+    const int tiles_m = (M + I4_BM - 1) / I4_BM;
+    const int t = xcd_tile(blockIdx.x, tiles_n * tiles_m);
+    const int n0 = (t % tiles_n) * I4_BN, m0 = (t / tiles_n) * I4_BM;
     const int G = K >> 6;
-    const int KB = K >> 1;     // code bytes per row
+    const int KB = K >> 1;                  // code bytes per row
+    const int steps = (G + 1) >> 1;
 
-    // loader: thread t moves 16 code bytes of row t/2 (both tiles) and one scale
-    const int lrow = tid >> 1, lhalf = tid & 1;
-    const bool wrow_ok = n0 + lrow < N, xrow_ok = m0 + lrow < M;
-    const uint8_t *wsrc = wq + (size_t)(wrow_ok ? n0 + lrow : 0) * KB + lhalf * 16;
-    const uint8_t *xsrc = xq + (size_t)(xrow_ok ? m0 + lrow : 0) * KB + lhalf * 16;
-    const bool is_w_scale = tid < BN;
-    const int srow = is_w_scale ? n0 + tid : m0 + (tid - BN);
-    const bool srow_ok = is_w_scale ? srow < N : srow < M;
-    const float *ssrc = (is_w_scale ? wscale : xscale) + (size_t)(srow_ok ? srow : 0) * G;
+    // loader: chunk = 16 code bytes (32 codes); W has BN*4 chunks per step, X BM*4
+    // thread t: W chunks t and t + 512, X chunk t
+    constexpr int WCH = I4_BN * 4, XCH = I4_BM * 4;
+    static_assert(WCH == 2 * I4_THREADS && XCH == I4_THREADS, "loader shape");
     const uint4 z4 = {0u, 0u, 0u, 0u};
+    int lrow[3], lseg[3];
+    bool lok[3];
+    const uint8_t *lsrc[3];
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+        const bool isw = i < 2;
+        const int ch = isw ? tid + i * I4_THREADS : tid;
+        lrow[i] = ch >> 2;
+        lseg[i] = ch & 3;
+        const int grow = (isw ? n0 : m0) + lrow[i];
+        lok[i] = isw ? grow < N : grow < M;
+        lsrc[i] = (isw ? wq : xq) + (size_t)(lok[i] ? grow : 0) * KB + lseg[i] * 16;
+    }
+    // scale loader: threads [0, BN) -> sw row, [BN, BN + BM) -> sx row
+    const bool sc_w = tid < I4_BN, sc_x = tid >= I4_BN && tid < I4_BN + I4_BM;
+    const int srow = sc_w ? n0 + tid : m0 + (tid - I4_BN);
+    const bool sok = (sc_w && srow < N) || (sc_x && srow < M);
+    const float *ssrc = (sc_w ? wscale : xscale) + (size_t)(sok ? srow : 0) * G;
 
-    uint4 rw, rx;
-    float rs;
-    auto gload = [&](int g) {
-        rw = wrow_ok ? *reinterpret_cast<const uint4 *>(wsrc + g * 32) : z4;
-        rx = xrow_ok ? *reinterpret_cast<const uint4 *>(xsrc + g * 32) : z4;
-        rs = srow_ok ? ssrc[g] : 0.0f;
+    uint4 rg[3];
+    float rs[2];
+    auto gload = [&](int st) {
+#pragma unroll
+        for (int i = 0; i < 3; ++i) {
+            const int kb = st * 64 + lseg[i] * 16;          // byte offset of the chunk in the row
+            rg[i] = (lok[i] && kb < KB) ? *reinterpret_cast<const uint4 *>(lsrc[i] + st * 64) : z4;
+        }
+        rs[0] = (sok && 2 * st < G) ? ssrc[2 * st] : 0.0f;
+        rs[1] = (sok && 2 * st + 1 < G) ? ssrc[2 * st + 1] : 0.0f;
     };
     auto lstore = [&](int buf) {
-        *reinterpret_cast<uint4 *>(&sW[buf][lrow * I4_STRIDE + lhalf * 16]) = rw;
-        *reinterpret_cast<uint4 *>(&sX[buf][lrow * I4_STRIDE + lhalf * 16]) = rx;
-        if (is_w_scale) sSw[buf][tid] = rs;
-        else sSx[buf][tid - BN] = rs;
+#pragma unroll
+        for (int i = 0; i < 3; ++i) {
+            uint4 a, b;
+            widen_fp8(rg[i], a, b);
+            uint8_t *dst = (i < 2 ? sm.w[buf] : sm.x[buf]) + lrow[i] * I4_ROWB + lseg[i] * 32;
+            *reinterpret_cast<uint4 *>(dst) = a;
+            *reinterpret_cast<uint4 *>(dst + 16) = b;
+        }
+        if (sc_w) {
+            sm.sw[buf][0][tid] = rs[0] * kTwo18;
+            sm.sw[buf][1][tid] = rs[1] * kTwo18;
+        } else if (sc_x) {
+            sm.sx[buf][0][tid - I4_BN] = rs[0];
+            sm.sx[buf][1][tid - I4_BN] = rs[1];
+        }
     };
 
-    f32x4 acc[TN][TM];
+    f32x16 acc[I4_TN][I4_TM];
 #pragma unroll
-    for (int a = 0; a < TN; ++a)
+    for (int a = 0; a < I4_TN; ++a)
 #pragma unroll
-        for (int b = 0; b < TM; ++b) acc[a][b] = (f32x4){0.f, 0.f, 0.f, 0.f};
+        for (int b = 0; b < I4_TM; ++b)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.0f;
 
-    if (G > 0) {
+    if (steps > 0) {
         gload(0);
         lstore(0);
     }
     __syncthreads();
-    const int l16 = lane & 15, c = lane >> 4;
-    const i32x4 zi = {0, 0, 0, 0};
-    for (int g = 0; g < G; ++g) {
-        const int buf = g & 1;
-        if (g + 1 < G) gload(g + 1);
-        i32x4 aw[TN], bx[TM];
-        float4 sw[TN];
-        float sx[TM];
+    const int l32 = lane & 31, hk = lane >> 5;
+    const f32x16 zero16 = {};
+    for (int st = 0; st < steps; ++st) {
+        const int buf = st & 1;
+        if (st + 1 < steps) gload(st + 1);
 #pragma unroll
-        for (int tn = 0; tn < TN; ++tn) {
-            const int r = wn * WN + tn * 16 + l16;
-            aw[tn] = widen16(*reinterpret_cast<const uint2 *>(&sW[buf][r * I4_STRIDE + 8 * c]));
-            sw[tn] = *reinterpret_cast<const float4 *>(&sSw[buf][wn * WN + tn * 16 + 4 * c]);
-        }
+        for (int q = 0; q < 2; ++q) {
+            if (2 * st + q >= G) break;
+            i32x8 aw[I4_TN], bx[I4_TM];
 #pragma unroll
-        for (int tm = 0; tm < TM; ++tm) {
-            const int r = wm * WM + tm * 16 + l16;
-            bx[tm] = widen16(*reinterpret_cast<const uint2 *>(&sX[buf][r * I4_STRIDE + 8 * c]));
-            sx[tm] = sSx[buf][r];
-        }
+            for (int tn = 0; tn < I4_TN; ++tn) {
+                const uint8_t *p = sm.w[buf] + (wn * I4_WN + tn * 32 + l32) * I4_ROWB + q * 64 + hk * 32;
+                const uint4 u0 = *reinterpret_cast<const uint4 *>(p);
+                const uint4 u1 = *reinterpret_cast<const uint4 *>(p + 16);
+                aw[tn] = (i32x8){(int)u0.x, (int)u0.y, (int)u0.z, (int)u0.w,
+                                 (int)u1.x, (int)u1.y, (int)u1.z, (int)u1.w};
+            }
 #pragma unroll
-        for (int tn = 0; tn < TN; ++tn) {
+            for (int tm = 0; tm < I4_TM; ++tm) {
+                const uint8_t *p = sm.x[buf] + (wm * I4_WM + tm * 32 + l32) * I4_ROWB + q * 64 + hk * 32;
+                const uint4 u0 = *reinterpret_cast<const uint4 *>(p);
+                const uint4 u1 = *reinterpret_cast<const uint4 *>(p + 16);
+                bx[tm] = (i32x8){(int)u0.x, (int)u0.y, (int)u0.z, (int)u0.w,
+                                 (int)u1.x, (int)u1.y, (int)u1.z, (int)u1.w};
+            }
+            float sx[I4_TM];
 #pragma unroll
-            for (int tm = 0; tm < TM; ++tm) {
-                const i32x4 p = __builtin_amdgcn_mfma_i32_16x16x64_i8(aw[tn], bx[tm], zi, 0, 0, 0);
-                acc[tn][tm][0] = __builtin_fmaf((float)p[0], sw[tn].x * sx[tm], acc[tn][tm][0]);
-                acc[tn][tm][1] = __builtin_fmaf((float)p[1], sw[tn].y * sx[tm], acc[tn][tm][1]);
-                acc[tn][tm][2] = __builtin_fmaf((float)p[2], sw[tn].z * sx[tm], acc[tn][tm][2]);
-                acc[tn][tm][3] = __builtin_fmaf((float)p[3], sw[tn].w * sx[tm], acc[tn][tm][3]);
+            for (int tm = 0; tm < I4_TM; ++tm) sx[tm] = sm.sx[buf][q][wm * I4_WM + tm * 32 + l32];
+#pragma unroll
+            for (int tn = 0; tn < I4_TN; ++tn) {
+                float sw[16];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const float4 v =
+                        *reinterpret_cast<const float4 *>(&sm.sw[buf][q][wn * I4_WN + tn * 32 + 8 * j + 4 * hk]);
+                    sw[4 * j] = v.x; sw[4 * j + 1] = v.y; sw[4 * j + 2] = v.z; sw[4 * j + 3] = v.w;
+                }
+#pragma unroll
+                for (int tm = 0; tm < I4_TM; ++tm) {
+                    const f32x16 p = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                        aw[tn], bx[tm], zero16, 0, 0, 0, 127, 0, 127);
+#pragma unroll
+                    for (int i = 0; i < 16; ++i)
+                        acc[tn][tm][i] = __builtin_fmaf(p[i], sw[i] * sx[tm], acc[tn][tm][i]);
+                }
             }
         }
-        if (g + 1 < G) lstore(buf ^ 1);
+        if (st + 1 < steps) lstore(buf ^ 1);
         __syncthreads();
     }
-    epilogue(acc, 1.0f / 256.0f, h, up, bias, M, N, gelu, Y, m0 + wm * WM, n0 + wn * WN, lane);
+
+    // epilogue: low-rank term via v_mfma_f32_32x32x16_bf16 (rank 32 = two k
+    // steps of 16, each with the hi and the lo part of h), then bias, GELU, store
+    const int mb = m0 + wm * I4_WM, nb = n0 + wn * I4_WN;
+    bf16x8 hhi[I4_TM][2], hlo[I4_TM][2];
+#pragma unroll
+    for (int tm = 0; tm < I4_TM; ++tm)
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            float hv[8];
+            load_h8(h, mb + tm * 32 + l32, M, 16 * s + 8 * hk, hv);
+            split_h(hv, hhi[tm][s], hlo[tm][s]);
+        }
+#pragma unroll
+    for (int tn = 0; tn < I4_TN; ++tn) {
+        const int nrow = nb + tn * 32 + l32;
+        bf16x8 ua[2];
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            uint4 uv = {0u, 0u, 0u, 0u};
+            if (nrow < N) uv = *reinterpret_cast<const uint4 *>(up + (size_t)nrow * 32 + 16 * s + 8 * hk);
+            ua[s] = __builtin_bit_cast(bf16x8, uv);
+        }
+#pragma unroll
+        for (int tm = 0; tm < I4_TM; ++tm) {
+            f32x16 lr = {};
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                lr = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ua[s], hhi[tm][s], lr, 0, 0, 0);
+                lr = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ua[s], hlo[tm][s], lr, 0, 0, 0);
+            }
+            const int m = mb + tm * 32 + l32;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                float a4[4] = {acc[tn][tm][4 * j], acc[tn][tm][4 * j + 1], acc[tn][tm][4 * j + 2],
+                               acc[tn][tm][4 * j + 3]};
+                float l4[4] = {lr[4 * j], lr[4 * j + 1], lr[4 * j + 2], lr[4 * j + 3]};
+                finish4(a4, 1.0f, l4, bias, gelu, Y, m, nb + tn * 32 + 8 * j + 4 * hk, M, N);
+            }
+        }
+    }
 }
 
-// ---------------------------------------------------------------- MXFP4
+// ===================================================================== MXFP4
 
+constexpr int MX_BM = 128, MX_BN = 128;        // block tile (m, n)
+constexpr int MX_WM = 64, MX_WN = 64;          // wave tile
+constexpr int MX_TM = MX_WM / 16, MX_TN = MX_WN / 16;
+constexpr int MX_THREADS = 256;
 constexpr int MX_STRIDE = 80;   // LDS bytes per row: 64 code bytes (128 fp4) + 16 pad
 
-__global__ __launch_bounds__(NTHREADS) void w4a4_mxfp4_kernel(
+__global__ __launch_bounds__(MX_THREADS) void w4a4_mxfp4_kernel(
     const uint8_t *__restrict__ xq, const uint8_t *__restrict__ xscale, const float *__restrict__ h,
     const uint8_t *__restrict__ wq, const uint8_t *__restrict__ wscale, const uint16_t *__restrict__ up,
     const uint16_t *__restrict__ bias, int M, int N, int K, int gelu, uint16_t *__restrict__ Y)
 {
-    __shared__ __attribute__((aligned(16))) uint8_t sW[2][BN * MX_STRIDE];
-    __shared__ __attribute__((aligned(16))) uint8_t sX[2][BM * MX_STRIDE];
-    __shared__ uint32_t sEw[2][BN];
-    __shared__ uint32_t sEx[2][BM];
+    __shared__ __attribute__((aligned(16))) uint8_t sW[2][MX_BN * MX_STRIDE];
+    __shared__ __attribute__((aligned(16))) uint8_t sX[2][MX_BM * MX_STRIDE];
+    __shared__ uint32_t sEw[2][MX_BN];
+    __shared__ uint32_t sEx[2][MX_BM];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wn = wave & 1, wm = wave >> 1;
-    const int m0 = blockIdx.x * BM, n0 = blockIdx.y * BN;
+    const int m0 = blockIdx.x * MX_BM, n0 = blockIdx.y * MX_BN;
     const int KB = K >> 1;          // code bytes per row
     const int NB = K >> 5;          // E8M0 scales per row
     const int steps = (K + 127) >> 7;
@@ -262,8 +358,8 @@ __global__ __launch_bounds__(NTHREADS) void w4a4_mxfp4_kernel(
     const bool wrow_ok = n0 + lrow < N, xrow_ok = m0 + lrow < M;
     const uint8_t *wsrc = wq + (size_t)(wrow_ok ? n0 + lrow : 0) * KB;
     const uint8_t *xsrc = xq + (size_t)(xrow_ok ? m0 + lrow : 0) * KB;
-    const bool is_w_scale = tid < BN;
-    const int srow = is_w_scale ? n0 + tid : m0 + (tid - BN);
+    const bool is_w_scale = tid < MX_BN;
+    const int srow = is_w_scale ? n0 + tid : m0 + (tid - MX_BN);
     const bool srow_ok = is_w_scale ? srow < N : srow < M;
     const uint8_t *ssrc = (is_w_scale ? wscale : xscale) + (size_t)(srow_ok ? srow : 0) * NB;
     const uint4 z4 = {0u, 0u, 0u, 0u};
@@ -293,14 +389,14 @@ __global__ __launch_bounds__(NTHREADS) void w4a4_mxfp4_kernel(
             *reinterpret_cast<uint4 *>(&sX[buf][lrow * MX_STRIDE + (lseg + s) * 16]) = rx[s];
         }
         if (is_w_scale) sEw[buf][tid] = rs;
-        else sEx[buf][tid - BN] = rs;
+        else sEx[buf][tid - MX_BN] = rs;
     };
 
-    f32x4 acc[TN][TM];
+    f32x4 acc[MX_TN][MX_TM];
 #pragma unroll
-    for (int a = 0; a < TN; ++a)
+    for (int a = 0; a < MX_TN; ++a)
 #pragma unroll
-        for (int b = 0; b < TM; ++b) acc[a][b] = (f32x4){0.f, 0.f, 0.f, 0.f};
+        for (int b = 0; b < MX_TM; ++b) acc[a][b] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
     if (steps > 0) {
         gload(0);
@@ -311,32 +407,58 @@ __global__ __launch_bounds__(NTHREADS) void w4a4_mxfp4_kernel(
     for (int st = 0; st < steps; ++st) {
         const int buf = st & 1;
         if (st + 1 < steps) gload(st + 1);
-        i32x8 aw[TN], bx[TM];
-        int ew[TN], ex[TM];
+        i32x8 aw[MX_TN], bx[MX_TM];
+        int ew[MX_TN], ex[MX_TM];
 #pragma unroll
-        for (int tn = 0; tn < TN; ++tn) {
-            const int r = wn * WN + tn * 16 + l16;
+        for (int tn = 0; tn < MX_TN; ++tn) {
+            const int r = wn * MX_WN + tn * 16 + l16;
             const uint4 v = *reinterpret_cast<const uint4 *>(&sW[buf][r * MX_STRIDE + 16 * c]);
             aw[tn] = (i32x8){(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
             ew[tn] = (int)((sEw[buf][r] >> (8 * c)) & 0xFFu);
         }
 #pragma unroll
-        for (int tm = 0; tm < TM; ++tm) {
-            const int r = wm * WM + tm * 16 + l16;
+        for (int tm = 0; tm < MX_TM; ++tm) {
+            const int r = wm * MX_WM + tm * 16 + l16;
             const uint4 v = *reinterpret_cast<const uint4 *>(&sX[buf][r * MX_STRIDE + 16 * c]);
             bx[tm] = (i32x8){(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
             ex[tm] = (int)((sEx[buf][r] >> (8 * c)) & 0xFFu);
         }
 #pragma unroll
-        for (int tn = 0; tn < TN; ++tn)
+        for (int tn = 0; tn < MX_TN; ++tn)
 #pragma unroll
-            for (int tm = 0; tm < TM; ++tm)
+            for (int tm = 0; tm < MX_TM; ++tm)
                 acc[tn][tm] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
                     aw[tn], bx[tm], acc[tn][tm], 4, 4, 0, ew[tn], 0, ex[tm]);
         if (st + 1 < steps) lstore(buf ^ 1);
         __syncthreads();
     }
-    epilogue(acc, 1.0f, h, up, bias, M, N, gelu, Y, m0 + wm * WM, n0 + wn * WN, lane);
+
+    // epilogue (16x16 tiles): lane holds token m = mb + tm*16 + (lane&15) and
+    // channels n = nb + tn*16 + 4*(lane>>4) + i
+    const int mb = m0 + wm * MX_WM, nb = n0 + wn * MX_WN;
+    bf16x8 hhi[MX_TM], hlo[MX_TM];
+#pragma unroll
+    for (int tm = 0; tm < MX_TM; ++tm) {
+        float hv[8];
+        load_h8(h, mb + tm * 16 + l16, M, 8 * c, hv);
+        split_h(hv, hhi[tm], hlo[tm]);
+    }
+#pragma unroll
+    for (int tn = 0; tn < MX_TN; ++tn) {
+        const int nrow = nb + tn * 16 + l16;       // A-operand row of `up`
+        uint4 uv = {0u, 0u, 0u, 0u};
+        if (nrow < N) uv = *reinterpret_cast<const uint4 *>(up + (size_t)nrow * 32 + 8 * c);
+        const bf16x8 ua = __builtin_bit_cast(bf16x8, uv);
+#pragma unroll
+        for (int tm = 0; tm < MX_TM; ++tm) {
+            f32x4 lr = {0.f, 0.f, 0.f, 0.f};
+            lr = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ua, hhi[tm], lr, 0, 0, 0);
+            lr = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ua, hlo[tm], lr, 0, 0, 0);
+            float a4[4] = {acc[tn][tm][0], acc[tn][tm][1], acc[tn][tm][2], acc[tn][tm][3]};
+            float l4[4] = {lr[0], lr[1], lr[2], lr[3]};
+            finish4(a4, 1.0f, l4, bias, gelu, Y, mb + tm * 16 + l16, nb + tn * 16 + 4 * c, M, N);
+        }
+    }
 }
 
 }  // namespace
@@ -345,14 +467,16 @@ hipError_t launch_w4a4_linear(const uint8_t *xq, const void *xscale, const float
                               const void *wscale, const uint16_t *up, const uint16_t *bias, int M, int N,
                               int K, svdq_precision prec, svdq_epilogue epi, uint16_t *Y, hipStream_t stream)
 {
-    const dim3 grid((unsigned)((M + BM - 1) / BM), (unsigned)((N + BN - 1) / BN)), block(NTHREADS);
     const int gelu = epi == SVDQ_EPI_GELU_TANH ? 1 : 0;
-    if (prec == SVDQ_INT4)
-        hipLaunchKernelGGL(w4a4_int4_kernel, grid, block, 0, stream, xq, (const float *)xscale, h, wq,
-                           (const float *)wscale, up, bias, M, N, K, gelu, Y);
-    else
-        hipLaunchKernelGGL(w4a4_mxfp4_kernel, grid, block, 0, stream, xq, (const uint8_t *)xscale, h, wq,
-                           (const uint8_t *)wscale, up, bias, M, N, K, gelu, Y);
+    if (prec == SVDQ_INT4) {
+        const int tiles = ((N + I4_BN - 1) / I4_BN) * ((M + I4_BM - 1) / I4_BM);
+        hipLaunchKernelGGL(w4a4_int4_kernel, dim3((unsigned)tiles), dim3(I4_THREADS), 0, stream, xq,
+                           (const float *)xscale, h, wq, (const float *)wscale, up, bias, M, N, K, gelu, Y);
+    } else {
+        const dim3 grid((unsigned)((M + MX_BM - 1) / MX_BM), (unsigned)((N + MX_BN - 1) / MX_BN));
+        hipLaunchKernelGGL(w4a4_mxfp4_kernel, grid, dim3(MX_THREADS), 0, stream, xq, (const uint8_t *)xscale, h,
+                           wq, (const uint8_t *)wscale, up, bias, M, N, K, gelu, Y);
+    }
     return hipGetLastError();
 }
 

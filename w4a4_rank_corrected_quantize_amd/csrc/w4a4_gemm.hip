@@ -108,6 +108,12 @@ __device__ __forceinline__ void finish4(const float *acc, float acc_scale, const
     *reinterpret_cast<uint2 *>(Y + (size_t)m * N + n) = st;
 }
 
+// c ? v : 0, element-wise (a whole-vector select can end up in scratch memory)
+__device__ __forceinline__ uint4 keep_if(bool c, uint4 v)
+{
+    return make_uint4(c ? v.x : 0u, c ? v.y : 0u, c ? v.z : 0u, c ? v.w : 0u);
+}
+
 // Tile order: with 8 XCDs, consecutive workgroup ids land on different XCDs;
 // give each XCD a contiguous range of tiles (n fastest) so the activation tile
 // of a row of tiles stays in that XCD's L2.
@@ -168,58 +174,61 @@ __global__ __launch_bounds__(I4_THREADS) void w4a4_int4_kernel(
     const int KB = K >> 1;                  // code bytes per row
     const int steps = (G + 1) >> 1;
 
-    // loader: chunk = 16 code bytes (32 codes); W has BN*4 chunks per step, X BM*4
-    // thread t: W chunks t and t + 512, X chunk t
+    // Loader: a chunk is 16 code bytes (32 codes) of one row; per step W has
+    // BN*4 chunks and X BM*4.  Thread t moves W chunks t and t + 512 and X
+    // chunk t (all with segment t & 3).  Loads are unconditional: rows past
+    // N / M are clamped to the last row (their outputs are never stored) and
+    // channels past K are zeroed when the chunk is written to LDS, so every
+    // path has the same number of loads in flight.
     constexpr int WCH = I4_BN * 4, XCH = I4_BM * 4;
     static_assert(WCH == 2 * I4_THREADS && XCH == I4_THREADS, "loader shape");
-    const uint4 z4 = {0u, 0u, 0u, 0u};
-    int lrow[3], lseg[3];
-    bool lok[3];
-    const uint8_t *lsrc[3];
-#pragma unroll
-    for (int i = 0; i < 3; ++i) {
-        const bool isw = i < 2;
-        const int ch = isw ? tid + i * I4_THREADS : tid;
-        lrow[i] = ch >> 2;
-        lseg[i] = ch & 3;
-        const int grow = (isw ? n0 : m0) + lrow[i];
-        lok[i] = isw ? grow < N : grow < M;
-        lsrc[i] = (isw ? wq : xq) + (size_t)(lok[i] ? grow : 0) * KB + lseg[i] * 16;
-    }
-    // scale loader: threads [0, BN) -> sw row, [BN, BN + BM) -> sx row
+    const int lseg = tid & 3, lr = tid >> 2;
+    const uint8_t *__restrict__ pw0 = wq + (size_t)min(n0 + lr, N - 1) * KB + lseg * 16;
+    const uint8_t *__restrict__ pw1 = wq + (size_t)min(n0 + lr + I4_BN / 2, N - 1) * KB + lseg * 16;
+    const uint8_t *__restrict__ px0 = xq + (size_t)min(m0 + lr, M - 1) * KB + lseg * 16;
+    // scales: threads [0, BN) -> sw row, [BN, BN + BM) -> sx row, others idle
     const bool sc_w = tid < I4_BN, sc_x = tid >= I4_BN && tid < I4_BN + I4_BM;
-    const int srow = sc_w ? n0 + tid : m0 + (tid - I4_BN);
-    const bool sok = (sc_w && srow < N) || (sc_x && srow < M);
-    const float *ssrc = (sc_w ? wscale : xscale) + (size_t)(sok ? srow : 0) * G;
+    const float *__restrict__ ps = sc_w ? wscale + (size_t)min(n0 + tid, N - 1) * G
+                                        : xscale + (size_t)min(m0 + (sc_x ? tid - I4_BN : 0), M - 1) * G;
+    const uint4 z4 = {0u, 0u, 0u, 0u};
 
-    uint4 rg[3];
-    float rs[2];
-    auto gload = [&](int st) {
-#pragma unroll
-        for (int i = 0; i < 3; ++i) {
-            const int kb = st * 64 + lseg[i] * 16;          // byte offset of the chunk in the row
-            rg[i] = (lok[i] && kb < KB) ? *reinterpret_cast<const uint4 *>(lsrc[i] + st * 64) : z4;
-        }
-        rs[0] = (sok && 2 * st < G) ? ssrc[2 * st] : 0.0f;
-        rs[1] = (sok && 2 * st + 1 < G) ? ssrc[2 * st + 1] : 0.0f;
-    };
-    auto lstore = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < 3; ++i) {
-            uint4 a, b;
-            widen_fp8(rg[i], a, b);
-            uint8_t *dst = (i < 2 ? sm.w[buf] : sm.x[buf]) + lrow[i] * I4_ROWB + lseg[i] * 32;
-            *reinterpret_cast<uint4 *>(dst) = a;
-            *reinterpret_cast<uint4 *>(dst + 16) = b;
-        }
-        if (sc_w) {
-            sm.sw[buf][0][tid] = rs[0] * kTwo18;
-            sm.sw[buf][1][tid] = rs[1] * kTwo18;
-        } else if (sc_x) {
-            sm.sx[buf][0][tid - I4_BN] = rs[0];
-            sm.sx[buf][1][tid - I4_BN] = rs[1];
-        }
-    };
+    uint4 rg0, rg1, rg2;
+    float rs0, rs1;
+#define I4_GLOAD(st)                                                                   \
+    do {                                                                               \
+        const int koff_ = ((st) * 64 + lseg * 16 < KB) ? (st) * 64 : 0;                \
+        rg0 = *reinterpret_cast<const uint4 *>(pw0 + koff_);                           \
+        rg1 = *reinterpret_cast<const uint4 *>(pw1 + koff_);                           \
+        rg2 = *reinterpret_cast<const uint4 *>(px0 + koff_);                           \
+        rs0 = ps[min(2 * (st), G - 1)];                                                \
+        rs1 = ps[min(2 * (st) + 1, G - 1)];                                            \
+    } while (0)
+#define I4_LSTORE(st, buf)                                                             \
+    do {                                                                               \
+        const bool kv_ = (st) * 64 + lseg * 16 < KB;                                   \
+        uint4 a_, b_;                                                                  \
+        widen_fp8(keep_if(kv_, rg0), a_, b_);                                             \
+        uint8_t *d_ = sm.w[buf] + lr * I4_ROWB + lseg * 32;                            \
+        *reinterpret_cast<uint4 *>(d_) = a_;                                           \
+        *reinterpret_cast<uint4 *>(d_ + 16) = b_;                                      \
+        widen_fp8(keep_if(kv_, rg1), a_, b_);                                             \
+        d_ = sm.w[buf] + (lr + I4_BN / 2) * I4_ROWB + lseg * 32;                       \
+        *reinterpret_cast<uint4 *>(d_) = a_;                                           \
+        *reinterpret_cast<uint4 *>(d_ + 16) = b_;                                      \
+        widen_fp8(keep_if(kv_, rg2), a_, b_);                                             \
+        d_ = sm.x[buf] + lr * I4_ROWB + lseg * 32;                                     \
+        *reinterpret_cast<uint4 *>(d_) = a_;                                           \
+        *reinterpret_cast<uint4 *>(d_ + 16) = b_;                                      \
+        const float s0_ = 2 * (st) < G ? rs0 : 0.0f;                                   \
+        const float s1_ = 2 * (st) + 1 < G ? rs1 : 0.0f;                               \
+        if (sc_w) {                                                                    \
+            sm.sw[buf][0][tid] = s0_ * kTwo18;                                         \
+            sm.sw[buf][1][tid] = s1_ * kTwo18;                                         \
+        } else if (sc_x) {                                                             \
+            sm.sx[buf][0][tid - I4_BN] = s0_;                                          \
+            sm.sx[buf][1][tid - I4_BN] = s1_;                                          \
+        }                                                                              \
+    } while (0)
 
     f32x16 acc[I4_TN][I4_TM];
 #pragma unroll
@@ -230,15 +239,15 @@ __global__ __launch_bounds__(I4_THREADS) void w4a4_int4_kernel(
             for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.0f;
 
     if (steps > 0) {
-        gload(0);
-        lstore(0);
+        I4_GLOAD(0);
+        I4_LSTORE(0, 0);
     }
     __syncthreads();
     const int l32 = lane & 31, hk = lane >> 5;
     const f32x16 zero16 = {};
     for (int st = 0; st < steps; ++st) {
         const int buf = st & 1;
-        if (st + 1 < steps) gload(st + 1);
+        if (st + 1 < steps) I4_GLOAD(st + 1);
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
             if (2 * st + q >= G) break;
@@ -281,9 +290,11 @@ __global__ __launch_bounds__(I4_THREADS) void w4a4_int4_kernel(
                 }
             }
         }
-        if (st + 1 < steps) lstore(buf ^ 1);
+        if (st + 1 < steps) I4_LSTORE(st + 1, buf ^ 1);
         __syncthreads();
     }
+#undef I4_GLOAD
+#undef I4_LSTORE
 
     // epilogue: low-rank term via v_mfma_f32_32x32x16_bf16 (rank 32 = two k
     // steps of 16, each with the hi and the lo part of h), then bias, GELU, store
@@ -352,45 +363,48 @@ __global__ __launch_bounds__(MX_THREADS) void w4a4_mxfp4_kernel(
     const int NB = K >> 5;          // E8M0 scales per row
     const int steps = (K + 127) >> 7;
 
-    // loader: thread t moves 2 x 16 code bytes of row t/2 for each tile, and
-    // the 4 scale bytes of one row
-    const int lrow = tid >> 1, lseg = (tid & 1) * 2;   // segments lseg, lseg+1 of 4
-    const bool wrow_ok = n0 + lrow < N, xrow_ok = m0 + lrow < M;
-    const uint8_t *wsrc = wq + (size_t)(wrow_ok ? n0 + lrow : 0) * KB;
-    const uint8_t *xsrc = xq + (size_t)(xrow_ok ? m0 + lrow : 0) * KB;
+    // Loader: thread t moves the 32-code segments lseg, lseg+1 (of 4 per
+    // step) of row t/2 of both tiles, and the 4 E8M0 bytes of one row.  Loads
+    // are unconditional (rows clamped, channels past K zeroed at the LDS
+    // store), so every path keeps the same number of loads in flight.
+    const int lrow = tid >> 1, lseg = (tid & 1) * 2;
+    const uint8_t *__restrict__ wsrc = wq + (size_t)min(n0 + lrow, N - 1) * KB;
+    const uint8_t *__restrict__ xsrc = xq + (size_t)min(m0 + lrow, M - 1) * KB;
     const bool is_w_scale = tid < MX_BN;
-    const int srow = is_w_scale ? n0 + tid : m0 + (tid - MX_BN);
-    const bool srow_ok = is_w_scale ? srow < N : srow < M;
-    const uint8_t *ssrc = (is_w_scale ? wscale : xscale) + (size_t)(srow_ok ? srow : 0) * NB;
+    const uint8_t *__restrict__ ssrc = is_w_scale ? wscale + (size_t)min(n0 + tid, N - 1) * NB
+                                                  : xscale + (size_t)min(m0 + (tid - MX_BN), M - 1) * NB;
+    const bool aligned_scales = (NB & 3) == 0;
     const uint4 z4 = {0u, 0u, 0u, 0u};
 
-    uint4 rw[2], rx[2];
+    uint4 rw0, rw1, rx0, rx1;
     uint32_t rs;
-    auto gload = [&](int st) {
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            const int blk = st * 4 + lseg + s;          // 32-wide block index
-            const bool kv = blk < NB;
-            rw[s] = (wrow_ok && kv) ? *reinterpret_cast<const uint4 *>(wsrc + blk * 16) : z4;
-            rx[s] = (xrow_ok && kv) ? *reinterpret_cast<const uint4 *>(xsrc + blk * 16) : z4;
-        }
-        rs = 0;
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            const int blk = st * 4 + b;
-            const uint32_t e = (srow_ok && blk < NB) ? (uint32_t)ssrc[blk] : 127u;
-            rs |= e << (8 * b);
-        }
-    };
-    auto lstore = [&](int buf) {
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            *reinterpret_cast<uint4 *>(&sW[buf][lrow * MX_STRIDE + (lseg + s) * 16]) = rw[s];
-            *reinterpret_cast<uint4 *>(&sX[buf][lrow * MX_STRIDE + (lseg + s) * 16]) = rx[s];
-        }
-        if (is_w_scale) sEw[buf][tid] = rs;
-        else sEx[buf][tid - MX_BN] = rs;
-    };
+#define MX_GLOAD(st)                                                                       \
+    do {                                                                                   \
+        const int b0_ = min((st) * 4 + lseg, NB - 1), b1_ = min((st) * 4 + lseg + 1, NB - 1); \
+        rw0 = *reinterpret_cast<const uint4 *>(wsrc + b0_ * 16);                           \
+        rw1 = *reinterpret_cast<const uint4 *>(wsrc + b1_ * 16);                           \
+        rx0 = *reinterpret_cast<const uint4 *>(xsrc + b0_ * 16);                           \
+        rx1 = *reinterpret_cast<const uint4 *>(xsrc + b1_ * 16);                           \
+        if (aligned_scales) {                                                              \
+            rs = *reinterpret_cast<const uint32_t *>(ssrc + min((st) * 4, NB - 4));        \
+        } else {                                                                           \
+            rs = 0;                                                                        \
+            for (int b_ = 0; b_ < 4; ++b_)                                                 \
+                rs |= (uint32_t)ssrc[min((st) * 4 + b_, NB - 1)] << (8 * b_);              \
+        }                                                                                  \
+    } while (0)
+#define MX_LSTORE(st, buf)                                                                 \
+    do {                                                                                   \
+        const bool k0_ = (st) * 4 + lseg < NB, k1_ = (st) * 4 + lseg + 1 < NB;             \
+        uint8_t *dw_ = &sW[buf][lrow * MX_STRIDE + lseg * 16];                             \
+        uint8_t *dx_ = &sX[buf][lrow * MX_STRIDE + lseg * 16];                             \
+        *reinterpret_cast<uint4 *>(dw_) = keep_if(k0_, rw0);                                \
+        *reinterpret_cast<uint4 *>(dw_ + 16) = keep_if(k1_, rw1);                            \
+        *reinterpret_cast<uint4 *>(dx_) = keep_if(k0_, rx0);                                \
+        *reinterpret_cast<uint4 *>(dx_ + 16) = keep_if(k1_, rx1);                            \
+        if (is_w_scale) sEw[buf][tid] = rs;                                                \
+        else sEx[buf][tid - MX_BN] = rs;                                                   \
+    } while (0)
 
     f32x4 acc[MX_TN][MX_TM];
 #pragma unroll
@@ -399,14 +413,14 @@ __global__ __launch_bounds__(MX_THREADS) void w4a4_mxfp4_kernel(
         for (int b = 0; b < MX_TM; ++b) acc[a][b] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
     if (steps > 0) {
-        gload(0);
-        lstore(0);
+        MX_GLOAD(0);
+        MX_LSTORE(0, 0);
     }
     __syncthreads();
     const int l16 = lane & 15, c = lane >> 4;
     for (int st = 0; st < steps; ++st) {
         const int buf = st & 1;
-        if (st + 1 < steps) gload(st + 1);
+        if (st + 1 < steps) MX_GLOAD(st + 1);
         i32x8 aw[MX_TN], bx[MX_TM];
         int ew[MX_TN], ex[MX_TM];
 #pragma unroll
@@ -429,9 +443,11 @@ __global__ __launch_bounds__(MX_THREADS) void w4a4_mxfp4_kernel(
             for (int tm = 0; tm < MX_TM; ++tm)
                 acc[tn][tm] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
                     aw[tn], bx[tm], acc[tn][tm], 4, 4, 0, ew[tn], 0, ex[tm]);
-        if (st + 1 < steps) lstore(buf ^ 1);
+        if (st + 1 < steps) MX_LSTORE(st + 1, buf ^ 1);
         __syncthreads();
     }
+#undef MX_GLOAD
+#undef MX_LSTORE
 
     // epilogue (16x16 tiles): lane holds token m = mb + tm*16 + (lane&15) and
     // channels n = nb + tn*16 + 4*(lane>>4) + i

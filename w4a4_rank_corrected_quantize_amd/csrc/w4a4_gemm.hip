@@ -41,18 +41,26 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
 __device__ __forceinline__ float bf16_to_f32(uint32_t b) { return bits_f32(b << 16); }
 
-__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f)
+// two fp32 -> two bf16 (round to nearest even), packed low | high << 16
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
 {
-    uint32_t u = f32_bits(f);
-    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+    const f32x2 v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
+// GELU, tanh form: 0.5 y (1 + tanh(u)) = y / (1 + exp(-2u)),
+// u = sqrt(2/pi) (y + 0.044715 y^3); exp via the hardware exp2.
 __device__ __forceinline__ float gelu_tanh(float y)
 {
-    const float k0 = 0.7978845608028654f;   // sqrt(2/pi)
-    return 0.5f * y * (1.0f + tanhf(k0 * (y + 0.044715f * y * y * y)));
+    const float k1 = -2.302208198f;      // -2 sqrt(2/pi) log2(e)
+    const float k3 = -0.102943836f;      // -2 sqrt(2/pi) 0.044715 log2(e)
+    const float t = y * __builtin_fmaf(k3, y * y, k1);
+    return y * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(t));
 }
 
 // 8 fp32 values of h -> bf16 hi and lo parts (hi = bf16(h), lo = bf16(h - hi)).
@@ -61,11 +69,8 @@ __device__ __forceinline__ void split_h(const float *hv, bf16x8 &hi8, bf16x8 &lo
     uint32_t hi[4], lo[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const uint32_t h0 = f32_to_bf16_rne(hv[2 * i]), h1 = f32_to_bf16_rne(hv[2 * i + 1]);
-        const uint32_t l0 = f32_to_bf16_rne(hv[2 * i] - bf16_to_f32(h0));
-        const uint32_t l1 = f32_to_bf16_rne(hv[2 * i + 1] - bf16_to_f32(h1));
-        hi[i] = h0 | (h1 << 16);
-        lo[i] = l0 | (l1 << 16);
+        hi[i] = pack_bf16x2(hv[2 * i], hv[2 * i + 1]);
+        lo[i] = pack_bf16x2(hv[2 * i] - bf16_to_f32(hi[i] & 0xFFFFu), hv[2 * i + 1] - bf16_to_f32(hi[i] >> 16));
     }
     hi8 = __builtin_bit_cast(bf16x8, (uint4){hi[0], hi[1], hi[2], hi[3]});
     lo8 = __builtin_bit_cast(bf16x8, (uint4){lo[0], lo[1], lo[2], lo[3]});
@@ -84,28 +89,48 @@ __device__ __forceinline__ void load_h8(const float *__restrict__ h, int m, int 
     }
 }
 
-// y = acc * acc_scale + lr + b (+ GELU) for 4 consecutive channels n..n+3 of
-// token m, stored as bf16.
-__device__ __forceinline__ void finish4(const float *acc, float acc_scale, const float *lr,
-                                        const uint16_t *__restrict__ bias, int gelu, uint16_t *__restrict__ Y,
-                                        int m, int n, int M, int N)
+// Bias of 4 consecutive channels n..n+3 (zero when there is no bias or n >= N).
+__device__ __forceinline__ float4 bias4(const uint16_t *__restrict__ bias, int n, int N)
 {
-    if (m >= M || n >= N) return;
-    float bv[4] = {0.f, 0.f, 0.f, 0.f};
-    if (bias) {
-        const uint2 b2 = *reinterpret_cast<const uint2 *>(bias + n);
-        bv[0] = bf16_to_f32(b2.x & 0xFFFFu); bv[1] = bf16_to_f32(b2.x >> 16);
-        bv[2] = bf16_to_f32(b2.y & 0xFFFFu); bv[3] = bf16_to_f32(b2.y >> 16);
+    if (!bias || n >= N) return make_float4(0.f, 0.f, 0.f, 0.f);
+    const uint2 b2 = *reinterpret_cast<const uint2 *>(bias + n);
+    return make_float4(bf16_to_f32(b2.x & 0xFFFFu), bf16_to_f32(b2.x >> 16), bf16_to_f32(b2.y & 0xFFFFu),
+                       bf16_to_f32(b2.y >> 16));
+}
+
+// y = acc + lr + b (+ GELU) for 4 consecutive channels, packed as 4 bf16.
+__device__ __forceinline__ uint2 finish4(const float *acc, const float *lr, float4 b, int gelu)
+{
+    float y0 = acc[0] + lr[0] + b.x, y1 = acc[1] + lr[1] + b.y;
+    float y2 = acc[2] + lr[2] + b.z, y3 = acc[3] + lr[3] + b.w;
+    if (gelu) {
+        y0 = gelu_tanh(y0); y1 = gelu_tanh(y1); y2 = gelu_tanh(y2); y3 = gelu_tanh(y3);
     }
-    uint32_t o[4];
+    return make_uint2(pack_bf16x2(y0, y1), pack_bf16x2(y2, y3));
+}
+
+// Output staging: each wave writes its 64 x 64 bf16 tile into its own LDS
+// area (row stride 136 bytes, conflict-free for 8-byte writes from 32 rows),
+// then stores it as 64 full 128-byte row segments.
+constexpr int OUT_STRIDE = 136;
+constexpr int OUT_TILE_BYTES = 64 * OUT_STRIDE;
+
+__device__ __forceinline__ void stage4(uint8_t *tile, int ml, int nl, uint2 v)
+{
+    *reinterpret_cast<uint2 *>(tile + ml * OUT_STRIDE + nl * 2) = v;
+}
+
+__device__ __forceinline__ void flush_tile(const uint8_t *tile, uint16_t *__restrict__ Y, int mb, int nb, int M,
+                                           int N, int lane)
+{
+    const int seg = lane & 7;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        float y = acc[i] * acc_scale + lr[i] + bv[i];
-        if (gelu) y = gelu_tanh(y);
-        o[i] = f32_to_bf16_rne(y);
+    for (int it = 0; it < 8; ++it) {
+        const int r = (lane >> 3) + 8 * it;
+        const uint4 v = *reinterpret_cast<const uint4 *>(tile + r * OUT_STRIDE + seg * 16);
+        const int m = mb + r, n = nb + seg * 8;
+        if (m < M && n < N) *reinterpret_cast<uint4 *>(Y + (size_t)m * N + n) = v;
     }
-    const uint2 st = {o[0] | (o[1] << 16), o[2] | (o[3] << 16)};
-    *reinterpret_cast<uint2 *>(Y + (size_t)m * N + n) = st;
 }
 
 // c ? v : 0, element-wise (a whole-vector select can end up in scratch memory)
@@ -114,13 +139,23 @@ __device__ __forceinline__ uint4 keep_if(bool c, uint4 v)
     return make_uint4(c ? v.x : 0u, c ? v.y : 0u, c ? v.z : 0u, c ? v.w : 0u);
 }
 
-// Tile order: with 8 XCDs, consecutive workgroup ids land on different XCDs;
-// give each XCD a contiguous range of tiles (n fastest) so the activation tile
-// of a row of tiles stays in that XCD's L2.
-__device__ __forceinline__ int xcd_tile(int b, int T)
+// Tile order.  Consecutive workgroup ids land on different XCDs (8 on
+// MI355X), each with its own L2: first give every XCD a contiguous range of
+// tile indices, then walk the tiles in groups of GN weight tiles with the
+// token tiles fastest, so an XCD keeps ~GN weight tiles in its L2 while it
+// sweeps the activation tiles.
+constexpr int TILE_GROUP_N = 6;
+
+__device__ __forceinline__ void tile_coords(int b, int tiles_n, int tiles_m, int &tn, int &tm)
 {
-    if (T % 8 != 0) return b;
-    return (b & 7) * (T >> 3) + (b >> 3);
+    const int T = tiles_n * tiles_m;
+    const int t = (T % 8 == 0) ? (b & 7) * (T >> 3) + (b >> 3) : b;
+    const int per_group = TILE_GROUP_N * tiles_m;
+    const int first_n = (t / per_group) * TILE_GROUP_N;
+    const int gsize = min(tiles_n - first_n, TILE_GROUP_N);
+    const int in = t % per_group;
+    tn = first_n + in % gsize;
+    tm = in / gsize;
 }
 
 // ================================================================ INT4 (fp8 path)
@@ -168,8 +203,9 @@ __global__ __launch_bounds__(I4_THREADS) void w4a4_int4_kernel(
     const int wn = wave % I4_WAVES_N, wm = wave / I4_WAVES_N;
     const int tiles_n = (N + I4_BN - 1) / I4_BN;
     const int tiles_m = (M + I4_BM - 1) / I4_BM;
-    const int t = xcd_tile(blockIdx.x, tiles_n * tiles_m);
-    const int n0 = (t % tiles_n) * I4_BN, m0 = (t / tiles_n) * I4_BM;
+    int tn_, tm_;
+    tile_coords(blockIdx.x, tiles_n, tiles_m, tn_, tm_);
+    const int n0 = tn_ * I4_BN, m0 = tm_ * I4_BM;
     const int G = K >> 6;
     const int KB = K >> 1;                  // code bytes per row
     const int steps = (G + 1) >> 1;
@@ -192,35 +228,37 @@ __global__ __launch_bounds__(I4_THREADS) void w4a4_int4_kernel(
                                         : xscale + (size_t)min(m0 + (sc_x ? tid - I4_BN : 0), M - 1) * G;
     const uint4 z4 = {0u, 0u, 0u, 0u};
 
-    uint4 rg0, rg1, rg2;
-    float rs0, rs1;
-#define I4_GLOAD(st)                                                                   \
+    // Two register sets: the global loads of step st + 2 are issued at the
+    // start of step st and written to LDS at the end of step st + 1.
+    uint4 rgA0, rgA1, rgA2, rgB0, rgB1, rgB2;
+    float rsA0, rsA1, rsB0, rsB1;
+#define I4_GLOAD(st, R)                                                                \
     do {                                                                               \
         const int koff_ = ((st) * 64 + lseg * 16 < KB) ? (st) * 64 : 0;                \
-        rg0 = *reinterpret_cast<const uint4 *>(pw0 + koff_);                           \
-        rg1 = *reinterpret_cast<const uint4 *>(pw1 + koff_);                           \
-        rg2 = *reinterpret_cast<const uint4 *>(px0 + koff_);                           \
-        rs0 = ps[min(2 * (st), G - 1)];                                                \
-        rs1 = ps[min(2 * (st) + 1, G - 1)];                                            \
+        rg##R##0 = *reinterpret_cast<const uint4 *>(pw0 + koff_);                      \
+        rg##R##1 = *reinterpret_cast<const uint4 *>(pw1 + koff_);                      \
+        rg##R##2 = *reinterpret_cast<const uint4 *>(px0 + koff_);                      \
+        rs##R##0 = ps[min(2 * (st), G - 1)];                                           \
+        rs##R##1 = ps[min(2 * (st) + 1, G - 1)];                                       \
     } while (0)
-#define I4_LSTORE(st, buf)                                                             \
+#define I4_LSTORE(st, buf, R)                                                          \
     do {                                                                               \
         const bool kv_ = (st) * 64 + lseg * 16 < KB;                                   \
         uint4 a_, b_;                                                                  \
-        widen_fp8(keep_if(kv_, rg0), a_, b_);                                             \
+        widen_fp8(keep_if(kv_, rg##R##0), a_, b_);                                     \
         uint8_t *d_ = sm.w[buf] + lr * I4_ROWB + lseg * 32;                            \
         *reinterpret_cast<uint4 *>(d_) = a_;                                           \
         *reinterpret_cast<uint4 *>(d_ + 16) = b_;                                      \
-        widen_fp8(keep_if(kv_, rg1), a_, b_);                                             \
+        widen_fp8(keep_if(kv_, rg##R##1), a_, b_);                                     \
         d_ = sm.w[buf] + (lr + I4_BN / 2) * I4_ROWB + lseg * 32;                       \
         *reinterpret_cast<uint4 *>(d_) = a_;                                           \
         *reinterpret_cast<uint4 *>(d_ + 16) = b_;                                      \
-        widen_fp8(keep_if(kv_, rg2), a_, b_);                                             \
+        widen_fp8(keep_if(kv_, rg##R##2), a_, b_);                                     \
         d_ = sm.x[buf] + lr * I4_ROWB + lseg * 32;                                     \
         *reinterpret_cast<uint4 *>(d_) = a_;                                           \
         *reinterpret_cast<uint4 *>(d_ + 16) = b_;                                      \
-        const float s0_ = 2 * (st) < G ? rs0 : 0.0f;                                   \
-        const float s1_ = 2 * (st) + 1 < G ? rs1 : 0.0f;                               \
+        const float s0_ = 2 * (st) < G ? rs##R##0 : 0.0f;                              \
+        const float s1_ = 2 * (st) + 1 < G ? rs##R##1 : 0.0f;                          \
         if (sc_w) {                                                                    \
             sm.sw[buf][0][tid] = s0_ * kTwo18;                                         \
             sm.sw[buf][1][tid] = s1_ * kTwo18;                                         \
@@ -238,59 +276,71 @@ __global__ __launch_bounds__(I4_THREADS) void w4a4_int4_kernel(
 #pragma unroll
             for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.0f;
 
-    if (steps > 0) {
-        I4_GLOAD(0);
-        I4_LSTORE(0, 0);
-    }
-    __syncthreads();
     const int l32 = lane & 31, hk = lane >> 5;
     const f32x16 zero16 = {};
-    for (int st = 0; st < steps; ++st) {
-        const int buf = st & 1;
-        if (st + 1 < steps) I4_GLOAD(st + 1);
+    // compute of one step from LDS buffer `buf` (groups 2st, 2st+1)
+    auto compute_step = [&](int st, int buf) {
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            if (2 * st + q >= G) break;
-            i32x8 aw[I4_TN], bx[I4_TM];
+            for (int q = 0; q < 2; ++q) {
+                if (2 * st + q >= G) break;
+                i32x8 aw[I4_TN], bx[I4_TM];
 #pragma unroll
-            for (int tn = 0; tn < I4_TN; ++tn) {
-                const uint8_t *p = sm.w[buf] + (wn * I4_WN + tn * 32 + l32) * I4_ROWB + q * 64 + hk * 32;
-                const uint4 u0 = *reinterpret_cast<const uint4 *>(p);
-                const uint4 u1 = *reinterpret_cast<const uint4 *>(p + 16);
-                aw[tn] = (i32x8){(int)u0.x, (int)u0.y, (int)u0.z, (int)u0.w,
-                                 (int)u1.x, (int)u1.y, (int)u1.z, (int)u1.w};
-            }
-#pragma unroll
-            for (int tm = 0; tm < I4_TM; ++tm) {
-                const uint8_t *p = sm.x[buf] + (wm * I4_WM + tm * 32 + l32) * I4_ROWB + q * 64 + hk * 32;
-                const uint4 u0 = *reinterpret_cast<const uint4 *>(p);
-                const uint4 u1 = *reinterpret_cast<const uint4 *>(p + 16);
-                bx[tm] = (i32x8){(int)u0.x, (int)u0.y, (int)u0.z, (int)u0.w,
-                                 (int)u1.x, (int)u1.y, (int)u1.z, (int)u1.w};
-            }
-            float sx[I4_TM];
-#pragma unroll
-            for (int tm = 0; tm < I4_TM; ++tm) sx[tm] = sm.sx[buf][q][wm * I4_WM + tm * 32 + l32];
-#pragma unroll
-            for (int tn = 0; tn < I4_TN; ++tn) {
-                float sw[16];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const float4 v =
-                        *reinterpret_cast<const float4 *>(&sm.sw[buf][q][wn * I4_WN + tn * 32 + 8 * j + 4 * hk]);
-                    sw[4 * j] = v.x; sw[4 * j + 1] = v.y; sw[4 * j + 2] = v.z; sw[4 * j + 3] = v.w;
+                for (int tn = 0; tn < I4_TN; ++tn) {
+                    const uint8_t *p = sm.w[buf] + (wn * I4_WN + tn * 32 + l32) * I4_ROWB + q * 64 + hk * 32;
+                    const uint4 u0 = *reinterpret_cast<const uint4 *>(p);
+                    const uint4 u1 = *reinterpret_cast<const uint4 *>(p + 16);
+                    aw[tn] = (i32x8){(int)u0.x, (int)u0.y, (int)u0.z, (int)u0.w,
+                                     (int)u1.x, (int)u1.y, (int)u1.z, (int)u1.w};
                 }
 #pragma unroll
                 for (int tm = 0; tm < I4_TM; ++tm) {
-                    const f32x16 p = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                        aw[tn], bx[tm], zero16, 0, 0, 0, 127, 0, 127);
+                    const uint8_t *p = sm.x[buf] + (wm * I4_WM + tm * 32 + l32) * I4_ROWB + q * 64 + hk * 32;
+                    const uint4 u0 = *reinterpret_cast<const uint4 *>(p);
+                    const uint4 u1 = *reinterpret_cast<const uint4 *>(p + 16);
+                    bx[tm] = (i32x8){(int)u0.x, (int)u0.y, (int)u0.z, (int)u0.w,
+                                     (int)u1.x, (int)u1.y, (int)u1.z, (int)u1.w};
+                }
+                float sx[I4_TM];
 #pragma unroll
-                    for (int i = 0; i < 16; ++i)
-                        acc[tn][tm][i] = __builtin_fmaf(p[i], sw[i] * sx[tm], acc[tn][tm][i]);
+                for (int tm = 0; tm < I4_TM; ++tm) sx[tm] = sm.sx[buf][q][wm * I4_WM + tm * 32 + l32];
+#pragma unroll
+                for (int tn = 0; tn < I4_TN; ++tn) {
+                    float sw[16];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const float4 v =
+                            *reinterpret_cast<const float4 *>(&sm.sw[buf][q][wn * I4_WN + tn * 32 + 8 * j + 4 * hk]);
+                        sw[4 * j] = v.x; sw[4 * j + 1] = v.y; sw[4 * j + 2] = v.z; sw[4 * j + 3] = v.w;
+                    }
+#pragma unroll
+                    for (int tm = 0; tm < I4_TM; ++tm) {
+                        const f32x16 p = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                            aw[tn], bx[tm], zero16, 0, 0, 0, 127, 0, 127);
+#pragma unroll
+                        for (int i = 0; i < 16; ++i)
+                            acc[tn][tm][i] = __builtin_fmaf(p[i], sw[i] * sx[tm], acc[tn][tm][i]);
+                    }
                 }
             }
-        }
-        if (st + 1 < steps) I4_LSTORE(st + 1, buf ^ 1);
+    };
+
+    if (steps > 0) {
+        I4_GLOAD(0, A);
+        I4_LSTORE(0, 0, A);
+        I4_GLOAD(min(1, steps - 1), B);
+    }
+    __syncthreads();
+    for (int st = 0; st < steps; st += 2) {
+        // even step: LDS buffer 0, registers A are free for step st + 2
+        I4_GLOAD(min(st + 2, steps - 1), A);     // unconditional: same load count on every path
+        compute_step(st, 0);
+        if (st + 1 < steps) I4_LSTORE(st + 1, 1, B);
+        __syncthreads();
+        if (st + 1 >= steps) break;
+        // odd step: LDS buffer 1, registers B are free for step st + 3
+        I4_GLOAD(min(st + 3, steps - 1), B);
+        compute_step(st + 1, 1);
+        if (st + 2 < steps) I4_LSTORE(st + 2, 0, A);
         __syncthreads();
     }
 #undef I4_GLOAD
@@ -308,6 +358,8 @@ __global__ __launch_bounds__(I4_THREADS) void w4a4_int4_kernel(
             load_h8(h, mb + tm * 32 + l32, M, 16 * s + 8 * hk, hv);
             split_h(hv, hhi[tm][s], hlo[tm][s]);
         }
+    uint8_t *tile = reinterpret_cast<uint8_t *>(&sm) + wave * OUT_TILE_BYTES;
+    static_assert(8 * OUT_TILE_BYTES <= sizeof(I4Smem), "output staging fits in LDS");
 #pragma unroll
     for (int tn = 0; tn < I4_TN; ++tn) {
         const int nrow = nb + tn * 32 + l32;
@@ -318,6 +370,9 @@ __global__ __launch_bounds__(I4_THREADS) void w4a4_int4_kernel(
             if (nrow < N) uv = *reinterpret_cast<const uint4 *>(up + (size_t)nrow * 32 + 16 * s + 8 * hk);
             ua[s] = __builtin_bit_cast(bf16x8, uv);
         }
+        float4 bv[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) bv[j] = bias4(bias, nb + tn * 32 + 8 * j + 4 * hk, N);
 #pragma unroll
         for (int tm = 0; tm < I4_TM; ++tm) {
             f32x16 lr = {};
@@ -326,16 +381,17 @@ __global__ __launch_bounds__(I4_THREADS) void w4a4_int4_kernel(
                 lr = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ua[s], hhi[tm][s], lr, 0, 0, 0);
                 lr = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ua[s], hlo[tm][s], lr, 0, 0, 0);
             }
-            const int m = mb + tm * 32 + l32;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 float a4[4] = {acc[tn][tm][4 * j], acc[tn][tm][4 * j + 1], acc[tn][tm][4 * j + 2],
                                acc[tn][tm][4 * j + 3]};
                 float l4[4] = {lr[4 * j], lr[4 * j + 1], lr[4 * j + 2], lr[4 * j + 3]};
-                finish4(a4, 1.0f, l4, bias, gelu, Y, m, nb + tn * 32 + 8 * j + 4 * hk, M, N);
+                stage4(tile, tm * 32 + l32, tn * 32 + 8 * j + 4 * hk, finish4(a4, l4, bv[j], gelu));
             }
         }
     }
+    __syncthreads();
+    flush_tile(tile, Y, mb, nb, M, N, lane);
 }
 
 // ===================================================================== MXFP4
@@ -344,64 +400,80 @@ constexpr int MX_BM = 128, MX_BN = 128;        // block tile (m, n)
 constexpr int MX_WM = 64, MX_WN = 64;          // wave tile
 constexpr int MX_TM = MX_WM / 16, MX_TN = MX_WN / 16;
 constexpr int MX_THREADS = 256;
-constexpr int MX_STRIDE = 80;   // LDS bytes per row: 64 code bytes (128 fp4) + 16 pad
+constexpr int MX_STRIDE = 64;   // LDS bytes per row: 64 code bytes (128 fp4), segments swizzled
+
+// 16-byte segment s of LDS row r lives at segment s ^ ((r >> 1) & 3): the
+// loader's 4 consecutive segments of 2 rows and the fragment reads of 8
+// rows at one segment both hit 8 distinct 4-bank groups.
+__device__ __forceinline__ int mx_seg(int r, int s) { return s ^ ((r >> 1) & 3); }
+
+struct __attribute__((aligned(16))) MXSmem {
+    uint8_t w[2][MX_BN * MX_STRIDE];
+    uint8_t x[2][MX_BM * MX_STRIDE];
+    uint32_t ew[2][MX_BN];
+    uint32_t ex[2][MX_BM];
+};
 
 __global__ __launch_bounds__(MX_THREADS) void w4a4_mxfp4_kernel(
     const uint8_t *__restrict__ xq, const uint8_t *__restrict__ xscale, const float *__restrict__ h,
     const uint8_t *__restrict__ wq, const uint8_t *__restrict__ wscale, const uint16_t *__restrict__ up,
     const uint16_t *__restrict__ bias, int M, int N, int K, int gelu, uint16_t *__restrict__ Y)
 {
-    __shared__ __attribute__((aligned(16))) uint8_t sW[2][MX_BN * MX_STRIDE];
-    __shared__ __attribute__((aligned(16))) uint8_t sX[2][MX_BM * MX_STRIDE];
-    __shared__ uint32_t sEw[2][MX_BN];
-    __shared__ uint32_t sEx[2][MX_BM];
+    __shared__ MXSmem sm;
+    auto &sW = sm.w;
+    auto &sX = sm.x;
+    auto &sEw = sm.ew;
+    auto &sEx = sm.ex;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wn = wave & 1, wm = wave >> 1;
-    const int m0 = blockIdx.x * MX_BM, n0 = blockIdx.y * MX_BN;
+    int tn_, tm_;
+    tile_coords(blockIdx.x, (N + MX_BN - 1) / MX_BN, (M + MX_BM - 1) / MX_BM, tn_, tm_);
+    const int n0 = tn_ * MX_BN, m0 = tm_ * MX_BM;
     const int KB = K >> 1;          // code bytes per row
     const int NB = K >> 5;          // E8M0 scales per row
     const int steps = (K + 127) >> 7;
 
-    // Loader: thread t moves the 32-code segments lseg, lseg+1 (of 4 per
-    // step) of row t/2 of both tiles, and the 4 E8M0 bytes of one row.  Loads
+    // Loader: thread t moves segment t & 3 (32 codes, 16 bytes) of rows t/4
+    // and t/4 + 64 of both tiles, and the 4 E8M0 bytes of one row.  Loads
     // are unconditional (rows clamped, channels past K zeroed at the LDS
     // store), so every path keeps the same number of loads in flight.
-    const int lrow = tid >> 1, lseg = (tid & 1) * 2;
-    const uint8_t *__restrict__ wsrc = wq + (size_t)min(n0 + lrow, N - 1) * KB;
-    const uint8_t *__restrict__ xsrc = xq + (size_t)min(m0 + lrow, M - 1) * KB;
+    const int lrow = tid >> 2, lseg = tid & 3;
+    const uint8_t *__restrict__ wsrc0 = wq + (size_t)min(n0 + lrow, N - 1) * KB;
+    const uint8_t *__restrict__ wsrc1 = wq + (size_t)min(n0 + lrow + 64, N - 1) * KB;
+    const uint8_t *__restrict__ xsrc0 = xq + (size_t)min(m0 + lrow, M - 1) * KB;
+    const uint8_t *__restrict__ xsrc1 = xq + (size_t)min(m0 + lrow + 64, M - 1) * KB;
     const bool is_w_scale = tid < MX_BN;
     const uint8_t *__restrict__ ssrc = is_w_scale ? wscale + (size_t)min(n0 + tid, N - 1) * NB
                                                   : xscale + (size_t)min(m0 + (tid - MX_BN), M - 1) * NB;
     const bool aligned_scales = (NB & 3) == 0;
-    const uint4 z4 = {0u, 0u, 0u, 0u};
+    const int wofs0 = lrow * MX_STRIDE + mx_seg(lrow, lseg) * 16;
+    const int wofs1 = (lrow + 64) * MX_STRIDE + mx_seg(lrow + 64, lseg) * 16;
 
     uint4 rw0, rw1, rx0, rx1;
     uint32_t rs;
 #define MX_GLOAD(st)                                                                       \
     do {                                                                                   \
-        const int b0_ = min((st) * 4 + lseg, NB - 1), b1_ = min((st) * 4 + lseg + 1, NB - 1); \
-        rw0 = *reinterpret_cast<const uint4 *>(wsrc + b0_ * 16);                           \
-        rw1 = *reinterpret_cast<const uint4 *>(wsrc + b1_ * 16);                           \
-        rx0 = *reinterpret_cast<const uint4 *>(xsrc + b0_ * 16);                           \
-        rx1 = *reinterpret_cast<const uint4 *>(xsrc + b1_ * 16);                           \
+        const int b_ = min((st) * 4 + lseg, NB - 1);                                       \
+        rw0 = *reinterpret_cast<const uint4 *>(wsrc0 + b_ * 16);                           \
+        rw1 = *reinterpret_cast<const uint4 *>(wsrc1 + b_ * 16);                           \
+        rx0 = *reinterpret_cast<const uint4 *>(xsrc0 + b_ * 16);                           \
+        rx1 = *reinterpret_cast<const uint4 *>(xsrc1 + b_ * 16);                           \
         if (aligned_scales) {                                                              \
             rs = *reinterpret_cast<const uint32_t *>(ssrc + min((st) * 4, NB - 4));        \
         } else {                                                                           \
             rs = 0;                                                                        \
-            for (int b_ = 0; b_ < 4; ++b_)                                                 \
-                rs |= (uint32_t)ssrc[min((st) * 4 + b_, NB - 1)] << (8 * b_);              \
+            for (int q_ = 0; q_ < 4; ++q_)                                                 \
+                rs |= (uint32_t)ssrc[min((st) * 4 + q_, NB - 1)] << (8 * q_);              \
         }                                                                                  \
     } while (0)
 #define MX_LSTORE(st, buf)                                                                 \
     do {                                                                                   \
-        const bool k0_ = (st) * 4 + lseg < NB, k1_ = (st) * 4 + lseg + 1 < NB;             \
-        uint8_t *dw_ = &sW[buf][lrow * MX_STRIDE + lseg * 16];                             \
-        uint8_t *dx_ = &sX[buf][lrow * MX_STRIDE + lseg * 16];                             \
-        *reinterpret_cast<uint4 *>(dw_) = keep_if(k0_, rw0);                                \
-        *reinterpret_cast<uint4 *>(dw_ + 16) = keep_if(k1_, rw1);                            \
-        *reinterpret_cast<uint4 *>(dx_) = keep_if(k0_, rx0);                                \
-        *reinterpret_cast<uint4 *>(dx_ + 16) = keep_if(k1_, rx1);                            \
+        const bool kv_ = (st) * 4 + lseg < NB;                                             \
+        *reinterpret_cast<uint4 *>(&sW[buf][wofs0]) = keep_if(kv_, rw0);                   \
+        *reinterpret_cast<uint4 *>(&sW[buf][wofs1]) = keep_if(kv_, rw1);                   \
+        *reinterpret_cast<uint4 *>(&sX[buf][wofs0]) = keep_if(kv_, rx0);                   \
+        *reinterpret_cast<uint4 *>(&sX[buf][wofs1]) = keep_if(kv_, rx1);                   \
         if (is_w_scale) sEw[buf][tid] = rs;                                                \
         else sEx[buf][tid - MX_BN] = rs;                                                   \
     } while (0)
@@ -426,14 +498,14 @@ __global__ __launch_bounds__(MX_THREADS) void w4a4_mxfp4_kernel(
 #pragma unroll
         for (int tn = 0; tn < MX_TN; ++tn) {
             const int r = wn * MX_WN + tn * 16 + l16;
-            const uint4 v = *reinterpret_cast<const uint4 *>(&sW[buf][r * MX_STRIDE + 16 * c]);
+            const uint4 v = *reinterpret_cast<const uint4 *>(&sW[buf][r * MX_STRIDE + 16 * mx_seg(r, c)]);
             aw[tn] = (i32x8){(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
             ew[tn] = (int)((sEw[buf][r] >> (8 * c)) & 0xFFu);
         }
 #pragma unroll
         for (int tm = 0; tm < MX_TM; ++tm) {
             const int r = wm * MX_WM + tm * 16 + l16;
-            const uint4 v = *reinterpret_cast<const uint4 *>(&sX[buf][r * MX_STRIDE + 16 * c]);
+            const uint4 v = *reinterpret_cast<const uint4 *>(&sX[buf][r * MX_STRIDE + 16 * mx_seg(r, c)]);
             bx[tm] = (i32x8){(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
             ex[tm] = (int)((sEx[buf][r] >> (8 * c)) & 0xFFu);
         }
@@ -459,12 +531,15 @@ __global__ __launch_bounds__(MX_THREADS) void w4a4_mxfp4_kernel(
         load_h8(h, mb + tm * 16 + l16, M, 8 * c, hv);
         split_h(hv, hhi[tm], hlo[tm]);
     }
+    uint8_t *tile = reinterpret_cast<uint8_t *>(&sm) + wave * OUT_TILE_BYTES;
+    static_assert(4 * OUT_TILE_BYTES <= sizeof(MXSmem), "output staging fits in LDS");
 #pragma unroll
     for (int tn = 0; tn < MX_TN; ++tn) {
         const int nrow = nb + tn * 16 + l16;       // A-operand row of `up`
         uint4 uv = {0u, 0u, 0u, 0u};
         if (nrow < N) uv = *reinterpret_cast<const uint4 *>(up + (size_t)nrow * 32 + 8 * c);
         const bf16x8 ua = __builtin_bit_cast(bf16x8, uv);
+        const float4 bv = bias4(bias, nb + tn * 16 + 4 * c, N);
 #pragma unroll
         for (int tm = 0; tm < MX_TM; ++tm) {
             f32x4 lr = {0.f, 0.f, 0.f, 0.f};
@@ -472,9 +547,11 @@ __global__ __launch_bounds__(MX_THREADS) void w4a4_mxfp4_kernel(
             lr = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ua, hlo[tm], lr, 0, 0, 0);
             float a4[4] = {acc[tn][tm][0], acc[tn][tm][1], acc[tn][tm][2], acc[tn][tm][3]};
             float l4[4] = {lr[0], lr[1], lr[2], lr[3]};
-            finish4(a4, 1.0f, l4, bias, gelu, Y, mb + tm * 16 + l16, nb + tn * 16 + 4 * c, M, N);
+            stage4(tile, tm * 16 + l16, tn * 16 + 4 * c, finish4(a4, l4, bv, gelu));
         }
     }
+    __syncthreads();
+    flush_tile(tile, Y, mb, nb, M, N, lane);
 }
 
 }  // namespace
@@ -489,8 +566,8 @@ hipError_t launch_w4a4_linear(const uint8_t *xq, const void *xscale, const float
         hipLaunchKernelGGL(w4a4_int4_kernel, dim3((unsigned)tiles), dim3(I4_THREADS), 0, stream, xq,
                            (const float *)xscale, h, wq, (const float *)wscale, up, bias, M, N, K, gelu, Y);
     } else {
-        const dim3 grid((unsigned)((M + MX_BM - 1) / MX_BM), (unsigned)((N + MX_BN - 1) / MX_BN));
-        hipLaunchKernelGGL(w4a4_mxfp4_kernel, grid, dim3(MX_THREADS), 0, stream, xq, (const uint8_t *)xscale, h,
+        const int tiles = ((N + MX_BN - 1) / MX_BN) * ((M + MX_BM - 1) / MX_BM);
+        hipLaunchKernelGGL(w4a4_mxfp4_kernel, dim3((unsigned)tiles), dim3(MX_THREADS), 0, stream, xq, (const uint8_t *)xscale, h,
                            wq, (const uint8_t *)wscale, up, bias, M, N, K, gelu, Y);
     }
     return hipGetLastError();

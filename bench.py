@@ -32,6 +32,33 @@ PEAK_INT8_TOPS = 5000.0     # MI355X dense int8 matrix peak, 5.0 POP/s
 PEAK_FP4_TFLOPS = 10100.0   # MI355X dense MXFP4 matrix peak, 10.1 PFLOP/s
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, 8 TB/s
 
+# HBM traffic of svdq_w4a4_linear per launch, from two rocprofv3 --pmc runs
+# (FETCH_SIZE, then WRITE_SIZE) of this script, each divided by what the same
+# counter reads for a plain 512 MiB copy (--copy-calibration).  An entry is
+# only reported while the kernel source still hashes to the value it was
+# measured on; otherwise traffic is null.
+TRAFFIC = {}
+
+
+def _source_sha(name):
+    import hashlib
+    path = os.path.join(ROOT, "w4a4_rank_corrected_quantize_amd", "csrc", name)
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def copy_calibration(mib):
+    """A plain device-to-device copy of known size, for scaling HBM counters."""
+    import torch
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": n, "bytes_written": n, "launches": 3}), flush=True)
+
 
 def k1_bytes(M, K, r, prec):
     scales = (M * K // 64) * 4 if prec == 0 else M * K // 32
@@ -50,6 +77,10 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--prec", choices=["int4", "mxfp4"], default="int4")
+    ap.add_argument("--layer", choices=["fc1", "qkv", "fc2"], default="fc1",
+                    help="fc1 is the headline workload; fc2 takes fc1's output (computed on the GPU)")
+    ap.add_argument("--copy-calibration", type=int, metavar="MIB", default=0,
+                    help="only run a plain copy of MIB MiB (to scale the HBM byte counters)")
     ap.add_argument("--sets", type=int, default=3, help="rotating buffer sets")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle sample time")
@@ -61,17 +92,35 @@ def main():
 
     import torch
 
+    if args.copy_calibration:
+        torch.cuda.set_device(0)
+        copy_calibration(args.copy_calibration)
+        return
+
     import w4a4_rank_corrected_quantize_amd as svdq
     from w4a4_rank_corrected_quantize_amd import synth
 
     torch.cuda.set_device(0)
     svdq.check_device()
     prec = svdq.INT4 if args.prec == "int4" else svdq.MXFP4
-    spec = synth.SPECS["fc1" if prec == svdq.INT4 else "mx_fc1"]
+    spec = synth.SPECS[("" if prec == svdq.INT4 else "mx_") + args.layer]
     M, K, N, r = spec.M, spec.K, spec.N, svdq.RANK
+    X_bits = None
+    if args.layer == "fc2":
+        # fc2's input is fc1's bf16 output: run fc1 once on the GPU to make it
+        f1 = synth.SPECS[("" if prec == svdq.INT4 else "mx_") + "fc1"]
+        print(f"[bench] making fc2's input with {f1.name} on the GPU", file=sys.stderr, flush=True)
+        L1 = synth.make_layer(f1)
+        d1 = svdq.to_device(svdq.pack_weights(L1["W"], L1["act_absmax"], prec=prec))
+        xq1, xs1, h1 = svdq.quantize_act(svdq.bf16_tensor(L1["X"]), d1["smooth"], d1["down"], prec)
+        Y1 = svdq.w4a4_linear(xq1, xs1, h1, d1["wq"], d1["wscale"], d1["up"], svdq.bf16_tensor(L1["bias"]),
+                              prec, svdq.EPI_GELU_TANH)
+        X_bits = svdq.bf16_bits(Y1)
+        del L1, d1, xq1, xs1, h1, Y1
     print(f"[bench] generating {spec.name} {M}x{K}->{N} and packing on the host", file=sys.stderr,
           flush=True)
-    L = synth.make_layer(spec)
+    L = synth.make_layer(spec, X_bits=X_bits)
+    epi = svdq.EPI_GELU_TANH if spec.gelu else svdq.EPI_NONE
     t0 = time.time()
     p = svdq.pack_weights(L["W"], L["act_absmax"], prec=prec)
     pack_s = time.time() - t0
@@ -83,12 +132,12 @@ def main():
         d = svdq.to_device(p)
         sets.append(dict(
             X=svdq.bf16_tensor(L["X"]), smooth=d["smooth"], down=d["down"], up=d["up"], wq=d["wq"],
-            wscale=d["wscale"], bias=svdq.bf16_tensor(L["bias"]),
+            wscale=d["wscale"], bias=None if L["bias"] is None else svdq.bf16_tensor(L["bias"]),
             xq=torch.empty((M, K // 2), dtype=torch.uint8, device="cuda"),
             xscale=torch.empty((M, K // g), dtype=sdt, device="cuda"),
             h=torch.empty((M, r), dtype=torch.float32, device="cuda"),
             Y=torch.empty((M, N), dtype=torch.bfloat16, device="cuda")))
-    ws_mb = sum(t.numel() * t.element_size() for t in sets[0].values()) / 1e6
+    ws_mb = sum(t.numel() * t.element_size() for t in sets[0].values() if t is not None) / 1e6
 
     def step(b, ev=None):
         if ev is not None:
@@ -97,7 +146,7 @@ def main():
         if ev is not None:
             ev[1].record()
         svdq.w4a4_linear(b["xq"], b["xscale"], b["h"], b["wq"], b["wscale"], b["up"], b["bias"], prec,
-                         svdq.EPI_GELU_TANH, Y=b["Y"])
+                         epi, Y=b["Y"])
         if ev is not None:
             ev[2].record()
 
@@ -124,7 +173,11 @@ def main():
     k2_tops = ops / (k2_ms * 1e-3) / 1e12
     peak = PEAK_INT8_TOPS if prec == svdq.INT4 else PEAK_FP4_TFLOPS
     k1_gbs = k1_bytes(M, K, r, prec) / (k1_ms * 1e-3) / 1e9
-    k2_gbs = k2_bytes(M, N, K, r, prec) / (k2_ms * 1e-3) / 1e9
+    k2_gbs = k2_bytes(M, N, K, r, prec, bias=L["bias"] is not None) / (k2_ms * 1e-3) / 1e9
+    traffic = None
+    t = TRAFFIC.get((args.prec, args.layer))
+    if t is not None and t["source_sha"] == _source_sha("w4a4_gemm.hip"):
+        traffic = t["bytes"]
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -133,12 +186,12 @@ def main():
         rows = 8
         t0 = time.time()
         xq, xs, h = O.quant_act(L["X"][:rows], p["smooth"], p["down"], prec)
-        O.linear(xq, xs, h, p["wq"], p["wscale"], p["up"], L["bias"], prec, gelu=True)
+        O.linear(xq, xs, h, p["wq"], p["wscale"], p["up"], L["bias"], prec, gelu=spec.gelu)
         probe = max(time.time() - t0, 1e-3)
         rows = int(min(M, max(8, rows * args.cpu_seconds / probe)))
         t0 = time.time()
         xq, xs, h = O.quant_act(L["X"][:rows], p["smooth"], p["down"], prec)
-        O.linear(xq, xs, h, p["wq"], p["wscale"], p["up"], L["bias"], prec, gelu=True)
+        O.linear(xq, xs, h, p["wq"], p["wscale"], p["up"], L["bias"], prec, gelu=spec.gelu)
         t_cpu = time.time() - t0
         cpu = {"value": round(2.0 * rows * N * K / t_cpu / 1e12, 6), "unit": "TOPS", "cores": O.num_threads(),
                "kind": "oracle",
@@ -156,17 +209,19 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int4 codes on int8 matrix cores, int32 partials, fp32 rescale" if prec == svdq.INT4
+        "dtype": "int4 codes (exact fp8 values) on the fp8 matrix cores, exact per-group partials, "
+                 "fp32 rescale" if prec == svdq.INT4
         else "mxfp4 (e2m1 x e2m1, e8m0 scales) on the scaled fp4 matrix cores, fp32 accumulation",
         "data": "synthetic (seeded Student-t activations with outlier channels, N(0,0.02^2) weights)",
         "config": {"workload": f"{spec.name}: {M} tokens x {K} -> {N}, rank {r}, "
-                               f"{'INT4 g64' if prec == svdq.INT4 else 'MXFP4 g32'}, bias, GELU-tanh; "
+                               f"{'INT4 g64' if prec == svdq.INT4 else 'MXFP4 g32'}, bias"
+                               f"{', GELU-tanh' if spec.gelu else ''}; "
                                "step = svdq_quantize_act + svdq_w4a4_linear",
                    "M": M, "K": K, "N": N, "rank": r, "buffer_sets": len(sets),
                    "working_set_MB_per_set": round(ws_mb, 1)},
         "roofline": {"bound": "mfma", "kernel": "svdq_w4a4_linear",
                      "achieved": round(k2_tops, 2), "peak": peak,
-                     "unit": "TFLOP/s", "frac": round(k2_tops / peak, 4), "traffic": None,
+                     "unit": "TFLOP/s", "frac": round(k2_tops / peak, 4), "traffic": traffic,
                      "avg_ms": round(k2_ms, 5)},
         "activation_kernel": {"kernel": "svdq_quantize_act", "bound": "hbm", "avg_ms": round(k1_ms, 5),
                               "achieved_GBs": round(k1_gbs, 1), "peak_GBs": PEAK_HBM_GBS,

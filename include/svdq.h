@@ -172,8 +172,9 @@ svdq_status svdq_quantize_act(const uint16_t *X, int M, int K, const float *smoo
  *   M, N, K         M >= 0, N >= 0 (either 0: no-op), N % 8 == 0, K % group == 0
  *   epi             SVDQ_EPI_NONE or SVDQ_EPI_GELU_TANH
  *   Y               [M][N] bf16 bits (device, out), round-to-nearest-even
- * INT4: per 64-group exact int32 partial products from the int8 matrix
- * cores, rescaled by sx * sw in fp32; MXFP4: the scaled f8f6f4 matrix
+ * INT4: per 64-group exact integer partial products from the matrix
+ * cores (each code enters the fp8 matrix instruction as an exact E4M3
+ * value), rescaled by sx * sw in fp32; MXFP4: the scaled f8f6f4 matrix
  * instruction applies both E8M0 scales.  The low-rank term uses h split
  * into a bf16 high and low part.  One kernel launch.  Errors as for
  * svdq_quantize_act.

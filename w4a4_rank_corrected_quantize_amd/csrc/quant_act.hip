@@ -9,13 +9,23 @@
 //   group absmax -> scale -> 4-bit codes, nibble-packed
 //   h_mj = sum_k X_mk down[j][k]     (bf16 matrix cores, fp32 accumulation)
 //
-// Work decomposition (gfx950, wave64): a block owns 16 rows and all of K; its
-// WAVES waves take the groups g = wave, wave + WAVES, ...  In a wave, lane l
-// holds row l % 16 and the 16 consecutive channels 16 * (l / 16) .. + 15 of the
-// group, which is exactly the operand layout of v_mfma_f32_16x16x32_bf16 (two
-// instructions per group and per 16-column half of the rank).  The group
-// absmax needs the four lanes l, l^16, l^32, l^48.  The per-wave partial h
-// tiles are summed in a fixed order through LDS at the end (deterministic).
+// Work decomposition (gfx950, wave64).  The kernel is HBM-bound, so every
+// global access is a run of full 128-byte lines:
+//   * a block owns R = 2 * NLD consecutive rows (R at most 24, chosen so that
+//     there is about one block per CU) and all of K; its 4 waves take the
+//     256-channel chunks c = wave, wave + 4, ...
+//   * a chunk is loaded as R/2 row pairs: lanes 0-31 read 512 contiguous bytes
+//     of one row, lanes 32-63 of the next (lane l holds channels 8 (l % 32) ..
+//     + 7); the next chunk's loads are in flight while this one is processed;
+//   * a quantization group is 8 neighbouring lanes (4 for MXFP4), so the
+//     group absmax takes three DPP steps, and each lane writes its 8 codes as
+//     one dword: 128 contiguous code bytes per row per load;
+//   * the down projection needs X in the matrix-core operand layout (one row
+//     per lane), so each wave copies its chunk into its own LDS tile and reads
+//     it back transposed for v_mfma_f32_32x32x16_bf16 (A = down rows j,
+//     B = X^T columns m: one 32-row tile covers the block);
+//   * the per-wave partial h tiles are summed in a fixed order through LDS at
+//     the end (deterministic).
 //
 // Roofline: HBM-bound.  Algorithmic bytes per call: 2MK (X) + MK/2 (codes)
 // + 4MK/64 (INT4 scales) or MK/32 (E8M0) + 4Mr (h) + 4K (s) + 2rK (down).
@@ -26,169 +36,204 @@ namespace svdq {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int K1_ROWS = 16;
-constexpr int K1_WAVES = 8;
+constexpr int K1_WAVES = 4;
+constexpr int K1_CH = 256;                  // channels per chunk
+constexpr int K1_TILE_STRIDE = 2 * K1_CH + 16;   // LDS bytes per row of a wave's X tile
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
 __device__ __forceinline__ float bf_lo(uint32_t w) { return bits_f32(w << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t w) { return bits_f32(w & 0xFFFF0000u); }
 
-// 16 consecutive channels of one row: bf16 -> fp32 and smoothing product.
-__device__ __forceinline__ void smooth16(uint4 xa, uint4 xb, const float4 *s, float *v)
+// max over the 8 (or 4) lanes of a quantization group, via DPP
+template <int LANES>
+__device__ __forceinline__ float group_max(float a)
 {
-    const uint32_t w[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
-    const float sv[16] = {s[0].x, s[0].y, s[0].z, s[0].w, s[1].x, s[1].y, s[1].z, s[1].w,
-                          s[2].x, s[2].y, s[2].z, s[2].w, s[3].x, s[3].y, s[3].z, s[3].w};
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        v[2 * i] = bf_lo(w[i]) * sv[2 * i];
-        v[2 * i + 1] = bf_hi(w[i]) * sv[2 * i + 1];
-    }
+    a = __builtin_fmaxf(a, bits_f32((uint32_t)__builtin_amdgcn_mov_dpp((int)f32_bits(a), 0xB1, 0xF, 0xF, false)));
+    a = __builtin_fmaxf(a, bits_f32((uint32_t)__builtin_amdgcn_mov_dpp((int)f32_bits(a), 0x4E, 0xF, 0xF, false)));
+    if constexpr (LANES == 8)   // row_half_mirror: lane i <-> 7 - i within each group of 8
+        a = __builtin_fmaxf(a, bits_f32((uint32_t)__builtin_amdgcn_mov_dpp((int)f32_bits(a), 0x141, 0xF, 0xF, false)));
+    return a;
 }
 
-struct K1Load {
-    uint4 xa, xb;          // 16 channels of X (bf16)
-    uint4 d0a, d0b;        // down[rl][16 channels]
-    uint4 d1a, d1b;        // down[rl + 16][16 channels]
-    float4 s[4];           // smoothing factors of the 16 channels
+// Sign bits of the lane's 8 values xhat, at bit 3 of each code nibble
+// (element 2e -> bit 8e + 3, element 2e + 1 -> bit 8e + 7): byte 3 of each
+// fp32 value carries its sign in bit 7.
+__device__ __forceinline__ uint32_t sign_bits(const float *v)
+{
+    const uint32_t ea = __builtin_amdgcn_perm(f32_bits(v[2]), f32_bits(v[0]), 0x0c0c0703u);   // v0 v2 . .
+    const uint32_t eb = __builtin_amdgcn_perm(f32_bits(v[6]), f32_bits(v[4]), 0x07030c0cu);   // . . v4 v6
+    const uint32_t oa = __builtin_amdgcn_perm(f32_bits(v[3]), f32_bits(v[1]), 0x0c0c0703u);
+    const uint32_t ob = __builtin_amdgcn_perm(f32_bits(v[7]), f32_bits(v[5]), 0x07030c0cu);
+    return (((ea | eb) >> 4) & 0x08080808u) | ((oa | ob) & 0x80808080u);
+}
+
+template <int NLD>
+struct K1Chunk {
+    uint4 x[NLD];          // row pair i: lanes 0-31 row 2i, lanes 32-63 row 2i + 1
+    float4 s0, s1;         // smoothing factors of the lane's 8 channels
 };
 
-template <bool MX>
+template <bool MX, int NLD>
 __global__ __launch_bounds__(64 * K1_WAVES) void quant_act_kernel(
     const uint16_t *__restrict__ X, int M, int K, const float *__restrict__ smooth,
     const uint16_t *__restrict__ down, uint8_t *__restrict__ xq, void *__restrict__ xscale,
     float *__restrict__ h)
 {
-    __shared__ float red[K1_WAVES][K1_ROWS][2 * 16 + 1];
+    __shared__ __attribute__((aligned(16))) uint8_t tile[K1_WAVES][32 * K1_TILE_STRIDE];
+    __shared__ float red[K1_WAVES][32][33];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int rl = lane & 15, c = lane >> 4;
-    const int row0 = blockIdx.x * K1_ROWS;
-    const int row = row0 + rl;
-    const bool rv = row < M;
-    const int G = K >> 6;                       // INT4 groups per row
-    const int steps = (K + 63) >> 6;            // 64-channel steps (MXFP4 may end on half a step)
-    const size_t rowK = (size_t)(rv ? row : 0) * (size_t)K;
-    const uint4 z4 = {0u, 0u, 0u, 0u};
+    constexpr int R = 2 * NLD;
+    const int row0 = blockIdx.x * R;
+    const int nrow = min(R, M - row0);      // >= 1 (the grid is sized by the host)
+    const int nch = (K + K1_CH - 1) / K1_CH;
+    const int rh = lane >> 5;               // row within a pair
+    const int kl = 8 * (lane & 31);         // first channel of the lane within a chunk
+    const int KB = K >> 1;                  // code bytes per row
+    uint8_t *mytile = tile[wave];
 
-    // Loads are unconditional (addresses clamped into the buffers) so that the
-    // number of loads in flight is the same on every path and the next
-    // group's loads can stay in flight while the current group is processed.
-    // Rows >= M read row 0 and are never stored; channels past K (a trailing
-    // half step of MXFP4) are masked out of the down projection at use.
-    auto fetch = [&](int g, K1Load &L) {
-        const int k0 = min(g * 64 + c * 16, K - 16);
-        L.xa = *reinterpret_cast<const uint4 *>(X + rowK + k0);
-        L.xb = *reinterpret_cast<const uint4 *>(X + rowK + k0 + 8);
+    // Loads are unconditional (addresses clamped into the buffers), so the
+    // number of loads in flight is the same on every path: a row past the
+    // block's last row reads that last row and stores nothing; channels past
+    // K read the last 8 channels and store nothing (their groups lie entirely
+    // past K, since K is a multiple of the group size).
+    auto fetch = [&](int c, K1Chunk<NLD> &L) {
+        const int k = min(c * K1_CH + kl, K - 8);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) L.s[i] = *reinterpret_cast<const float4 *>(smooth + k0 + 4 * i);
-        L.d0a = *reinterpret_cast<const uint4 *>(down + (size_t)rl * K + k0);
-        L.d0b = *reinterpret_cast<const uint4 *>(down + (size_t)rl * K + k0 + 8);
-        L.d1a = *reinterpret_cast<const uint4 *>(down + (size_t)(rl + 16) * K + k0);
-        L.d1b = *reinterpret_cast<const uint4 *>(down + (size_t)(rl + 16) * K + k0 + 8);
+        for (int i = 0; i < NLD; ++i) {
+            const int r = min(2 * i + rh, nrow - 1);
+            L.x[i] = *reinterpret_cast<const uint4 *>(X + (size_t)(row0 + r) * K + k);
+        }
+        L.s0 = *reinterpret_cast<const float4 *>(smooth + k);
+        L.s1 = *reinterpret_cast<const float4 *>(smooth + k + 4);
     };
 
-    f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-    auto process = [&](int g, const K1Load &L) {
-            const int k0 = g * 64 + c * 16;
-            const bool kv = k0 < K;                 // false only in a trailing half step
-
-            // down projection: D[m][j] += sum_k X[m][k] down[j][k]
-            uint4 d0a = L.d0a, d0b = L.d0b, d1a = L.d1a, d1b = L.d1b;
-            if (MX && !kv) d0a = d0b = d1a = d1b = z4;
-            acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(L.xa), as_bf16x8(d0a), acc0, 0, 0, 0);
-            acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(L.xb), as_bf16x8(d0b), acc0, 0, 0, 0);
-            acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(L.xa), as_bf16x8(d1a), acc1, 0, 0, 0);
-            acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(L.xb), as_bf16x8(d1b), acc1, 0, 0, 0);
-
-            float v[16];
-            smooth16(L.xa, L.xb, L.s, v);
+    f32x16 acc = {};
+    auto process = [&](int c, const K1Chunk<NLD> &L) {
+        const int kc = c * K1_CH + kl;
+        const bool kv = kc < K;
+        // down operand of the chunk's 16 products (A: row j = lane % 32,
+        // channels 16 t + 8 (lane / 32) .. + 7); zero past K
+        uint4 dn[16];
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+            const int kk = c * K1_CH + 16 * t + 8 * rh;
+            dn[t] = kk < K ? *reinterpret_cast<const uint4 *>(down + (size_t)(lane & 31) * K + kk)
+                           : (uint4){0u, 0u, 0u, 0u};
+        }
+        const float sv[8] = {L.s0.x, L.s0.y, L.s0.z, L.s0.w, L.s1.x, L.s1.y, L.s1.z, L.s1.w};
+#pragma unroll
+        for (int i = 0; i < NLD; ++i) {
+            const uint4 w = L.x[i];
+            *reinterpret_cast<uint4 *>(mytile + (2 * i + rh) * K1_TILE_STRIDE + 2 * kl) = w;
+            const int rloc = 2 * i + rh;
+            const bool st = kv && rloc < nrow;
+            const size_t row = (size_t)(row0 + rloc);
+            const uint32_t wv[4] = {w.x, w.y, w.z, w.w};
+            float v[8];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                v[2 * e] = bf_lo(wv[e]) * sv[2 * e];
+                v[2 * e + 1] = bf_hi(wv[e]) * sv[2 * e + 1];
+            }
             float a = 0.0f;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) a = __builtin_fmaxf(a, __builtin_fabsf(v[i]));
-            // sign bits of the 16 codes (bit 3 of each nibble), from the fp32 values
-            uint32_t sg0 = 0, sg1 = 0;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                sg0 |= (f32_bits(v[i]) >> 31) << (4 * i + 3);
-                sg1 |= (f32_bits(v[8 + i]) >> 31) << (4 * i + 3);
-            }
-            uint32_t p0 = 0, p1 = 0;
+            for (int e = 0; e < 8; ++e) a = __builtin_fmaxf(a, __builtin_fabsf(v[e]));
+            uint32_t code;
             if constexpr (!MX) {
-                a = __builtin_fmaxf(a, __shfl_xor(a, 16));
-                a = __builtin_fmaxf(a, __shfl_xor(a, 32));
+                a = group_max<8>(a);
                 const float scale = int4_group_scale(a);
                 const bool lifted = scale < 7.88860905e-31f;      // 2^-100: exact path only
                 const float inv = scale == 0.0f ? 0.0f : __builtin_amdgcn_rcpf(scale);
-                bool near = lifted;
+                float q[8], dmax = 0.0f;
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const float t = __builtin_fabsf(v[i]) * inv;
-                    const float q = __builtin_rintf(t);
-                    near |= __builtin_fabsf(t - q) >= kNearTie;
-                    const uint32_t m = (uint32_t)q;
-                    if (i < 8) p0 |= m << (4 * i);
-                    else p1 |= m << (4 * (i - 8));
+                for (int e = 0; e < 8; ++e) {
+                    const float t = __builtin_fabsf(v[e]) * inv;
+                    q[e] = __builtin_rintf(t);
+                    dmax = __builtin_fmaxf(dmax, __builtin_fabsf(t - q[e]));
                 }
-                if (near) {                                       // rare: exact remainder test
+                if (lifted || dmax >= kNearTie) {                 // rare: exact remainder test
                     const Int4Group gq = int4_group_prepare(scale);
-                    p0 = p1 = 0;
 #pragma unroll
-                    for (int i = 0; i < 8; ++i) {
-                        p0 |= int4_mag(__builtin_fabsf(v[i]), gq) << (4 * i);
-                        p1 |= int4_mag(__builtin_fabsf(v[8 + i]), gq) << (4 * i);
-                    }
+                    for (int e = 0; e < 8; ++e) q[e] = (float)int4_mag(__builtin_fabsf(v[e]), gq);
                 }
-                p0 |= sg0;
-                p1 |= sg1;
-                if (rv && c == 0) reinterpret_cast<float *>(xscale)[(size_t)row * G + g] = scale;
+                uint32_t ev = 0, od = 0;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    ev = __builtin_amdgcn_cvt_pk_u8_f32(q[2 * e], e, ev);
+                    od = __builtin_amdgcn_cvt_pk_u8_f32(q[2 * e + 1], e, od);
+                }
+                code = (ev | (od << 4)) | sign_bits(v);
+                if (st && (lane & 7) == 0) reinterpret_cast<float *>(xscale)[row * (K >> 6) + (kc >> 6)] = scale;
             } else {
-                // two 32-wide blocks per step: lanes c = 0,1 -> block 2g, c = 2,3 -> block 2g+1
-                a = __builtin_fmaxf(a, __shfl_xor(a, 16));
-                const uint32_t e = mx_block_e8m0(a);
-                const float inv = mx_inv_scale(e);
+                a = group_max<4>(a);
+                const uint32_t e8 = mx_block_e8m0(a);
+                const float inv = mx_inv_scale(e8);
+                code = 0;
 #pragma unroll
-                for (int i = 0; i < 8; ++i) p0 |= e2m1_code(v[i], inv) << (4 * i);
+                for (int e = 0; e < 8; ++e) code |= e2m1_code(v[e], inv) << (4 * e);
+                if (st && (lane & 3) == 0) reinterpret_cast<uint8_t *>(xscale)[row * (K >> 5) + (kc >> 5)] = (uint8_t)e8;
+            }
+            if (st) *reinterpret_cast<uint32_t *>(xq + row * KB + (kc >> 1)) = code;
+        }
+        // the tile rows written above are read back by other lanes of this wave
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        // h^T[j][m] += sum_k down[j][k] X[m][k] over the chunk; rows m >= nrow
+        // read the last row (their outputs are dropped)
+        const uint8_t *src = mytile + min(lane & 31, nrow - 1) * K1_TILE_STRIDE + 16 * rh;
 #pragma unroll
-                for (int i = 0; i < 8; ++i) p1 |= e2m1_code(v[8 + i], inv) << (4 * i);
-                if (rv && kv && (c & 1) == 0)
-                    reinterpret_cast<uint8_t *>(xscale)[(size_t)row * (K >> 5) + 2 * g + (c >> 1)] = (uint8_t)e;
-            }
-            if (rv && kv) {
-                uint2 pk = {p0, p1};
-                *reinterpret_cast<uint2 *>(xq + (size_t)row * (K >> 1) + (k0 >> 1)) = pk;
-            }
+        for (int t = 0; t < 16; ++t) {
+            const uint4 b = *reinterpret_cast<const uint4 *>(src + 32 * t);
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(dn[t]), as_bf16x8(b), acc, 0, 0, 0);
+        }
+        // the next chunk overwrites the tile only after every lane has read it
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     };
 
-    // ping-pong register buffers: the loads of the next group are in flight
-    // while the current one is processed
-    K1Load bufA, bufB;
-    int g = wave;
-    if (g < steps) fetch(g, bufA);
-    for (; g < steps; g += 2 * K1_WAVES) {
-        const int g1 = g + K1_WAVES;
-        fetch(min(g1, steps - 1), bufB);
-        process(g, bufA);
-        if (g1 >= steps) break;
-        fetch(min(g1 + K1_WAVES, steps - 1), bufA);
-        process(g1, bufB);
+    // ping-pong register buffers: the next chunk's loads are in flight while
+    // the current one is processed
+    K1Chunk<NLD> bufA, bufB;
+    int c = wave;
+    if (c < nch) fetch(c, bufA);
+    for (; c < nch; c += 2 * K1_WAVES) {
+        const int c1 = c + K1_WAVES;
+        fetch(min(c1, nch - 1), bufB);          // unconditional: same load count on every path
+        process(c, bufA);
+        if (c1 >= nch) break;
+        fetch(min(c1 + K1_WAVES, nch - 1), bufA);
+        process(c1, bufB);
     }
 
-    // fixed-order reduction of the per-wave partial h tiles
+    // fixed-order reduction of the per-wave partial h^T tiles; lane l holds
+    // column m = l % 32 and rows j = 8 (i / 4) + 4 (l / 32) + i % 4
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        red[wave][4 * c + i][rl] = acc0[i];
-        red[wave][4 * c + i][rl + 16] = acc1[i];
-    }
+    for (int i = 0; i < 16; ++i) red[wave][lane & 31][8 * (i >> 2) + 4 * rh + (i & 3)] = acc[i];
     __syncthreads();
-    for (int t = threadIdx.x; t < K1_ROWS * 32; t += 64 * K1_WAVES) {
+    for (int t = threadIdx.x; t < nrow * 32; t += 64 * K1_WAVES) {
         const int m = t >> 5, j = t & 31;
         float sum = 0.0f;
 #pragma unroll
         for (int w = 0; w < K1_WAVES; ++w) sum += red[w][m][j];
-        if (row0 + m < M) h[(size_t)(row0 + m) * 32 + j] = sum;
+        h[(size_t)(row0 + m) * 32 + j] = sum;
     }
+}
+
+int device_cu_count()
+{
+    static int cached[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cached[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
 }
 
 }  // namespace
@@ -196,13 +241,29 @@ __global__ __launch_bounds__(64 * K1_WAVES) void quant_act_kernel(
 hipError_t launch_quant_act(const uint16_t *X, int M, int K, const float *smooth, const uint16_t *down,
                             svdq_precision prec, uint8_t *xq, void *xscale, float *h, hipStream_t stream)
 {
-    const dim3 grid((unsigned)((M + K1_ROWS - 1) / K1_ROWS)), block(64 * K1_WAVES);
-    if (prec == SVDQ_INT4)
-        hipLaunchKernelGGL(quant_act_kernel<false>, grid, block, 0, stream, X, M, K, smooth, down, xq,
-                           xscale, h);
-    else
-        hipLaunchKernelGGL(quant_act_kernel<true>, grid, block, 0, stream, X, M, K, smooth, down, xq,
-                           xscale, h);
+    // rows per block: about one block per CU, R = 2 * NLD from a small menu
+    const int ncu = device_cu_count();
+    const int want = (M + 2 * ncu - 1) / (2 * ncu);      // row pairs per block
+    const int nld = want <= 1 ? 1 : want <= 2 ? 2 : want <= 4 ? 4 : want <= 6 ? 6 : want <= 9 ? 9 : 12;
+    const dim3 grid((unsigned)((M + 2 * nld - 1) / (2 * nld))), block(64 * K1_WAVES);
+#define K1_LAUNCH(N)                                                                                    \
+    case N:                                                                                             \
+        if (prec == SVDQ_INT4)                                                                          \
+            hipLaunchKernelGGL((quant_act_kernel<false, N>), grid, block, 0, stream, X, M, K, smooth,    \
+                               down, xq, xscale, h);                                                    \
+        else                                                                                            \
+            hipLaunchKernelGGL((quant_act_kernel<true, N>), grid, block, 0, stream, X, M, K, smooth,     \
+                               down, xq, xscale, h);                                                    \
+        break;
+    switch (nld) {
+        K1_LAUNCH(1)
+        K1_LAUNCH(2)
+        K1_LAUNCH(4)
+        K1_LAUNCH(6)
+        K1_LAUNCH(9)
+        K1_LAUNCH(12)
+    }
+#undef K1_LAUNCH
     return hipGetLastError();
 }
 

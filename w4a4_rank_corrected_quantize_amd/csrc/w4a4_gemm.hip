@@ -13,9 +13,14 @@
 // per-group integer dot product P_mng * 2^-18 in fp32 (|P| <= 3136): one
 // instruction covers exactly one 64-wide group of a 32x32 tile.  The nibbles
 // are widened once per block while staging them into LDS (three bit
-// operations per four codes).  The rescale acc += P * (sx * sw) costs one
-// multiply and one fma per element and group on the fp32 VALU, which is what
-// bounds this kernel on gfx950 (the 2^18 is folded into the staged sw).
+// operations per four codes).
+//
+// The per-group scale of a 32x32 tile is the outer product sx_g (x) sw_g; it
+// comes from the bf16 matrix instruction as well, from hi/lo splits of both
+// scales (s = hi + lo, hi = bf16(s), lo = bf16(s - hi)):
+//     C_nm = sw_hi sx_hi + sw_lo sx_hi + sw_hi sx_lo      (relative error ~2^-16)
+// so the fp32 VALU only runs acc = fma(P, C, acc), one instruction per
+// element and group (the 2^18 is folded into the staged sw).
 //
 // MXFP4: the E2M1 nibbles are the native fp4 operand format of
 // v_mfma_scale_f32_16x16x128_f8f6f4 and the E8M0 block scales are its scale
@@ -186,11 +191,28 @@ __device__ __forceinline__ void widen_fp8(uint4 p, uint4 &lo, uint4 &hi)
     hi = (uint4){o[4], o[5], o[6], o[7]};
 }
 
+// Scale operands of the outer-product instruction (A = weights, B = tokens):
+// row n of A holds k = 0..2 = (sw_hi, sw_lo, sw_hi), column m of B holds
+// (sx_hi, sx_hi, sx_lo); every other k is zero.
+__device__ __forceinline__ uint2 scale_operand_w(float s)
+{
+    const uint32_t hi = pack_bf16x2(s, 0.0f) & 0xFFFFu;
+    const uint32_t lo = pack_bf16x2(s - bf16_to_f32(hi), 0.0f) & 0xFFFFu;
+    return make_uint2(hi | lo << 16, hi);
+}
+
+__device__ __forceinline__ uint2 scale_operand_x(float s)
+{
+    const uint32_t hi = pack_bf16x2(s, 0.0f) & 0xFFFFu;
+    const uint32_t lo = pack_bf16x2(s - bf16_to_f32(hi), 0.0f) & 0xFFFFu;
+    return make_uint2(hi | hi << 16, lo);
+}
+
 struct __attribute__((aligned(16))) I4Smem {
     uint8_t w[2][I4_BN * I4_ROWB];
     uint8_t x[2][I4_BM * I4_ROWB];
-    float sw[2][2][I4_BN];     // [buf][group in step][n], times 2^18
-    float sx[2][2][I4_BM];     // [buf][group in step][m]
+    uint2 sw[2][2][I4_BN];     // [buf][group in step][n], scale_operand_w(sw * 2^18)
+    uint2 sx[2][2][I4_BM];     // [buf][group in step][m], scale_operand_x(sx)
 };
 
 __global__ __launch_bounds__(I4_THREADS) void w4a4_int4_kernel(
@@ -241,30 +263,29 @@ __global__ __launch_bounds__(I4_THREADS) void w4a4_int4_kernel(
         rs##R##0 = ps[min(2 * (st), G - 1)];                                           \
         rs##R##1 = ps[min(2 * (st) + 1, G - 1)];                                       \
     } while (0)
+    // When G is odd, the second half of the last step holds codes that the
+    // compute loop never reads.
 #define I4_LSTORE(st, buf, R)                                                          \
     do {                                                                               \
-        const bool kv_ = (st) * 64 + lseg * 16 < KB;                                   \
         uint4 a_, b_;                                                                  \
-        widen_fp8(keep_if(kv_, rg##R##0), a_, b_);                                     \
+        widen_fp8(rg##R##0, a_, b_);                                                   \
         uint8_t *d_ = sm.w[buf] + lr * I4_ROWB + lseg * 32;                            \
         *reinterpret_cast<uint4 *>(d_) = a_;                                           \
         *reinterpret_cast<uint4 *>(d_ + 16) = b_;                                      \
-        widen_fp8(keep_if(kv_, rg##R##1), a_, b_);                                     \
+        widen_fp8(rg##R##1, a_, b_);                                                   \
         d_ = sm.w[buf] + (lr + I4_BN / 2) * I4_ROWB + lseg * 32;                       \
         *reinterpret_cast<uint4 *>(d_) = a_;                                           \
         *reinterpret_cast<uint4 *>(d_ + 16) = b_;                                      \
-        widen_fp8(keep_if(kv_, rg##R##2), a_, b_);                                     \
+        widen_fp8(rg##R##2, a_, b_);                                                   \
         d_ = sm.x[buf] + lr * I4_ROWB + lseg * 32;                                     \
         *reinterpret_cast<uint4 *>(d_) = a_;                                           \
         *reinterpret_cast<uint4 *>(d_ + 16) = b_;                                      \
-        const float s0_ = 2 * (st) < G ? rs##R##0 : 0.0f;                              \
-        const float s1_ = 2 * (st) + 1 < G ? rs##R##1 : 0.0f;                          \
         if (sc_w) {                                                                    \
-            sm.sw[buf][0][tid] = s0_ * kTwo18;                                         \
-            sm.sw[buf][1][tid] = s1_ * kTwo18;                                         \
+            sm.sw[buf][0][tid] = scale_operand_w(rs##R##0 * kTwo18);                   \
+            sm.sw[buf][1][tid] = scale_operand_w(rs##R##1 * kTwo18);                   \
         } else if (sc_x) {                                                             \
-            sm.sx[buf][0][tid - I4_BN] = s0_;                                          \
-            sm.sx[buf][1][tid - I4_BN] = s1_;                                          \
+            sm.sx[buf][0][tid - I4_BN] = scale_operand_x(rs##R##0);                    \
+            sm.sx[buf][1][tid - I4_BN] = scale_operand_x(rs##R##1);                    \
         }                                                                              \
     } while (0)
 
@@ -278,50 +299,49 @@ __global__ __launch_bounds__(I4_THREADS) void w4a4_int4_kernel(
 
     const int l32 = lane & 31, hk = lane >> 5;
     const f32x16 zero16 = {};
-    // compute of one step from LDS buffer `buf` (groups 2st, 2st+1)
+    // Compute of one step from LDS buffer `buf`: two groups (one for the last
+    // step of an odd G), each 4 tiles of 32x32 with one fp8 product, one scale
+    // outer product and 16 fmas.  (The per-group exit also keeps the compiler
+    // from hoisting the second group's reads and products into the first,
+    // which would run out of registers.)
     auto compute_step = [&](int st, int buf) {
 #pragma unroll
-            for (int q = 0; q < 2; ++q) {
-                if (2 * st + q >= G) break;
-                i32x8 aw[I4_TN], bx[I4_TM];
+        for (int q = 0; q < 2; ++q) {
+            if (2 * st + q >= G) break;   // odd G: the last step has one group
+            i32x8 aw[I4_TN], bx[I4_TM];
+            bf16x8 cw[I4_TN], cx[I4_TM];
 #pragma unroll
-                for (int tn = 0; tn < I4_TN; ++tn) {
-                    const uint8_t *p = sm.w[buf] + (wn * I4_WN + tn * 32 + l32) * I4_ROWB + q * 64 + hk * 32;
-                    const uint4 u0 = *reinterpret_cast<const uint4 *>(p);
-                    const uint4 u1 = *reinterpret_cast<const uint4 *>(p + 16);
-                    aw[tn] = (i32x8){(int)u0.x, (int)u0.y, (int)u0.z, (int)u0.w,
-                                     (int)u1.x, (int)u1.y, (int)u1.z, (int)u1.w};
-                }
+            for (int tn = 0; tn < I4_TN; ++tn) {
+                const uint8_t *p = sm.w[buf] + (wn * I4_WN + tn * 32 + l32) * I4_ROWB + q * 64 + hk * 32;
+                const uint4 u0 = *reinterpret_cast<const uint4 *>(p);
+                const uint4 u1 = *reinterpret_cast<const uint4 *>(p + 16);
+                aw[tn] = (i32x8){(int)u0.x, (int)u0.y, (int)u0.z, (int)u0.w,
+                                 (int)u1.x, (int)u1.y, (int)u1.z, (int)u1.w};
+                // scale operands: lanes 0-31 carry k = 0..7, lanes 32-63 (k = 8..15) are zero
+                const uint2 v = sm.sw[buf][q][wn * I4_WN + tn * 32 + l32];
+                cw[tn] = __builtin_bit_cast(bf16x8, (uint4){hk ? 0u : v.x, hk ? 0u : v.y, 0u, 0u});
+            }
+#pragma unroll
+            for (int tm = 0; tm < I4_TM; ++tm) {
+                const uint8_t *p = sm.x[buf] + (wm * I4_WM + tm * 32 + l32) * I4_ROWB + q * 64 + hk * 32;
+                const uint4 u0 = *reinterpret_cast<const uint4 *>(p);
+                const uint4 u1 = *reinterpret_cast<const uint4 *>(p + 16);
+                bx[tm] = (i32x8){(int)u0.x, (int)u0.y, (int)u0.z, (int)u0.w,
+                                 (int)u1.x, (int)u1.y, (int)u1.z, (int)u1.w};
+                const uint2 v = sm.sx[buf][q][wm * I4_WM + tm * 32 + l32];
+                cx[tm] = __builtin_bit_cast(bf16x8, (uint4){hk ? 0u : v.x, hk ? 0u : v.y, 0u, 0u});
+            }
+#pragma unroll
+            for (int tn = 0; tn < I4_TN; ++tn)
 #pragma unroll
                 for (int tm = 0; tm < I4_TM; ++tm) {
-                    const uint8_t *p = sm.x[buf] + (wm * I4_WM + tm * 32 + l32) * I4_ROWB + q * 64 + hk * 32;
-                    const uint4 u0 = *reinterpret_cast<const uint4 *>(p);
-                    const uint4 u1 = *reinterpret_cast<const uint4 *>(p + 16);
-                    bx[tm] = (i32x8){(int)u0.x, (int)u0.y, (int)u0.z, (int)u0.w,
-                                     (int)u1.x, (int)u1.y, (int)u1.z, (int)u1.w};
+                    const f32x16 p = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(aw[tn], bx[tm], zero16, 0, 0, 0,
+                                                                                     127, 0, 127);
+                    const f32x16 c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cw[tn], cx[tm], zero16, 0, 0, 0);
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) acc[tn][tm][i] = __builtin_fmaf(p[i], c[i], acc[tn][tm][i]);
                 }
-                float sx[I4_TM];
-#pragma unroll
-                for (int tm = 0; tm < I4_TM; ++tm) sx[tm] = sm.sx[buf][q][wm * I4_WM + tm * 32 + l32];
-#pragma unroll
-                for (int tn = 0; tn < I4_TN; ++tn) {
-                    float sw[16];
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const float4 v =
-                            *reinterpret_cast<const float4 *>(&sm.sw[buf][q][wn * I4_WN + tn * 32 + 8 * j + 4 * hk]);
-                        sw[4 * j] = v.x; sw[4 * j + 1] = v.y; sw[4 * j + 2] = v.z; sw[4 * j + 3] = v.w;
-                    }
-#pragma unroll
-                    for (int tm = 0; tm < I4_TM; ++tm) {
-                        const f32x16 p = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                            aw[tn], bx[tm], zero16, 0, 0, 0, 127, 0, 127);
-#pragma unroll
-                        for (int i = 0; i < 16; ++i)
-                            acc[tn][tm][i] = __builtin_fmaf(p[i], sw[i] * sx[tm], acc[tn][tm][i]);
-                    }
-                }
-            }
+        }
     };
 
     if (steps > 0) {

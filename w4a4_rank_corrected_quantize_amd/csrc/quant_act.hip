@@ -110,18 +110,21 @@ __global__ __launch_bounds__(64 * K1_WAVES) void quant_act_kernel(
     };
 
     f32x16 acc = {};
-    auto process = [&](int c, const K1Chunk<NLD> &L) {
+    // Process chunk c from L while the loads of chunk cn go into Ln.  The
+    // down operand of chunk c is loaded first, so waiting for it before the
+    // products does not wait for chunk cn.
+    auto process = [&](int c, const K1Chunk<NLD> &L, int cn, K1Chunk<NLD> &Ln) {
         const int kc = c * K1_CH + kl;
         const bool kv = kc < K;
         // down operand of the chunk's 16 products (A: row j = lane % 32,
-        // channels 16 t + 8 (lane / 32) .. + 7); zero past K
+        // channels 16 t + 8 (lane / 32) .. + 7), clamped into the buffer
         uint4 dn[16];
 #pragma unroll
         for (int t = 0; t < 16; ++t) {
-            const int kk = c * K1_CH + 16 * t + 8 * rh;
-            dn[t] = kk < K ? *reinterpret_cast<const uint4 *>(down + (size_t)(lane & 31) * K + kk)
-                           : (uint4){0u, 0u, 0u, 0u};
+            const int kk = min(c * K1_CH + 16 * t + 8 * rh, K - 8);
+            dn[t] = *reinterpret_cast<const uint4 *>(down + (size_t)(lane & 31) * K + kk);
         }
+        fetch(cn, Ln);
         const float sv[8] = {L.s0.x, L.s0.y, L.s0.z, L.s0.w, L.s1.x, L.s1.y, L.s1.z, L.s1.w};
 #pragma unroll
         for (int i = 0; i < NLD; ++i) {
@@ -183,6 +186,11 @@ __global__ __launch_bounds__(64 * K1_WAVES) void quant_act_kernel(
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         // h^T[j][m] += sum_k down[j][k] X[m][k] over the chunk; rows m >= nrow
         // read the last row (their outputs are dropped)
+        if ((c + 1) * K1_CH > K) {              // last, partial chunk: channels past K add nothing
+#pragma unroll
+            for (int t = 0; t < 16; ++t)
+                if (c * K1_CH + 16 * t + 8 * rh >= K) dn[t] = (uint4){0u, 0u, 0u, 0u};
+        }
         const uint8_t *src = mytile + min(lane & 31, nrow - 1) * K1_TILE_STRIDE + 16 * rh;
 #pragma unroll
         for (int t = 0; t < 16; ++t) {
@@ -201,12 +209,11 @@ __global__ __launch_bounds__(64 * K1_WAVES) void quant_act_kernel(
     int c = wave;
     if (c < nch) fetch(c, bufA);
     for (; c < nch; c += 2 * K1_WAVES) {
+        // the prefetch is unconditional (clamped): same load count on every path
         const int c1 = c + K1_WAVES;
-        fetch(min(c1, nch - 1), bufB);          // unconditional: same load count on every path
-        process(c, bufA);
+        process(c, bufA, min(c1, nch - 1), bufB);
         if (c1 >= nch) break;
-        fetch(min(c1 + K1_WAVES, nch - 1), bufA);
-        process(c1, bufB);
+        process(c1, bufB, min(c1 + K1_WAVES, nch - 1), bufA);
     }
 
     // fixed-order reduction of the per-wave partial h^T tiles; lane l holds

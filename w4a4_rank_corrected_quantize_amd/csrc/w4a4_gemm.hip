@@ -416,9 +416,12 @@ __global__ __launch_bounds__(I4_THREADS) void w4a4_int4_kernel(
 
 // ===================================================================== MXFP4
 
-constexpr int MX_BM = 128, MX_BN = 128;        // block tile (m, n)
-constexpr int MX_WM = 64, MX_WN = 64;          // wave tile
-constexpr int MX_TM = MX_WM / 16, MX_TN = MX_WN / 16;
+// Block tile 256 (n) x 128 (m), 4 waves of 128 x 64, each 4 x 2 tiles of
+// 32x32 from v_mfma_scale_f32_32x32x64_f8f6f4 (fp4 x fp4, 8 passes): per
+// 128-channel step a wave issues 16 products from 12 fragment reads.
+constexpr int MX_BN = 256, MX_BM = 128;        // block tile (n, m)
+constexpr int MX_WN = 128, MX_WM = 64;         // wave tile
+constexpr int MX_TN = MX_WN / 32, MX_TM = MX_WM / 32;
 constexpr int MX_THREADS = 256;
 constexpr int MX_STRIDE = 64;   // LDS bytes per row: 64 code bytes (128 fp4), segments swizzled
 
@@ -430,7 +433,7 @@ __device__ __forceinline__ int mx_seg(int r, int s) { return s ^ ((r >> 1) & 3);
 struct __attribute__((aligned(16))) MXSmem {
     uint8_t w[2][MX_BN * MX_STRIDE];
     uint8_t x[2][MX_BM * MX_STRIDE];
-    uint32_t ew[2][MX_BN];
+    uint32_t ew[2][MX_BN];     // the 4 E8M0 bytes of the step's 4 blocks, per row
     uint32_t ex[2][MX_BM];
 };
 
@@ -440,11 +443,6 @@ __global__ __launch_bounds__(MX_THREADS) void w4a4_mxfp4_kernel(
     const uint16_t *__restrict__ bias, int M, int N, int K, int gelu, uint16_t *__restrict__ Y)
 {
     __shared__ MXSmem sm;
-    auto &sW = sm.w;
-    auto &sX = sm.x;
-    auto &sEw = sm.ew;
-    auto &sEx = sm.ex;
-
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wn = wave & 1, wm = wave >> 1;
     int tn_, tm_;
@@ -454,124 +452,169 @@ __global__ __launch_bounds__(MX_THREADS) void w4a4_mxfp4_kernel(
     const int NB = K >> 5;          // E8M0 scales per row
     const int steps = (K + 127) >> 7;
 
-    // Loader: thread t moves segment t & 3 (32 codes, 16 bytes) of rows t/4
-    // and t/4 + 64 of both tiles, and the 4 E8M0 bytes of one row.  Loads
-    // are unconditional (rows clamped, channels past K zeroed at the LDS
-    // store), so every path keeps the same number of loads in flight.
+    // Loader: thread t moves segment t & 3 (32 codes, 16 bytes) of weight rows
+    // t/4 + 64 i (i < 4) and token rows t/4 + 64 i (i < 2), and the E8M0
+    // bytes of weight row t and (t < 128) token row t.  Loads are
+    // unconditional (rows clamped, blocks past K zeroed at the LDS store), so
+    // every path keeps the same number of loads in flight.
     const int lrow = tid >> 2, lseg = tid & 3;
-    const uint8_t *__restrict__ wsrc0 = wq + (size_t)min(n0 + lrow, N - 1) * KB;
-    const uint8_t *__restrict__ wsrc1 = wq + (size_t)min(n0 + lrow + 64, N - 1) * KB;
+    const uint8_t *__restrict__ wsrc = wq + (size_t)min(n0 + lrow, N - 1) * KB;
+    const size_t wstep = (size_t)KB * 64;                 // 64 rows further
+    const int wlast = N - 1 - n0;                        // rows past N clamp to the last row
     const uint8_t *__restrict__ xsrc0 = xq + (size_t)min(m0 + lrow, M - 1) * KB;
     const uint8_t *__restrict__ xsrc1 = xq + (size_t)min(m0 + lrow + 64, M - 1) * KB;
-    const bool is_w_scale = tid < MX_BN;
-    const uint8_t *__restrict__ ssrc = is_w_scale ? wscale + (size_t)min(n0 + tid, N - 1) * NB
-                                                  : xscale + (size_t)min(m0 + (tid - MX_BN), M - 1) * NB;
+    const uint8_t *__restrict__ wssrc = wscale + (size_t)min(n0 + tid, N - 1) * NB;
+    const uint8_t *__restrict__ xssrc = xscale + (size_t)min(m0 + (tid & 127), M - 1) * NB;
     const bool aligned_scales = (NB & 3) == 0;
-    const int wofs0 = lrow * MX_STRIDE + mx_seg(lrow, lseg) * 16;
-    const int wofs1 = (lrow + 64) * MX_STRIDE + mx_seg(lrow + 64, lseg) * 16;
+    int wofs[4], xofs[2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) wofs[i] = (lrow + 64 * i) * MX_STRIDE + mx_seg(lrow + 64 * i, lseg) * 16;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) xofs[i] = (lrow + 64 * i) * MX_STRIDE + mx_seg(lrow + 64 * i, lseg) * 16;
+    const uint8_t *wrow[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) wrow[i] = (lrow + 64 * i <= wlast) ? wsrc + wstep * i : wq + (size_t)(N - 1) * KB;
 
-    uint4 rw0, rw1, rx0, rx1;
-    uint32_t rs;
+    uint4 rw[4], rx[2];
+    uint32_t rsw, rsx;
+    auto scale4 = [&](const uint8_t *src, int st) -> uint32_t {
+        if (aligned_scales) return *reinterpret_cast<const uint32_t *>(src + min(st * 4, NB - 4));
+        uint32_t v = 0;
+        for (int q = 0; q < 4; ++q) v |= (uint32_t)src[min(st * 4 + q, NB - 1)] << (8 * q);
+        return v;
+    };
 #define MX_GLOAD(st)                                                                       \
     do {                                                                                   \
         const int b_ = min((st) * 4 + lseg, NB - 1);                                       \
-        rw0 = *reinterpret_cast<const uint4 *>(wsrc0 + b_ * 16);                           \
-        rw1 = *reinterpret_cast<const uint4 *>(wsrc1 + b_ * 16);                           \
-        rx0 = *reinterpret_cast<const uint4 *>(xsrc0 + b_ * 16);                           \
-        rx1 = *reinterpret_cast<const uint4 *>(xsrc1 + b_ * 16);                           \
-        if (aligned_scales) {                                                              \
-            rs = *reinterpret_cast<const uint32_t *>(ssrc + min((st) * 4, NB - 4));        \
-        } else {                                                                           \
-            rs = 0;                                                                        \
-            for (int q_ = 0; q_ < 4; ++q_)                                                 \
-                rs |= (uint32_t)ssrc[min((st) * 4 + q_, NB - 1)] << (8 * q_);              \
-        }                                                                                  \
+        rw[0] = *reinterpret_cast<const uint4 *>(wrow[0] + b_ * 16);                       \
+        rw[1] = *reinterpret_cast<const uint4 *>(wrow[1] + b_ * 16);                       \
+        rw[2] = *reinterpret_cast<const uint4 *>(wrow[2] + b_ * 16);                       \
+        rw[3] = *reinterpret_cast<const uint4 *>(wrow[3] + b_ * 16);                       \
+        rx[0] = *reinterpret_cast<const uint4 *>(xsrc0 + b_ * 16);                         \
+        rx[1] = *reinterpret_cast<const uint4 *>(xsrc1 + b_ * 16);                         \
+        rsw = scale4(wssrc, (st));                                                         \
+        rsx = scale4(xssrc, (st));                                                         \
     } while (0)
 #define MX_LSTORE(st, buf)                                                                 \
     do {                                                                                   \
         const bool kv_ = (st) * 4 + lseg < NB;                                             \
-        *reinterpret_cast<uint4 *>(&sW[buf][wofs0]) = keep_if(kv_, rw0);                   \
-        *reinterpret_cast<uint4 *>(&sW[buf][wofs1]) = keep_if(kv_, rw1);                   \
-        *reinterpret_cast<uint4 *>(&sX[buf][wofs0]) = keep_if(kv_, rx0);                   \
-        *reinterpret_cast<uint4 *>(&sX[buf][wofs1]) = keep_if(kv_, rx1);                   \
-        if (is_w_scale) sEw[buf][tid] = rs;                                                \
-        else sEx[buf][tid - MX_BN] = rs;                                                   \
+        _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_)                                   \
+            *reinterpret_cast<uint4 *>(&sm.w[buf][wofs[i_]]) = keep_if(kv_, rw[i_]);       \
+        _Pragma("unroll") for (int i_ = 0; i_ < 2; ++i_)                                   \
+            *reinterpret_cast<uint4 *>(&sm.x[buf][xofs[i_]]) = keep_if(kv_, rx[i_]);       \
+        sm.ew[buf][tid] = rsw;                                                             \
+        if (tid < MX_BM) sm.ex[buf][tid] = rsx;                                            \
     } while (0)
 
-    f32x4 acc[MX_TN][MX_TM];
+    f32x16 acc[MX_TN][MX_TM];
 #pragma unroll
     for (int a = 0; a < MX_TN; ++a)
 #pragma unroll
-        for (int b = 0; b < MX_TM; ++b) acc[a][b] = (f32x4){0.f, 0.f, 0.f, 0.f};
+        for (int b = 0; b < MX_TM; ++b)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.0f;
 
     if (steps > 0) {
         MX_GLOAD(0);
         MX_LSTORE(0, 0);
+        MX_GLOAD(min(1, steps - 1));
     }
     __syncthreads();
-    const int l16 = lane & 15, c = lane >> 4;
+    const int l32 = lane & 31, hk = lane >> 5;
     for (int st = 0; st < steps; ++st) {
         const int buf = st & 1;
-        if (st + 1 < steps) MX_GLOAD(st + 1);
-        i32x8 aw[MX_TN], bx[MX_TM];
-        int ew[MX_TN], ex[MX_TM];
 #pragma unroll
-        for (int tn = 0; tn < MX_TN; ++tn) {
-            const int r = wn * MX_WN + tn * 16 + l16;
-            const uint4 v = *reinterpret_cast<const uint4 *>(&sW[buf][r * MX_STRIDE + 16 * mx_seg(r, c)]);
-            aw[tn] = (i32x8){(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
-            ew[tn] = (int)((sEw[buf][r] >> (8 * c)) & 0xFFu);
+        for (int sl = 0; sl < 2; ++sl) {           // two 64-channel slices of the step
+            const int seg = 2 * sl + hk;           // the lane's 32-channel block
+            i32x8 aw[MX_TN], bx[MX_TM];
+            int ew[MX_TN], ex[MX_TM];
+#pragma unroll
+            for (int tn = 0; tn < MX_TN; ++tn) {
+                const int r = wn * MX_WN + tn * 32 + l32;
+                const uint4 v = *reinterpret_cast<const uint4 *>(&sm.w[buf][r * MX_STRIDE + 16 * mx_seg(r, seg)]);
+                aw[tn] = (i32x8){(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+                ew[tn] = (int)((sm.ew[buf][r] >> (8 * seg)) & 0xFFu);
+            }
+#pragma unroll
+            for (int tm = 0; tm < MX_TM; ++tm) {
+                const int r = wm * MX_WM + tm * 32 + l32;
+                const uint4 v = *reinterpret_cast<const uint4 *>(&sm.x[buf][r * MX_STRIDE + 16 * mx_seg(r, seg)]);
+                bx[tm] = (i32x8){(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+                ex[tm] = (int)((sm.ex[buf][r] >> (8 * seg)) & 0xFFu);
+            }
+#pragma unroll
+            for (int tn = 0; tn < MX_TN; ++tn)
+#pragma unroll
+                for (int tm = 0; tm < MX_TM; ++tm)
+                    acc[tn][tm] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                        aw[tn], bx[tm], acc[tn][tm], 4, 4, 0, ew[tn], 0, ex[tm]);
         }
-#pragma unroll
-        for (int tm = 0; tm < MX_TM; ++tm) {
-            const int r = wm * MX_WM + tm * 16 + l16;
-            const uint4 v = *reinterpret_cast<const uint4 *>(&sX[buf][r * MX_STRIDE + 16 * mx_seg(r, c)]);
-            bx[tm] = (i32x8){(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
-            ex[tm] = (int)((sEx[buf][r] >> (8 * c)) & 0xFFu);
+        if (st + 1 < steps) {
+            MX_LSTORE(st + 1, buf ^ 1);
+            MX_GLOAD(min(st + 2, steps - 1));   // unconditional: same load count on every path
         }
-#pragma unroll
-        for (int tn = 0; tn < MX_TN; ++tn)
-#pragma unroll
-            for (int tm = 0; tm < MX_TM; ++tm)
-                acc[tn][tm] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                    aw[tn], bx[tm], acc[tn][tm], 4, 4, 0, ew[tn], 0, ex[tm]);
-        if (st + 1 < steps) MX_LSTORE(st + 1, buf ^ 1);
         __syncthreads();
     }
 #undef MX_GLOAD
 #undef MX_LSTORE
 
-    // epilogue (16x16 tiles): lane holds token m = mb + tm*16 + (lane&15) and
-    // channels n = nb + tn*16 + 4*(lane>>4) + i
+    // epilogue: low-rank term via v_mfma_f32_32x32x16_bf16 (rank 32 = two k
+    // steps of 16, each with the hi and the lo part of h), then bias, GELU,
+    // and the store, staged per wave in two 64 x 64 halves
     const int mb = m0 + wm * MX_WM, nb = n0 + wn * MX_WN;
-    bf16x8 hhi[MX_TM], hlo[MX_TM];
+    bf16x8 hhi[MX_TM][2], hlo[MX_TM][2];
 #pragma unroll
-    for (int tm = 0; tm < MX_TM; ++tm) {
-        float hv[8];
-        load_h8(h, mb + tm * 16 + l16, M, 8 * c, hv);
-        split_h(hv, hhi[tm], hlo[tm]);
-    }
+    for (int tm = 0; tm < MX_TM; ++tm)
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+            float hv[8];
+            load_h8(h, mb + tm * 32 + l32, M, 16 * s2 + 8 * hk, hv);
+            split_h(hv, hhi[tm][s2], hlo[tm][s2]);
+        }
     uint8_t *tile = reinterpret_cast<uint8_t *>(&sm) + wave * OUT_TILE_BYTES;
     static_assert(4 * OUT_TILE_BYTES <= sizeof(MXSmem), "output staging fits in LDS");
 #pragma unroll
-    for (int tn = 0; tn < MX_TN; ++tn) {
-        const int nrow = nb + tn * 16 + l16;       // A-operand row of `up`
-        uint4 uv = {0u, 0u, 0u, 0u};
-        if (nrow < N) uv = *reinterpret_cast<const uint4 *>(up + (size_t)nrow * 32 + 8 * c);
-        const bf16x8 ua = __builtin_bit_cast(bf16x8, uv);
-        const float4 bv = bias4(bias, nb + tn * 16 + 4 * c, N);
+    for (int half = 0; half < 2; ++half) {
 #pragma unroll
-        for (int tm = 0; tm < MX_TM; ++tm) {
-            f32x4 lr = {0.f, 0.f, 0.f, 0.f};
-            lr = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ua, hhi[tm], lr, 0, 0, 0);
-            lr = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ua, hlo[tm], lr, 0, 0, 0);
-            float a4[4] = {acc[tn][tm][0], acc[tn][tm][1], acc[tn][tm][2], acc[tn][tm][3]};
-            float l4[4] = {lr[0], lr[1], lr[2], lr[3]};
-            stage4(tile, tm * 16 + l16, tn * 16 + 4 * c, finish4(a4, l4, bv, gelu));
+        for (int th = 0; th < 2; ++th) {
+            const int tn = 2 * half + th;
+            const int nrow = nb + tn * 32 + l32;
+            bf16x8 ua[2];
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) {
+                uint4 uv = {0u, 0u, 0u, 0u};
+                if (nrow < N) uv = *reinterpret_cast<const uint4 *>(up + (size_t)nrow * 32 + 16 * s2 + 8 * hk);
+                ua[s2] = __builtin_bit_cast(bf16x8, uv);
+            }
+            float4 bv[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) bv[j] = bias4(bias, nb + tn * 32 + 8 * j + 4 * hk, N);
+#pragma unroll
+            for (int tm = 0; tm < MX_TM; ++tm) {
+                f32x16 lr = {};
+#pragma unroll
+                for (int s2 = 0; s2 < 2; ++s2) {
+                    lr = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ua[s2], hhi[tm][s2], lr, 0, 0, 0);
+                    lr = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ua[s2], hlo[tm][s2], lr, 0, 0, 0);
+                }
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    float a4[4] = {acc[tn][tm][4 * j], acc[tn][tm][4 * j + 1], acc[tn][tm][4 * j + 2],
+                                   acc[tn][tm][4 * j + 3]};
+                    float l4[4] = {lr[4 * j], lr[4 * j + 1], lr[4 * j + 2], lr[4 * j + 3]};
+                    stage4(tile, tm * 32 + l32, th * 32 + 8 * j + 4 * hk, finish4(a4, l4, bv[j], gelu));
+                }
+            }
         }
+        // the staged half is read back by other lanes of this wave
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        flush_tile(tile, Y, mb, nb + 64 * half, M, N, lane);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
-    __syncthreads();
-    flush_tile(tile, Y, mb, nb, M, N, lane);
 }
 
 }  // namespace

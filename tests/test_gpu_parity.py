@@ -172,6 +172,7 @@ def test_quantize_act_deterministic_and_empty():
 @pytest.mark.parametrize("M,K,N,bias,gelu", [
     (128, 256, 256, False, False),       # the small configuration
     (1, 64, 8, True, False),
+    (50, 128, 40, True, True),           # a single 128-channel step
     (37, 192, 24, True, True),
     (130, 320, 136, True, False),
     (257, 512, 264, False, True),

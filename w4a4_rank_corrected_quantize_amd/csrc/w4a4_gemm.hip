@@ -437,12 +437,77 @@ struct __attribute__((aligned(16))) MXSmem {
     uint32_t ex[2][MX_BM];
 };
 
+// Epilogue of the MXFP4 kernels: low-rank term via v_mfma_f32_32x32x16_bf16
+// (rank 32 = two k steps of 16, each with the hi and the lo part of h), then
+// bias, GELU, and the store, staged in the wave's own LDS area `tile` in two
+// 64 x 64 halves.  (mb, nb) is the wave tile's first token and channel.
+__device__ __forceinline__ void mx_epilogue(const f32x16 (&acc)[4][2], const float *__restrict__ h,
+                                            const uint16_t *__restrict__ up, const uint16_t *__restrict__ bias,
+                                            int M, int N, int gelu, uint16_t *__restrict__ Y, int mb, int nb,
+                                            uint8_t *tile, int lane)
+{
+    constexpr int MX_TN = 4, MX_TM = 2;
+    const int l32 = lane & 31, hk = lane >> 5;
+    bf16x8 hhi[MX_TM][2], hlo[MX_TM][2];
+#pragma unroll
+    for (int tm = 0; tm < MX_TM; ++tm)
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+            float hv[8];
+            load_h8(h, mb + tm * 32 + l32, M, 16 * s2 + 8 * hk, hv);
+            split_h(hv, hhi[tm][s2], hlo[tm][s2]);
+        }
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+#pragma unroll
+        for (int th = 0; th < 2; ++th) {
+            const int tn = 2 * half + th;
+            const int nrow = nb + tn * 32 + l32;
+            bf16x8 ua[2];
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) {
+                uint4 uv = {0u, 0u, 0u, 0u};
+                if (nrow < N) uv = *reinterpret_cast<const uint4 *>(up + (size_t)nrow * 32 + 16 * s2 + 8 * hk);
+                ua[s2] = __builtin_bit_cast(bf16x8, uv);
+            }
+            float4 bv[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) bv[j] = bias4(bias, nb + tn * 32 + 8 * j + 4 * hk, N);
+#pragma unroll
+            for (int tm = 0; tm < MX_TM; ++tm) {
+                f32x16 lr = {};
+#pragma unroll
+                for (int s2 = 0; s2 < 2; ++s2) {
+                    lr = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ua[s2], hhi[tm][s2], lr, 0, 0, 0);
+                    lr = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ua[s2], hlo[tm][s2], lr, 0, 0, 0);
+                }
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    float a4[4] = {acc[tn][tm][4 * j], acc[tn][tm][4 * j + 1], acc[tn][tm][4 * j + 2],
+                                   acc[tn][tm][4 * j + 3]};
+                    float l4[4] = {lr[4 * j], lr[4 * j + 1], lr[4 * j + 2], lr[4 * j + 3]};
+                    stage4(tile, tm * 32 + l32, th * 32 + 8 * j + 4 * hk, finish4(a4, l4, bv[j], gelu));
+                }
+            }
+        }
+        // the staged half is read back by other lanes of this wave
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        flush_tile(tile, Y, mb, nb + 64 * half, M, N, lane);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+}
+
 __global__ __launch_bounds__(MX_THREADS) void w4a4_mxfp4_kernel(
     const uint8_t *__restrict__ xq, const uint8_t *__restrict__ xscale, const float *__restrict__ h,
     const uint8_t *__restrict__ wq, const uint8_t *__restrict__ wscale, const uint16_t *__restrict__ up,
     const uint16_t *__restrict__ bias, int M, int N, int K, int gelu, uint16_t *__restrict__ Y)
 {
     __shared__ MXSmem sm;
+    static_assert(4 * OUT_TILE_BYTES <= sizeof(MXSmem), "output staging fits in LDS");
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wn = wave & 1, wm = wave >> 1;
     int tn_, tm_;
@@ -558,63 +623,155 @@ __global__ __launch_bounds__(MX_THREADS) void w4a4_mxfp4_kernel(
 #undef MX_GLOAD
 #undef MX_LSTORE
 
-    // epilogue: low-rank term via v_mfma_f32_32x32x16_bf16 (rank 32 = two k
-    // steps of 16, each with the hi and the lo part of h), then bias, GELU,
-    // and the store, staged per wave in two 64 x 64 halves
-    const int mb = m0 + wm * MX_WM, nb = n0 + wn * MX_WN;
-    bf16x8 hhi[MX_TM][2], hlo[MX_TM][2];
+    mx_epilogue(acc, h, up, bias, M, N, gelu, Y, m0 + wm * MX_WM, n0 + wn * MX_WN,
+                reinterpret_cast<uint8_t *>(&sm) + wave * OUT_TILE_BYTES, lane);
+}
+
+// --------------------------------------------------- MXFP4, LDS-DMA pipeline
+//
+// For K % 128 == 0 (every DiT shape): the same tiles and products, but the
+// operands go from HBM straight into LDS with global_load_lds_dwordx4 /
+// _dword (no register staging), three stages deep, so the loads of step
+// st + 2 are in flight while step st computes.  Each wave moves 8 loads per
+// step (4 weight blocks and 2 token blocks of 16 rows x 64 bytes, one
+// 64-row slice of weight scales, one 32-row slice of token scales); an
+// LDS-DMA load writes its 64 lanes' 16 (or 4) bytes contiguously from the
+// wave-uniform base in M0, so each lane fetches the global segment that
+// belongs at its slot of the swizzled layout.  The compiler does not see
+// these loads: completion is awaited by hand (vmcnt) before the barrier that
+// publishes a stage, and M0 is restored after each load.
+constexpr int MXD_STAGES = 3;
+
+struct __attribute__((aligned(16))) MXDSmem {
+    uint8_t w[MXD_STAGES][MX_BN * MX_STRIDE];
+    uint8_t x[MXD_STAGES][MX_BM * MX_STRIDE];
+    uint32_t ew[MXD_STAGES][MX_BN];          // row r at [r]
+    uint32_t ex[MXD_STAGES][2 * MX_BM];      // row r at [64 (r / 32) + r % 32]
+};
+
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+__device__ __forceinline__ uint32_t lds_offset(const void *p)
+{
+    return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const lds_u8 *)p);
+}
+
+// One LDS-DMA load per lane: 16 (or 4) bytes from sbase + voff to LDS
+// lds + 16 * lane (4 * lane).  M0 is saved and restored around it.
+__device__ __forceinline__ void dma_b128(uint32_t lds, uint32_t voff, const void *sbase)
+{
+    uint32_t keep;
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %2, %3\n\ts_mov_b32 m0, %0"
+                 : "=&s"(keep) : "s"(lds), "v"(voff), "s"(sbase) : "memory");
+}
+__device__ __forceinline__ void dma_b32(uint32_t lds, uint32_t voff, const void *sbase)
+{
+    uint32_t keep;
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %2, %3\n\ts_mov_b32 m0, %0"
+                 : "=&s"(keep) : "s"(lds), "v"(voff), "s"(sbase) : "memory");
+}
+
+__global__ __launch_bounds__(MX_THREADS) void w4a4_mxfp4_dma_kernel(
+    const uint8_t *__restrict__ xq, const uint8_t *__restrict__ xscale, const float *__restrict__ h,
+    const uint8_t *__restrict__ wq, const uint8_t *__restrict__ wscale, const uint16_t *__restrict__ up,
+    const uint16_t *__restrict__ bias, int M, int N, int K, int gelu, uint16_t *__restrict__ Y)
+{
+    __shared__ MXDSmem sm;
+    static_assert(4 * OUT_TILE_BYTES <= sizeof(MXDSmem), "output staging fits in LDS");
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wn = wave & 1, wm = wave >> 1;
+    int tn_, tm_;
+    tile_coords(blockIdx.x, (N + MX_BN - 1) / MX_BN, (M + MX_BM - 1) / MX_BM, tn_, tm_);
+    const int n0 = tn_ * MX_BN, m0 = tm_ * MX_BM;
+    const int KB = K >> 1;          // code bytes per row
+    const int NB = K >> 5;          // E8M0 scales per row (a multiple of 4 here)
+    const int steps = K >> 7;
+
+    // Per-lane source offsets (bytes from the step's base); rows past N / M
+    // read the last row (their outputs are never stored).
+    uint32_t wvo[4], xvo[2];
 #pragma unroll
-    for (int tm = 0; tm < MX_TM; ++tm)
+    for (int i = 0; i < 4; ++i) {
+        const int r = 16 * (4 * i + wave) + (lane >> 2);           // weight block 4 i + wave
+        const int seg = (lane & 3) ^ ((r >> 1) & 3);
+        wvo[i] = (uint32_t)(min(n0 + r, N - 1) * KB + 16 * seg);
+    }
 #pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-            float hv[8];
-            load_h8(h, mb + tm * 32 + l32, M, 16 * s2 + 8 * hk, hv);
-            split_h(hv, hhi[tm][s2], hlo[tm][s2]);
-        }
-    uint8_t *tile = reinterpret_cast<uint8_t *>(&sm) + wave * OUT_TILE_BYTES;
-    static_assert(4 * OUT_TILE_BYTES <= sizeof(MXSmem), "output staging fits in LDS");
+    for (int i = 0; i < 2; ++i) {
+        const int r = 16 * (4 * i + wave) + (lane >> 2);           // token block 4 i + wave
+        const int seg = (lane & 3) ^ ((r >> 1) & 3);
+        xvo[i] = (uint32_t)(min(m0 + r, M - 1) * KB + 16 * seg);
+    }
+    const uint32_t ewo = (uint32_t)(min(n0 + 64 * wave + lane, N - 1) * NB);
+    const uint32_t exo = (uint32_t)(min(m0 + 32 * wave + (lane & 31), M - 1) * NB);
+
+    auto issue = [&](int st, int sg) {
+        const uint8_t *wb = wq + 64 * st, *xb = xq + 64 * st;
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
+        for (int i = 0; i < 4; ++i) dma_b128(lds_offset(&sm.w[sg][1024 * (4 * i + wave)]), wvo[i], wb);
 #pragma unroll
-        for (int th = 0; th < 2; ++th) {
-            const int tn = 2 * half + th;
-            const int nrow = nb + tn * 32 + l32;
-            bf16x8 ua[2];
+        for (int i = 0; i < 2; ++i) dma_b128(lds_offset(&sm.x[sg][1024 * (4 * i + wave)]), xvo[i], xb);
+        dma_b32(lds_offset(&sm.ew[sg][64 * wave]), ewo, wscale + 4 * st);
+        dma_b32(lds_offset(&sm.ex[sg][64 * wave]), exo, xscale + 4 * st);
+    };
+
+    f32x16 acc[MX_TN][MX_TM];
 #pragma unroll
-            for (int s2 = 0; s2 < 2; ++s2) {
-                uint4 uv = {0u, 0u, 0u, 0u};
-                if (nrow < N) uv = *reinterpret_cast<const uint4 *>(up + (size_t)nrow * 32 + 16 * s2 + 8 * hk);
-                ua[s2] = __builtin_bit_cast(bf16x8, uv);
+    for (int a = 0; a < MX_TN; ++a)
+#pragma unroll
+        for (int b = 0; b < MX_TM; ++b)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.0f;
+
+    const int l32 = lane & 31, hk = lane >> 5;
+    issue(0, 0);
+    if (steps > 1) {
+        issue(1, 1);
+        asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    } else {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+    asm volatile("s_barrier" ::: "memory");
+    int sg = 0;
+    for (int st = 0; st < steps; ++st) {
+        const bool more = st + 2 < steps;
+        if (more) issue(st + 2, sg == 0 ? 2 : sg - 1);     // stage (st + 2) % 3
+#pragma unroll
+        for (int sl = 0; sl < 2; ++sl) {           // two 64-channel slices of the step
+            const int seg = 2 * sl + hk;           // the lane's 32-channel block
+            i32x8 aw[MX_TN], bx[MX_TM];
+            int ew[MX_TN], ex[MX_TM];
+#pragma unroll
+            for (int tn = 0; tn < MX_TN; ++tn) {
+                const int r = wn * MX_WN + tn * 32 + l32;
+                const uint4 v = *reinterpret_cast<const uint4 *>(&sm.w[sg][r * MX_STRIDE + 16 * mx_seg(r, seg)]);
+                aw[tn] = (i32x8){(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+                ew[tn] = (int)((sm.ew[sg][r] >> (8 * seg)) & 0xFFu);
             }
-            float4 bv[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) bv[j] = bias4(bias, nb + tn * 32 + 8 * j + 4 * hk, N);
 #pragma unroll
             for (int tm = 0; tm < MX_TM; ++tm) {
-                f32x16 lr = {};
-#pragma unroll
-                for (int s2 = 0; s2 < 2; ++s2) {
-                    lr = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ua[s2], hhi[tm][s2], lr, 0, 0, 0);
-                    lr = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ua[s2], hlo[tm][s2], lr, 0, 0, 0);
-                }
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    float a4[4] = {acc[tn][tm][4 * j], acc[tn][tm][4 * j + 1], acc[tn][tm][4 * j + 2],
-                                   acc[tn][tm][4 * j + 3]};
-                    float l4[4] = {lr[4 * j], lr[4 * j + 1], lr[4 * j + 2], lr[4 * j + 3]};
-                    stage4(tile, tm * 32 + l32, th * 32 + 8 * j + 4 * hk, finish4(a4, l4, bv[j], gelu));
-                }
+                const int r = wm * MX_WM + tm * 32 + l32;
+                const uint4 v = *reinterpret_cast<const uint4 *>(&sm.x[sg][r * MX_STRIDE + 16 * mx_seg(r, seg)]);
+                bx[tm] = (i32x8){(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+                ex[tm] = (int)((sm.ex[sg][64 * (r >> 5) + (r & 31)] >> (8 * seg)) & 0xFFu);
             }
+#pragma unroll
+            for (int tn = 0; tn < MX_TN; ++tn)
+#pragma unroll
+                for (int tm = 0; tm < MX_TM; ++tm)
+                    acc[tn][tm] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                        aw[tn], bx[tm], acc[tn][tm], 4, 4, 0, ew[tn], 0, ex[tm]);
         }
-        // the staged half is read back by other lanes of this wave
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        flush_tile(tile, Y, mb, nb + 64 * half, M, N, lane);
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        // step st + 1 has landed (this wave's part) once at most the 8 loads
+        // just issued are outstanding; the barrier publishes it and frees
+        // stage st for the loads of step st + 3
+        // (lgkmcnt: this wave's fragment reads of stage st are complete too)
+        if (more) asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)" ::: "memory");
+        else asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+        asm volatile("s_barrier" ::: "memory");
+        sg = sg == 2 ? 0 : sg + 1;
     }
+    mx_epilogue(acc, h, up, bias, M, N, gelu, Y, m0 + wm * MX_WM, n0 + wn * MX_WN,
+                reinterpret_cast<uint8_t *>(&sm) + wave * OUT_TILE_BYTES, lane);
 }
 
 }  // namespace
@@ -630,8 +787,11 @@ hipError_t launch_w4a4_linear(const uint8_t *xq, const void *xscale, const float
                            (const float *)xscale, h, wq, (const float *)wscale, up, bias, M, N, K, gelu, Y);
     } else {
         const int tiles = ((N + MX_BN - 1) / MX_BN) * ((M + MX_BM - 1) / MX_BM);
-        hipLaunchKernelGGL(w4a4_mxfp4_kernel, dim3((unsigned)tiles), dim3(MX_THREADS), 0, stream, xq, (const uint8_t *)xscale, h,
-                           wq, (const uint8_t *)wscale, up, bias, M, N, K, gelu, Y);
+        // the LDS-DMA kernel takes whole 128-channel steps and 32-bit offsets
+        const bool dma = K % 128 == 0 && (int64_t)(M > N ? M : N) * (K / 2) < ((int64_t)1 << 31);
+        hipLaunchKernelGGL(dma ? w4a4_mxfp4_dma_kernel : w4a4_mxfp4_kernel, dim3((unsigned)tiles),
+                           dim3(MX_THREADS), 0, stream, xq, (const uint8_t *)xscale, h, wq,
+                           (const uint8_t *)wscale, up, bias, M, N, K, gelu, Y);
     }
     return hipGetLastError();
 }

@@ -437,20 +437,22 @@ struct __attribute__((aligned(16))) MXSmem {
     uint32_t ex[2][MX_BM];
 };
 
-// Epilogue of the MXFP4 kernels: low-rank term via v_mfma_f32_32x32x16_bf16
-// (rank 32 = two k steps of 16, each with the hi and the lo part of h), then
-// bias, GELU, and the store, staged in the wave's own LDS area `tile` in two
-// 64 x 64 halves.  (mb, nb) is the wave tile's first token and channel.
-__device__ __forceinline__ void mx_epilogue(const f32x16 (&acc)[4][2], const float *__restrict__ h,
-                                            const uint16_t *__restrict__ up, const uint16_t *__restrict__ bias,
-                                            int M, int N, int gelu, uint16_t *__restrict__ Y, int mb, int nb,
-                                            uint8_t *tile, int lane)
+// Epilogue of a wave tile of TN x TM 32x32 tiles (TN even): low-rank term
+// via v_mfma_f32_32x32x16_bf16 (rank 32 = two k steps of 16, each with the hi
+// and the lo part of h), then bias, GELU, and the store, staged in the wave's
+// own LDS area `tile` one 64 x 64 block at a time.  (mb, nb) is the wave
+// tile's first token and channel.
+template <int TN, int TM>
+__device__ __forceinline__ void wave_epilogue(const f32x16 (&acc)[TN][TM], const float *__restrict__ h,
+                                              const uint16_t *__restrict__ up, const uint16_t *__restrict__ bias,
+                                              int M, int N, int gelu, uint16_t *__restrict__ Y, int mb, int nb,
+                                              uint8_t *tile, int lane)
 {
-    constexpr int MX_TN = 4, MX_TM = 2;
+    static_assert(TN % 2 == 0 && TM == 2, "64 x 64 staging blocks");
     const int l32 = lane & 31, hk = lane >> 5;
-    bf16x8 hhi[MX_TM][2], hlo[MX_TM][2];
+    bf16x8 hhi[TM][2], hlo[TM][2];
 #pragma unroll
-    for (int tm = 0; tm < MX_TM; ++tm)
+    for (int tm = 0; tm < TM; ++tm)
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
             float hv[8];
@@ -458,7 +460,7 @@ __device__ __forceinline__ void mx_epilogue(const f32x16 (&acc)[4][2], const flo
             split_h(hv, hhi[tm][s2], hlo[tm][s2]);
         }
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
+    for (int half = 0; half < TN / 2; ++half) {
 #pragma unroll
         for (int th = 0; th < 2; ++th) {
             const int tn = 2 * half + th;
@@ -474,7 +476,7 @@ __device__ __forceinline__ void mx_epilogue(const f32x16 (&acc)[4][2], const flo
 #pragma unroll
             for (int j = 0; j < 4; ++j) bv[j] = bias4(bias, nb + tn * 32 + 8 * j + 4 * hk, N);
 #pragma unroll
-            for (int tm = 0; tm < MX_TM; ++tm) {
+            for (int tm = 0; tm < TM; ++tm) {
                 f32x16 lr = {};
 #pragma unroll
                 for (int s2 = 0; s2 < 2; ++s2) {
@@ -623,7 +625,7 @@ __global__ __launch_bounds__(MX_THREADS) void w4a4_mxfp4_kernel(
 #undef MX_GLOAD
 #undef MX_LSTORE
 
-    mx_epilogue(acc, h, up, bias, M, N, gelu, Y, m0 + wm * MX_WM, n0 + wn * MX_WN,
+    wave_epilogue<MX_TN, MX_TM>(acc, h, up, bias, M, N, gelu, Y, m0 + wm * MX_WM, n0 + wn * MX_WN,
                 reinterpret_cast<uint8_t *>(&sm) + wave * OUT_TILE_BYTES, lane);
 }
 
@@ -770,7 +772,7 @@ __global__ __launch_bounds__(MX_THREADS) void w4a4_mxfp4_dma_kernel(
         asm volatile("s_barrier" ::: "memory");
         sg = sg == 2 ? 0 : sg + 1;
     }
-    mx_epilogue(acc, h, up, bias, M, N, gelu, Y, m0 + wm * MX_WM, n0 + wn * MX_WN,
+    wave_epilogue<MX_TN, MX_TM>(acc, h, up, bias, M, N, gelu, Y, m0 + wm * MX_WM, n0 + wn * MX_WN,
                 reinterpret_cast<uint8_t *>(&sm) + wave * OUT_TILE_BYTES, lane);
 }
 
@@ -781,6 +783,7 @@ hipError_t launch_w4a4_linear(const uint8_t *xq, const void *xscale, const float
                               int K, svdq_precision prec, svdq_epilogue epi, uint16_t *Y, hipStream_t stream)
 {
     const int gelu = epi == SVDQ_EPI_GELU_TANH ? 1 : 0;
+    const int64_t rows = M > N ? M : N;
     if (prec == SVDQ_INT4) {
         const int tiles = ((N + I4_BN - 1) / I4_BN) * ((M + I4_BM - 1) / I4_BM);
         hipLaunchKernelGGL(w4a4_int4_kernel, dim3((unsigned)tiles), dim3(I4_THREADS), 0, stream, xq,
@@ -788,7 +791,7 @@ hipError_t launch_w4a4_linear(const uint8_t *xq, const void *xscale, const float
     } else {
         const int tiles = ((N + MX_BN - 1) / MX_BN) * ((M + MX_BM - 1) / MX_BM);
         // the LDS-DMA kernel takes whole 128-channel steps and 32-bit offsets
-        const bool dma = K % 128 == 0 && (int64_t)(M > N ? M : N) * (K / 2) < ((int64_t)1 << 31);
+        const bool dma = K % 128 == 0 && rows * (K / 2) < ((int64_t)1 << 31);
         hipLaunchKernelGGL(dma ? w4a4_mxfp4_dma_kernel : w4a4_mxfp4_kernel, dim3((unsigned)tiles),
                            dim3(MX_THREADS), 0, stream, xq, (const uint8_t *)xscale, h, wq,
                            (const uint8_t *)wscale, up, bias, M, N, K, gelu, Y);

@@ -11,15 +11,16 @@
 //
 // Work decomposition (gfx950, wave64).  The kernel is HBM-bound, so every
 // global access is a run of full 128-byte lines:
-//   * a block owns R = 2 * NLD consecutive rows (R at most 24, chosen so that
-//     there is about one block per CU) and all of K; its 4 waves take the
-//     256-channel chunks c = wave, wave + 4, ...
-//   * a chunk is loaded as R/2 row pairs: lanes 0-31 read 512 contiguous bytes
-//     of one row, lanes 32-63 of the next (lane l holds channels 8 (l % 32) ..
-//     + 7); the next chunk's loads are in flight while this one is processed;
+//   * a block owns R consecutive rows (R at most 32, chosen so that there is
+//     about one block per CU) and all of K; its 8 waves (two per SIMD) take
+//     the 128-channel chunks c = wave, wave + 8, ...
+//   * a chunk is loaded as NL = ceil(R / 4) loads of 4 rows: each quarter of
+//     the wave reads 256 contiguous bytes of one row (lane l holds channels
+//     8 (l % 16) .. + 7 of row 4 i + l / 16); the next chunk's loads are in
+//     flight while this one is processed;
 //   * a quantization group is 8 neighbouring lanes (4 for MXFP4), so the
 //     group absmax takes three DPP steps, and each lane writes its 8 codes as
-//     one dword: 128 contiguous code bytes per row per load;
+//     one dword: 64 contiguous code bytes per row per load;
 //   * the down projection needs X in the matrix-core operand layout (one row
 //     per lane), so each wave copies its chunk into its own LDS tile and reads
 //     it back transposed for v_mfma_f32_32x32x16_bf16 (A = down rows j,
@@ -38,8 +39,11 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int K1_WAVES = 4;
-constexpr int K1_CH = 256;                  // channels per chunk
+constexpr int K1_WAVES = 8;
+constexpr int K1_CH = 128;                  // channels per chunk
+constexpr int K1_LPR = K1_CH / 8;           // lanes per row in a load (8 channels each)
+constexpr int K1_RPL = 64 / K1_LPR;         // rows per load
+constexpr int K1_RMAX = 32;                 // rows per block, at most (one 32-row product tile)
 constexpr int K1_TILE_STRIDE = 2 * K1_CH + 16;   // LDS bytes per row of a wave's X tile
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
@@ -69,27 +73,27 @@ __device__ __forceinline__ uint32_t sign_bits(const float *v)
     return (((ea | eb) >> 4) & 0x08080808u) | ((oa | ob) & 0x80808080u);
 }
 
-template <int NLD>
+template <int NL>
 struct K1Chunk {
-    uint4 x[NLD];          // row pair i: lanes 0-31 row 2i, lanes 32-63 row 2i + 1
+    uint4 x[NL];           // load i: lane l holds row 4 i + l / 16
     float4 s0, s1;         // smoothing factors of the lane's 8 channels
 };
 
-template <bool MX, int NLD>
+template <bool MX, int NL>
 __global__ __launch_bounds__(64 * K1_WAVES) void quant_act_kernel(
-    const uint16_t *__restrict__ X, int M, int K, const float *__restrict__ smooth,
+    const uint16_t *__restrict__ X, int M, int K, int R, const float *__restrict__ smooth,
     const uint16_t *__restrict__ down, uint8_t *__restrict__ xq, void *__restrict__ xscale,
     float *__restrict__ h)
 {
-    __shared__ __attribute__((aligned(16))) uint8_t tile[K1_WAVES][32 * K1_TILE_STRIDE];
+    __shared__ __attribute__((aligned(16))) uint8_t tile[K1_WAVES][K1_RMAX * K1_TILE_STRIDE];
     __shared__ float red[K1_WAVES][32][33];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    constexpr int R = 2 * NLD;
     const int row0 = blockIdx.x * R;
-    const int nrow = min(R, M - row0);      // >= 1 (the grid is sized by the host)
+    const int nrow = min(R, M - row0);      // 1 <= nrow <= 4 NL (the grid is sized by the host)
     const int nch = (K + K1_CH - 1) / K1_CH;
-    const int rh = lane >> 5;               // row within a pair
-    const int kl = 8 * (lane & 31);         // first channel of the lane within a chunk
+    const int rq = lane / K1_LPR;           // row within a load
+    const int kl = 8 * (lane % K1_LPR);     // first channel of the lane within a chunk
+    const int hk = lane >> 5;               // half of the product operand (channels 8 hk .. + 7)
     const int KB = K >> 1;                  // code bytes per row
     uint8_t *mytile = tile[wave];
 
@@ -98,11 +102,11 @@ __global__ __launch_bounds__(64 * K1_WAVES) void quant_act_kernel(
     // block's last row reads that last row and stores nothing; channels past
     // K read the last 8 channels and store nothing (their groups lie entirely
     // past K, since K is a multiple of the group size).
-    auto fetch = [&](int c, K1Chunk<NLD> &L) {
+    auto fetch = [&](int c, K1Chunk<NL> &L) {
         const int k = min(c * K1_CH + kl, K - 8);
 #pragma unroll
-        for (int i = 0; i < NLD; ++i) {
-            const int r = min(2 * i + rh, nrow - 1);
+        for (int i = 0; i < NL; ++i) {
+            const int r = min(K1_RPL * i + rq, nrow - 1);
             L.x[i] = *reinterpret_cast<const uint4 *>(X + (size_t)(row0 + r) * K + k);
         }
         L.s0 = *reinterpret_cast<const float4 *>(smooth + k);
@@ -113,24 +117,24 @@ __global__ __launch_bounds__(64 * K1_WAVES) void quant_act_kernel(
     // Process chunk c from L while the loads of chunk cn go into Ln.  The
     // down operand of chunk c is loaded first, so waiting for it before the
     // products does not wait for chunk cn.
-    auto process = [&](int c, const K1Chunk<NLD> &L, int cn, K1Chunk<NLD> &Ln) {
+    auto process = [&](int c, const K1Chunk<NL> &L, int cn, K1Chunk<NL> &Ln) {
         const int kc = c * K1_CH + kl;
         const bool kv = kc < K;
-        // down operand of the chunk's 16 products (A: row j = lane % 32,
+        // down operand of the chunk's 8 products (A: row j = lane % 32,
         // channels 16 t + 8 (lane / 32) .. + 7), clamped into the buffer
-        uint4 dn[16];
+        uint4 dn[K1_CH / 16];
 #pragma unroll
-        for (int t = 0; t < 16; ++t) {
-            const int kk = min(c * K1_CH + 16 * t + 8 * rh, K - 8);
+        for (int t = 0; t < K1_CH / 16; ++t) {
+            const int kk = min(c * K1_CH + 16 * t + 8 * hk, K - 8);
             dn[t] = *reinterpret_cast<const uint4 *>(down + (size_t)(lane & 31) * K + kk);
         }
         fetch(cn, Ln);
         const float sv[8] = {L.s0.x, L.s0.y, L.s0.z, L.s0.w, L.s1.x, L.s1.y, L.s1.z, L.s1.w};
 #pragma unroll
-        for (int i = 0; i < NLD; ++i) {
+        for (int i = 0; i < NL; ++i) {
             const uint4 w = L.x[i];
-            *reinterpret_cast<uint4 *>(mytile + (2 * i + rh) * K1_TILE_STRIDE + 2 * kl) = w;
-            const int rloc = 2 * i + rh;
+            const int rloc = K1_RPL * i + rq;
+            if (rloc < K1_RMAX) *reinterpret_cast<uint4 *>(mytile + rloc * K1_TILE_STRIDE + 2 * kl) = w;
             const bool st = kv && rloc < nrow;
             const size_t row = (size_t)(row0 + rloc);
             const uint32_t wv[4] = {w.x, w.y, w.z, w.w};
@@ -188,12 +192,12 @@ __global__ __launch_bounds__(64 * K1_WAVES) void quant_act_kernel(
         // read the last row (their outputs are dropped)
         if ((c + 1) * K1_CH > K) {              // last, partial chunk: channels past K add nothing
 #pragma unroll
-            for (int t = 0; t < 16; ++t)
-                if (c * K1_CH + 16 * t + 8 * rh >= K) dn[t] = (uint4){0u, 0u, 0u, 0u};
+            for (int t = 0; t < K1_CH / 16; ++t)
+                if (c * K1_CH + 16 * t + 8 * hk >= K) dn[t] = (uint4){0u, 0u, 0u, 0u};
         }
-        const uint8_t *src = mytile + min(lane & 31, nrow - 1) * K1_TILE_STRIDE + 16 * rh;
+        const uint8_t *src = mytile + min(lane & 31, nrow - 1) * K1_TILE_STRIDE + 16 * hk;
 #pragma unroll
-        for (int t = 0; t < 16; ++t) {
+        for (int t = 0; t < K1_CH / 16; ++t) {
             const uint4 b = *reinterpret_cast<const uint4 *>(src + 32 * t);
             acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(dn[t]), as_bf16x8(b), acc, 0, 0, 0);
         }
@@ -205,7 +209,7 @@ __global__ __launch_bounds__(64 * K1_WAVES) void quant_act_kernel(
 
     // ping-pong register buffers: the next chunk's loads are in flight while
     // the current one is processed
-    K1Chunk<NLD> bufA, bufB;
+    K1Chunk<NL> bufA, bufB;
     int c = wave;
     if (c < nch) fetch(c, bufA);
     for (; c < nch; c += 2 * K1_WAVES) {
@@ -219,7 +223,7 @@ __global__ __launch_bounds__(64 * K1_WAVES) void quant_act_kernel(
     // fixed-order reduction of the per-wave partial h^T tiles; lane l holds
     // column m = l % 32 and rows j = 8 (i / 4) + 4 (l / 32) + i % 4
 #pragma unroll
-    for (int i = 0; i < 16; ++i) red[wave][lane & 31][8 * (i >> 2) + 4 * rh + (i & 3)] = acc[i];
+    for (int i = 0; i < 16; ++i) red[wave][lane & 31][8 * (i >> 2) + 4 * hk + (i & 3)] = acc[i];
     __syncthreads();
     for (int t = threadIdx.x; t < nrow * 32; t += 64 * K1_WAVES) {
         const int m = t >> 5, j = t & 31;
@@ -248,27 +252,30 @@ int device_cu_count()
 hipError_t launch_quant_act(const uint16_t *X, int M, int K, const float *smooth, const uint16_t *down,
                             svdq_precision prec, uint8_t *xq, void *xscale, float *h, hipStream_t stream)
 {
-    // rows per block: about one block per CU, R = 2 * NLD from a small menu
+    // rows per block: about one block per CU, at most one 32-row product tile
     const int ncu = device_cu_count();
-    const int want = (M + 2 * ncu - 1) / (2 * ncu);      // row pairs per block
-    const int nld = want <= 1 ? 1 : want <= 2 ? 2 : want <= 4 ? 4 : want <= 6 ? 6 : want <= 9 ? 9 : 12;
-    const dim3 grid((unsigned)((M + 2 * nld - 1) / (2 * nld))), block(64 * K1_WAVES);
+    int R = (M + ncu - 1) / ncu;
+    R = R < 1 ? 1 : (R > K1_RMAX ? K1_RMAX : R);
+    const int nl = (R + K1_RPL - 1) / K1_RPL;           // loads per chunk
+    const dim3 grid((unsigned)((M + R - 1) / R)), block(64 * K1_WAVES);
 #define K1_LAUNCH(N)                                                                                    \
     case N:                                                                                             \
         if (prec == SVDQ_INT4)                                                                          \
-            hipLaunchKernelGGL((quant_act_kernel<false, N>), grid, block, 0, stream, X, M, K, smooth,    \
+            hipLaunchKernelGGL((quant_act_kernel<false, N>), grid, block, 0, stream, X, M, K, R, smooth, \
                                down, xq, xscale, h);                                                    \
         else                                                                                            \
-            hipLaunchKernelGGL((quant_act_kernel<true, N>), grid, block, 0, stream, X, M, K, smooth,     \
+            hipLaunchKernelGGL((quant_act_kernel<true, N>), grid, block, 0, stream, X, M, K, R, smooth,  \
                                down, xq, xscale, h);                                                    \
         break;
-    switch (nld) {
+    switch (nl) {
         K1_LAUNCH(1)
         K1_LAUNCH(2)
+        K1_LAUNCH(3)
         K1_LAUNCH(4)
+        K1_LAUNCH(5)
         K1_LAUNCH(6)
-        K1_LAUNCH(9)
-        K1_LAUNCH(12)
+        K1_LAUNCH(7)
+        K1_LAUNCH(8)
     }
 #undef K1_LAUNCH
     return hipGetLastError();

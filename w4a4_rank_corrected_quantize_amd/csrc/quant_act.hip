@@ -177,9 +177,15 @@ __global__ __launch_bounds__(64 * K1_WAVES) void quant_act_kernel(
                 a = group_max<4>(a);
                 const uint32_t e8 = mx_block_e8m0(a);
                 const float inv = mx_inv_scale(e8);
-                code = 0;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) code |= e2m1_code(v[e], inv) << (4 * e);
+                // t = xhat 2^-X is exact; the hardware E2M1 conversion (unit
+                // scale) rounds to the grid with ties to the even index,
+                // saturates at 6 and keeps the sign of zero, i.e. it is
+                // e2m1_code (checked on the GPU against e2m1_code for every fp32
+                // t with |t| < 16, both signs)
+                code = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, v[0] * inv, v[1] * inv, 1.0f, 0);
+                code = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(code, v[2] * inv, v[3] * inv, 1.0f, 1);
+                code = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(code, v[4] * inv, v[5] * inv, 1.0f, 2);
+                code = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(code, v[6] * inv, v[7] * inv, 1.0f, 3);
                 if (st && (lane & 3) == 0) reinterpret_cast<uint8_t *>(xscale)[row * (K >> 5) + (kc >> 5)] = (uint8_t)e8;
             }
             if (st) *reinterpret_cast<uint32_t *>(xq + row * KB + (kc >> 1)) = code;

@@ -31,9 +31,15 @@ SVDQ_HD float bits_f32(uint32_t u) { return __builtin_bit_cast(float, u); }
 
 // ------------------------------------------------------------------ INT4
 
+// fl32(absmax / 7): the reciprocal product corrected once by its exact fma
+// remainder is the correctly rounded quotient for every finite absmax >= 0
+// (checked exhaustively, subnormal quotients included); below the normal
+// range the result is then moved up one ulp when it lies under absmax / 7.
 SVDQ_HD float int4_group_scale(float absmax)
 {
-    float sc = absmax / 7.0f;                      // correctly rounded
+    const float c = 0.142857149f;                  // fl32(1 / 7)
+    float sc = absmax * c;
+    sc = __builtin_fmaf(__builtin_fmaf(-sc, 7.0f, absmax), c, sc);
     if (sc < 1.17549435e-38f && __builtin_fmaf(sc, 7.0f, -absmax) < 0.0f)
         sc = bits_f32(f32_bits(sc) + 1u);          // next fp32 upward (sc >= 0)
     return sc;

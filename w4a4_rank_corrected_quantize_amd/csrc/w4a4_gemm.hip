@@ -631,24 +631,33 @@ __global__ __launch_bounds__(MX_THREADS) void w4a4_mxfp4_kernel(
 
 // --------------------------------------------------- MXFP4, LDS-DMA pipeline
 //
-// For K % 128 == 0 (every DiT shape): the same tiles and products, but the
-// operands go from HBM straight into LDS with global_load_lds_dwordx4 /
-// _dword (no register staging), three stages deep, so the loads of step
-// st + 2 are in flight while step st computes.  Each wave moves 8 loads per
-// step (4 weight blocks and 2 token blocks of 16 rows x 64 bytes, one
-// 64-row slice of weight scales, one 32-row slice of token scales); an
-// LDS-DMA load writes its 64 lanes' 16 (or 4) bytes contiguously from the
-// wave-uniform base in M0, so each lane fetches the global segment that
-// belongs at its slot of the swizzled layout.  The compiler does not see
-// these loads: completion is awaited by hand (vmcnt) before the barrier that
-// publishes a stage, and M0 is restored after each load.
-constexpr int MXD_STAGES = 3;
+// For K % 256 == 0 (every DiT shape): the operands go from HBM straight into
+// LDS with global_load_lds_dwordx4 / _dword (no register staging), double
+// buffered, in 256-channel steps so that every row access is a whole
+// 128-byte line (the address unit handles each line once).  Block tile
+// 256 (n) x 256 (m) with 8 waves (2 per SIMD) of 128 x 64, the same per-wave
+// products as above.  Per step each wave moves 10 loads: 4 weight and 4 token
+// blocks of 8 rows x 128 bytes, and one 32-row slice of the weight and of the
+// token E8M0 bytes (two dwords per row).  An LDS-DMA load writes its 64
+// lanes' 16 (or 4) bytes contiguously from the wave-uniform base in M0, so
+// each lane fetches the global segment that belongs at its slot of the
+// swizzled layout.  The compiler does not see these loads: completion is
+// awaited by hand (vmcnt) before the barrier that publishes a stage, and M0
+// is restored after each load.
+constexpr int MXD_BN = 256, MXD_BM = 256;
+constexpr int MXD_THREADS = 512;
+constexpr int MXD_ROW = 128;        // LDS bytes per row and step: 256 fp4, 16-byte segments swizzled
+
+// 16-byte segment s of LDS row r lives at segment s ^ (r & 7): the loads'
+// 8 segments of a row and the fragment reads of 8 rows at one segment both
+// hit 8 distinct 4-bank groups.
+__device__ __forceinline__ int mxd_seg(int r, int s) { return s ^ (r & 7); }
 
 struct __attribute__((aligned(16))) MXDSmem {
-    uint8_t w[MXD_STAGES][MX_BN * MX_STRIDE];
-    uint8_t x[MXD_STAGES][MX_BM * MX_STRIDE];
-    uint32_t ew[MXD_STAGES][MX_BN];          // row r at [r]
-    uint32_t ex[MXD_STAGES][2 * MX_BM];      // row r at [64 (r / 32) + r % 32]
+    uint8_t w[2][MXD_BN * MXD_ROW];
+    uint8_t x[2][MXD_BM * MXD_ROW];
+    uint32_t ew[2][2 * MXD_BN];      // row r, dword d (blocks 4 d .. 4 d + 3) at [64 (r / 32) + 32 d + r % 32]
+    uint32_t ex[2][2 * MXD_BM];
 };
 
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
@@ -672,48 +681,43 @@ __device__ __forceinline__ void dma_b32(uint32_t lds, uint32_t voff, const void 
                  : "=&s"(keep) : "s"(lds), "v"(voff), "s"(sbase) : "memory");
 }
 
-__global__ __launch_bounds__(MX_THREADS) void w4a4_mxfp4_dma_kernel(
+__global__ __launch_bounds__(MXD_THREADS) void w4a4_mxfp4_dma_kernel(
     const uint8_t *__restrict__ xq, const uint8_t *__restrict__ xscale, const float *__restrict__ h,
     const uint8_t *__restrict__ wq, const uint8_t *__restrict__ wscale, const uint16_t *__restrict__ up,
     const uint16_t *__restrict__ bias, int M, int N, int K, int gelu, uint16_t *__restrict__ Y)
 {
     __shared__ MXDSmem sm;
-    static_assert(4 * OUT_TILE_BYTES <= sizeof(MXDSmem), "output staging fits in LDS");
+    static_assert(8 * OUT_TILE_BYTES <= sizeof(MXDSmem), "output staging fits in LDS");
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wn = wave & 1, wm = wave >> 1;
+    const int wn = wave & 1, wm = wave >> 1;            // 2 (n) x 4 (m) waves
     int tn_, tm_;
-    tile_coords(blockIdx.x, (N + MX_BN - 1) / MX_BN, (M + MX_BM - 1) / MX_BM, tn_, tm_);
-    const int n0 = tn_ * MX_BN, m0 = tm_ * MX_BM;
+    tile_coords(blockIdx.x, (N + MXD_BN - 1) / MXD_BN, (M + MXD_BM - 1) / MXD_BM, tn_, tm_);
+    const int n0 = tn_ * MXD_BN, m0 = tm_ * MXD_BM;
     const int KB = K >> 1;          // code bytes per row
-    const int NB = K >> 5;          // E8M0 scales per row (a multiple of 4 here)
-    const int steps = K >> 7;
+    const int NB = K >> 5;          // E8M0 scales per row (a multiple of 8 here)
+    const int steps = K >> 8;
 
     // Per-lane source offsets (bytes from the step's base); rows past N / M
     // read the last row (their outputs are never stored).
-    uint32_t wvo[4], xvo[2];
+    uint32_t wvo[4], xvo[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const int r = 16 * (4 * i + wave) + (lane >> 2);           // weight block 4 i + wave
-        const int seg = (lane & 3) ^ ((r >> 1) & 3);
+        const int r = 8 * (8 * i + wave) + (lane >> 3);            // block 8 i + wave
+        const int seg = (lane & 7) ^ (r & 7);
         wvo[i] = (uint32_t)(min(n0 + r, N - 1) * KB + 16 * seg);
-    }
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int r = 16 * (4 * i + wave) + (lane >> 2);           // token block 4 i + wave
-        const int seg = (lane & 3) ^ ((r >> 1) & 3);
         xvo[i] = (uint32_t)(min(m0 + r, M - 1) * KB + 16 * seg);
     }
-    const uint32_t ewo = (uint32_t)(min(n0 + 64 * wave + lane, N - 1) * NB);
-    const uint32_t exo = (uint32_t)(min(m0 + 32 * wave + (lane & 31), M - 1) * NB);
+    const uint32_t ewo = (uint32_t)(min(n0 + 32 * wave + (lane & 31), N - 1) * NB + 4 * (lane >> 5));
+    const uint32_t exo = (uint32_t)(min(m0 + 32 * wave + (lane & 31), M - 1) * NB + 4 * (lane >> 5));
 
     auto issue = [&](int st, int sg) {
-        const uint8_t *wb = wq + 64 * st, *xb = xq + 64 * st;
+        const uint8_t *wb = wq + 128 * st, *xb = xq + 128 * st;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) dma_b128(lds_offset(&sm.w[sg][1024 * (4 * i + wave)]), wvo[i], wb);
+        for (int i = 0; i < 4; ++i) dma_b128(lds_offset(&sm.w[sg][1024 * (8 * i + wave)]), wvo[i], wb);
 #pragma unroll
-        for (int i = 0; i < 2; ++i) dma_b128(lds_offset(&sm.x[sg][1024 * (4 * i + wave)]), xvo[i], xb);
-        dma_b32(lds_offset(&sm.ew[sg][64 * wave]), ewo, wscale + 4 * st);
-        dma_b32(lds_offset(&sm.ex[sg][64 * wave]), exo, xscale + 4 * st);
+        for (int i = 0; i < 4; ++i) dma_b128(lds_offset(&sm.x[sg][1024 * (8 * i + wave)]), xvo[i], xb);
+        dma_b32(lds_offset(&sm.ew[sg][64 * wave]), ewo, wscale + 8 * st);
+        dma_b32(lds_offset(&sm.ex[sg][64 * wave]), exo, xscale + 8 * st);
     };
 
     f32x16 acc[MX_TN][MX_TM];
@@ -726,54 +730,61 @@ __global__ __launch_bounds__(MX_THREADS) void w4a4_mxfp4_dma_kernel(
 
     const int l32 = lane & 31, hk = lane >> 5;
     issue(0, 0);
-    if (steps > 1) {
-        issue(1, 1);
-        asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-    } else {
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     asm volatile("s_barrier" ::: "memory");
-    int sg = 0;
     for (int st = 0; st < steps; ++st) {
-        const bool more = st + 2 < steps;
-        if (more) issue(st + 2, sg == 0 ? 2 : sg - 1);     // stage (st + 2) % 3
-#pragma unroll
-        for (int sl = 0; sl < 2; ++sl) {           // two 64-channel slices of the step
-            const int seg = 2 * sl + hk;           // the lane's 32-channel block
-            i32x8 aw[MX_TN], bx[MX_TM];
-            int ew[MX_TN], ex[MX_TM];
+        const int sg = st & 1;
+        if (st + 1 < steps) issue(st + 1, sg ^ 1);
+        // four 64-channel slices per step; the fragments of slice sl + 1 are
+        // read while the products of slice sl run
+        struct Frag { i32x8 aw[MX_TN], bx[MX_TM]; int ew[MX_TN], ex[MX_TM]; };
+        auto read_slice = [&](int sl, Frag &f) {
+            const int blk = 2 * sl + hk;           // the lane's 32-channel block (segment) of the step
 #pragma unroll
             for (int tn = 0; tn < MX_TN; ++tn) {
                 const int r = wn * MX_WN + tn * 32 + l32;
-                const uint4 v = *reinterpret_cast<const uint4 *>(&sm.w[sg][r * MX_STRIDE + 16 * mx_seg(r, seg)]);
-                aw[tn] = (i32x8){(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
-                ew[tn] = (int)((sm.ew[sg][r] >> (8 * seg)) & 0xFFu);
+                const uint4 v = *reinterpret_cast<const uint4 *>(&sm.w[sg][r * MXD_ROW + 16 * mxd_seg(r, blk)]);
+                f.aw[tn] = (i32x8){(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+                f.ew[tn] = (int)((sm.ew[sg][64 * (r >> 5) + 32 * (blk >> 2) + (r & 31)] >> (8 * (blk & 3))) & 0xFFu);
             }
 #pragma unroll
             for (int tm = 0; tm < MX_TM; ++tm) {
                 const int r = wm * MX_WM + tm * 32 + l32;
-                const uint4 v = *reinterpret_cast<const uint4 *>(&sm.x[sg][r * MX_STRIDE + 16 * mx_seg(r, seg)]);
-                bx[tm] = (i32x8){(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
-                ex[tm] = (int)((sm.ex[sg][64 * (r >> 5) + (r & 31)] >> (8 * seg)) & 0xFFu);
+                const uint4 v = *reinterpret_cast<const uint4 *>(&sm.x[sg][r * MXD_ROW + 16 * mxd_seg(r, blk)]);
+                f.bx[tm] = (i32x8){(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+                f.ex[tm] = (int)((sm.ex[sg][64 * (r >> 5) + 32 * (blk >> 2) + (r & 31)] >> (8 * (blk & 3))) & 0xFFu);
             }
+        };
+        Frag fa, fb;
+        read_slice(0, fa);
+#pragma unroll
+        for (int sl = 0; sl < 4; ++sl) {
+            Frag &cur = (sl & 1) ? fb : fa;
+            Frag &nxt = (sl & 1) ? fa : fb;
+            if (sl < 3) read_slice(sl + 1, nxt);
 #pragma unroll
             for (int tn = 0; tn < MX_TN; ++tn)
 #pragma unroll
                 for (int tm = 0; tm < MX_TM; ++tm)
                     acc[tn][tm] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                        aw[tn], bx[tm], acc[tn][tm], 4, 4, 0, ew[tn], 0, ex[tm]);
+                        cur.aw[tn], cur.bx[tm], acc[tn][tm], 4, 4, 0, cur.ew[tn], 0, cur.ex[tm]);
         }
-        // step st + 1 has landed (this wave's part) once at most the 8 loads
-        // just issued are outstanding; the barrier publishes it and frees
-        // stage st for the loads of step st + 3
-        // (lgkmcnt: this wave's fragment reads of stage st are complete too)
-        if (more) asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)" ::: "memory");
-        else asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+        // issue order: the first slice's reads, then per slice the next
+        // slice's reads (6 b128 + up to 6 small) ahead of its 8 products
+        __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);
+#pragma unroll
+        for (int sl = 0; sl < 4; ++sl) {
+            if (sl < 3) __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+        }
+        // step st + 1 has landed (this wave's part) and this wave's fragment
+        // reads of stage st are complete; the barrier publishes the one and
+        // frees the other for the loads of step st + 2
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
         asm volatile("s_barrier" ::: "memory");
-        sg = sg == 2 ? 0 : sg + 1;
     }
     wave_epilogue<MX_TN, MX_TM>(acc, h, up, bias, M, N, gelu, Y, m0 + wm * MX_WM, n0 + wn * MX_WN,
-                reinterpret_cast<uint8_t *>(&sm) + wave * OUT_TILE_BYTES, lane);
+                                reinterpret_cast<uint8_t *>(&sm) + wave * OUT_TILE_BYTES, lane);
 }
 
 }  // namespace
@@ -789,12 +800,16 @@ hipError_t launch_w4a4_linear(const uint8_t *xq, const void *xscale, const float
         hipLaunchKernelGGL(w4a4_int4_kernel, dim3((unsigned)tiles), dim3(I4_THREADS), 0, stream, xq,
                            (const float *)xscale, h, wq, (const float *)wscale, up, bias, M, N, K, gelu, Y);
     } else {
-        const int tiles = ((N + MX_BN - 1) / MX_BN) * ((M + MX_BM - 1) / MX_BM);
-        // the LDS-DMA kernel takes whole 128-channel steps and 32-bit offsets
-        const bool dma = K % 128 == 0 && rows * (K / 2) < ((int64_t)1 << 31);
-        hipLaunchKernelGGL(dma ? w4a4_mxfp4_dma_kernel : w4a4_mxfp4_kernel, dim3((unsigned)tiles),
-                           dim3(MX_THREADS), 0, stream, xq, (const uint8_t *)xscale, h, wq,
-                           (const uint8_t *)wscale, up, bias, M, N, K, gelu, Y);
+        // the LDS-DMA kernel takes whole 256-channel steps and 32-bit offsets
+        if (K % 256 == 0 && rows * (K / 2) < ((int64_t)1 << 31)) {
+            const int tiles = ((N + MXD_BN - 1) / MXD_BN) * ((M + MXD_BM - 1) / MXD_BM);
+            hipLaunchKernelGGL(w4a4_mxfp4_dma_kernel, dim3((unsigned)tiles), dim3(MXD_THREADS), 0, stream, xq,
+                               (const uint8_t *)xscale, h, wq, (const uint8_t *)wscale, up, bias, M, N, K, gelu, Y);
+        } else {
+            const int tiles = ((N + MX_BN - 1) / MX_BN) * ((M + MX_BM - 1) / MX_BM);
+            hipLaunchKernelGGL(w4a4_mxfp4_kernel, dim3((unsigned)tiles), dim3(MX_THREADS), 0, stream, xq,
+                               (const uint8_t *)xscale, h, wq, (const uint8_t *)wscale, up, bias, M, N, K, gelu, Y);
+        }
     }
     return hipGetLastError();
 }

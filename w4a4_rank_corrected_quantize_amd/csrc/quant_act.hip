@@ -240,19 +240,6 @@ __global__ __launch_bounds__(64 * K1_WAVES) void quant_act_kernel(
     }
 }
 
-int device_cu_count()
-{
-    static int cached[64] = {};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (cached[dev] == 0) {
-        int n = 0;
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-        cached[dev] = n;
-    }
-    return cached[dev];
-}
-
 }  // namespace
 
 hipError_t launch_quant_act(const uint16_t *X, int M, int K, const float *smooth, const uint16_t *down,

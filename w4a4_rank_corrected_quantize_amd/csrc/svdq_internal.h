@@ -11,6 +11,9 @@ namespace svdq {
 
 int group_size(svdq_precision prec);
 
+// Compute units of the current device (cached per device; 256 if unknown).
+int device_cu_count();
+
 // Kernel launchers; arguments are already validated.  They return the HIP
 // status of the launch.
 hipError_t launch_quant_act(const uint16_t *X, int M, int K, const float *smooth, const uint16_t *down,

@@ -653,12 +653,13 @@ constexpr int MXD_ROW = 128;        // LDS bytes per row and step: 256 fp4, 16-b
 // hit 8 distinct 4-bank groups.
 __device__ __forceinline__ int mxd_seg(int r, int s) { return s ^ (r & 7); }
 
-struct __attribute__((aligned(16))) MXDSmem {
-    uint8_t w[2][MXD_BN * MXD_ROW];
-    uint8_t x[2][MXD_BM * MXD_ROW];
-    uint32_t ew[2][2 * MXD_BN];      // row r, dword d (blocks 4 d .. 4 d + 3) at [64 (r / 32) + 32 d + r % 32]
-    uint32_t ex[2][2 * MXD_BM];
+struct __attribute__((aligned(16))) MXDStage {
+    uint8_t w[MXD_BN * MXD_ROW];
+    uint8_t x[MXD_BM * MXD_ROW];
+    uint32_t ew[2 * MXD_BN];         // row r, dword d (blocks 4 d .. 4 d + 3) at [64 (r / 32) + 32 d + r % 32]
+    uint32_t ex[2 * MXD_BM];
 };
+static_assert(8 * OUT_TILE_BYTES <= sizeof(MXDStage), "output staging fits in one stage");
 
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
 __device__ __forceinline__ uint32_t lds_offset(const void *p)
@@ -681,110 +682,141 @@ __device__ __forceinline__ void dma_b32(uint32_t lds, uint32_t voff, const void 
                  : "=&s"(keep) : "s"(lds), "v"(voff), "s"(sbase) : "memory");
 }
 
+// Persistent: block b takes the tiles b, b + gridDim.x, ...  The two stages
+// alternate over the global step count, and the first step of the next tile
+// is loaded into the free stage while the epilogue of the current tile runs
+// (its output staging uses the other stage).
 __global__ __launch_bounds__(MXD_THREADS) void w4a4_mxfp4_dma_kernel(
     const uint8_t *__restrict__ xq, const uint8_t *__restrict__ xscale, const float *__restrict__ h,
     const uint8_t *__restrict__ wq, const uint8_t *__restrict__ wscale, const uint16_t *__restrict__ up,
     const uint16_t *__restrict__ bias, int M, int N, int K, int gelu, uint16_t *__restrict__ Y)
 {
-    __shared__ MXDSmem sm;
-    static_assert(8 * OUT_TILE_BYTES <= sizeof(MXDSmem), "output staging fits in LDS");
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    __shared__ MXDStage stage[2];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform
     const int wn = wave & 1, wm = wave >> 1;            // 2 (n) x 4 (m) waves
-    int tn_, tm_;
-    tile_coords(blockIdx.x, (N + MXD_BN - 1) / MXD_BN, (M + MXD_BM - 1) / MXD_BM, tn_, tm_);
-    const int n0 = tn_ * MXD_BN, m0 = tm_ * MXD_BM;
+    const int tiles_n = (N + MXD_BN - 1) / MXD_BN, tiles_m = (M + MXD_BM - 1) / MXD_BM;
+    const int tiles = tiles_n * tiles_m;
     const int KB = K >> 1;          // code bytes per row
     const int NB = K >> 5;          // E8M0 scales per row (a multiple of 8 here)
     const int steps = K >> 8;
+    const int l32 = lane & 31, hk = lane >> 5;
 
-    // Per-lane source offsets (bytes from the step's base); rows past N / M
-    // read the last row (their outputs are never stored).
-    uint32_t wvo[4], xvo[4];
+    // Per-lane source offsets of a tile (bytes from the step's base); rows
+    // past N / M read the last row (their outputs are never stored).
+    uint32_t wvo[4], xvo[4], ewo, exo;
+    auto set_tile = [&](int t, int &n0, int &m0) {
+        int tn_, tm_;
+        tile_coords(t, tiles_n, tiles_m, tn_, tm_);
+        n0 = tn_ * MXD_BN;
+        m0 = tm_ * MXD_BM;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int r = 8 * (8 * i + wave) + (lane >> 3);            // block 8 i + wave
-        const int seg = (lane & 7) ^ (r & 7);
-        wvo[i] = (uint32_t)(min(n0 + r, N - 1) * KB + 16 * seg);
-        xvo[i] = (uint32_t)(min(m0 + r, M - 1) * KB + 16 * seg);
-    }
-    const uint32_t ewo = (uint32_t)(min(n0 + 32 * wave + (lane & 31), N - 1) * NB + 4 * (lane >> 5));
-    const uint32_t exo = (uint32_t)(min(m0 + 32 * wave + (lane & 31), M - 1) * NB + 4 * (lane >> 5));
-
+        for (int i = 0; i < 4; ++i) {
+            const int r = 8 * (8 * i + wave) + (lane >> 3);        // block 8 i + wave
+            const int seg = (lane & 7) ^ (r & 7);
+            wvo[i] = (uint32_t)(min(n0 + r, N - 1) * KB + 16 * seg);
+            xvo[i] = (uint32_t)(min(m0 + r, M - 1) * KB + 16 * seg);
+        }
+        ewo = (uint32_t)(min(n0 + 32 * wave + l32, N - 1) * NB + 4 * hk);
+        exo = (uint32_t)(min(m0 + 32 * wave + l32, M - 1) * NB + 4 * hk);
+    };
     auto issue = [&](int st, int sg) {
+        MXDStage &S = stage[sg];
         const uint8_t *wb = wq + 128 * st, *xb = xq + 128 * st;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) dma_b128(lds_offset(&sm.w[sg][1024 * (8 * i + wave)]), wvo[i], wb);
+        for (int i = 0; i < 4; ++i) dma_b128(lds_offset(&S.w[1024 * (8 * i + wave)]), wvo[i], wb);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) dma_b128(lds_offset(&sm.x[sg][1024 * (8 * i + wave)]), xvo[i], xb);
-        dma_b32(lds_offset(&sm.ew[sg][64 * wave]), ewo, wscale + 8 * st);
-        dma_b32(lds_offset(&sm.ex[sg][64 * wave]), exo, xscale + 8 * st);
+        for (int i = 0; i < 4; ++i) dma_b128(lds_offset(&S.x[1024 * (8 * i + wave)]), xvo[i], xb);
+        dma_b32(lds_offset(&S.ew[64 * wave]), ewo, wscale + 8 * st);
+        dma_b32(lds_offset(&S.ex[64 * wave]), exo, xscale + 8 * st);
     };
 
-    f32x16 acc[MX_TN][MX_TM];
-#pragma unroll
-    for (int a = 0; a < MX_TN; ++a)
-#pragma unroll
-        for (int b = 0; b < MX_TM; ++b)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.0f;
-
-    const int l32 = lane & 31, hk = lane >> 5;
+    int t = blockIdx.x;
+    if (t >= tiles) return;
+    int n0, m0;
+    set_tile(t, n0, m0);
+    int g = 0;                      // global step count: step st of the current tile uses stage (g + st) & 1
     issue(0, 0);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    asm volatile("s_barrier" ::: "memory");
-    for (int st = 0; st < steps; ++st) {
-        const int sg = st & 1;
-        if (st + 1 < steps) issue(st + 1, sg ^ 1);
-        // four 64-channel slices per step; the fragments of slice sl + 1 are
-        // read while the products of slice sl run
-        struct Frag { i32x8 aw[MX_TN], bx[MX_TM]; int ew[MX_TN], ex[MX_TM]; };
-        auto read_slice = [&](int sl, Frag &f) {
-            const int blk = 2 * sl + hk;           // the lane's 32-channel block (segment) of the step
+    while (true) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        asm volatile("s_barrier" ::: "memory");
+        f32x16 acc[MX_TN][MX_TM];
 #pragma unroll
-            for (int tn = 0; tn < MX_TN; ++tn) {
-                const int r = wn * MX_WN + tn * 32 + l32;
-                const uint4 v = *reinterpret_cast<const uint4 *>(&sm.w[sg][r * MXD_ROW + 16 * mxd_seg(r, blk)]);
-                f.aw[tn] = (i32x8){(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
-                f.ew[tn] = (int)((sm.ew[sg][64 * (r >> 5) + 32 * (blk >> 2) + (r & 31)] >> (8 * (blk & 3))) & 0xFFu);
+        for (int a = 0; a < MX_TN; ++a)
+#pragma unroll
+            for (int b = 0; b < MX_TM; ++b)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.0f;
+        for (int st = 0; st < steps; ++st) {
+            const int sg = (g + st) & 1;
+            if (st + 1 < steps) issue(st + 1, sg ^ 1);
+            const MXDStage &S = stage[sg];
+            // four 64-channel slices per step; the fragments of slice sl + 1
+            // are read while the products of slice sl run
+            struct Frag { i32x8 aw[MX_TN], bx[MX_TM]; int ew[MX_TN], ex[MX_TM]; };
+            auto read_slice = [&](int sl, Frag &f) {
+                const int blk = 2 * sl + hk;       // the lane's 32-channel block (segment) of the step
+#pragma unroll
+                for (int tn = 0; tn < MX_TN; ++tn) {
+                    const int r = wn * MX_WN + tn * 32 + l32;
+                    const uint4 v = *reinterpret_cast<const uint4 *>(&S.w[r * MXD_ROW + 16 * mxd_seg(r, blk)]);
+                    f.aw[tn] = (i32x8){(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+                    f.ew[tn] = (int)((S.ew[64 * (r >> 5) + 32 * (blk >> 2) + (r & 31)] >> (8 * (blk & 3))) & 0xFFu);
+                }
+#pragma unroll
+                for (int tm = 0; tm < MX_TM; ++tm) {
+                    const int r = wm * MX_WM + tm * 32 + l32;
+                    const uint4 v = *reinterpret_cast<const uint4 *>(&S.x[r * MXD_ROW + 16 * mxd_seg(r, blk)]);
+                    f.bx[tm] = (i32x8){(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+                    f.ex[tm] = (int)((S.ex[64 * (r >> 5) + 32 * (blk >> 2) + (r & 31)] >> (8 * (blk & 3))) & 0xFFu);
+                }
+            };
+            Frag fa, fb;
+            read_slice(0, fa);
+#pragma unroll
+            for (int sl = 0; sl < 4; ++sl) {
+                Frag &cur = (sl & 1) ? fb : fa;
+                Frag &nxt = (sl & 1) ? fa : fb;
+                if (sl < 3) read_slice(sl + 1, nxt);
+#pragma unroll
+                for (int tn = 0; tn < MX_TN; ++tn)
+#pragma unroll
+                    for (int tm = 0; tm < MX_TM; ++tm)
+                        acc[tn][tm] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                            cur.aw[tn], cur.bx[tm], acc[tn][tm], 4, 4, 0, cur.ew[tn], 0, cur.ex[tm]);
             }
+            // issue order: the first slice's reads, then per slice the next
+            // slice's reads (6 b128 + up to 6 small) ahead of its 8 products
+            __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);
 #pragma unroll
-            for (int tm = 0; tm < MX_TM; ++tm) {
-                const int r = wm * MX_WM + tm * 32 + l32;
-                const uint4 v = *reinterpret_cast<const uint4 *>(&sm.x[sg][r * MXD_ROW + 16 * mxd_seg(r, blk)]);
-                f.bx[tm] = (i32x8){(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
-                f.ex[tm] = (int)((sm.ex[sg][64 * (r >> 5) + 32 * (blk >> 2) + (r & 31)] >> (8 * (blk & 3))) & 0xFFu);
+            for (int sl = 0; sl < 4; ++sl) {
+                if (sl < 3) __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
             }
-        };
-        Frag fa, fb;
-        read_slice(0, fa);
-#pragma unroll
-        for (int sl = 0; sl < 4; ++sl) {
-            Frag &cur = (sl & 1) ? fb : fa;
-            Frag &nxt = (sl & 1) ? fa : fb;
-            if (sl < 3) read_slice(sl + 1, nxt);
-#pragma unroll
-            for (int tn = 0; tn < MX_TN; ++tn)
-#pragma unroll
-                for (int tm = 0; tm < MX_TM; ++tm)
-                    acc[tn][tm] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                        cur.aw[tn], cur.bx[tm], acc[tn][tm], 4, 4, 0, cur.ew[tn], 0, cur.ex[tm]);
+            // this wave's loads of step st + 1 have landed and its fragment
+            // reads of stage sg are complete; the barrier publishes the one
+            // and frees the other
+            asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+            asm volatile("s_barrier" ::: "memory");
         }
-        // issue order: the first slice's reads, then per slice the next
-        // slice's reads (6 b128 + up to 6 small) ahead of its 8 products
-        __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);
-#pragma unroll
-        for (int sl = 0; sl < 4; ++sl) {
-            if (sl < 3) __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);
-            __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+        // the last step used stage (g + steps - 1) & 1: the other one takes
+        // the next tile's first step while this tile's epilogue runs
+        const int last = (g + steps - 1) & 1;
+        const int mb = m0 + wm * MX_WM, nb = n0 + wn * MX_WN;
+        const int tnext = t + (int)gridDim.x;
+        if (tnext < tiles) {
+            set_tile(tnext, n0, m0);
+            issue(0, last ^ 1);
         }
-        // step st + 1 has landed (this wave's part) and this wave's fragment
-        // reads of stage st are complete; the barrier publishes the one and
-        // frees the other for the loads of step st + 2
-        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+        wave_epilogue<MX_TN, MX_TM>(acc, h, up, bias, M, N, gelu, Y, mb, nb,
+                                    reinterpret_cast<uint8_t *>(&stage[last]) + wave * OUT_TILE_BYTES, lane);
+        if (tnext >= tiles) break;
+        g += steps;
+        t = tnext;
+        // the staging area becomes the second stage of the next tile
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         asm volatile("s_barrier" ::: "memory");
     }
-    wave_epilogue<MX_TN, MX_TM>(acc, h, up, bias, M, N, gelu, Y, m0 + wm * MX_WM, n0 + wn * MX_WN,
-                                reinterpret_cast<uint8_t *>(&sm) + wave * OUT_TILE_BYTES, lane);
 }
 
 }  // namespace
@@ -803,7 +835,9 @@ hipError_t launch_w4a4_linear(const uint8_t *xq, const void *xscale, const float
         // the LDS-DMA kernel takes whole 256-channel steps and 32-bit offsets
         if (K % 256 == 0 && rows * (K / 2) < ((int64_t)1 << 31)) {
             const int tiles = ((N + MXD_BN - 1) / MXD_BN) * ((M + MXD_BM - 1) / MXD_BM);
-            hipLaunchKernelGGL(w4a4_mxfp4_dma_kernel, dim3((unsigned)tiles), dim3(MXD_THREADS), 0, stream, xq,
+            const int ncu = device_cu_count();
+            const int blocks = tiles < ncu ? tiles : ncu;      // persistent: one block per CU
+            hipLaunchKernelGGL(w4a4_mxfp4_dma_kernel, dim3((unsigned)blocks), dim3(MXD_THREADS), 0, stream, xq,
                                (const uint8_t *)xscale, h, wq, (const uint8_t *)wscale, up, bias, M, N, K, gelu, Y);
         } else {
             const int tiles = ((N + MX_BN - 1) / MX_BN) * ((M + MX_BM - 1) / MX_BM);

@@ -38,10 +38,10 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, 8 TB/s
 # only reported while the kernel source still hashes to the value it was
 # measured on; otherwise traffic is null.
 TRAFFIC = {
-    # FETCH_SIZE 106848 KiB / 0.50003 + WRITE_SIZE 110592 KiB / 1.0 (per dispatch)
-    ("int4", "fc1"): {"source_sha": "2bd1f2692f14ea71", "bytes": 332059226},
-    # FETCH_SIZE 72831 KiB / 0.50003 + WRITE_SIZE 110592 KiB / 1.0
-    ("mxfp4", "fc1"): {"source_sha": "2bd1f2692f14ea71", "bytes": 262396130},
+    # FETCH_SIZE 106864 KiB / 0.50003 + WRITE_SIZE 110592 KiB / 1.0 (per dispatch)
+    ("int4", "fc1"): {"source_sha": "e85964210e96e2e5", "bytes": 332092214},
+    # FETCH_SIZE 77247 KiB / 0.50003 + WRITE_SIZE 111104 KiB / 1.0
+    ("mxfp4", "fc1"): {"source_sha": "e85964210e96e2e5", "bytes": 271964117},
 }
 
 

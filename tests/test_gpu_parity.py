@@ -231,6 +231,24 @@ def _rows(M, n, seed=7):
 
 
 @pytest.mark.parametrize("prec", PRECS)
+@pytest.mark.parametrize("K", [256, 768])
+def test_linear_many_tiles_ragged(prec, K):
+    """More output tiles than CUs (the persistent kernels take several each),
+    ragged in both M and N, one and an odd number of 256-channel steps per
+    tile; all outputs of sampled rows, the last row included."""
+    M, N = 2000, 9000
+    _say(f"linear many tiles prec={prec} M={M} K={K} N={N}")
+    L, p = _layer("qkv", M, K, N, prec)
+    xq, xs, h, oh = _quant_act_check(L["X"], p["smooth"], p["down"], prec)
+    Y = svdq.w4a4_linear(xq, xs, h, _t(p["wq"]), _t(p["wscale"]), _t(p["up"]), _t(L["bias"]), prec,
+                         svdq.EPI_GELU_TANH)
+    torch.cuda.synchronize()
+    rows = _rows(M, 40, seed=11)
+    y_ref = O.linear(_np(xq), _np(xs), oh, p["wq"], p["wscale"], p["up"], L["bias"], prec, gelu=True, rows=rows)
+    _y_check(Y[torch.from_numpy(rows).long().cuda()], y_ref, "many tiles")
+
+
+@pytest.mark.parametrize("prec", PRECS)
 def test_full_size_dit_block(prec):
     """QKV and the fc1 -> fc2 MLP pair at 4608 tokens, hidden 3072: codes,
     scales and h of every row bit-exact / bounded; outputs on sampled rows."""

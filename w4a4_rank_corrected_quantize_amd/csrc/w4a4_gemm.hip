@@ -20,7 +20,9 @@
 // scales (s = hi + lo, hi = bf16(s), lo = bf16(s - hi)):
 //     C_nm = sw_hi sx_hi + sw_lo sx_hi + sw_hi sx_lo      (relative error ~2^-16)
 // so the fp32 VALU only runs acc = fma(P, C, acc), one instruction per
-// element and group (the 2^18 is folded into the staged sw).
+// element and group.  Both halves of the wave feed the same three terms (k =
+// 0..2 and 8..10), which doubles C; that 2 and the 2^18 are folded into the
+// staged sw as 2^17.
 //
 // MXFP4: the E2M1 nibbles are the native fp4 operand format of
 // v_mfma_scale_f32_16x16x128_f8f6f4 and the E8M0 block scales are its scale
@@ -172,7 +174,7 @@ constexpr int I4_TN = I4_WN / 32, I4_TM = I4_WM / 32;                   // 2 x 2
 constexpr int I4_THREADS = 64 * I4_WAVES_N * I4_WAVES_M;
 constexpr int I4_KSTEP = 128;                    // channels per pipeline step (two groups)
 constexpr int I4_ROWB = I4_KSTEP + 16;           // LDS bytes per row: 128 fp8 + 16 pad
-constexpr float kTwo18 = 262144.0f;
+constexpr float kTwo17 = 131072.0f;
 
 // 16 nibble bytes (32 sign-magnitude codes) -> 32 E4M3 bytes (q * 2^-9).
 // Dword j of the input gives E (codes 8j, 8j+2, 8j+4, 8j+6) and O (the odd
@@ -192,8 +194,9 @@ __device__ __forceinline__ void widen_fp8(uint4 p, uint4 &lo, uint4 &hi)
 }
 
 // Scale operands of the outer-product instruction (A = weights, B = tokens):
-// row n of A holds k = 0..2 = (sw_hi, sw_lo, sw_hi), column m of B holds
-// (sx_hi, sx_hi, sx_lo); every other k is zero.
+// row n of A holds (sw_hi, sw_lo, sw_hi) at k = 0..2 and again at k = 8..10,
+// column m of B holds (sx_hi, sx_hi, sx_lo) at the same k; every other k is
+// zero.
 __device__ __forceinline__ uint2 scale_operand_w(float s)
 {
     const uint32_t hi = pack_bf16x2(s, 0.0f) & 0xFFFFu;
@@ -211,7 +214,7 @@ __device__ __forceinline__ uint2 scale_operand_x(float s)
 struct __attribute__((aligned(16))) I4Smem {
     uint8_t w[2][I4_BN * I4_ROWB];
     uint8_t x[2][I4_BM * I4_ROWB];
-    uint2 sw[2][2][I4_BN];     // [buf][group in step][n], scale_operand_w(sw * 2^18)
+    uint2 sw[2][2][I4_BN];     // [buf][group in step][n], scale_operand_w(sw * 2^17)
     uint2 sx[2][2][I4_BM];     // [buf][group in step][m], scale_operand_x(sx)
 };
 
@@ -281,8 +284,8 @@ __global__ __launch_bounds__(I4_THREADS) void w4a4_int4_kernel(
         *reinterpret_cast<uint4 *>(d_) = a_;                                           \
         *reinterpret_cast<uint4 *>(d_ + 16) = b_;                                      \
         if (sc_w) {                                                                    \
-            sm.sw[buf][0][tid] = scale_operand_w(rs##R##0 * kTwo18);                   \
-            sm.sw[buf][1][tid] = scale_operand_w(rs##R##1 * kTwo18);                   \
+            sm.sw[buf][0][tid] = scale_operand_w(rs##R##0 * kTwo17);                   \
+            sm.sw[buf][1][tid] = scale_operand_w(rs##R##1 * kTwo17);                   \
         } else if (sc_x) {                                                             \
             sm.sx[buf][0][tid - I4_BN] = scale_operand_x(rs##R##0);                    \
             sm.sx[buf][1][tid - I4_BN] = scale_operand_x(rs##R##1);                    \
@@ -304,6 +307,11 @@ __global__ __launch_bounds__(I4_THREADS) void w4a4_int4_kernel(
     // outer product and 16 fmas.  (The per-group exit also keeps the compiler
     // from hoisting the second group's reads and products into the first,
     // which would run out of registers.)
+    uint4 cwv[I4_TN], cxv[I4_TM];
+#pragma unroll
+    for (int t = 0; t < I4_TN; ++t) cwv[t] = (uint4){0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int t = 0; t < I4_TM; ++t) cxv[t] = (uint4){0u, 0u, 0u, 0u};
     auto compute_step = [&](int st, int buf) {
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
@@ -317,9 +325,11 @@ __global__ __launch_bounds__(I4_THREADS) void w4a4_int4_kernel(
                 const uint4 u1 = *reinterpret_cast<const uint4 *>(p + 16);
                 aw[tn] = (i32x8){(int)u0.x, (int)u0.y, (int)u0.z, (int)u0.w,
                                  (int)u1.x, (int)u1.y, (int)u1.z, (int)u1.w};
-                // scale operands: lanes 0-31 carry k = 0..7, lanes 32-63 (k = 8..15) are zero
+                // scale operands: both lane halves (k = 0..7 and 8..15) carry the
+                // same three terms, so the product is twice the outer product
                 const uint2 v = sm.sw[buf][q][wn * I4_WN + tn * 32 + l32];
-                cw[tn] = __builtin_bit_cast(bf16x8, (uint4){hk ? 0u : v.x, hk ? 0u : v.y, 0u, 0u});
+                cwv[tn].x = v.x; cwv[tn].y = v.y;
+                cw[tn] = __builtin_bit_cast(bf16x8, cwv[tn]);
             }
 #pragma unroll
             for (int tm = 0; tm < I4_TM; ++tm) {
@@ -329,7 +339,8 @@ __global__ __launch_bounds__(I4_THREADS) void w4a4_int4_kernel(
                 bx[tm] = (i32x8){(int)u0.x, (int)u0.y, (int)u0.z, (int)u0.w,
                                  (int)u1.x, (int)u1.y, (int)u1.z, (int)u1.w};
                 const uint2 v = sm.sx[buf][q][wm * I4_WM + tm * 32 + l32];
-                cx[tm] = __builtin_bit_cast(bf16x8, (uint4){hk ? 0u : v.x, hk ? 0u : v.y, 0u, 0u});
+                cxv[tm].x = v.x; cxv[tm].y = v.y;
+                cx[tm] = __builtin_bit_cast(bf16x8, cxv[tm]);
             }
 #pragma unroll
             for (int tn = 0; tn < I4_TN; ++tn)

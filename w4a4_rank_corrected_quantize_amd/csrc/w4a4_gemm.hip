@@ -96,20 +96,19 @@ __device__ __forceinline__ void load_h8(const float *__restrict__ h, int m, int 
     }
 }
 
-// Bias of 4 consecutive channels n..n+3 (zero when there is no bias or n >= N).
-__device__ __forceinline__ float4 bias4(const uint16_t *__restrict__ bias, int n, int N)
+// Bias of 4 consecutive channels n..n+3 as 4 bf16 (zero when there is no
+// bias or n >= N).
+__device__ __forceinline__ uint2 bias4(const uint16_t *__restrict__ bias, int n, int N)
 {
-    if (!bias || n >= N) return make_float4(0.f, 0.f, 0.f, 0.f);
-    const uint2 b2 = *reinterpret_cast<const uint2 *>(bias + n);
-    return make_float4(bf16_to_f32(b2.x & 0xFFFFu), bf16_to_f32(b2.x >> 16), bf16_to_f32(b2.y & 0xFFFFu),
-                       bf16_to_f32(b2.y >> 16));
+    if (!bias || n >= N) return make_uint2(0u, 0u);
+    return *reinterpret_cast<const uint2 *>(bias + n);
 }
 
 // y = acc + lr + b (+ GELU) for 4 consecutive channels, packed as 4 bf16.
-__device__ __forceinline__ uint2 finish4(const float *acc, const float *lr, float4 b, int gelu)
+__device__ __forceinline__ uint2 finish4(const float *acc, const float *lr, uint2 b, int gelu)
 {
-    float y0 = acc[0] + lr[0] + b.x, y1 = acc[1] + lr[1] + b.y;
-    float y2 = acc[2] + lr[2] + b.z, y3 = acc[3] + lr[3] + b.w;
+    float y0 = acc[0] + lr[0] + bf16_to_f32(b.x & 0xFFFFu), y1 = acc[1] + lr[1] + bf16_to_f32(b.x >> 16);
+    float y2 = acc[2] + lr[2] + bf16_to_f32(b.y & 0xFFFFu), y3 = acc[3] + lr[3] + bf16_to_f32(b.y >> 16);
     if (gelu) {
         y0 = gelu_tanh(y0); y1 = gelu_tanh(y1); y2 = gelu_tanh(y2); y3 = gelu_tanh(y3);
     }
@@ -238,9 +237,10 @@ __global__ __launch_bounds__(I4_THREADS) void w4a4_int4_kernel(
     // Loader: a chunk is 16 code bytes (32 codes) of one row; per step W has
     // BN*4 chunks and X BM*4.  Thread t moves W chunks t and t + 512 and X
     // chunk t (all with segment t & 3).  Loads are unconditional: rows past
-    // N / M are clamped to the last row (their outputs are never stored) and
-    // channels past K are zeroed when the chunk is written to LDS, so every
-    // path has the same number of loads in flight.
+    // N / M are clamped to the last row (their outputs are never stored), and
+    // for an odd G the missing second group of the last step re-reads the
+    // row's first chunk (the compute loop never reads it), so every path has
+    // the same number of loads in flight.
     constexpr int WCH = I4_BN * 4, XCH = I4_BM * 4;
     static_assert(WCH == 2 * I4_THREADS && XCH == I4_THREADS, "loader shape");
     const int lseg = tid & 3, lr = tid >> 2;
@@ -401,7 +401,7 @@ __global__ __launch_bounds__(I4_THREADS) void w4a4_int4_kernel(
             if (nrow < N) uv = *reinterpret_cast<const uint4 *>(up + (size_t)nrow * 32 + 16 * s + 8 * hk);
             ua[s] = __builtin_bit_cast(bf16x8, uv);
         }
-        float4 bv[4];
+        uint2 bv[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) bv[j] = bias4(bias, nb + tn * 32 + 8 * j + 4 * hk, N);
 #pragma unroll
@@ -483,7 +483,7 @@ __device__ __forceinline__ void wave_epilogue(const f32x16 (&acc)[TN][TM], const
                 if (nrow < N) uv = *reinterpret_cast<const uint4 *>(up + (size_t)nrow * 32 + 16 * s2 + 8 * hk);
                 ua[s2] = __builtin_bit_cast(bf16x8, uv);
             }
-            float4 bv[4];
+            uint2 bv[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) bv[j] = bias4(bias, nb + tn * 32 + 8 * j + 4 * hk, N);
 #pragma unroll

@@ -36,6 +36,15 @@
 namespace svdq {
 namespace {
 
+// X is read exactly once: non-temporal loads leave the L2 to the outputs,
+// which the linear kernel reads next.
+__device__ __forceinline__ uint4 load_nt(const uint16_t *p)
+{
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
@@ -107,7 +116,7 @@ __global__ __launch_bounds__(64 * K1_WAVES) void quant_act_kernel(
 #pragma unroll
         for (int i = 0; i < NL; ++i) {
             const int r = min(K1_RPL * i + rq, nrow - 1);
-            L.x[i] = *reinterpret_cast<const uint4 *>(X + (size_t)(row0 + r) * K + k);
+            L.x[i] = load_nt(X + (size_t)(row0 + r) * K + k);
         }
         L.s0 = *reinterpret_cast<const float4 *>(smooth + k);
         L.s1 = *reinterpret_cast<const float4 *>(smooth + k + 4);

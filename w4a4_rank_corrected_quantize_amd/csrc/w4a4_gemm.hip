@@ -126,6 +126,14 @@ __device__ __forceinline__ void stage4(uint8_t *tile, int ml, int nl, uint2 v)
     *reinterpret_cast<uint2 *>(tile + ml * OUT_STRIDE + nl * 2) = v;
 }
 
+// Y is written once and not read back by this kernel: non-temporal stores
+// keep it from pushing the operand tiles out of the L2.
+__device__ __forceinline__ void store_nt(uint16_t *p, uint4 v)
+{
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    __builtin_nontemporal_store((u32x4){v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4 *>(p));
+}
+
 __device__ __forceinline__ void flush_tile(const uint8_t *tile, uint16_t *__restrict__ Y, int mb, int nb, int M,
                                            int N, int lane)
 {
@@ -135,7 +143,7 @@ __device__ __forceinline__ void flush_tile(const uint8_t *tile, uint16_t *__rest
         const int r = (lane >> 3) + 8 * it;
         const uint4 v = *reinterpret_cast<const uint4 *>(tile + r * OUT_STRIDE + seg * 16);
         const int m = mb + r, n = nb + seg * 8;
-        if (m < M && n < N) *reinterpret_cast<uint4 *>(Y + (size_t)m * N + n) = v;
+        if (m < M && n < N) store_nt(Y + (size_t)m * N + n, v);
     }
 }
 

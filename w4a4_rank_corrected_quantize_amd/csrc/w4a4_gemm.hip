@@ -675,7 +675,7 @@ __device__ __forceinline__ int mxd_seg(int r, int s) { return s ^ (r & 7); }
 struct __attribute__((aligned(16))) MXDStage {
     uint8_t w[MXD_BN * MXD_ROW];
     uint8_t x[MXD_BM * MXD_ROW];
-    uint32_t ew[2 * MXD_BN];         // row r, dword d (blocks 4 d .. 4 d + 3) at [64 (r / 32) + 32 d + r % 32]
+    uint32_t ew[2 * MXD_BN];         // row r, dword d (blocks 4 d .. 4 d + 3) at [64 (r / 32) + 2 (r % 32) + d]
     uint32_t ex[2 * MXD_BM];
 };
 static_assert(8 * OUT_TILE_BYTES <= sizeof(MXDStage), "output staging fits in one stage");
@@ -736,8 +736,8 @@ __global__ __launch_bounds__(MXD_THREADS) void w4a4_mxfp4_dma_kernel(
             wvo[i] = (uint32_t)(min(n0 + r, N - 1) * KB + 16 * seg);
             xvo[i] = (uint32_t)(min(m0 + r, M - 1) * KB + 16 * seg);
         }
-        ewo = (uint32_t)(min(n0 + 32 * wave + l32, N - 1) * NB + 4 * hk);
-        exo = (uint32_t)(min(m0 + 32 * wave + l32, M - 1) * NB + 4 * hk);
+        ewo = (uint32_t)(min(n0 + 32 * wave + (lane >> 1), N - 1) * NB + 4 * (lane & 1));
+        exo = (uint32_t)(min(m0 + 32 * wave + (lane >> 1), M - 1) * NB + 4 * (lane & 1));
     };
     auto issue = [&](int st, int sg) {
         MXDStage &S = stage[sg];
@@ -772,7 +772,21 @@ __global__ __launch_bounds__(MXD_THREADS) void w4a4_mxfp4_dma_kernel(
             const MXDStage &S = stage[sg];
             // four 64-channel slices per step; the fragments of slice sl + 1
             // are read while the products of slice sl run
-            struct Frag { i32x8 aw[MX_TN], bx[MX_TM]; int ew[MX_TN], ex[MX_TM]; };
+            // the step's E8M0 bytes of the wave's rows (8 per row: two dwords)
+            uint2 esw[MX_TN], esx[MX_TM];
+#pragma unroll
+            for (int tn = 0; tn < MX_TN; ++tn) {
+                const int r = wn * MX_WN + tn * 32 + l32;
+                esw[tn] = *reinterpret_cast<const uint2 *>(&S.ew[64 * (r >> 5) + 2 * (r & 31)]);
+            }
+#pragma unroll
+            for (int tm = 0; tm < MX_TM; ++tm) {
+                const int r = wm * MX_WM + tm * 32 + l32;
+                esx[tm] = *reinterpret_cast<const uint2 *>(&S.ex[64 * (r >> 5) + 2 * (r & 31)]);
+            }
+            // four 64-channel slices per step; the fragments of slice sl + 1
+            // are read while the products of slice sl run
+            struct Frag { i32x8 aw[MX_TN], bx[MX_TM]; };
             auto read_slice = [&](int sl, Frag &f) {
                 const int blk = 2 * sl + hk;       // the lane's 32-channel block (segment) of the step
 #pragma unroll
@@ -780,15 +794,17 @@ __global__ __launch_bounds__(MXD_THREADS) void w4a4_mxfp4_dma_kernel(
                     const int r = wn * MX_WN + tn * 32 + l32;
                     const uint4 v = *reinterpret_cast<const uint4 *>(&S.w[r * MXD_ROW + 16 * mxd_seg(r, blk)]);
                     f.aw[tn] = (i32x8){(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
-                    f.ew[tn] = (int)((S.ew[64 * (r >> 5) + 32 * (blk >> 2) + (r & 31)] >> (8 * (blk & 3))) & 0xFFu);
                 }
 #pragma unroll
                 for (int tm = 0; tm < MX_TM; ++tm) {
                     const int r = wm * MX_WM + tm * 32 + l32;
                     const uint4 v = *reinterpret_cast<const uint4 *>(&S.x[r * MXD_ROW + 16 * mxd_seg(r, blk)]);
                     f.bx[tm] = (i32x8){(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
-                    f.ex[tm] = (int)((S.ex[64 * (r >> 5) + 32 * (blk >> 2) + (r & 31)] >> (8 * (blk & 3))) & 0xFFu);
                 }
+            };
+            // E8M0 byte of block blk (= 2 sl + hk) from the row's two dwords
+            auto e8 = [&](uint2 e, int sl) -> int {
+                return (int)(((sl >> 1 ? e.y : e.x) >> (8 * (2 * (sl & 1) + hk))) & 0xFFu);
             };
             Frag fa, fb;
             read_slice(0, fa);
@@ -802,14 +818,14 @@ __global__ __launch_bounds__(MXD_THREADS) void w4a4_mxfp4_dma_kernel(
 #pragma unroll
                     for (int tm = 0; tm < MX_TM; ++tm)
                         acc[tn][tm] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                            cur.aw[tn], cur.bx[tm], acc[tn][tm], 4, 4, 0, cur.ew[tn], 0, cur.ex[tm]);
+                            cur.aw[tn], cur.bx[tm], acc[tn][tm], 4, 4, 0, e8(esw[tn], sl), 0, e8(esx[tm], sl));
             }
-            // issue order: the first slice's reads, then per slice the next
-            // slice's reads (6 b128 + up to 6 small) ahead of its 8 products
+            // issue order: the scale and first-slice reads, then per slice the
+            // next slice's 6 reads ahead of its 8 products
             __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);
 #pragma unroll
             for (int sl = 0; sl < 4; ++sl) {
-                if (sl < 3) __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);
+                if (sl < 3) __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
                 __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
             }
             // this wave's loads of step st + 1 have landed and its fragment

@@ -38,10 +38,10 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, 8 TB/s
 # only reported while the kernel source still hashes to the value it was
 # measured on; otherwise traffic is null.
 TRAFFIC = {
-    # FETCH_SIZE 106864 KiB / 0.50003 + WRITE_SIZE 110592 KiB / 1.0 (per dispatch)
-    ("int4", "fc1"): {"source_sha": "e85964210e96e2e5", "bytes": 332092214},
-    # FETCH_SIZE 77247 KiB / 0.50003 + WRITE_SIZE 111104 KiB / 1.0
-    ("mxfp4", "fc1"): {"source_sha": "e85964210e96e2e5", "bytes": 271964117},
+    # FETCH_SIZE 72636 KiB / 0.50003 + WRITE_SIZE 110593 KiB / 1.0 (per dispatch)
+    ("int4", "fc1"): {"source_sha": "74b80375e45af884", "bytes": 261997019},
+    # FETCH_SIZE 70932 KiB / 0.50003 + WRITE_SIZE 111106 KiB / 1.0
+    ("mxfp4", "fc1"): {"source_sha": "74b80375e45af884", "bytes": 259032745},
 }
 
 

@@ -82,8 +82,10 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--prec", choices=["int4", "mxfp4"], default="int4")
-    ap.add_argument("--layer", choices=["fc1", "qkv", "fc2"], default="fc1",
-                    help="fc1 is the headline workload; fc2 takes fc1's output (computed on the GPU)")
+    ap.add_argument("--layer", choices=["fc1", "qkv", "fc2", "mlp"], default="fc1",
+                    help="fc1 is the headline workload; fc2 takes fc1's output (computed on the GPU); "
+                         "mlp times fc1 -> fc2 with fc2's activation step fused into fc1's epilogue "
+                         "(INT4), next to the unfused pair")
     ap.add_argument("--copy-calibration", type=int, metavar="MIB", default=0,
                     help="only run a plain copy of MIB MiB (to scale the HBM byte counters)")
     ap.add_argument("--sets", type=int, default=3, help="rotating buffer sets")
@@ -107,6 +109,9 @@ def main():
 
     torch.cuda.set_device(0)
     svdq.check_device()
+    if args.layer == "mlp":
+        mlp_main(args, torch, svdq, synth)
+        return
     prec = svdq.INT4 if args.prec == "int4" else svdq.MXFP4
     spec = synth.SPECS[("" if prec == svdq.INT4 else "mx_") + args.layer]
     M, K, N, r = spec.M, spec.K, spec.N, svdq.RANK
@@ -251,6 +256,140 @@ def main():
         "linear_kernel_GBs": round(k2_gbs, 1),
         "host_pack_s": round(pack_s, 2),
         "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def mlp_main(args, torch, svdq, synth):
+    """fc1 (GELU) -> fc2 at M=4608 (INT4): the fused step runs fc1's
+    activation step, fc1's product whose epilogue writes fc2's codes, scales
+    and h (svdq_w4a4_linear_requant), then fc2's product.  The unfused step
+    stores fc1's Y and runs fc2's activation step on it."""
+    if args.prec != "int4":
+        print("--layer mlp: the fused requantization is INT4 only", file=sys.stderr)
+        sys.exit(2)
+    prec = svdq.INT4
+    f1s, f2s = synth.SPECS["fc1"], synth.SPECS["fc2"]
+    M, K1, N1, N2, r = f1s.M, f1s.K, f1s.N, f2s.N, svdq.RANK
+    print(f"[bench] generating and packing fc1 {M}x{K1}->{N1} and fc2 {M}x{N1}->{N2}", file=sys.stderr,
+          flush=True)
+    L1 = synth.make_layer(f1s)
+    p1 = svdq.pack_weights(L1["W"], L1["act_absmax"], prec=prec)
+    d1 = svdq.to_device(p1)
+    b1 = svdq.bf16_tensor(L1["bias"])
+    # fc2's calibration statistic comes from fc1's actual output
+    X1 = svdq.bf16_tensor(L1["X"])
+    xq, xs, h = svdq.quantize_act(X1, d1["smooth"], d1["down"], prec)
+    Y1 = svdq.w4a4_linear(xq, xs, h, d1["wq"], d1["wscale"], d1["up"], b1, prec, svdq.EPI_GELU_TANH)
+    L2 = synth.make_layer(f2s, X_bits=svdq.bf16_bits(Y1))
+    p2 = svdq.pack_weights(L2["W"], L2["act_absmax"], prec=prec)
+    del Y1, xq, xs, h
+    sets = []
+    for i in range(args.sets):
+        a, b = svdq.to_device(p1), svdq.to_device(p2)
+        sets.append(dict(
+            X=svdq.bf16_tensor(L1["X"]), d1=a, b1=svdq.bf16_tensor(L1["bias"]), d2=b,
+            b2=svdq.bf16_tensor(L2["bias"]),
+            xq=torch.empty((M, K1 // 2), dtype=torch.uint8, device="cuda"),
+            xs=torch.empty((M, K1 // 64), dtype=torch.float32, device="cuda"),
+            h=torch.empty((M, r), dtype=torch.float32, device="cuda"),
+            Y1=torch.empty((M, N1), dtype=torch.bfloat16, device="cuda"),
+            xq2=torch.empty((M, N1 // 2), dtype=torch.uint8, device="cuda"),
+            xs2=torch.empty((M, N1 // 64), dtype=torch.float32, device="cuda"),
+            h2=torch.empty((M, r), dtype=torch.float32, device="cuda"),
+            work=torch.empty((svdq.requant_workspace_bytes(M, N1),), dtype=torch.uint8, device="cuda"),
+            Y2=torch.empty((M, N2), dtype=torch.bfloat16, device="cuda")))
+
+    def act1(b):
+        svdq.quantize_act(b["X"], b["d1"]["smooth"], b["d1"]["down"], prec, xq=b["xq"], xscale=b["xs"], h=b["h"])
+
+    def fc1_fused(b):
+        d = b["d1"]
+        svdq.w4a4_linear_requant(b["xq"], b["xs"], b["h"], d["wq"], d["wscale"], d["up"], b["b1"],
+                                 b["d2"]["smooth"], b["d2"]["down"], prec, svdq.EPI_GELU_TANH,
+                                 out=(b["xq2"], b["xs2"], b["h2"]), work=b["work"])
+
+    def fc1_plain(b):
+        d = b["d1"]
+        svdq.w4a4_linear(b["xq"], b["xs"], b["h"], d["wq"], d["wscale"], d["up"], b["b1"], prec,
+                         svdq.EPI_GELU_TANH, Y=b["Y1"])
+
+    def act2(b):
+        svdq.quantize_act(b["Y1"], b["d2"]["smooth"], b["d2"]["down"], prec, xq=b["xq2"], xscale=b["xs2"],
+                          h=b["h2"])
+
+    def fc2(b):
+        d = b["d2"]
+        svdq.w4a4_linear(b["xq2"], b["xs2"], b["h2"], d["wq"], d["wscale"], d["up"], b["b2"], prec,
+                         svdq.EPI_NONE, Y=b["Y2"])
+
+    fused = [act1, fc1_fused, fc2]
+    plain = [act1, fc1_plain, act2, fc2]
+
+    def run(seq, n, per_launch=False):
+        evs = []
+        for i in range(n):
+            b = sets[i % len(sets)]
+            if per_launch:
+                e = [torch.cuda.Event(enable_timing=True) for _ in range(len(seq) + 1)]
+                e[0].record()
+                for j, f in enumerate(seq):
+                    f(b)
+                    e[j + 1].record()
+                evs.append(e)
+            else:
+                for f in seq:
+                    f(b)
+        return evs
+
+    for seq in (fused, plain):
+        run(seq, args.warmup)
+    torch.cuda.synchronize()
+    print(f"[bench] warmup done; timing {args.steps} fused and {args.steps} unfused steps", file=sys.stderr,
+          flush=True)
+    out = {}
+    # two rounds, fused and unfused alternating; the second round is reported
+    # (the first one lets the clocks settle for both)
+    for name, seq in (("fused", fused), ("plain", plain), ("fused", fused), ("plain", plain)):
+        s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        s0.record()
+        run(seq, args.steps)
+        s1.record()
+        torch.cuda.synchronize()
+        out[name] = s0.elapsed_time(s1) / args.steps
+        evs = run(seq, args.steps, per_launch=True)
+        torch.cuda.synchronize()
+        out[name + "_launch_ms"] = [round(float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs])), 5)
+                                    for j in range(len(seq))]
+    ops = 2.0 * M * N1 * K1 + 2.0 * M * N2 * N1
+    req_ms = out["fused_launch_ms"][1]
+    req_tops = 2.0 * M * N1 * K1 / (req_ms * 1e-3) / 1e12
+    line = {
+        "metric": "fc1 -> fc2 MLP pair, fc2's activation step fused into fc1's epilogue (TOPS)",
+        "value": round(ops / (out["fused"] * 1e-3) / 1e12, 2),
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(out["fused"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int4 codes (exact fp8 values) on the fp8 matrix cores, exact per-group partials, fp32 rescale",
+        "data": "synthetic (seeded Student-t activations with outlier channels, N(0,0.02^2) weights); "
+                "fc2's input is fc1's GPU output",
+        "config": {"workload": f"MLP: {M} tokens x {K1} -> {N1} (GELU) -> {N2}, rank {r}, INT4 g64, bias; "
+                               "fused step = quantize_act + w4a4_linear_requant + w4a4_linear; "
+                               "unfused step = quantize_act + w4a4_linear + quantize_act + w4a4_linear",
+                   "M": M, "K": K1, "N": N1, "N2": N2, "rank": r, "buffer_sets": len(sets)},
+        "unfused_ms_per_step": round(out["plain"], 5),
+        "fused_launch_ms": out["fused_launch_ms"],
+        "unfused_launch_ms": out["plain_launch_ms"],
+        "roofline": {"bound": "mfma", "kernel": "svdq_w4a4_linear_requant (fc1, with the h2 sum)",
+                     "achieved": round(req_tops, 2), "peak": PEAK_INT8_TOPS, "unit": "TFLOP/s",
+                     "frac": round(req_tops / PEAK_INT8_TOPS, 4), "traffic": None, "avg_ms": req_ms},
+        "cpu_baseline": None,
     }
     print(json.dumps(line), flush=True)
 

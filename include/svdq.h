@@ -38,7 +38,8 @@
  * Conventions.
  *   - Ownership: the caller allocates and frees every buffer.  No call
  *     allocates device memory or keeps a pointer after it returns.
- *   - Device calls (svdq_quantize_act, svdq_w4a4_linear) take device
+ *   - Device calls (svdq_quantize_act, svdq_w4a4_linear,
+ *     svdq_w4a4_linear_requant) take device
  *     pointers and a hipStream_t (as void*, NULL = the null stream); they
  *     validate everything first, enqueue kernels on `stream` and return
  *     without synchronizing.  On any error nothing has been enqueued or
@@ -57,6 +58,7 @@
 #ifndef SVDQ_H
 #define SVDQ_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -183,6 +185,48 @@ svdq_status svdq_w4a4_linear(const uint8_t *xq, const void *xscale, const float 
                              const uint8_t *wq, const void *wscale, const uint16_t *up,
                              const uint16_t *bias, int M, int N, int K, int rank,
                              svdq_precision prec, svdq_epilogue epi, uint16_t *Y, void *stream);
+
+/*
+ * svdq_requant_workspace_bytes -- device workspace that
+ * svdq_w4a4_linear_requant needs for M tokens and N output channels
+ * (ceil(N / 256) * M * rank fp32 partial sums); 0 for M or N <= 0.
+ */
+size_t svdq_requant_workspace_bytes(int M, int N, int rank, svdq_precision prec);
+
+/*
+ * svdq_w4a4_linear_requant -- svdq_w4a4_linear feeding the next layer's
+ * activation step directly (an MLP's fc1 -> fc2, "Introducing Nunchaku
+ * Lite": fused GELU/MLP paths): Y is not stored.  Each output is rounded to
+ * bf16 exactly as svdq_w4a4_linear would store it, then smoothed with the
+ * next layer's `smooth2`, quantized per 64 consecutive output channels, and
+ * multiplied into the next layer's `down2`.  The results are those of
+ * svdq_quantize_act(Y, M, N, smooth2, down2, ...) on that Y: codes and scales
+ * bit-exact, h2 up to the order of the fp32 sums (per-tile partial sums over
+ * 256 channels, added in ascending tile order, so h2 is deterministic).
+ *
+ *   xq ... epi   as for svdq_w4a4_linear (prec must be SVDQ_INT4; the next
+ *                layer uses INT4 too)
+ *   N            N % 64 == 0 (the next layer's K)
+ *   smooth2      [N] fp32, device                  next layer's s
+ *   down2        [rank][N] bf16 bits, device       next layer's down
+ *   xq2          [M][N/2] uint8, device (out)
+ *   xscale2      [M][N/64] fp32, device (out)
+ *   h2           [M][rank] fp32, device (out)
+ *   work         device scratch of at least svdq_requant_workspace_bytes(M,
+ *                N, rank, prec) bytes, caller-owned; its contents on entry
+ *                do not matter and are overwritten
+ *   stream       hipStream_t or NULL
+ * Two kernel launches on `stream` (the product with this epilogue, then the
+ * fixed-order sum of the partial h2).  Errors: as for svdq_w4a4_linear;
+ * SVDQ_ERR_UNSUPPORTED for MXFP4; SVDQ_ERR_SHAPE when N % 64 != 0;
+ * SVDQ_ERR_INVALID_ARG when work_bytes is too small.
+ */
+svdq_status svdq_w4a4_linear_requant(const uint8_t *xq, const void *xscale, const float *h,
+                                     const uint8_t *wq, const void *wscale, const uint16_t *up,
+                                     const uint16_t *bias, int M, int N, int K, int rank,
+                                     svdq_precision prec, svdq_epilogue epi, const float *smooth2,
+                                     const uint16_t *down2, uint8_t *xq2, void *xscale2, float *h2,
+                                     void *work, size_t work_bytes, void *stream);
 
 #ifdef __cplusplus
 }

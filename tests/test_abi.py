@@ -60,6 +60,39 @@ def test_device_call_validation_order():
     assert L.svdq_quantize_act(None, 0, K, None, p, 32, svdq.INT4, p, p, p, None) == -1   # smooth needed
 
 
+def test_requant_validation_and_workspace():
+    """The fused next-layer entry point: workspace size, and its argument
+    errors before the device check."""
+    L = svdq.lib()
+    assert L.svdq_requant_workspace_bytes(0, 256, 32, svdq.INT4) == 0
+    assert L.svdq_requant_workspace_bytes(100, 256, 32, svdq.INT4) == 1 * 100 * 32 * 4
+    assert L.svdq_requant_workspace_bytes(100, 320, 32, svdq.INT4) == 2 * 100 * 32 * 4
+    assert L.svdq_requant_workspace_bytes(4608, 12288, 32, svdq.INT4) == 48 * 4608 * 32 * 4
+    _, p = _host(1 << 20)
+    _, q = _host(1 << 16, offset=4)
+    M, N, K = 16, 128, 128
+    W = L.svdq_requant_workspace_bytes(M, N, 32, svdq.INT4)
+
+    def call(**kw):
+        a = dict(xq=p, xs=p, h=p, wq=p, ws=p, up=p, bias=None, M=M, N=N, K=K, r=32, prec=svdq.INT4, epi=0,
+                 s2=p, d2=p, xq2=p, xs2=p, h2=p, work=p, wb=W)
+        a.update(kw)
+        return L.svdq_w4a4_linear_requant(a["xq"], a["xs"], a["h"], a["wq"], a["ws"], a["up"], a["bias"], a["M"],
+                                          a["N"], a["K"], a["r"], a["prec"], a["epi"], a["s2"], a["d2"], a["xq2"],
+                                          a["xs2"], a["h2"], a["work"], a["wb"], None)
+    assert call(N=96) == -2                     # N must be a multiple of 64 (the next layer's K)
+    assert call(prec=svdq.MXFP4) == -4          # INT4 only
+    assert call(r=16) == -4
+    assert call(epi=3) == -1
+    assert call(wb=W - 1) == -1                 # workspace too small
+    assert call(s2=None) == -1
+    assert call(work=None) == -1
+    assert call(d2=q) == -3
+    assert call(work=q) == -3
+    if not _has_gpu():
+        assert call() == -5
+
+
 def _has_gpu():
     try:
         import torch

@@ -40,7 +40,8 @@ STATUS = {
     -7: "SVDQ_ERR_HIP",
 }
 EXPORTS = ("svdq_status_string", "svdq_version", "svdq_check_device", "svdq_pack_weights",
-           "svdq_pack_residual", "svdq_quantize_act", "svdq_w4a4_linear")
+           "svdq_pack_residual", "svdq_quantize_act", "svdq_w4a4_linear", "svdq_requant_workspace_bytes",
+           "svdq_w4a4_linear_requant")
 
 
 class SvdqError(RuntimeError):
@@ -75,6 +76,11 @@ def lib():
         L.svdq_quantize_act.argtypes = [P, I, I, P, P, I, I, P, P, P, P]
         L.svdq_w4a4_linear.restype = I
         L.svdq_w4a4_linear.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, P, P]
+        L.svdq_requant_workspace_bytes.restype = ctypes.c_size_t
+        L.svdq_requant_workspace_bytes.argtypes = [I, I, I, I]
+        L.svdq_w4a4_linear_requant.restype = I
+        L.svdq_w4a4_linear_requant.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, P, P, P, P, P, P,
+                                               ctypes.c_size_t, P]
         _lib = L
     return _lib
 
@@ -204,6 +210,43 @@ def w4a4_linear(xq, xscale, h, wq, wscale, up, bias, prec: int = INT4, epi: int 
         pbias, M, N, K, r, prec, epi, _dev(Y, (torch.bfloat16, torch.int16), "Y"), _stream(stream))
     _check(st, "svdq_w4a4_linear")
     return Y
+
+
+def requant_workspace_bytes(M: int, N: int, rank: int = RANK, prec: int = INT4) -> int:
+    """Device scratch bytes that w4a4_linear_requant needs."""
+    return int(lib().svdq_requant_workspace_bytes(M, N, rank, prec))
+
+
+def w4a4_linear_requant(xq, xscale, h, wq, wscale, up, bias, smooth2, down2, prec: int = INT4,
+                        epi: int = EPI_NONE, out=None, work=None, stream=None):
+    """w4a4_linear whose epilogue writes the next layer's activation codes,
+    scales and h (smooth2, down2 of that layer) instead of Y.  Returns
+    (xq2, xscale2, h2)."""
+    torch = _torch()
+    M = xq.shape[0]
+    K = xq.shape[1] * 2
+    N = wq.shape[0]
+    r = up.shape[1]
+    dev = xq.device
+    if out is None:
+        out = (torch.empty((M, N // 2), dtype=torch.uint8, device=dev),
+               torch.empty((M, max(N // 64, 1)), dtype=torch.float32, device=dev),
+               torch.empty((M, r), dtype=torch.float32, device=dev))
+    xq2, xs2, h2 = out
+    nbytes = requant_workspace_bytes(M, N, r, prec)
+    if work is None:
+        work = torch.empty((max(nbytes, 16),), dtype=torch.uint8, device=dev)
+    pbias = None if bias is None else _dev(bias, (torch.bfloat16, torch.int16), "bias")
+    st = lib().svdq_w4a4_linear_requant(
+        _dev(xq, (torch.uint8,), "xq"), _dev(xscale, (torch.float32, torch.uint8), "xscale"),
+        _dev(h, (torch.float32,), "h"), _dev(wq, (torch.uint8,), "wq"),
+        _dev(wscale, (torch.float32, torch.uint8), "wscale"), _dev(up, (torch.bfloat16, torch.int16), "up"),
+        pbias, M, N, K, r, prec, epi, _dev(smooth2, (torch.float32,), "smooth2"),
+        _dev(down2, (torch.bfloat16, torch.int16), "down2"), _dev(xq2, (torch.uint8,), "xq2"),
+        _dev(xs2, (torch.float32,), "xscale2"), _dev(h2, (torch.float32,), "h2"),
+        _dev(work, (torch.uint8, torch.float32), "work"), work.numel() * work.element_size(), _stream(stream))
+    _check(st, "svdq_w4a4_linear_requant")
+    return xq2, xs2, h2
 
 
 def to_device(packed: dict, device="cuda") -> dict:

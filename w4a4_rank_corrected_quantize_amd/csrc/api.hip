@@ -134,3 +134,41 @@ extern "C" svdq_status svdq_w4a4_linear(const uint8_t *xq, const void *xscale, c
                                       (hipStream_t)stream);
     return e == hipSuccess ? SVDQ_OK : SVDQ_ERR_HIP;
 }
+
+extern "C" size_t svdq_requant_workspace_bytes(int M, int N, int rank, svdq_precision prec)
+{
+    (void)rank;
+    (void)prec;
+    if (M <= 0 || N <= 0) return 0;
+    return requant_work_bytes(M, N);
+}
+
+extern "C" svdq_status svdq_w4a4_linear_requant(const uint8_t *xq, const void *xscale, const float *h,
+                                                const uint8_t *wq, const void *wscale, const uint16_t *up,
+                                                const uint16_t *bias, int M, int N, int K, int rank,
+                                                svdq_precision prec, svdq_epilogue epi, const float *smooth2,
+                                                const uint16_t *down2, uint8_t *xq2, void *xscale2, float *h2,
+                                                void *work, size_t work_bytes, void *stream)
+{
+    svdq_status st = check_common(M, K, rank, prec);
+    if (st != SVDQ_OK) return st;
+    if (N < 0) return SVDQ_ERR_INVALID_ARG;
+    if (epi != SVDQ_EPI_NONE && epi != SVDQ_EPI_GELU_TANH) return SVDQ_ERR_INVALID_ARG;
+    if (prec != SVDQ_INT4) return SVDQ_ERR_UNSUPPORTED;
+    if (N % 64 != 0) return SVDQ_ERR_SHAPE;
+    // buffers of zero size may be NULL (empty tensors have no storage)
+    if ((M > 0 && (!xq || !xscale || !h)) || (N > 0 && (!wq || !wscale || !up || !smooth2 || !down2)) ||
+        (M > 0 && N > 0 && (!xq2 || !xscale2 || !h2 || !work)))
+        return SVDQ_ERR_INVALID_ARG;
+    if (M > 0 && N > 0 && work_bytes < svdq_requant_workspace_bytes(M, N, rank, prec)) return SVDQ_ERR_INVALID_ARG;
+    if (!aligned16(xq) || !aligned16(xscale) || !aligned16(h) || !aligned16(wq) || !aligned16(wscale) ||
+        !aligned16(up) || (bias && !aligned16(bias)) || !aligned16(smooth2) || !aligned16(down2) ||
+        !aligned16(xq2) || !aligned16(xscale2) || !aligned16(h2) || !aligned16(work))
+        return SVDQ_ERR_MISALIGNED;
+    st = current_device_ok();
+    if (st != SVDQ_OK) return st;
+    if (M == 0 || N == 0) return SVDQ_OK;
+    hipError_t e = launch_w4a4_linear_requant(xq, xscale, h, wq, wscale, up, bias, M, N, K, epi, smooth2, down2,
+                                              xq2, (float *)xscale2, h2, (float *)work, (hipStream_t)stream);
+    return e == hipSuccess ? SVDQ_OK : SVDQ_ERR_HIP;
+}

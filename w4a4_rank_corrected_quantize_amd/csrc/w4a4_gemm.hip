@@ -225,10 +225,215 @@ struct __attribute__((aligned(16))) I4Smem {
     uint2 sx[2][2][I4_BM];     // [buf][group in step][m], scale_operand_x(sx)
 };
 
+// The next layer's activation step, computed from this layer's output in the
+// epilogue instead of storing Y (INT4): the bf16-rounded outputs are
+// smoothed with smooth2, quantized per 64 channels (each wave tile spans one
+// such group per token) and multiplied into down2 for a partial h2 over the
+// block's 256 channels; the partials are summed later in a fixed order.
+struct RequantArgs {
+    const float *smooth2;     // [N]
+    const uint16_t *down2;    // [32][N] bf16 bits
+    uint8_t *xq2;             // [M][N/2]
+    float *xscale2;           // [M][N/64]
+    float *hpart;             // [ceil(N/256)][M][32]
+};
+
+// Epilogue of the requantizing INT4 kernel for one wave tile (64 channels n
+// of one 64-group x 64 tokens m).  Lane (l32, hk) holds, per 32-token tile
+// tm, token m = mb + 32 tm + l32 and the channels nb + 32 tn + 8 j + 4 hk +
+// (0..3), tn < 2, j < 4: half of the token's group, the other half being in
+// lane l32 + 32 (hk = 1).  `P` is the block's LDS, free after the main loop.
+__device__ __forceinline__ void requant_epilogue(const f32x16 (&acc)[I4_TN][I4_TM], const bf16x8 (&hhi)[I4_TM][2],
+                                                 const bf16x8 (&hlo)[I4_TM][2], const uint16_t *__restrict__ up,
+                                                 const uint16_t *__restrict__ bias, int M, int N, int gelu,
+                                                 const RequantArgs &rq, int mb, int nb, int tile_n, int m0, int wn,
+                                                 int wm, int tid, int lane, float *P)
+{
+    const int l32 = lane & 31, hk = lane >> 5;
+    const bool live = nb < N;          // N % 64 == 0: a wave tile is all in or all out
+    // bf16 outputs, exactly as the plain epilogue would store them
+    uint2 yb[I4_TN][I4_TM][4];
+#pragma unroll
+    for (int tn = 0; tn < I4_TN; ++tn) {
+        const int nrow = nb + tn * 32 + l32;
+        bf16x8 ua[2];
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            uint4 uv = {0u, 0u, 0u, 0u};
+            if (nrow < N) uv = *reinterpret_cast<const uint4 *>(up + (size_t)nrow * 32 + 16 * s + 8 * hk);
+            ua[s] = __builtin_bit_cast(bf16x8, uv);
+        }
+        uint2 bv[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) bv[j] = bias4(bias, nb + tn * 32 + 8 * j + 4 * hk, N);
+#pragma unroll
+        for (int tm = 0; tm < I4_TM; ++tm) {
+            f32x16 lr = {};
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                lr = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ua[s], hhi[tm][s], lr, 0, 0, 0);
+                lr = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ua[s], hlo[tm][s], lr, 0, 0, 0);
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                float a4[4] = {acc[tn][tm][4 * j], acc[tn][tm][4 * j + 1], acc[tn][tm][4 * j + 2],
+                               acc[tn][tm][4 * j + 3]};
+                float l4[4] = {lr[4 * j], lr[4 * j + 1], lr[4 * j + 2], lr[4 * j + 3]};
+                yb[tn][tm][j] = finish4(a4, l4, bv[j], gelu);
+            }
+        }
+    }
+    // next layer's smoothing and down projection for the lane's channels
+    float4 s2[I4_TN][4];
+    bf16x8 dn[4];                      // A operands: down2 rows l32, k block kb
+#pragma unroll
+    for (int tn = 0; tn < I4_TN; ++tn)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            s2[tn][j] = live ? *reinterpret_cast<const float4 *>(rq.smooth2 + nb + tn * 32 + 8 * j + 4 * hk)
+                             : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+        // k block kb covers channels 16 kb .. 16 kb + 15 of the wave tile:
+        // tn = kb / 2, j = 2 (kb % 2) and j + 1; lane half hk holds k = 8 hk
+        // + 0..7, i.e. channels 8 j + 4 hk + 0..3 of both j
+        const int c = nb + (kb >> 1) * 32 + 16 * (kb & 1) + 4 * hk;
+        uint2 a = {0u, 0u}, b = {0u, 0u};
+        if (live) {
+            a = *reinterpret_cast<const uint2 *>(rq.down2 + (size_t)l32 * N + c);
+            b = *reinterpret_cast<const uint2 *>(rq.down2 + (size_t)l32 * N + c + 8);
+        }
+        dn[kb] = __builtin_bit_cast(bf16x8, (uint4){a.x, a.y, b.x, b.y});
+    }
+    f32x16 hp[I4_TM];
+#pragma unroll
+    for (int tm = 0; tm < I4_TM; ++tm) {
+        const int m = mb + tm * 32 + l32;
+        // smoothed values and the group absmax (this lane's 32, then its partner's)
+        float v[I4_TN][4][4];
+        float amax = 0.0f;
+#pragma unroll
+        for (int tn = 0; tn < I4_TN; ++tn)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint2 y = yb[tn][tm][j];
+                const float sv[4] = {s2[tn][j].x, s2[tn][j].y, s2[tn][j].z, s2[tn][j].w};
+                const float yv[4] = {bf16_to_f32(y.x & 0xFFFFu), bf16_to_f32(y.x >> 16), bf16_to_f32(y.y & 0xFFFFu),
+                                     bf16_to_f32(y.y >> 16)};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    v[tn][j][e] = yv[e] * sv[e];
+                    amax = __builtin_fmaxf(amax, __builtin_fabsf(v[tn][j][e]));
+                }
+            }
+        amax = __builtin_fmaxf(amax, __shfl_xor(amax, 32));
+        const float scale = int4_group_scale(amax);
+        // magnitudes: rint(|v| rcp(scale)) unless some quotient of the lane
+        // lies within 2^-19 of a half-integer (or the group needs the 2^64
+        // lift); then the exact remainder test decides every code of the lane
+        const bool lifted = scale < 7.88860905e-31f;
+        const float inv = scale == 0.0f ? 0.0f : __builtin_amdgcn_rcpf(scale);
+        float q[I4_TN][4][4];
+        float dmax = 0.0f;
+#pragma unroll
+        for (int tn = 0; tn < I4_TN; ++tn)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float t = __builtin_fabsf(v[tn][j][e]) * inv;
+                    q[tn][j][e] = __builtin_rintf(t);
+                    dmax = __builtin_fmaxf(dmax, __builtin_fabsf(t - q[tn][j][e]));
+                }
+        if (lifted || dmax >= kNearTie) {
+            const Int4Group g = int4_group_prepare(scale);
+#pragma unroll
+            for (int tn = 0; tn < I4_TN; ++tn)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) q[tn][j][e] = (float)int4_mag(__builtin_fabsf(v[tn][j][e]), g);
+        }
+        // 4 codes (16 bits) per (tn, j): magnitudes packed as bytes, the odd
+        // ones shifted into the high nibbles, sign bits from the values; lane
+        // half hk keeps tn = hk and trades the other tn with its partner
+        uint32_t keep[4], give[4];
+#pragma unroll
+        for (int tn = 0; tn < I4_TN; ++tn)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint32_t ev = __builtin_amdgcn_cvt_pk_u8_f32(q[tn][j][2], 1,
+                                                                   __builtin_amdgcn_cvt_pk_u8_f32(q[tn][j][0], 0, 0u));
+                const uint32_t od = __builtin_amdgcn_cvt_pk_u8_f32(q[tn][j][3], 1,
+                                                                   __builtin_amdgcn_cvt_pk_u8_f32(q[tn][j][1], 0, 0u));
+                const uint32_t sg = ((f32_bits(v[tn][j][0]) >> 28) & 8u) | ((f32_bits(v[tn][j][1]) >> 24) & 0x80u) |
+                                    ((f32_bits(v[tn][j][2]) >> 20) & 0x800u) | ((f32_bits(v[tn][j][3]) >> 16) & 0x8000u);
+                const uint32_t piece = (ev | od << 4) | sg;
+                if (tn == hk) keep[j] = piece;
+                else give[j] = piece;
+            }
+        const uint32_t g01 = give[0] | give[1] << 16, g23 = give[2] | give[3] << 16;
+        const uint32_t r01 = (uint32_t)__shfl_xor((int)g01, 32), r23 = (uint32_t)__shfl_xor((int)g23, 32);
+        const uint32_t got[4] = {r01 & 0xFFFFu, r01 >> 16, r23 & 0xFFFFu, r23 >> 16};
+        // bytes 16 hk .. 16 hk + 15 of the token's 32-byte group: byte 4 j +
+        // 2 half holds the codes of lane half `half`
+        uint4 out;
+        uint32_t o[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) o[j] = hk ? (got[j] | keep[j] << 16) : (keep[j] | got[j] << 16);
+        out = make_uint4(o[0], o[1], o[2], o[3]);
+        if (live && m < M) {
+            *reinterpret_cast<uint4 *>(rq.xq2 + (size_t)m * (N / 2) + nb / 2 + 16 * hk) = out;
+            if (hk == 0) rq.xscale2[(size_t)m * (N / 64) + nb / 64] = scale;
+        }
+        // partial h2 = Y down2^T over the wave tile's 64 channels
+        f32x16 d = {};
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+            const int tn = kb >> 1, ja = 2 * (kb & 1);
+            const uint2 y0 = yb[tn][tm][ja], y1 = yb[tn][tm][ja + 1];
+            const bf16x8 bop = __builtin_bit_cast(bf16x8, live ? (uint4){y0.x, y0.y, y1.x, y1.y}
+                                                               : (uint4){0u, 0u, 0u, 0u});
+            d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dn[kb], bop, d, 0, 0, 0);
+        }
+        hp[tm] = d;
+    }
+    // sum the 4 channel quarters of the block in LDS (fixed order), then one
+    // row of 32 partial sums per token goes to hpart
+    __syncthreads();                  // every wave is done with the operand LDS
+#pragma unroll
+    for (int tm = 0; tm < I4_TM; ++tm) {
+        const int ml = wm * I4_WM + tm * 32 + l32;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            // rows j = 8 q + 4 hk + (0..3) of the 32x32 result, column ml
+            const float4 w4 = make_float4(hp[tm][4 * q], hp[tm][4 * q + 1], hp[tm][4 * q + 2], hp[tm][4 * q + 3]);
+            *reinterpret_cast<float4 *>(P + ((size_t)wn * I4_BM + ml) * 32 + 8 * q + 4 * hk) = w4;
+        }
+    }
+    __syncthreads();
+    const int ml = tid >> 2, j0 = 8 * (tid & 3);
+    float4 s0 = make_float4(0.f, 0.f, 0.f, 0.f), s1 = s0;
+#pragma unroll
+    for (int w = 0; w < I4_WAVES_N; ++w) {
+        const float *src = P + ((size_t)w * I4_BM + ml) * 32 + j0;
+        const float4 a = *reinterpret_cast<const float4 *>(src), b = *reinterpret_cast<const float4 *>(src + 4);
+        s0.x += a.x; s0.y += a.y; s0.z += a.z; s0.w += a.w;
+        s1.x += b.x; s1.y += b.y; s1.z += b.z; s1.w += b.w;
+    }
+    const int m = m0 + ml;
+    if (m < M) {
+        float *dst = rq.hpart + ((size_t)tile_n * M + m) * 32 + j0;
+        *reinterpret_cast<float4 *>(dst) = s0;
+        *reinterpret_cast<float4 *>(dst + 4) = s1;
+    }
+}
+
+template <bool REQ>
 __global__ __launch_bounds__(I4_THREADS) void w4a4_int4_kernel(
     const uint8_t *__restrict__ xq, const float *__restrict__ xscale, const float *__restrict__ h,
     const uint8_t *__restrict__ wq, const float *__restrict__ wscale, const uint16_t *__restrict__ up,
-    const uint16_t *__restrict__ bias, int M, int N, int K, int gelu, uint16_t *__restrict__ Y)
+    const uint16_t *__restrict__ bias, int M, int N, int K, int gelu, uint16_t *__restrict__ Y, RequantArgs rq)
 {
     __shared__ I4Smem sm;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -397,6 +602,11 @@ __global__ __launch_bounds__(I4_THREADS) void w4a4_int4_kernel(
             load_h8(h, mb + tm * 32 + l32, M, 16 * s + 8 * hk, hv);
             split_h(hv, hhi[tm][s], hlo[tm][s]);
         }
+    if constexpr (REQ) {
+        requant_epilogue(acc, hhi, hlo, up, bias, M, N, gelu, rq, mb, nb, tn_, m0, wn, wm, tid, lane,
+                         reinterpret_cast<float *>(&sm));
+        return;
+    }
     uint8_t *tile = reinterpret_cast<uint8_t *>(&sm) + wave * OUT_TILE_BYTES;
     static_assert(8 * OUT_TILE_BYTES <= sizeof(I4Smem), "output staging fits in LDS");
 #pragma unroll
@@ -431,6 +641,28 @@ __global__ __launch_bounds__(I4_THREADS) void w4a4_int4_kernel(
     }
     __syncthreads();
     flush_tile(tile, Y, mb, nb, M, N, lane);
+}
+
+// Fixed-order sum of the per-tile partial h2: h2[m][j] = sum_t hpart[t][m][j],
+// t ascending.
+__global__ __launch_bounds__(256) void requant_h_reduce(const float *__restrict__ hpart, int T, int M,
+                                                        float *__restrict__ h2)
+{
+    const int i = blockIdx.x * 256 + threadIdx.x;      // (m * 32 + j) / 4
+    if (i >= M * 8) return;
+    f32x4 s = {0.f, 0.f, 0.f, 0.f};
+    const f32x4 *p = reinterpret_cast<const f32x4 *>(hpart) + i;
+    const size_t step = (size_t)M * 8;
+    int t = 0;
+    for (; t + 8 <= T; t += 8) {          // 8 loads in flight, added in order
+        f32x4 a[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) a[u] = __builtin_nontemporal_load(p + (t + u) * step);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) s += a[u];
+    }
+    for (; t < T; ++t) s += __builtin_nontemporal_load(p + t * step);
+    reinterpret_cast<f32x4 *>(h2)[i] = s;
 }
 
 // ===================================================================== MXFP4
@@ -864,8 +1096,9 @@ hipError_t launch_w4a4_linear(const uint8_t *xq, const void *xscale, const float
     const int64_t rows = M > N ? M : N;
     if (prec == SVDQ_INT4) {
         const int tiles = ((N + I4_BN - 1) / I4_BN) * ((M + I4_BM - 1) / I4_BM);
-        hipLaunchKernelGGL(w4a4_int4_kernel, dim3((unsigned)tiles), dim3(I4_THREADS), 0, stream, xq,
-                           (const float *)xscale, h, wq, (const float *)wscale, up, bias, M, N, K, gelu, Y);
+        hipLaunchKernelGGL(w4a4_int4_kernel<false>, dim3((unsigned)tiles), dim3(I4_THREADS), 0, stream, xq,
+                           (const float *)xscale, h, wq, (const float *)wscale, up, bias, M, N, K, gelu, Y,
+                           RequantArgs{});
     } else {
         // the LDS-DMA kernel takes whole 256-channel steps and 32-bit offsets
         if (K % 256 == 0 && rows * (K / 2) < ((int64_t)1 << 31)) {
@@ -880,6 +1113,27 @@ hipError_t launch_w4a4_linear(const uint8_t *xq, const void *xscale, const float
                                (const uint8_t *)xscale, h, wq, (const uint8_t *)wscale, up, bias, M, N, K, gelu, Y);
         }
     }
+    return hipGetLastError();
+}
+
+size_t requant_work_bytes(int M, int N) { return (size_t)((N + I4_BN - 1) / I4_BN) * M * 32 * sizeof(float); }
+
+hipError_t launch_w4a4_linear_requant(const uint8_t *xq, const void *xscale, const float *h, const uint8_t *wq,
+                                      const void *wscale, const uint16_t *up, const uint16_t *bias, int M, int N,
+                                      int K, svdq_epilogue epi, const float *smooth2, const uint16_t *down2,
+                                      uint8_t *xq2, float *xscale2, float *h2, float *work, hipStream_t stream)
+{
+    const int gelu = epi == SVDQ_EPI_GELU_TANH ? 1 : 0;
+    const int tiles_n = (N + I4_BN - 1) / I4_BN;
+    const int tiles = tiles_n * ((M + I4_BM - 1) / I4_BM);
+    const RequantArgs rq{smooth2, down2, xq2, xscale2, work};
+    hipLaunchKernelGGL(w4a4_int4_kernel<true>, dim3((unsigned)tiles), dim3(I4_THREADS), 0, stream, xq,
+                       (const float *)xscale, h, wq, (const float *)wscale, up, bias, M, N, K, gelu,
+                       (uint16_t *)nullptr, rq);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(requant_h_reduce, dim3((unsigned)((M * 8 + 255) / 256)), dim3(256), 0, stream,
+                       (const float *)work, tiles_n, M, h2);
     return hipGetLastError();
 }
 

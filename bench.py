@@ -84,8 +84,8 @@ def main():
     ap.add_argument("--prec", choices=["int4", "mxfp4"], default="int4")
     ap.add_argument("--layer", choices=["fc1", "qkv", "fc2", "mlp"], default="fc1",
                     help="fc1 is the headline workload; fc2 takes fc1's output (computed on the GPU); "
-                         "mlp times fc1 -> fc2 with fc2's activation step fused into fc1's epilogue "
-                         "(INT4), next to the unfused pair")
+                         "mlp times fc1 -> fc2 with fc2's activation step fused into fc1's epilogue, "
+                         "next to the unfused pair")
     ap.add_argument("--copy-calibration", type=int, metavar="MIB", default=0,
                     help="only run a plain copy of MIB MiB (to scale the HBM byte counters)")
     ap.add_argument("--sets", type=int, default=3, help="rotating buffer sets")
@@ -261,15 +261,15 @@ def main():
 
 
 def mlp_main(args, torch, svdq, synth):
-    """fc1 (GELU) -> fc2 at M=4608 (INT4): the fused step runs fc1's
+    """fc1 (GELU) -> fc2 at M=4608: the fused step runs fc1's
     activation step, fc1's product whose epilogue writes fc2's codes, scales
     and h (svdq_w4a4_linear_requant), then fc2's product.  The unfused step
     stores fc1's Y and runs fc2's activation step on it."""
-    if args.prec != "int4":
-        print("--layer mlp: the fused requantization is INT4 only", file=sys.stderr)
-        sys.exit(2)
-    prec = svdq.INT4
-    f1s, f2s = synth.SPECS["fc1"], synth.SPECS["fc2"]
+    prec = svdq.INT4 if args.prec == "int4" else svdq.MXFP4
+    pre = "" if prec == svdq.INT4 else "mx_"
+    f1s, f2s = synth.SPECS[pre + "fc1"], synth.SPECS[pre + "fc2"]
+    g = svdq.group_of(prec)
+    sdt = torch.float32 if prec == svdq.INT4 else torch.uint8
     M, K1, N1, N2, r = f1s.M, f1s.K, f1s.N, f2s.N, svdq.RANK
     print(f"[bench] generating and packing fc1 {M}x{K1}->{N1} and fc2 {M}x{N1}->{N2}", file=sys.stderr,
           flush=True)
@@ -291,13 +291,13 @@ def mlp_main(args, torch, svdq, synth):
             X=svdq.bf16_tensor(L1["X"]), d1=a, b1=svdq.bf16_tensor(L1["bias"]), d2=b,
             b2=svdq.bf16_tensor(L2["bias"]),
             xq=torch.empty((M, K1 // 2), dtype=torch.uint8, device="cuda"),
-            xs=torch.empty((M, K1 // 64), dtype=torch.float32, device="cuda"),
+            xs=torch.empty((M, K1 // g), dtype=sdt, device="cuda"),
             h=torch.empty((M, r), dtype=torch.float32, device="cuda"),
             Y1=torch.empty((M, N1), dtype=torch.bfloat16, device="cuda"),
             xq2=torch.empty((M, N1 // 2), dtype=torch.uint8, device="cuda"),
-            xs2=torch.empty((M, N1 // 64), dtype=torch.float32, device="cuda"),
+            xs2=torch.empty((M, N1 // g), dtype=sdt, device="cuda"),
             h2=torch.empty((M, r), dtype=torch.float32, device="cuda"),
-            work=torch.empty((svdq.requant_workspace_bytes(M, N1),), dtype=torch.uint8, device="cuda"),
+            work=torch.empty((svdq.requant_workspace_bytes(M, N1, prec=prec),), dtype=torch.uint8, device="cuda"),
             Y2=torch.empty((M, N2), dtype=torch.bfloat16, device="cuda")))
 
     def act1(b):
@@ -365,6 +365,8 @@ def mlp_main(args, torch, svdq, synth):
     ops = 2.0 * M * N1 * K1 + 2.0 * M * N2 * N1
     req_ms = out["fused_launch_ms"][1]
     req_tops = 2.0 * M * N1 * K1 / (req_ms * 1e-3) / 1e12
+    peak = PEAK_INT8_TOPS if prec == svdq.INT4 else PEAK_FP4_TFLOPS
+    fmt = "INT4 g64" if prec == svdq.INT4 else "MXFP4 g32"
     line = {
         "metric": "fc1 -> fc2 MLP pair, fc2's activation step fused into fc1's epilogue (TOPS)",
         "value": round(ops / (out["fused"] * 1e-3) / 1e12, 2),
@@ -376,10 +378,12 @@ def mlp_main(args, torch, svdq, synth):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int4 codes (exact fp8 values) on the fp8 matrix cores, exact per-group partials, fp32 rescale",
+        "dtype": "int4 codes (exact fp8 values) on the fp8 matrix cores, exact per-group partials, fp32 rescale"
+                 if prec == svdq.INT4
+                 else "mxfp4 (e2m1 x e2m1, e8m0 scales) on the scaled fp4 matrix cores, fp32 accumulation",
         "data": "synthetic (seeded Student-t activations with outlier channels, N(0,0.02^2) weights); "
                 "fc2's input is fc1's GPU output",
-        "config": {"workload": f"MLP: {M} tokens x {K1} -> {N1} (GELU) -> {N2}, rank {r}, INT4 g64, bias; "
+        "config": {"workload": f"MLP: {M} tokens x {K1} -> {N1} (GELU) -> {N2}, rank {r}, {fmt}, bias; "
                                "fused step = quantize_act + w4a4_linear_requant + w4a4_linear; "
                                "unfused step = quantize_act + w4a4_linear + quantize_act + w4a4_linear",
                    "M": M, "K": K1, "N": N1, "N2": N2, "rank": r, "buffer_sets": len(sets)},
@@ -387,8 +391,8 @@ def mlp_main(args, torch, svdq, synth):
         "fused_launch_ms": out["fused_launch_ms"],
         "unfused_launch_ms": out["plain_launch_ms"],
         "roofline": {"bound": "mfma", "kernel": "svdq_w4a4_linear_requant (fc1, with the h2 sum)",
-                     "achieved": round(req_tops, 2), "peak": PEAK_INT8_TOPS, "unit": "TFLOP/s",
-                     "frac": round(req_tops / PEAK_INT8_TOPS, 4), "traffic": None, "avg_ms": req_ms},
+                     "achieved": round(req_tops, 2), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(req_tops / peak, 4), "traffic": None, "avg_ms": req_ms},
         "cpu_baseline": None,
     }
     print(json.dumps(line), flush=True)

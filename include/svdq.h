@@ -198,19 +198,20 @@ size_t svdq_requant_workspace_bytes(int M, int N, int rank, svdq_precision prec)
  * activation step directly (an MLP's fc1 -> fc2, "Introducing Nunchaku
  * Lite": fused GELU/MLP paths): Y is not stored.  Each output is rounded to
  * bf16 exactly as svdq_w4a4_linear would store it, then smoothed with the
- * next layer's `smooth2`, quantized per 64 consecutive output channels, and
- * multiplied into the next layer's `down2`.  The results are those of
- * svdq_quantize_act(Y, M, N, smooth2, down2, ...) on that Y: codes and scales
- * bit-exact, h2 up to the order of the fp32 sums (per-tile partial sums over
- * 256 channels, added in ascending tile order, so h2 is deterministic).
+ * next layer's `smooth2`, quantized per group of consecutive output channels
+ * (64 INT4, 32 MXFP4), and multiplied into the next layer's `down2`.  The
+ * results are those of svdq_quantize_act(Y, M, N, smooth2, down2, ...) on
+ * that Y: codes and scales bit-exact, h2 up to the order of the fp32 sums
+ * (per-tile partial sums over 256 channels, added in ascending tile order,
+ * so h2 is deterministic).
  *
- *   xq ... epi   as for svdq_w4a4_linear (prec must be SVDQ_INT4; the next
- *                layer uses INT4 too)
+ *   xq ... epi   as for svdq_w4a4_linear; `prec` is that of both layers.
+ *                MXFP4 needs K % 256 == 0 (SVDQ_ERR_UNSUPPORTED otherwise)
  *   N            N % 64 == 0 (the next layer's K)
  *   smooth2      [N] fp32, device                  next layer's s
  *   down2        [rank][N] bf16 bits, device       next layer's down
  *   xq2          [M][N/2] uint8, device (out)
- *   xscale2      [M][N/64] fp32, device (out)
+ *   xscale2      INT4: [M][N/64] fp32; MXFP4: [M][N/32] uint8 (E8M0), device (out)
  *   h2           [M][rank] fp32, device (out)
  *   work         device scratch of at least svdq_requant_workspace_bytes(M,
  *                N, rank, prec) bytes, caller-owned; its contents on entry
@@ -218,8 +219,8 @@ size_t svdq_requant_workspace_bytes(int M, int N, int rank, svdq_precision prec)
  *   stream       hipStream_t or NULL
  * Two kernel launches on `stream` (the product with this epilogue, then the
  * fixed-order sum of the partial h2).  Errors: as for svdq_w4a4_linear;
- * SVDQ_ERR_UNSUPPORTED for MXFP4; SVDQ_ERR_SHAPE when N % 64 != 0;
- * SVDQ_ERR_INVALID_ARG when work_bytes is too small.
+ * SVDQ_ERR_SHAPE when N % 64 != 0; SVDQ_ERR_UNSUPPORTED for MXFP4 with
+ * K % 256 != 0; SVDQ_ERR_INVALID_ARG when work_bytes is too small.
  */
 svdq_status svdq_w4a4_linear_requant(const uint8_t *xq, const void *xscale, const float *h,
                                      const uint8_t *wq, const void *wscale, const uint16_t *up,

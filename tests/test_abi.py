@@ -81,7 +81,7 @@ def test_requant_validation_and_workspace():
                                           a["N"], a["K"], a["r"], a["prec"], a["epi"], a["s2"], a["d2"], a["xq2"],
                                           a["xs2"], a["h2"], a["work"], a["wb"], None)
     assert call(N=96) == -2                     # N must be a multiple of 64 (the next layer's K)
-    assert call(prec=svdq.MXFP4) == -4          # INT4 only
+    assert call(prec=svdq.MXFP4) == -4          # MXFP4 needs K % 256 == 0
     assert call(r=16) == -4
     assert call(epi=3) == -1
     assert call(wb=W - 1) == -1                 # workspace too small
@@ -91,6 +91,7 @@ def test_requant_validation_and_workspace():
     assert call(work=q) == -3
     if not _has_gpu():
         assert call() == -5
+        assert call(prec=svdq.MXFP4, K=256) == -5
 
 
 def _has_gpu():

@@ -225,54 +225,57 @@ def test_linear_deterministic_and_empty():
 
 # --------------------------------------------- fused next-layer requantization
 
-def _requant_case(M, K, N, bias, gelu, rows=None):
+def _requant_case(M, K, N, bias, gelu, prec, rows=None):
     """fc1 -> fc2 with fc2's activation step fused into fc1's epilogue: the
     codes and scales must equal the separate activation step on the Y the
     plain kernel stores (bit-exact), and the oracle's on that Y; h2 within the
     blocked-summation bound."""
-    L, p = _layer("qkv", M, K, N, svdq.INT4, bias=bias)
-    xq, xs, h = svdq.quantize_act(_t(L["X"]), _t(p["smooth"]), _t(p["down"]))
+    L, p = _layer("qkv", M, K, N, prec, bias=bias)
+    xq, xs, h = svdq.quantize_act(_t(L["X"]), _t(p["smooth"]), _t(p["down"]), prec)
     epi = svdq.EPI_GELU_TANH if gelu else svdq.EPI_NONE
     args = (xq, xs, h, _t(p["wq"]), _t(p["wscale"]), _t(p["up"]), _t(L["bias"]))
-    Y = svdq.w4a4_linear(*args, svdq.INT4, epi)
+    Y = svdq.w4a4_linear(*args, prec, epi)
     torch.cuda.synchronize()
     Yb = _np(Y)
     f2 = synth.make_layer(synth.SPECS["fc2"], M=M, K=N, N=64, X_bits=Yb)
-    p2 = svdq.pack_weights(f2["W"], f2["act_absmax"], prec=svdq.INT4)
+    p2 = svdq.pack_weights(f2["W"], f2["act_absmax"], prec=prec)
     s2, d2 = _t(p2["smooth"]), _t(p2["down"])
-    uq, us, uh = svdq.quantize_act(Y, s2, d2)
-    fq, fs, fh = svdq.w4a4_linear_requant(*args, s2, d2, svdq.INT4, epi)
+    uq, us, uh = svdq.quantize_act(Y, s2, d2, prec)
+    fq, fs, fh = svdq.w4a4_linear_requant(*args, s2, d2, prec, epi)
     torch.cuda.synchronize()
     assert torch.equal(fq, uq), f"codes differ at {torch.nonzero(fq != uq)[:5].tolist()}"
-    assert torch.equal(fs.view(torch.int32), us.view(torch.int32)), "scales differ"
+    assert torch.equal(fs.view(torch.uint8), us.view(torch.uint8)), "scales differ"
     rows = np.arange(M) if rows is None else rows
-    oq, os_, oh = O.quant_act(Yb[rows], p2["smooth"], p2["down"], svdq.INT4)
+    oq, os_, oh = O.quant_act(Yb[rows], p2["smooth"], p2["down"], prec)
     assert np.array_equal(_np(fq)[rows], oq)
-    assert np.array_equal(_np(fs)[rows].view(np.uint32), os_.view(np.uint32))
+    assert np.array_equal(_np(fs)[rows].view(np.uint8), os_.view(np.uint8))
     assert np.all(np.abs(_np(fh)[rows].astype(np.float64) - oh) <= _h_bound(Yb[rows], p2["down"]))
     # the fused h2 is deterministic
-    fq2, fs2, fh2 = svdq.w4a4_linear_requant(*args, s2, d2, svdq.INT4, epi)
+    fq2, fs2, fh2 = svdq.w4a4_linear_requant(*args, s2, d2, prec, epi)
     torch.cuda.synchronize()
     assert torch.equal(fh2, fh) and torch.equal(fq2, fq)
 
 
+@pytest.mark.parametrize("prec", PRECS)
 @pytest.mark.parametrize("M,K,N,bias,gelu", [
     (130, 256, 512, True, True),       # ragged M, two 256-channel tiles
-    (64, 192, 320, False, False),      # last channel tile 64 wide, odd group count along K
-    (1, 64, 64, True, True),
+    (64, 512, 320, False, False),      # last channel tile 64 wide
+    (1, 256, 64, True, True),
     (300, 512, 1024, True, True),
+    (600, 768, 768, True, True),       # three tiles of N, M over two MX token tiles
 ])
-def test_requant_matches_unfused(M, K, N, bias, gelu):
-    _say(f"requant M={M} K={K} N={N} bias={bias} gelu={gelu}")
-    _requant_case(M, K, N, bias, gelu)
+def test_requant_matches_unfused(prec, M, K, N, bias, gelu):
+    _say(f"requant prec={prec} M={M} K={K} N={N} bias={bias} gelu={gelu}")
+    _requant_case(M, K, N, bias, gelu, prec)
 
 
-def test_requant_mlp_full_size():
+@pytest.mark.parametrize("prec", PRECS)
+def test_requant_mlp_full_size(prec):
     """fc1 (4608 x 3072 -> 12288, GELU) feeding fc2's activation step at the
     bench's size: every row's codes and scales against the separate step,
     sampled rows against the oracle."""
-    _say("requant full-size fc1 -> fc2")
-    _requant_case(4608, 3072, 12288, True, True, rows=_rows(4608, 24, seed=5))
+    _say(f"requant full-size fc1 -> fc2 prec={prec}")
+    _requant_case(4608, 3072, 12288, True, True, prec, rows=_rows(4608, 24, seed=5))
 
 
 # ------------------------------------------------- full sizes, bench launches

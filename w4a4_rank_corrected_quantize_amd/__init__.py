@@ -229,8 +229,9 @@ def w4a4_linear_requant(xq, xscale, h, wq, wscale, up, bias, smooth2, down2, pre
     r = up.shape[1]
     dev = xq.device
     if out is None:
-        out = (torch.empty((M, N // 2), dtype=torch.uint8, device=dev),
-               torch.empty((M, max(N // 64, 1)), dtype=torch.float32, device=dev),
+        scales = (torch.empty((M, max(N // 64, 1)), dtype=torch.float32, device=dev) if prec == INT4
+                  else torch.empty((M, max(N // 32, 1)), dtype=torch.uint8, device=dev))
+        out = (torch.empty((M, N // 2), dtype=torch.uint8, device=dev), scales,
                torch.empty((M, r), dtype=torch.float32, device=dev))
     xq2, xs2, h2 = out
     nbytes = requant_workspace_bytes(M, N, r, prec)
@@ -243,7 +244,7 @@ def w4a4_linear_requant(xq, xscale, h, wq, wscale, up, bias, smooth2, down2, pre
         _dev(wscale, (torch.float32, torch.uint8), "wscale"), _dev(up, (torch.bfloat16, torch.int16), "up"),
         pbias, M, N, K, r, prec, epi, _dev(smooth2, (torch.float32,), "smooth2"),
         _dev(down2, (torch.bfloat16, torch.int16), "down2"), _dev(xq2, (torch.uint8,), "xq2"),
-        _dev(xs2, (torch.float32,), "xscale2"), _dev(h2, (torch.float32,), "h2"),
+        _dev(xs2, (torch.float32, torch.uint8), "xscale2"), _dev(h2, (torch.float32,), "h2"),
         _dev(work, (torch.uint8, torch.float32), "work"), work.numel() * work.element_size(), _stream(stream))
     _check(st, "svdq_w4a4_linear_requant")
     return xq2, xs2, h2

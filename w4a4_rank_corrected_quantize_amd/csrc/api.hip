@@ -154,8 +154,8 @@ extern "C" svdq_status svdq_w4a4_linear_requant(const uint8_t *xq, const void *x
     if (st != SVDQ_OK) return st;
     if (N < 0) return SVDQ_ERR_INVALID_ARG;
     if (epi != SVDQ_EPI_NONE && epi != SVDQ_EPI_GELU_TANH) return SVDQ_ERR_INVALID_ARG;
-    if (prec != SVDQ_INT4) return SVDQ_ERR_UNSUPPORTED;
     if (N % 64 != 0) return SVDQ_ERR_SHAPE;
+    if (!requant_supported(M, N, K, prec)) return SVDQ_ERR_UNSUPPORTED;
     // buffers of zero size may be NULL (empty tensors have no storage)
     if ((M > 0 && (!xq || !xscale || !h)) || (N > 0 && (!wq || !wscale || !up || !smooth2 || !down2)) ||
         (M > 0 && N > 0 && (!xq2 || !xscale2 || !h2 || !work)))
@@ -168,7 +168,7 @@ extern "C" svdq_status svdq_w4a4_linear_requant(const uint8_t *xq, const void *x
     st = current_device_ok();
     if (st != SVDQ_OK) return st;
     if (M == 0 || N == 0) return SVDQ_OK;
-    hipError_t e = launch_w4a4_linear_requant(xq, xscale, h, wq, wscale, up, bias, M, N, K, epi, smooth2, down2,
-                                              xq2, (float *)xscale2, h2, (float *)work, (hipStream_t)stream);
+    hipError_t e = launch_w4a4_linear_requant(xq, xscale, h, wq, wscale, up, bias, M, N, K, prec, epi, smooth2,
+                                              down2, xq2, xscale2, h2, (float *)work, (hipStream_t)stream);
     return e == hipSuccess ? SVDQ_OK : SVDQ_ERR_HIP;
 }

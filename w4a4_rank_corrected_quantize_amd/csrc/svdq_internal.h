@@ -24,13 +24,16 @@ hipError_t launch_w4a4_linear(const uint8_t *xq, const void *xscale, const float
                               int K, svdq_precision prec, svdq_epilogue epi, uint16_t *Y,
                               hipStream_t stream);
 
-// Fused requantization (INT4): the product's epilogue writes the next
-// layer's codes, scales and h instead of Y.  `work` holds the per-tile
-// partial h (requant_work_bytes(M, N) bytes).
+// Fused requantization: the product's epilogue writes the next layer's
+// codes, scales and h instead of Y.  `work` holds the per-tile partial h
+// (requant_work_bytes(M, N) bytes).  MXFP4 runs on the LDS-DMA kernel only
+// (requant_supported).
 size_t requant_work_bytes(int M, int N);
+bool requant_supported(int M, int N, int K, svdq_precision prec);
 hipError_t launch_w4a4_linear_requant(const uint8_t *xq, const void *xscale, const float *h, const uint8_t *wq,
                                       const void *wscale, const uint16_t *up, const uint16_t *bias, int M, int N,
-                                      int K, svdq_epilogue epi, const float *smooth2, const uint16_t *down2,
-                                      uint8_t *xq2, float *xscale2, float *h2, float *work, hipStream_t stream);
+                                      int K, svdq_precision prec, svdq_epilogue epi, const float *smooth2,
+                                      const uint16_t *down2, uint8_t *xq2, void *xscale2, float *h2, float *work,
+                                      hipStream_t stream);
 
 }  // namespace svdq

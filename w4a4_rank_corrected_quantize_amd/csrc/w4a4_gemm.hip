@@ -234,7 +234,7 @@ struct RequantArgs {
     const float *smooth2;     // [N]
     const uint16_t *down2;    // [32][N] bf16 bits
     uint8_t *xq2;             // [M][N/2]
-    float *xscale2;           // [M][N/64]
+    void *xscale2;            // INT4: fp32 [M][N/64]; MXFP4: E8M0 [M][N/32]
     float *hpart;             // [ceil(N/256)][M][32]
 };
 
@@ -384,7 +384,7 @@ __device__ __forceinline__ void requant_epilogue(const f32x16 (&acc)[I4_TN][I4_T
         out = make_uint4(o[0], o[1], o[2], o[3]);
         if (live && m < M) {
             *reinterpret_cast<uint4 *>(rq.xq2 + (size_t)m * (N / 2) + nb / 2 + 16 * hk) = out;
-            if (hk == 0) rq.xscale2[(size_t)m * (N / 64) + nb / 64] = scale;
+            if (hk == 0) static_cast<float *>(rq.xscale2)[(size_t)m * (N / 64) + nb / 64] = scale;
         }
         // partial h2 = Y down2^T over the wave tile's 64 channels
         f32x16 d = {};
@@ -933,14 +933,172 @@ __device__ __forceinline__ void dma_b32(uint32_t lds, uint32_t voff, const void 
                  : "=&s"(keep) : "s"(lds), "v"(voff), "s"(sbase) : "memory");
 }
 
+// Epilogue of the requantizing MXFP4 kernel for one wave tile (128 channels,
+// four 32-channel blocks, x 64 tokens): as requant_epilogue, with E8M0 block
+// scales and E2M1 codes.  Lane (l32, hk) holds, per 32-token tile tm and
+// block tn, channels nb + 32 tn + 8 j + 4 hk + (0..3): half of the token's
+// block.  Blocks at or past N (N % 32 == 0) are neither stored nor summed.
+// `P` is LDS that no wave reads any more (the stage of the tile's last step).
+__device__ __forceinline__ void requant_epilogue_mx(const f32x16 (&acc)[MX_TN][MX_TM], const float *__restrict__ h,
+                                                    const uint16_t *__restrict__ up,
+                                                    const uint16_t *__restrict__ bias, int M, int N, int gelu,
+                                                    const RequantArgs &rq, int mb, int nb, int tile_n, int m0, int wn,
+                                                    int wm, int tid, int lane, float *P)
+{
+    const int l32 = lane & 31, hk = lane >> 5;
+    bf16x8 hhi[MX_TM][2], hlo[MX_TM][2];
+#pragma unroll
+    for (int tm = 0; tm < MX_TM; ++tm)
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+            float hv[8];
+            load_h8(h, mb + tm * 32 + l32, M, 16 * s2 + 8 * hk, hv);
+            split_h(hv, hhi[tm][s2], hlo[tm][s2]);
+        }
+    f32x16 hp[MX_TM] = {};
+    uint32_t e8s[MX_TM] = {};           // E8M0 of the 4 blocks, one byte each (lanes hk = 0)
+#pragma unroll
+    for (int tn = 0; tn < MX_TN; ++tn) {
+        const int c0 = nb + tn * 32;
+        const bool live = c0 < N;
+        const int nrow = c0 + l32;
+        bf16x8 ua[2];
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+            uint4 uv = {0u, 0u, 0u, 0u};
+            if (nrow < N) uv = *reinterpret_cast<const uint4 *>(up + (size_t)nrow * 32 + 16 * s2 + 8 * hk);
+            ua[s2] = __builtin_bit_cast(bf16x8, uv);
+        }
+        uint2 bv[4];
+        float4 s2v[4];
+        bf16x8 dn[2];                    // A operands: down2 rows l32, k blocks 2 tn and 2 tn + 1
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            bv[j] = bias4(bias, c0 + 8 * j + 4 * hk, N);
+            s2v[j] = live ? *reinterpret_cast<const float4 *>(rq.smooth2 + c0 + 8 * j + 4 * hk)
+                          : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh) {
+            const int c = c0 + 16 * kh + 4 * hk;
+            uint2 a = {0u, 0u}, b = {0u, 0u};
+            if (live) {
+                a = *reinterpret_cast<const uint2 *>(rq.down2 + (size_t)l32 * N + c);
+                b = *reinterpret_cast<const uint2 *>(rq.down2 + (size_t)l32 * N + c + 8);
+            }
+            dn[kh] = __builtin_bit_cast(bf16x8, (uint4){a.x, a.y, b.x, b.y});
+        }
+#pragma unroll
+        for (int tm = 0; tm < MX_TM; ++tm) {
+            const int m = mb + tm * 32 + l32;
+            f32x16 lr = {};
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) {
+                lr = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ua[s2], hhi[tm][s2], lr, 0, 0, 0);
+                lr = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ua[s2], hlo[tm][s2], lr, 0, 0, 0);
+            }
+            uint2 yb[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                float a4[4] = {acc[tn][tm][4 * j], acc[tn][tm][4 * j + 1], acc[tn][tm][4 * j + 2],
+                               acc[tn][tm][4 * j + 3]};
+                float l4[4] = {lr[4 * j], lr[4 * j + 1], lr[4 * j + 2], lr[4 * j + 3]};
+                yb[j] = finish4(a4, l4, bv[j], gelu);
+            }
+            // smoothed values, block absmax over both lane halves, E8M0
+            float v[4][4];
+            float amax = 0.0f;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float sv[4] = {s2v[j].x, s2v[j].y, s2v[j].z, s2v[j].w};
+                const float yv[4] = {bf16_to_f32(yb[j].x & 0xFFFFu), bf16_to_f32(yb[j].x >> 16),
+                                     bf16_to_f32(yb[j].y & 0xFFFFu), bf16_to_f32(yb[j].y >> 16)};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    v[j][e] = yv[e] * sv[e];
+                    amax = __builtin_fmaxf(amax, __builtin_fabsf(v[j][e]));
+                }
+            }
+            amax = __builtin_fmaxf(amax, __shfl_xor(amax, 32));
+            const uint32_t e8 = mx_block_e8m0(amax);
+            const float inv = mx_inv_scale(e8);
+            // E2M1 codes (the hardware conversion at unit scale of the exactly
+            // pre-scaled values): pieces j = 0, 1 in dword lo, 2, 3 in hi
+            uint32_t lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, v[0][0] * inv, v[0][1] * inv, 1.0f, 0);
+            lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo, v[0][2] * inv, v[0][3] * inv, 1.0f, 1);
+            lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo, v[1][0] * inv, v[1][1] * inv, 1.0f, 2);
+            lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo, v[1][2] * inv, v[1][3] * inv, 1.0f, 3);
+            uint32_t hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, v[2][0] * inv, v[2][1] * inv, 1.0f, 0);
+            hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi, v[2][2] * inv, v[2][3] * inv, 1.0f, 1);
+            hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi, v[3][0] * inv, v[3][1] * inv, 1.0f, 2);
+            hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi, v[3][2] * inv, v[3][3] * inv, 1.0f, 3);
+            // byte 4 j + 2 half of the block's 16 code bytes is lane half
+            // `half`'s piece j: half 0 keeps j = 0, 1 and takes its partner's,
+            // half 1 keeps j = 2, 3
+            const uint32_t got = (uint32_t)__shfl_xor((int)(hk ? lo : hi), 32);
+            const uint32_t own = hk ? hi : lo;
+            uint2 out;
+            if (hk == 0) out = make_uint2((own & 0xFFFFu) | got << 16, (own >> 16) | (got & 0xFFFF0000u));
+            else out = make_uint2((got & 0xFFFFu) | own << 16, (got >> 16) | (own & 0xFFFF0000u));
+            if (live && m < M) *reinterpret_cast<uint2 *>(rq.xq2 + (size_t)m * (N / 2) + c0 / 2 + 8 * hk) = out;
+            e8s[tm] |= e8 << (8 * tn);
+            // partial h2 over the block's 32 channels
+            const bf16x8 b0 = __builtin_bit_cast(bf16x8, live ? (uint4){yb[0].x, yb[0].y, yb[1].x, yb[1].y}
+                                                              : (uint4){0u, 0u, 0u, 0u});
+            const bf16x8 b1 = __builtin_bit_cast(bf16x8, live ? (uint4){yb[2].x, yb[2].y, yb[3].x, yb[3].y}
+                                                              : (uint4){0u, 0u, 0u, 0u});
+            hp[tm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dn[0], b0, hp[tm], 0, 0, 0);
+            hp[tm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dn[1], b1, hp[tm], 0, 0, 0);
+        }
+    }
+#pragma unroll
+    for (int tm = 0; tm < MX_TM; ++tm) {
+        const int m = mb + tm * 32 + l32;
+        if (hk == 0 && m < M) {
+            uint8_t *dst = static_cast<uint8_t *>(rq.xscale2) + (size_t)m * (N / 32) + nb / 32;
+#pragma unroll
+            for (int tn = 0; tn < MX_TN; ++tn)
+                if (nb + tn * 32 < N) dst[tn] = (uint8_t)(e8s[tm] >> (8 * tn));
+        }
+    }
+    // the block's two channel halves summed in LDS (fixed order), one row of
+    // 32 partial sums per token to hpart
+    __syncthreads();
+#pragma unroll
+    for (int tm = 0; tm < MX_TM; ++tm) {
+        const int ml = wm * MX_WM + tm * 32 + l32;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const float4 w4 = make_float4(hp[tm][4 * q], hp[tm][4 * q + 1], hp[tm][4 * q + 2], hp[tm][4 * q + 3]);
+            *reinterpret_cast<float4 *>(P + ((size_t)wn * MXD_BM + ml) * 32 + 8 * q + 4 * hk) = w4;
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const int idx = tid + MXD_THREADS * k;          // (token, 8-float slice) of the block's 256 x 32
+        const int ml = idx >> 2, j0 = 8 * (idx & 3);
+        const float *s0p = P + (size_t)ml * 32 + j0, *s1p = P + ((size_t)MXD_BM + ml) * 32 + j0;
+        const float4 a0 = *reinterpret_cast<const float4 *>(s0p), a1 = *reinterpret_cast<const float4 *>(s0p + 4);
+        const float4 b0 = *reinterpret_cast<const float4 *>(s1p), b1 = *reinterpret_cast<const float4 *>(s1p + 4);
+        const int m = m0 + ml;
+        if (m < M) {
+            float *dst = rq.hpart + ((size_t)tile_n * M + m) * 32 + j0;
+            *reinterpret_cast<float4 *>(dst) = make_float4(a0.x + b0.x, a0.y + b0.y, a0.z + b0.z, a0.w + b0.w);
+            *reinterpret_cast<float4 *>(dst + 4) = make_float4(a1.x + b1.x, a1.y + b1.y, a1.z + b1.z, a1.w + b1.w);
+        }
+    }
+}
+
 // Persistent: block b takes the tiles b, b + gridDim.x, ...  The two stages
 // alternate over the global step count, and the first step of the next tile
 // is loaded into the free stage while the epilogue of the current tile runs
 // (its output staging uses the other stage).
+template <bool REQ>
 __global__ __launch_bounds__(MXD_THREADS) void w4a4_mxfp4_dma_kernel(
     const uint8_t *__restrict__ xq, const uint8_t *__restrict__ xscale, const float *__restrict__ h,
     const uint8_t *__restrict__ wq, const uint8_t *__restrict__ wscale, const uint16_t *__restrict__ up,
-    const uint16_t *__restrict__ bias, int M, int N, int K, int gelu, uint16_t *__restrict__ Y)
+    const uint16_t *__restrict__ bias, int M, int N, int K, int gelu, uint16_t *__restrict__ Y, RequantArgs rq)
 {
     __shared__ MXDStage stage[2];
     const int tid = threadIdx.x, lane = tid & 63;
@@ -1070,13 +1228,20 @@ __global__ __launch_bounds__(MXD_THREADS) void w4a4_mxfp4_dma_kernel(
         // the next tile's first step while this tile's epilogue runs
         const int last = (g + steps - 1) & 1;
         const int mb = m0 + wm * MX_WM, nb = n0 + wn * MX_WN;
+        const int tile_n = n0 / MXD_BN, tile_m0 = m0;
         const int tnext = t + (int)gridDim.x;
         if (tnext < tiles) {
             set_tile(tnext, n0, m0);
             issue(0, last ^ 1);
         }
-        wave_epilogue<MX_TN, MX_TM>(acc, h, up, bias, M, N, gelu, Y, mb, nb,
-                                    reinterpret_cast<uint8_t *>(&stage[last]) + wave * OUT_TILE_BYTES, lane);
+        if constexpr (REQ) {
+            static_assert(2 * MXD_BM * 32 * sizeof(float) <= sizeof(MXDStage), "partial sums fit in a stage");
+            requant_epilogue_mx(acc, h, up, bias, M, N, gelu, rq, mb, nb, tile_n, tile_m0, wn, wm, tid, lane,
+                                reinterpret_cast<float *>(&stage[last]));
+        } else {
+            wave_epilogue<MX_TN, MX_TM>(acc, h, up, bias, M, N, gelu, Y, mb, nb,
+                                        reinterpret_cast<uint8_t *>(&stage[last]) + wave * OUT_TILE_BYTES, lane);
+        }
         if (tnext >= tiles) break;
         g += steps;
         t = tnext;
@@ -1105,8 +1270,9 @@ hipError_t launch_w4a4_linear(const uint8_t *xq, const void *xscale, const float
             const int tiles = ((N + MXD_BN - 1) / MXD_BN) * ((M + MXD_BM - 1) / MXD_BM);
             const int ncu = device_cu_count();
             const int blocks = tiles < ncu ? tiles : ncu;      // persistent: one block per CU
-            hipLaunchKernelGGL(w4a4_mxfp4_dma_kernel, dim3((unsigned)blocks), dim3(MXD_THREADS), 0, stream, xq,
-                               (const uint8_t *)xscale, h, wq, (const uint8_t *)wscale, up, bias, M, N, K, gelu, Y);
+            hipLaunchKernelGGL(w4a4_mxfp4_dma_kernel<false>, dim3((unsigned)blocks), dim3(MXD_THREADS), 0, stream, xq,
+                               (const uint8_t *)xscale, h, wq, (const uint8_t *)wscale, up, bias, M, N, K, gelu, Y,
+                               RequantArgs{});
         } else {
             const int tiles = ((N + MX_BN - 1) / MX_BN) * ((M + MX_BM - 1) / MX_BM);
             hipLaunchKernelGGL(w4a4_mxfp4_kernel, dim3((unsigned)tiles), dim3(MX_THREADS), 0, stream, xq,
@@ -1118,18 +1284,36 @@ hipError_t launch_w4a4_linear(const uint8_t *xq, const void *xscale, const float
 
 size_t requant_work_bytes(int M, int N) { return (size_t)((N + I4_BN - 1) / I4_BN) * M * 32 * sizeof(float); }
 
+bool requant_supported(int M, int N, int K, svdq_precision prec)
+{
+    if (prec == SVDQ_INT4) return true;
+    const int64_t rows = M > N ? M : N;
+    return K % 256 == 0 && rows * (K / 2) < ((int64_t)1 << 31);      // the LDS-DMA kernel's range
+}
+
 hipError_t launch_w4a4_linear_requant(const uint8_t *xq, const void *xscale, const float *h, const uint8_t *wq,
                                       const void *wscale, const uint16_t *up, const uint16_t *bias, int M, int N,
-                                      int K, svdq_epilogue epi, const float *smooth2, const uint16_t *down2,
-                                      uint8_t *xq2, float *xscale2, float *h2, float *work, hipStream_t stream)
+                                      int K, svdq_precision prec, svdq_epilogue epi, const float *smooth2,
+                                      const uint16_t *down2, uint8_t *xq2, void *xscale2, float *h2, float *work,
+                                      hipStream_t stream)
 {
     const int gelu = epi == SVDQ_EPI_GELU_TANH ? 1 : 0;
-    const int tiles_n = (N + I4_BN - 1) / I4_BN;
-    const int tiles = tiles_n * ((M + I4_BM - 1) / I4_BM);
+    const int tiles_n = (N + I4_BN - 1) / I4_BN;       // 256-channel tiles in both kernels
+    static_assert(I4_BN == MXD_BN, "one partial h row per 256 channels");
     const RequantArgs rq{smooth2, down2, xq2, xscale2, work};
-    hipLaunchKernelGGL(w4a4_int4_kernel<true>, dim3((unsigned)tiles), dim3(I4_THREADS), 0, stream, xq,
-                       (const float *)xscale, h, wq, (const float *)wscale, up, bias, M, N, K, gelu,
-                       (uint16_t *)nullptr, rq);
+    if (prec == SVDQ_INT4) {
+        const int tiles = tiles_n * ((M + I4_BM - 1) / I4_BM);
+        hipLaunchKernelGGL(w4a4_int4_kernel<true>, dim3((unsigned)tiles), dim3(I4_THREADS), 0, stream, xq,
+                           (const float *)xscale, h, wq, (const float *)wscale, up, bias, M, N, K, gelu,
+                           (uint16_t *)nullptr, rq);
+    } else {
+        const int tiles = tiles_n * ((M + MXD_BM - 1) / MXD_BM);
+        const int ncu = device_cu_count();
+        const int blocks = tiles < ncu ? tiles : ncu;
+        hipLaunchKernelGGL(w4a4_mxfp4_dma_kernel<true>, dim3((unsigned)blocks), dim3(MXD_THREADS), 0, stream, xq,
+                           (const uint8_t *)xscale, h, wq, (const uint8_t *)wscale, up, bias, M, N, K, gelu,
+                           (uint16_t *)nullptr, rq);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(requant_h_reduce, dim3((unsigned)((M * 8 + 255) / 256)), dim3(256), 0, stream,

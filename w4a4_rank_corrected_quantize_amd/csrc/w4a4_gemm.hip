@@ -676,10 +676,12 @@ constexpr int MX_TN = MX_WN / 32, MX_TM = MX_WM / 32;
 constexpr int MX_THREADS = 256;
 constexpr int MX_STRIDE = 64;   // LDS bytes per row: 64 code bytes (128 fp4), segments swizzled
 
-// 16-byte segment s of LDS row r lives at segment s ^ ((r >> 1) & 3): the
-// loader's 4 consecutive segments of 2 rows and the fragment reads of 8
-// rows at one segment both hit 8 distinct 4-bank groups.
-__device__ __forceinline__ int mx_seg(int r, int s) { return s ^ ((r >> 1) & 3); }
+// 16-byte segment s of LDS row r lives at segment s ^ ((r >> 1) & 3) ^
+// ((r >> 3) & 1).  A fragment read takes one segment of 32 consecutive rows;
+// the LDS serves 16 lanes (256 bytes, 64 banks) per cycle, and those 16 rows
+// land in 16 distinct 16-byte bank groups (as do any 8 aligned rows within
+// a 128-byte window).  The loader's stores fill whole rows.
+__device__ __forceinline__ int mx_seg(int r, int s) { return s ^ ((r >> 1) & 3) ^ ((r >> 3) & 1); }
 
 struct __attribute__((aligned(16))) MXSmem {
     uint8_t w[2][MX_BN * MX_STRIDE];
@@ -899,10 +901,13 @@ constexpr int MXD_BN = 256, MXD_BM = 256;
 constexpr int MXD_THREADS = 512;
 constexpr int MXD_ROW = 128;        // LDS bytes per row and step: 256 fp4, 16-byte segments swizzled
 
-// 16-byte segment s of LDS row r lives at segment s ^ (r & 7): the loads'
-// 8 segments of a row and the fragment reads of 8 rows at one segment both
-// hit 8 distinct 4-bank groups.
-__device__ __forceinline__ int mxd_seg(int r, int s) { return s ^ (r & 7); }
+// 16-byte segment s of LDS row r lives at segment s ^ (r & 7) ^ ((r >> 3) & 1).
+// A fragment read takes one segment of 32 consecutive rows; the LDS serves
+// 16 lanes (256 bytes, 64 banks) per cycle, and those 16 rows land in 16
+// distinct 16-byte bank groups (as do any 8 aligned rows within a 128-byte
+// window).  The loads write whole rows.
+__device__ __forceinline__ int mxd_swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+__device__ __forceinline__ int mxd_seg(int r, int s) { return s ^ mxd_swz(r); }
 
 struct __attribute__((aligned(16))) MXDStage {
     uint8_t w[MXD_BN * MXD_ROW];
@@ -1122,7 +1127,7 @@ __global__ __launch_bounds__(MXD_THREADS) void w4a4_mxfp4_dma_kernel(
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int r = 8 * (8 * i + wave) + (lane >> 3);        // block 8 i + wave
-            const int seg = (lane & 7) ^ (r & 7);
+            const int seg = mxd_seg(r, lane & 7);      // LDS slot lane & 7 holds this global segment
             wvo[i] = (uint32_t)(min(n0 + r, N - 1) * KB + 16 * seg);
             xvo[i] = (uint32_t)(min(m0 + r, M - 1) * KB + 16 * seg);
         }

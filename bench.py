@@ -38,10 +38,10 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, 8 TB/s
 # only reported while the kernel source still hashes to the value it was
 # measured on; otherwise traffic is null.
 TRAFFIC = {
-    # FETCH_SIZE 72704 KiB / 0.50003 + WRITE_SIZE 110598 KiB / 1.0 (per dispatch)
-    ("int4", "fc1"): {"source_sha": "9bab31ac582f7a45", "bytes": 262142234},
-    # FETCH_SIZE 70923 KiB / 0.50003 + WRITE_SIZE 111107 KiB / 1.0
-    ("mxfp4", "fc1"): {"source_sha": "9bab31ac582f7a45", "bytes": 259017029},
+    # FETCH_SIZE 72636 KiB / 0.50003 + WRITE_SIZE 110593 KiB / 1.00000 (per dispatch)
+    ("int4", "fc1"): {"source_sha": "6abc002afff30598", "bytes": 261997435},
+    # FETCH_SIZE 70905 KiB / 0.50003 + WRITE_SIZE 111109 KiB / 1.00000
+    ("mxfp4", "fc1"): {"source_sha": "6abc002afff30598", "bytes": 258982047},
 }
 
 

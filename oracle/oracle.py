@@ -13,7 +13,9 @@ the low-rank down projection is fused with the quantization and the up
 projection with the 4-bit product), and section "Native loading in
 Diffusers" (rank 32, bfloat16 compute dtype, 4-bit weight groups).
 The formulas, with the readings that fix what the prose leaves open, are at
-the top of svdq_oracle.c.
+the top of svdq_oracle.c.  The same file holds the weight-only AWQ W4A16
+layer of those pages (section "Native loading in Diffusers": awq_w4a16,
+int4, group size 64, for the modulation layers), with its readings.
 
 Parity unpinned: the exact bits of the low-rank factors (several results are
 correct: signs of singular-vector pairs, rotations inside repeated singular
@@ -64,6 +66,10 @@ def lib():
         L.oracle_gelu_tanh.restype = ctypes.c_double
         L.oracle_gelu_tanh.argtypes = [ctypes.c_double]
         L.oracle_num_threads.restype = ctypes.c_int
+        L.oracle_awq_code.restype = I
+        L.oracle_awq_code.argtypes = [P, I]
+        L.oracle_awq_pack.argtypes = [P, I, I, P, P]
+        L.oracle_awq_linear.argtypes = [P, P, P, P, I, I, I, P]
         _lib = L
     return _lib
 
@@ -273,3 +279,43 @@ def unpack_nibbles(codes: np.ndarray) -> np.ndarray:
     out[..., 0::2] = c & 0x0F
     out[..., 1::2] = c >> 4
     return out
+
+
+# ----------------------------------------------------------- AWQ W4A16 (INT4)
+# The weight-only family of the same pages (section "Native loading in
+# Diffusers": awq_w4a16, int4, group size 64, for the memory-bound modulation
+# layers); the storage layout and the readings are stated in svdq_oracle.c.
+
+def awq_pack(W):
+    """bf16 bits [N][K] (K % 256 == 0) -> (wq uint8 [N][K/2], wscale fp32 [N][K/64])."""
+    W = _c(W, np.uint16)
+    N, K = W.shape
+    wq = np.zeros((N, K // 2), np.uint8)
+    wscale = np.zeros((N, K // 64), np.float32)
+    lib().oracle_awq_pack(_p(W), N, K, _p(wq), _p(wscale))
+    return wq, wscale
+
+
+def awq_codes(wq) -> np.ndarray:
+    """Stored rows -> int8 q [N][K] in natural k order."""
+    wq = _c(wq, np.uint8)
+    N, KB = wq.shape
+    out = np.zeros((N, 2 * KB), np.int8)
+    for n in range(N):
+        row = np.ascontiguousarray(wq[n])
+        for k in range(2 * KB):
+            out[n, k] = lib().oracle_awq_code(_p(row), k)
+    return out
+
+
+def awq_linear(X, wq, wscale, bias=None):
+    """fp64 y [M][N] of the weight-only layer (no bf16 rounding)."""
+    X = _c(X, np.uint16)
+    wq = _c(wq, np.uint8)
+    wscale = _c(wscale, np.float32)
+    bias = None if bias is None else _c(bias, np.uint16)
+    M, K = X.shape
+    N = wq.shape[0]
+    y = np.zeros((M, N), np.float64)
+    lib().oracle_awq_linear(_p(X), _p(wq), _p(wscale), _p(bias), M, N, K, _p(y))
+    return y

@@ -343,6 +343,84 @@ void oracle_linear(const uint8_t *xq, const void *xscale, const double *h,
     }
 }
 
+/* ------------------------------------------------------- AWQ W4A16 (INT4) */
+
+/*
+ * Weight-only 4-bit layer of the same pages ("Bringing Nunchaku 4-bit
+ * Diffusion Inference to Diffusers", section "Native loading in Diffusers":
+ * the awq_w4a16 family, int4 with group size 64, used for the modulation
+ * layers, which are memory-bound and precision-sensitive).  Readings (the
+ * pages give only precision and group size): the group quantizer is the
+ * symmetric INT4 one above, applied to fl32(W) per (n, 64-group along k);
+ * the activation-aware channel scaling is a calibration step and is assumed
+ * folded into W by the caller; activations stay bf16 and
+ *   y_mn = sum_g sw_ng sum_{k in g} X_mk q_nk + b_n.
+ *
+ * Storage (K % 256 == 0): code c = q + 8 in [1, 15] (offset binary), row n
+ * takes K/2 bytes.  For k = 256 C + 64 g + 32 h + 8 b + i (g < 4, h < 2,
+ * b < 4, i < 8) the code sits in byte 128 C + 32 b + 4 (2 g + h) + p / 2,
+ * low nibble when p is even, with p = i / 2 for even i and 4 + (i - 1) / 2
+ * for odd i.
+ */
+static int awq_byte(int k, int *high)
+{
+    int C = k / 256, r = k % 256;
+    int g = r / 64, h = (r % 64) / 32, b = (r % 32) / 8, i = r % 8;
+    int p = (i % 2 == 0) ? i / 2 : 4 + (i - 1) / 2;
+    *high = p % 2;
+    return 128 * C + 32 * b + 4 * (2 * g + h) + p / 2;
+}
+
+/* q of weight (row, k) from the stored row */
+int oracle_awq_code(const uint8_t *row, int k)
+{
+    int high;
+    int byte = awq_byte(k, &high);
+    int c = high ? (row[byte] >> 4) : (row[byte] & 15);
+    return c - 8;
+}
+
+void oracle_awq_pack(const uint16_t *W, int N, int K, uint8_t *wq, float *wscale)
+{
+    float *v = (float *)malloc(sizeof(float) * 64);
+    int8_t q[64];
+    memset(wq, 0, (size_t)N * (K / 2));
+    for (int n = 0; n < N; ++n) {
+        uint8_t *row = wq + (size_t)n * (K / 2);
+        for (int g = 0; g < K / 64; ++g) {
+            for (int i = 0; i < 64; ++i) v[i] = (float)bf16_val(W[(size_t)n * K + 64 * g + i]);
+            wscale[(size_t)n * (K / 64) + g] = oracle_quant_group_int4(v, 64, q, NULL);
+            for (int i = 0; i < 64; ++i) {
+                int high;
+                int byte = awq_byte(64 * g + i, &high);
+                int c = q[i] + 8;
+                row[byte] |= (uint8_t)(high ? c << 4 : c);
+            }
+        }
+    }
+    free(v);
+}
+
+/* y [M][N] in fp64 (no bf16 rounding) */
+void oracle_awq_linear(const uint16_t *X, const uint8_t *wq, const float *wscale, const uint16_t *bias,
+                       int M, int N, int K, double *y)
+{
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int m = 0; m < M; ++m) {
+        for (int n = 0; n < N; ++n) {
+            const uint8_t *row = wq + (size_t)n * (K / 2);
+            double acc = 0.0;
+            for (int g = 0; g < K / 64; ++g) {
+                double P = 0.0;
+                for (int k = 64 * g; k < 64 * g + 64; ++k)
+                    P += bf16_val(X[(size_t)m * K + k]) * (double)oracle_awq_code(row, k);
+                acc += (double)wscale[(size_t)n * (K / 64) + g] * P;
+            }
+            y[(size_t)m * N + n] = acc + (bias ? bf16_val(bias[n]) : 0.0);
+        }
+    }
+}
+
 int oracle_num_threads(void)
 {
     int t = 1;

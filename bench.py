@@ -82,13 +82,15 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--prec", choices=["int4", "mxfp4"], default="int4")
-    ap.add_argument("--layer", choices=["fc1", "qkv", "fc2", "mlp"], default="fc1",
+    ap.add_argument("--layer", choices=["fc1", "qkv", "fc2", "mlp", "awq"], default="fc1",
                     help="fc1 is the headline workload; fc2 takes fc1's output (computed on the GPU); "
                          "mlp times fc1 -> fc2 with fc2's activation step fused into fc1's epilogue, "
-                         "next to the unfused pair")
+                         "next to the unfused pair; awq times the weight-only AWQ W4A16 modulation layer")
     ap.add_argument("--copy-calibration", type=int, metavar="MIB", default=0,
                     help="only run a plain copy of MIB MiB (to scale the HBM byte counters)")
-    ap.add_argument("--sets", type=int, default=3, help="rotating buffer sets")
+    ap.add_argument("--sets", type=int, default=0,
+                    help="rotating buffer sets (default 3; 12 for awq, whose 32 MB of weights per set "
+                         "would otherwise stay in the 256 MB last-level cache)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle sample time")
     args = ap.parse_args()
@@ -112,6 +114,11 @@ def main():
     if args.layer == "mlp":
         mlp_main(args, torch, svdq, synth)
         return
+    if args.layer == "awq":
+        awq_main(args, torch, svdq, synth)
+        return
+    if not args.sets:
+        args.sets = 3
     prec = svdq.INT4 if args.prec == "int4" else svdq.MXFP4
     spec = synth.SPECS[("" if prec == svdq.INT4 else "mx_") + args.layer]
     M, K, N, r = spec.M, spec.K, spec.N, svdq.RANK
@@ -260,6 +267,80 @@ def main():
     print(json.dumps(line), flush=True)
 
 
+def awq_bytes(M, N, K, bias=True):
+    return N * K // 2 + (N * K // 64) * 4 + 2 * M * K + 2 * M * N + (2 * N if bias else 0)
+
+
+def awq_main(args, torch, svdq, synth):
+    """The weight-only AWQ W4A16 layer (INT4 g64 weights, bf16 activations)
+    at the modulation shape: HBM-bound on the weight stream."""
+    spec = synth.SPECS["awq_mod"]
+    M, K, N = spec.M, spec.K, spec.N
+    nsets = args.sets or 12
+    print(f"[bench] generating {spec.name} {M}x{K}->{N} and packing on the host", file=sys.stderr, flush=True)
+    L = synth.make_layer(spec)
+    t0 = time.time()
+    wq, ws = svdq.awq_pack_weights(L["W"])
+    pack_s = time.time() - t0
+    sets = []
+    for i in range(nsets):
+        sets.append(dict(X=svdq.bf16_tensor(L["X"]), wq=torch.from_numpy(wq).cuda(),
+                         ws=torch.from_numpy(ws).cuda(), b=svdq.bf16_tensor(L["bias"]),
+                         Y=torch.empty((M, N), dtype=torch.bfloat16, device="cuda")))
+
+    def step(b):
+        svdq.awq_w4a16_linear(b["X"], b["wq"], b["ws"], b["b"], Y=b["Y"])
+
+    for i in range(args.warmup):
+        step(sets[i % nsets])
+    torch.cuda.synchronize()
+    print(f"[bench] warmup done ({args.warmup} steps); timing {args.steps} steps", file=sys.stderr, flush=True)
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(args.steps):
+        step(sets[i % nsets])
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / args.steps
+    nbytes = awq_bytes(M, N, K)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle import oracle as O
+        print("[bench] timing the CPU oracle on the same layer", file=sys.stderr, flush=True)
+        t0 = time.time()
+        O.awq_linear(L["X"], wq, ws, L["bias"])
+        t_cpu = time.time() - t0
+        cpu = {"value": round(nbytes / t_cpu / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+               "sample": f"the whole layer ({M} x {K} -> {N}) once, {t_cpu:.1f} s (one thread: the "
+                         "oracle distributes rows of X, and there is one)"}
+    line = {
+        "metric": "AWQ W4A16 modulation linear, algorithmic GB/s of the weight stream",
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int4 weights (g64, fp32 scales) x bf16 activations on the bf16 matrix cores, fp32 accumulation",
+        "data": "synthetic (seeded N(0,1) activations, N(0,0.02^2) weights, N(0,0.01^2) bias)",
+        "config": {"workload": f"{spec.name}: {M} x {K} -> {N}, INT4 g64 weight-only, bias; "
+                               "step = svdq_awq_w4a16_linear",
+                   "M": M, "K": K, "N": N, "buffer_sets": nsets,
+                   "weights_MB_per_set": round((wq.nbytes + ws.nbytes) / 1e6, 1)},
+        "roofline": {"bound": "hbm", "kernel": "svdq_awq_w4a16_linear", "achieved": round(gbs, 1),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                     "traffic": None, "avg_ms": round(ms, 5), "algorithmic_bytes": nbytes},
+        "host_pack_s": round(pack_s, 2),
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def mlp_main(args, torch, svdq, synth):
     """fc1 (GELU) -> fc2 at M=4608: the fused step runs fc1's
     activation step, fc1's product whose epilogue writes fc2's codes, scales
@@ -285,7 +366,7 @@ def mlp_main(args, torch, svdq, synth):
     p2 = svdq.pack_weights(L2["W"], L2["act_absmax"], prec=prec)
     del Y1, xq, xs, h
     sets = []
-    for i in range(args.sets):
+    for i in range(args.sets or 3):
         a, b = svdq.to_device(p1), svdq.to_device(p2)
         sets.append(dict(
             X=svdq.bf16_tensor(L1["X"]), d1=a, b1=svdq.bf16_tensor(L1["bias"]), d2=b,

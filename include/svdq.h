@@ -39,13 +39,14 @@
  *   - Ownership: the caller allocates and frees every buffer.  No call
  *     allocates device memory or keeps a pointer after it returns.
  *   - Device calls (svdq_quantize_act, svdq_w4a4_linear,
- *     svdq_w4a4_linear_requant) take device
+ *     svdq_w4a4_linear_requant, svdq_awq_w4a16_linear) take device
  *     pointers and a hipStream_t (as void*, NULL = the null stream); they
  *     validate everything first, enqueue kernels on `stream` and return
  *     without synchronizing.  On any error nothing has been enqueued or
  *     written.  The current HIP device must be a gfx950; otherwise
  *     SVDQ_ERR_UNSUPPORTED_DEVICE is returned and nothing runs.
- *   - Host calls (svdq_pack_weights, svdq_pack_residual) take host pointers,
+ *   - Host calls (svdq_pack_weights, svdq_pack_residual,
+ *     svdq_awq_pack_weights) take host pointers,
  *     run synchronously on the CPU and need no GPU.
  *   - Device pointers must be 16-byte aligned (SVDQ_ERR_MISALIGNED).  A
  *     buffer whose size is zero (M == 0 or N == 0) may be NULL.
@@ -228,6 +229,46 @@ svdq_status svdq_w4a4_linear_requant(const uint8_t *xq, const void *xscale, cons
                                      svdq_precision prec, svdq_epilogue epi, const float *smooth2,
                                      const uint16_t *down2, uint8_t *xq2, void *xscale2, float *h2,
                                      void *work, size_t work_bytes, void *stream);
+
+/*
+ * svdq_awq_pack_weights -- host packing for the weight-only AWQ W4A16 layer
+ * ("Native loading in Diffusers": the awq_w4a16 family, int4 with group size
+ * 64, used for modulation layers, which are memory-bound and
+ * precision-sensitive).  The activation-aware channel scaling of AWQ is a
+ * calibration step; a caller that uses it passes the already scaled weight.
+ *
+ *   W        [N][K] bf16 bits, host            N >= 1, K >= 256, K % 256 == 0
+ *   wq       [N][K/2] uint8, host (out)        codes q + 8, q in [-7, 7]
+ *   wscale   [N][K/64] fp32, host (out)
+ * q and the scale are the INT4 group quantizer of the header comment applied
+ * to fl32(W) per (n, 64-group along k).  Storage order (the operand order of
+ * the device kernel): in the 256-channel chunk C of a row, the 32 bytes at
+ * 128 C + 32 b are 8 little-endian dwords d = 2 g + h; nibble j of dword d is
+ * channel 256 C + 64 g + 32 h + 8 b + 2 j for j < 4 and + 2 (j - 4) + 1 for
+ * j >= 4.  Host, synchronous, all host cores; errors SVDQ_ERR_INVALID_ARG,
+ * SVDQ_ERR_SHAPE, SVDQ_ERR_NONFINITE (any non-finite W).
+ */
+svdq_status svdq_awq_pack_weights(const uint16_t *W, int N, int K, uint8_t *wq, float *wscale);
+
+/*
+ * svdq_awq_w4a16_linear -- y = X Wdq^T + b with Wdq_nk = wscale_ng q_nk and
+ * bf16 activations (the awq_w4a16 runtime layer).
+ *
+ *   X        [M][K] bf16 bits, device          M >= 0 (0: no-op)
+ *   wq, wscale   as written by svdq_awq_pack_weights (device copies)
+ *   bias     [N] bf16 bits, device, or NULL
+ *   N, K     N >= 0 (0: no-op), K >= 256, K % 256 == 0
+ *   Y        [M][N] bf16 bits, device (out), round-to-nearest-even of the
+ *            fp32 result
+ *   stream   hipStream_t or NULL
+ * Sums in fp32 on the bf16 matrix cores (each 64-channel group exactly, then
+ * scaled once); the kernel streams the weights once per 16 rows of X, so it
+ * is meant for the few rows of a modulation input.  One kernel launch.
+ * Errors: SVDQ_ERR_INVALID_ARG, SVDQ_ERR_SHAPE (K), SVDQ_ERR_MISALIGNED,
+ * SVDQ_ERR_UNSUPPORTED_DEVICE, SVDQ_ERR_HIP.
+ */
+svdq_status svdq_awq_w4a16_linear(const uint16_t *X, const uint8_t *wq, const float *wscale,
+                                  const uint16_t *bias, int M, int N, int K, uint16_t *Y, void *stream);
 
 #ifdef __cplusplus
 }

@@ -94,6 +94,27 @@ def test_requant_validation_and_workspace():
         assert call(prec=svdq.MXFP4, K=256) == -5
 
 
+def test_awq_validation():
+    """The weight-only AWQ W4A16 entry point: argument errors before the
+    device check."""
+    L = svdq.lib()
+    _, p = _host(1 << 16)
+    _, q = _host(1 << 16, offset=4)
+    M, N, K = 2, 32, 256
+    assert L.svdq_awq_w4a16_linear(p, p, p, None, M, N, 192, p, None) == -2      # K % 256
+    assert L.svdq_awq_w4a16_linear(p, p, p, None, M, N, 0, p, None) == -2
+    assert L.svdq_awq_w4a16_linear(p, p, p, None, -1, N, K, p, None) == -1
+    assert L.svdq_awq_w4a16_linear(None, p, p, None, M, N, K, p, None) == -1
+    assert L.svdq_awq_w4a16_linear(p, p, None, None, M, N, K, p, None) == -1
+    assert L.svdq_awq_w4a16_linear(p, p, p, None, M, N, K, None, None) == -1
+    assert L.svdq_awq_w4a16_linear(p, p, p, q, M, N, K, p, None) == -3
+    assert L.svdq_awq_w4a16_linear(q, p, p, None, M, N, K, p, None) == -3
+    assert L.svdq_awq_pack_weights(None, 4, 256, p, p) == -1
+    if not _has_gpu():
+        assert L.svdq_awq_w4a16_linear(p, p, p, None, M, N, K, p, None) == -5
+        assert L.svdq_awq_w4a16_linear(None, p, p, None, 0, N, K, None, None) == -5   # empty: still checks the device
+
+
 def _has_gpu():
     try:
         import torch

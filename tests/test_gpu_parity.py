@@ -336,3 +336,74 @@ def test_full_size_dit_block(prec):
     torch.cuda.synchronize()
     y_ref = O.linear(_np(xq), _np(xs), oh, p2["wq"], p2["wscale"], p2["up"], f2["bias"], prec, rows=rows)
     _y_check(Y2[torch.from_numpy(rows).long().cuda()], y_ref, names[2])
+
+
+# ------------------------------------------------------- AWQ W4A16 (INT4 g64)
+
+def _awq_case(M, K, N, bias=True, seed=0):
+    rng = np.random.default_rng(seed + 17 * M + K + N)
+    X = synth.f64_to_bf16_bits(rng.standard_normal((M, K)))
+    w = rng.normal(0, 0.02, (N, K))
+    w[:, rng.choice(K, 4, replace=False)] *= 30.0
+    W = synth.f64_to_bf16_bits(w)
+    b = synth.f64_to_bf16_bits(rng.normal(0, 0.01, N)) if bias else None
+    return X, W, b
+
+
+def _awq_run(X, W, b):
+    wq, ws = svdq.awq_pack_weights(W)
+    owq, ows = O.awq_pack(W)
+    assert np.array_equal(wq, owq) and np.array_equal(ws.view(np.uint32), ows.view(np.uint32))
+    Y = svdq.awq_w4a16_linear(_t(X), _t(wq), _t(ws), _t(b))
+    torch.cuda.synchronize()
+    return Y, wq, ws
+
+
+@pytest.mark.parametrize("M,K,N", [(1, 256, 16), (3, 768, 40), (16, 512, 33), (17, 256, 64), (40, 1024, 130)])
+def test_awq_exact_small_integers(M, K, N):
+    """Every step exact: X in {-1, 0, 1} (8 non-zeros per row), W = q 2^-4 with
+    a +-7 in every group (scale 2^-4), so y = (sum x q) / 16 is a bf16 number
+    and the kernel must return it bit for bit -- a check of the storage order,
+    the operand layout and the offset removal."""
+    rng = np.random.default_rng(M * 1000 + N)
+    x = np.zeros((M, K))
+    for m in range(M):
+        ks = rng.choice(K, 8, replace=False)
+        x[m, ks] = rng.choice([-1.0, 1.0], 8)
+    q = rng.integers(-7, 8, (N, K)).astype(np.float64)
+    q[:, ::64] = np.where(rng.random((N, K // 64)) < 0.5, 7.0, -7.0)
+    X = synth.f64_to_bf16_bits(x)
+    W = synth.f64_to_bf16_bits(q / 16.0)
+    Y, wq, ws = _awq_run(X, W, None)
+    assert np.all(ws == np.float32(1 / 16))
+    y_ref = O.awq_linear(X, wq, ws, None)
+    assert np.array_equal(bf16_bits_to_f32(_np(Y)).astype(np.float64), y_ref)
+
+
+@pytest.mark.parametrize("M,K,N,bias", [(1, 256, 48, True), (2, 3072, 9216, True), (5, 512, 130, False),
+                                        (16, 1024, 64, True), (33, 768, 96, True)])
+def test_awq_synthetic(M, K, N, bias):
+    X, W, b = _awq_case(M, K, N, bias)
+    _say(f"awq M={M} K={K} N={N} bias={bias}")
+    Y, wq, ws = _awq_run(X, W, b)
+    _y_check(Y, O.awq_linear(X, wq, ws, b), f"awq {M}x{K}x{N}")
+
+
+def test_awq_full_size_modulation():
+    """The modulation shape the benchmark times: 1 x 3072 -> 18432."""
+    lay = synth.make_layer(synth.SPECS["awq_mod"])
+    _say("awq full size 1 x 3072 -> 18432")
+    Y, wq, ws = _awq_run(lay["X"], lay["W"], lay["bias"])
+    _y_check(Y, O.awq_linear(lay["X"], wq, ws, lay["bias"]), "awq modulation")
+
+
+def test_awq_deterministic_and_empty():
+    X, W, b = _awq_case(4, 512, 64)
+    wq, ws = svdq.awq_pack_weights(W)
+    Y1 = svdq.awq_w4a16_linear(_t(X), _t(wq), _t(ws), _t(b))
+    Y2 = svdq.awq_w4a16_linear(_t(X), _t(wq), _t(ws), _t(b))
+    torch.cuda.synchronize()
+    assert torch.equal(Y1.view(torch.int16), Y2.view(torch.int16))
+    Y0 = svdq.awq_w4a16_linear(_t(X[:0]), _t(wq), _t(ws), _t(b))
+    torch.cuda.synchronize()
+    assert Y0.shape == (0, 64)

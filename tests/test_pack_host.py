@@ -152,3 +152,32 @@ def test_pack_errors():
     # MXFP4 accepts K % 32 == 0
     p = svdq.pack_weights(np.zeros((16, 96), np.uint16), np.ones(96, np.float32), prec=svdq.MXFP4)
     assert p["wscale"].shape == (16, 3)
+
+
+# ------------------------------------------------------------ AWQ W4A16 pack
+
+@pytest.mark.parametrize("N,K", [(1, 256), (7, 512), (33, 3072)])
+def test_awq_pack_matches_oracle(N, K):
+    rng = np.random.default_rng(N * 7 + K)
+    w = rng.normal(0, 0.02, (N, K))
+    w[:, rng.choice(K, 3, replace=False)] *= 40.0        # a few large channels
+    if N > 1:
+        w[1, :64] = 0.0                                   # an all-zero group (scale 0)
+        w[1, 64:128] = -w[1, 64:128]                      # and negative zeros stay code 8
+    W = synth.f64_to_bf16_bits(w)
+    wq, ws = svdq.awq_pack_weights(W)
+    owq, ows = O.awq_pack(W)
+    assert np.array_equal(wq, owq)
+    assert np.array_equal(ws.view(np.uint32), ows.view(np.uint32))
+
+
+def test_awq_pack_errors():
+    W = np.zeros((4, 256), np.uint16)
+    with pytest.raises(svdq.SvdqError, match="SHAPE"):
+        svdq.awq_pack_weights(np.zeros((4, 192), np.uint16))
+    Wn = W.copy()
+    Wn[2, 5] = 0x7FC0                                     # NaN
+    with pytest.raises(svdq.SvdqError, match="NONFINITE"):
+        svdq.awq_pack_weights(Wn)
+    wq, ws = svdq.awq_pack_weights(W)
+    assert np.all(wq == 0x88) and np.all(ws == 0)

@@ -11,6 +11,9 @@ Functions mirror the C ABI in include/svdq.h:
     pack_residual(W, smooth, down, up, prec=INT4)              host, numpy in/out
     quantize_act(X, smooth, down, prec=INT4, ...)              device, torch tensors
     w4a4_linear(xq, xscale, h, wq, wscale, up, bias, ...)      device, torch tensors
+    w4a4_linear_requant(...)                                    device, torch tensors
+    awq_pack_weights(W)                                         host, numpy in/out
+    awq_w4a16_linear(X, wq, wscale, bias, ...)                  device, torch tensors
 
 Device tensors: X bf16 [M][K], smooth fp32 [K], down bf16 [32][K],
 up bf16 [N][32], bias bf16 [N] or None, xq uint8 [M][K/2],
@@ -41,7 +44,7 @@ STATUS = {
 }
 EXPORTS = ("svdq_status_string", "svdq_version", "svdq_check_device", "svdq_pack_weights",
            "svdq_pack_residual", "svdq_quantize_act", "svdq_w4a4_linear", "svdq_requant_workspace_bytes",
-           "svdq_w4a4_linear_requant")
+           "svdq_w4a4_linear_requant", "svdq_awq_pack_weights", "svdq_awq_w4a16_linear")
 
 
 class SvdqError(RuntimeError):
@@ -81,6 +84,10 @@ def lib():
         L.svdq_w4a4_linear_requant.restype = I
         L.svdq_w4a4_linear_requant.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, P, P, P, P, P, P,
                                                ctypes.c_size_t, P]
+        L.svdq_awq_pack_weights.restype = I
+        L.svdq_awq_pack_weights.argtypes = [P, I, I, P, P]
+        L.svdq_awq_w4a16_linear.restype = I
+        L.svdq_awq_w4a16_linear.argtypes = [P, P, P, P, I, I, I, P, P]
         _lib = L
     return _lib
 
@@ -248,6 +255,34 @@ def w4a4_linear_requant(xq, xscale, h, wq, wscale, up, bias, smooth2, down2, pre
         _dev(work, (torch.uint8, torch.float32), "work"), work.numel() * work.element_size(), _stream(stream))
     _check(st, "svdq_w4a4_linear_requant")
     return xq2, xs2, h2
+
+
+def awq_pack_weights(W: np.ndarray):
+    """Weight-only AWQ W4A16 packing (host): bf16 bits [N][K] ->
+    (wq uint8 [N][K/2], wscale fp32 [N][K/64])."""
+    W, pW = _np(W, np.uint16)
+    N, K = W.shape
+    wq = np.zeros((N, K // 2), np.uint8)
+    wscale = np.zeros((N, max(K // 64, 0)), np.float32)
+    st = lib().svdq_awq_pack_weights(pW, N, K, wq.ctypes.data, wscale.ctypes.data)
+    _check(st, "svdq_awq_pack_weights")
+    return wq, wscale
+
+
+def awq_w4a16_linear(X, wq, wscale, bias=None, Y=None, stream=None):
+    """Weight-only 4-bit linear with bf16 activations -> bf16 (one kernel)."""
+    torch = _torch()
+    M, K = X.shape
+    N = wq.shape[0]
+    if Y is None:
+        Y = torch.empty((M, N), dtype=torch.bfloat16, device=X.device)
+    pbias = None if bias is None else _dev(bias, (torch.bfloat16, torch.int16), "bias")
+    st = lib().svdq_awq_w4a16_linear(
+        _dev(X, (torch.bfloat16, torch.int16), "X"), _dev(wq, (torch.uint8,), "wq"),
+        _dev(wscale, (torch.float32,), "wscale"), pbias, M, N, K,
+        _dev(Y, (torch.bfloat16, torch.int16), "Y"), _stream(stream))
+    _check(st, "svdq_awq_w4a16_linear")
+    return Y
 
 
 def to_device(packed: dict, device="cuda") -> dict:

@@ -31,6 +31,7 @@ SOURCES = {
     "pack_host.hip": ["-ffp-contract=off", "-Xarch_host", "-mavx2", "-Xarch_host", "-mfma"],
     "quant_act.hip": ["-ffp-contract=off"],
     "w4a4_gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "awq_gemv.hip": [],
 }
 
 

@@ -172,3 +172,20 @@ extern "C" svdq_status svdq_w4a4_linear_requant(const uint8_t *xq, const void *x
                                               down2, xq2, xscale2, h2, (float *)work, (hipStream_t)stream);
     return e == hipSuccess ? SVDQ_OK : SVDQ_ERR_HIP;
 }
+
+extern "C" svdq_status svdq_awq_w4a16_linear(const uint16_t *X, const uint8_t *wq, const float *wscale,
+                                             const uint16_t *bias, int M, int N, int K, uint16_t *Y,
+                                             void *stream)
+{
+    if (M < 0 || N < 0 || K < 0) return SVDQ_ERR_INVALID_ARG;
+    if (K < 256 || K % 256 != 0) return SVDQ_ERR_SHAPE;
+    // buffers of zero size may be NULL (empty tensors have no storage)
+    if ((M > 0 && !X) || (N > 0 && (!wq || !wscale)) || (M > 0 && N > 0 && !Y)) return SVDQ_ERR_INVALID_ARG;
+    if (!aligned16(X) || !aligned16(wq) || !aligned16(wscale) || (bias && !aligned16(bias)) || !aligned16(Y))
+        return SVDQ_ERR_MISALIGNED;
+    svdq_status st = current_device_ok();
+    if (st != SVDQ_OK) return st;
+    if (M == 0 || N == 0) return SVDQ_OK;
+    hipError_t e = launch_awq_linear(X, wq, wscale, bias, M, N, K, Y, (hipStream_t)stream);
+    return e == hipSuccess ? SVDQ_OK : SVDQ_ERR_HIP;
+}

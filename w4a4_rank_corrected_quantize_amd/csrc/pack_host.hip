@@ -430,3 +430,52 @@ extern "C" svdq_status svdq_pack_weights(const uint16_t *W, const float *act_abs
     // 4. residual
     return residual_impl(W, smooth, down, up, N, K, rank, prec, wq, wscale);
 }
+
+// Weight-only AWQ W4A16 packing ("Native loading in Diffusers": awq_w4a16,
+// int4, group size 64).  Codes are q + 8 (offset binary) of the symmetric
+// INT4 group quantizer above, applied to fl32(W) per (n, 64-group).  Storage
+// order, written byte by byte: in 256-channel chunk C of a row, the 32 bytes
+// at 128 C + 32 b hold, as 8 dwords d = 2 g + h, the codes of channels
+// 256 C + 64 g + 32 h + 8 b + i, where nibble j of the dword (j < 4) is
+// i = 2 j and nibble j + 4 is i = 2 j + 1 -- the operand order the linear
+// kernel decodes directly.
+extern "C" svdq_status svdq_awq_pack_weights(const uint16_t *W, int N, int K, uint8_t *wq, float *wscale)
+{
+    if (!W || !wq || !wscale) return SVDQ_ERR_INVALID_ARG;
+    if (N < 0 || K < 0) return SVDQ_ERR_INVALID_ARG;
+    if (N < 1 || K < 256 || K % 256 != 0) return SVDQ_ERR_SHAPE;
+    for (int64_t i = 0; i < (int64_t)N * K; ++i)
+        if (!bf16_finite(W[i])) return SVDQ_ERR_NONFINITE;
+    const int G = K / 64;
+    parallel_for(N, [&](int64_t n0, int64_t n1) {
+        std::vector<uint8_t> code(K);
+        for (int64_t n = n0; n < n1; ++n) {
+            const uint16_t *w = W + n * K;
+            for (int g = 0; g < G; ++g) {
+                float a = 0.0f;
+                for (int i = 0; i < 64; ++i) a = std::max(a, std::fabs(bits_f32((uint32_t)w[64 * g + i] << 16)));
+                const float scale = int4_group_scale(a);
+                const Int4Group Gq = int4_group_prepare(scale);
+                for (int i = 0; i < 64; ++i) {
+                    const float v = bits_f32((uint32_t)w[64 * g + i] << 16);
+                    const int q = (int)int4_mag(std::fabs(v), Gq);
+                    code[64 * g + i] = (uint8_t)((v < 0.0f ? -q : q) + 8);
+                }
+                wscale[n * G + g] = scale;
+            }
+            uint8_t *row = wq + n * (int64_t)(K / 2);
+            for (int C = 0; C < K / 256; ++C)
+                for (int b = 0; b < 4; ++b)
+                    for (int d = 0; d < 8; ++d) {
+                        const int kbase = 256 * C + 64 * (d / 2) + 32 * (d % 2) + 8 * b;
+                        uint32_t dw = 0;
+                        for (int j = 0; j < 4; ++j)
+                            dw |= (uint32_t)code[kbase + 2 * j] << (4 * j) |
+                                  (uint32_t)code[kbase + 2 * j + 1] << (4 * (j + 4));
+                        uint8_t *dst = row + 128 * C + 32 * b + 4 * d;
+                        for (int t = 0; t < 4; ++t) dst[t] = (uint8_t)(dw >> (8 * t));
+                    }
+        }
+    });
+    return SVDQ_OK;
+}

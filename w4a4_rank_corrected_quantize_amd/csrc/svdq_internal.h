@@ -36,4 +36,8 @@ hipError_t launch_w4a4_linear_requant(const uint8_t *xq, const void *xscale, con
                                       const uint16_t *down2, uint8_t *xq2, void *xscale2, float *h2, float *work,
                                       hipStream_t stream);
 
+// Weight-only AWQ W4A16 layer (K % 256 == 0).
+hipError_t launch_awq_linear(const uint16_t *X, const uint8_t *wq, const float *wscale, const uint16_t *bias,
+                             int M, int N, int K, uint16_t *Y, hipStream_t stream);
+
 }  // namespace svdq

@@ -90,6 +90,9 @@ SPECS = {
                         gelu=True, mx=True, w_stream=5, bias_stream=6),
     "mx_fc2": LayerSpec("mx_fc2", 4, 4608, 12288, 3072, "external", 0, 1.0,
                         mx=True, w_stream=7, bias_stream=8),
+    # weight-only AWQ W4A16 modulation layer: one conditioning vector per
+    # image, 3072 -> 6 x 3072 (shift, scale and gate of two norms)
+    "awq_mod": LayerSpec("awq_mod", 6, 1, 3072, 18432, "normal", 0, 1.0),
 }
 
 

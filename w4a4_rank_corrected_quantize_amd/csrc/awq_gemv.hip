@@ -9,10 +9,12 @@
 // The layer is meant for few rows of X (a modulation input is one vector per
 // image), so it is bound by the weight stream: K/2 code bytes and K/16 scale
 // bytes per output channel.  Design for gfx950:
-//   * a block (4 waves) owns 16 output channels; wave w takes the 256-channel
-//     chunks w, w + 4, ... of K, with the loads of up to 4 of them in flight
-//     before any is used, and the 4 partial results are summed in LDS in a
-//     fixed order (deterministic);
+//   * a block (4 waves) owns 16 output channels and walks K in slabs of
+//     1024 channels, one 256-channel chunk per wave; the pass's rows of X
+//     over the slab are staged in LDS by coalesced loads (one global read per
+//     16 bytes of X instead of one per lane and product), and the next slab's
+//     weights are in flight while the current one is computed; the 4 waves'
+//     partial results are summed in LDS in a fixed order (deterministic);
 //   * per chunk a lane (channel n = lane % 16, k-block b = lane / 16) reads
 //     the 32 code bytes that the storage order puts together for it (one
 //     coalesced 128-byte line per channel and chunk) with non-temporal loads;
@@ -42,7 +44,6 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int AWQ_WAVES = 4;
 constexpr int AWQ_COLS = 16;      // output channels per block
-constexpr int AWQ_BATCH = 4;      // chunks per wave whose loads are in flight together
 constexpr uint32_t kBf16_128 = 0x43004300u;   // bf16 128.0 in both halves
 constexpr uint32_t kBf16_m136 = 0xC308C308u;  // bf16 -136.0 in both halves
 
@@ -60,55 +61,70 @@ __device__ __forceinline__ bf16x8 awq_operand(uint32_t w)
     return __builtin_bit_cast(bf16x8, o);
 }
 
+constexpr int AWQ_SLAB = 256 * AWQ_WAVES;            // channels of X staged per slab (one chunk per wave)
+constexpr int AWQ_XSTRIDE = AWQ_SLAB + 8;            // bf16 per staged row (16 B pad: conflict-free rows)
+
 __global__ __launch_bounds__(64 * AWQ_WAVES) void awq_w4a16_kernel(const uint16_t *__restrict__ X,
                                                                    const uint8_t *__restrict__ wq,
                                                                    const float *__restrict__ wscale,
                                                                    const uint16_t *__restrict__ bias, int M,
                                                                    int N, int K, uint16_t *__restrict__ Y)
 {
+    extern __shared__ __attribute__((aligned(16))) uint16_t xs[];   // min(M, 16) rows x AWQ_XSTRIDE
     __shared__ f32x4 part[AWQ_WAVES][64];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int col = lane & 15, kb = lane >> 4;
     const int n = blockIdx.x * AWQ_COLS + col;
     const int nrow = n < N ? n : N - 1;              // rows past N read the last row, never stored
     const int chunks = K >> 8;
+    const int slabs = (chunks + AWQ_WAVES - 1) / AWQ_WAVES;
     const int KB = K >> 1, G = K >> 6;
     const uint8_t *wrow = wq + (size_t)nrow * KB + 32 * kb;
     const float *srow = wscale + (size_t)nrow * G;
     const bf16x8 neg136 = __builtin_bit_cast(bf16x8, (u32x4){kBf16_m136, kBf16_m136, kBf16_m136, kBf16_m136});
 
     for (int m0 = 0; m0 < M; m0 += 16) {
-        const int m = m0 + col;                      // this lane's row of the A operand
-        const bool mv = m < M;
-        const uint16_t *xrow = X + (size_t)(mv ? m : 0) * K + 8 * kb;
+        const int mb = M - m0 < 16 ? M - m0 : 16;    // rows of X in this pass
+        const bool mv = col < mb;
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        // up to AWQ_BATCH of the wave's chunks at a time, all loads issued first
-        for (int cb = wave; cb < chunks; cb += AWQ_BATCH * AWQ_WAVES) {
-            u32x4 wv[AWQ_BATCH][2];
-            float4 sv[AWQ_BATCH];
-#pragma unroll
-            for (int u = 0; u < AWQ_BATCH; ++u) {
-                const int c = cb + AWQ_WAVES * u;
-                if (c < chunks) {
-                    wv[u][0] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(wrow + 128 * c));
-                    wv[u][1] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(wrow + 128 * c + 16));
-                    sv[u] = *reinterpret_cast<const float4 *>(srow + 4 * c);
-                }
+        // weights of the wave's chunk in slab 0
+        u32x4 w0 = {0u, 0u, 0u, 0u}, w1 = {0u, 0u, 0u, 0u};
+        float4 sw = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (wave < chunks) {
+            w0 = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(wrow + 128 * wave));
+            w1 = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(wrow + 128 * wave + 16));
+            sw = *reinterpret_cast<const float4 *>(srow + 4 * wave);
+        }
+        for (int s = 0; s < slabs; ++s) {
+            // the pass's rows of X over the slab's channels into LDS
+            const int k0 = s * AWQ_SLAB;
+            for (int idx = tid; idx < mb * (AWQ_SLAB / 8); idx += 64 * AWQ_WAVES) {
+                const int r = idx / (AWQ_SLAB / 8), j = idx % (AWQ_SLAB / 8);
+                uint4 v = {0u, 0u, 0u, 0u};
+                if (k0 + 8 * j < K) v = *reinterpret_cast<const uint4 *>(X + (size_t)(m0 + r) * K + k0 + 8 * j);
+                *reinterpret_cast<uint4 *>(&xs[r * AWQ_XSTRIDE + 8 * j]) = v;
             }
-#pragma unroll
-            for (int u = 0; u < AWQ_BATCH; ++u) {
-                const int c = cb + AWQ_WAVES * u;
-                if (c >= chunks) break;
-                const uint32_t wd[8] = {wv[u][0].x, wv[u][0].y, wv[u][0].z, wv[u][0].w,
-                                        wv[u][1].x, wv[u][1].y, wv[u][1].z, wv[u][1].w};
-                const float swv[4] = {sv[u].x, sv[u].y, sv[u].z, sv[u].w};
+            __syncthreads();
+            const int c = s * AWQ_WAVES + wave;
+            const u32x4 cw0 = w0, cw1 = w1;
+            const float4 csw = sw;
+            // next slab's weights are in flight while this one is computed
+            const int cn = c + AWQ_WAVES;
+            if (cn < chunks) {
+                w0 = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(wrow + 128 * cn));
+                w1 = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(wrow + 128 * cn + 16));
+                sw = *reinterpret_cast<const float4 *>(srow + 4 * cn);
+            }
+            if (c < chunks) {
+                const uint32_t wd[8] = {cw0.x, cw0.y, cw0.z, cw0.w, cw1.x, cw1.y, cw1.z, cw1.w};
+                const float swv[4] = {csw.x, csw.y, csw.z, csw.w};
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
                     bf16x8 a[2];
 #pragma unroll
                     for (int h = 0; h < 2; ++h) {
                         uint4 xv = {0u, 0u, 0u, 0u};
-                        if (mv) xv = *reinterpret_cast<const uint4 *>(xrow + 256 * c + 64 * g + 32 * h);
+                        if (mv) xv = *reinterpret_cast<const uint4 *>(&xs[col * AWQ_XSTRIDE + 256 * wave + 64 * g + 32 * h + 8 * kb]);
                         a[h] = __builtin_bit_cast(bf16x8, xv);
                     }
                     f32x4 p = {0.f, 0.f, 0.f, 0.f};
@@ -120,22 +136,23 @@ __global__ __launch_bounds__(64 * AWQ_WAVES) void awq_w4a16_kernel(const uint16_
                     for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(p[i], swv[g], acc[i]);
                 }
             }
+            __syncthreads();
         }
         // the 4 waves' partial sums, added in wave order
         part[wave][lane] = acc;
         __syncthreads();
         if (wave == 0) {
-            f32x4 s = part[0][lane];
+            f32x4 t = part[0][lane];
 #pragma unroll
             for (int w = 1; w < AWQ_WAVES; ++w) {
-                const f32x4 t = part[w][lane];
-                s[0] += t[0]; s[1] += t[1]; s[2] += t[2]; s[3] += t[3];
+                const f32x4 u = part[w][lane];
+                t[0] += u[0]; t[1] += u[1]; t[2] += u[2]; t[3] += u[3];
             }
             const float b = (bias && n < N) ? __builtin_bit_cast(float, (uint32_t)bias[n] << 16) : 0.0f;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int mo = m0 + 4 * kb + i;     // output row of value i (D rows = A rows)
-                if (mo < M && n < N) Y[(size_t)mo * N + n] = (uint16_t)bf16_bits_rne(s[i] + b);
+                if (mo < M && n < N) Y[(size_t)mo * N + n] = (uint16_t)bf16_bits_rne(t[i] + b);
             }
         }
         __syncthreads();
@@ -148,7 +165,8 @@ hipError_t launch_awq_linear(const uint16_t *X, const uint8_t *wq, const float *
                              int M, int N, int K, uint16_t *Y, hipStream_t stream)
 {
     const int blocks = (N + AWQ_COLS - 1) / AWQ_COLS;
-    hipLaunchKernelGGL(awq_w4a16_kernel, dim3((unsigned)blocks), dim3(64 * AWQ_WAVES), 0, stream, X, wq, wscale,
+    const size_t lds = (size_t)(M < 16 ? M : 16) * AWQ_XSTRIDE * sizeof(uint16_t);
+    hipLaunchKernelGGL(awq_w4a16_kernel, dim3((unsigned)blocks), dim3(64 * AWQ_WAVES), lds, stream, X, wq, wscale,
                        bias, M, N, K, Y);
     return hipGetLastError();
 }

@@ -66,6 +66,7 @@ def lib():
         L.oracle_gelu_tanh.restype = ctypes.c_double
         L.oracle_gelu_tanh.argtypes = [ctypes.c_double]
         L.oracle_num_threads.restype = ctypes.c_int
+        L.oracle_qkv_norm_rope.argtypes = [P, I, I, P, P, ctypes.c_double, P, P, P]
         L.oracle_awq_code.restype = I
         L.oracle_awq_code.argtypes = [P, I]
         L.oracle_awq_pack.argtypes = [P, I, I, P, P]
@@ -319,3 +320,20 @@ def awq_linear(X, wq, wscale, bias=None):
     y = np.zeros((M, N), np.float64)
     lib().oracle_awq_linear(_p(X), _p(wq), _p(wscale), _p(bias), M, N, K, _p(y))
     return y
+
+
+# ---------------------------------------- QKV projection + Q/K RMS-norm + RoPE
+# The fused attention-input step (section "Quantizing models with structural
+# rewrites": the engine's fused_qkv_norm_rottary); readings in svdq_oracle.c.
+
+def qkv_norm_rope(ylin, norm_q, norm_k, eps: float, rope_cos, rope_sin):
+    """fp64 linear output [M][N] (N = 3 H 128, before bf16 rounding) ->
+    fp64 [M][N]: Q and K heads RMS-normalized and rotated, V rounded only."""
+    y = _c(ylin, np.float64)
+    M, N = y.shape
+    assert N % 384 == 0
+    wq_, wk_ = _c(norm_q, np.uint16), _c(norm_k, np.uint16)
+    c, s = _c(rope_cos, np.float32), _c(rope_sin, np.float32)
+    out = np.zeros((M, N), np.float64)
+    lib().oracle_qkv_norm_rope(_p(y), M, N, _p(wq_), _p(wk_), float(eps), _p(c), _p(s), _p(out))
+    return out

@@ -343,6 +343,63 @@ void oracle_linear(const uint8_t *xq, const void *xscale, const double *h,
     }
 }
 
+/* --------------------------------------- QKV projection + Q/K RMS-norm + RoPE */
+
+/*
+ * The fused attention-input step of the same pages ("Bringing Nunchaku 4-bit
+ * Diffusion Inference to Diffusers", section "Quantizing models with
+ * structural rewrites": the Nunchaku engine's fused_qkv_norm_rottary takes
+ * the hidden states, the QKV projection, the Q and K norms and the rotary
+ * embedding together).  Readings: the
+ * projection output is the W4A4 linear's, rounded to bf16 as the linear
+ * stores it; its N = 3 H 128 channels are H heads of Q, then of K, then of
+ * V, each 128 wide; Q and K heads are RMS-normalized over their 128
+ * channels, u_d = yb_d / sqrt(mean_d(yb_d^2) + eps) * w_d (w = the bf16 norm
+ * weight of Q or K), then rotated pairwise with the token's angle table,
+ * out_2p = u_2p cos_mp - u_2p+1 sin_mp, out_2p+1 = u_2p+1 cos_mp + u_2p sin_mp
+ * (p < 64); V heads pass through.  fp64 throughout after the bf16 rounding.
+ */
+static double bf16_round(double v)
+{
+    /* fp64 -> fp32 (nearest) -> bf16 (nearest even on the upper 16 bits) */
+    float f = (float)v;
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    uint32_t keep = u >> 16, rem = u & 0xFFFFu;
+    if (rem > 0x8000u || (rem == 0x8000u && (keep & 1u))) keep += 1u;
+    return bf16_val((uint16_t)keep);
+}
+
+void oracle_qkv_norm_rope(const double *ylin, int M, int N, const uint16_t *norm_q, const uint16_t *norm_k,
+                          double eps, const float *rope_cos, const float *rope_sin, double *out)
+{
+    const int H = N / 384;
+    for (int m = 0; m < M; ++m) {
+        for (int hd = 0; hd < 3 * H; ++hd) {
+            const double *y = ylin + (size_t)m * N + 128 * hd;
+            double *o = out + (size_t)m * N + 128 * hd;
+            double yb[128];
+            for (int d = 0; d < 128; ++d) yb[d] = bf16_round(y[d]);
+            if (hd >= 2 * H) {                    /* V */
+                for (int d = 0; d < 128; ++d) o[d] = yb[d];
+                continue;
+            }
+            const uint16_t *w = hd < H ? norm_q : norm_k;
+            double ms = 0.0;
+            for (int d = 0; d < 128; ++d) ms += yb[d] * yb[d];
+            ms /= 128.0;
+            const double rs = 1.0 / sqrt(ms + eps);
+            double u[128];
+            for (int d = 0; d < 128; ++d) u[d] = yb[d] * rs * bf16_val(w[d]);
+            for (int q = 0; q < 64; ++q) {
+                const double c = rope_cos[(size_t)m * 64 + q], sn = rope_sin[(size_t)m * 64 + q];
+                o[2 * q] = u[2 * q] * c - u[2 * q + 1] * sn;
+                o[2 * q + 1] = u[2 * q + 1] * c + u[2 * q] * sn;
+            }
+        }
+    }
+}
+
 /* ------------------------------------------------------- AWQ W4A16 (INT4) */
 
 /*

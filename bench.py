@@ -82,10 +82,11 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--prec", choices=["int4", "mxfp4"], default="int4")
-    ap.add_argument("--layer", choices=["fc1", "qkv", "fc2", "mlp", "awq"], default="fc1",
+    ap.add_argument("--layer", choices=["fc1", "qkv", "fc2", "mlp", "awq", "qkvnorm"], default="fc1",
                     help="fc1 is the headline workload; fc2 takes fc1's output (computed on the GPU); "
                          "mlp times fc1 -> fc2 with fc2's activation step fused into fc1's epilogue, "
-                         "next to the unfused pair; awq times the weight-only AWQ W4A16 modulation layer")
+                         "next to the unfused pair; awq times the weight-only AWQ W4A16 modulation layer; "
+                         "qkvnorm is qkv with the Q/K RMS-norm and rotary embedding fused into the epilogue")
     ap.add_argument("--copy-calibration", type=int, metavar="MIB", default=0,
                     help="only run a plain copy of MIB MiB (to scale the HBM byte counters)")
     ap.add_argument("--sets", type=int, default=0,
@@ -120,7 +121,11 @@ def main():
     if not args.sets:
         args.sets = 3
     prec = svdq.INT4 if args.prec == "int4" else svdq.MXFP4
-    spec = synth.SPECS[("" if prec == svdq.INT4 else "mx_") + args.layer]
+    qkvnorm = args.layer == "qkvnorm"
+    if qkvnorm and prec != svdq.INT4:
+        print("--layer qkvnorm is INT4 only", file=sys.stderr)
+        sys.exit(2)
+    spec = synth.SPECS[("" if prec == svdq.INT4 else "mx_") + ("qkv" if qkvnorm else args.layer)]
     M, K, N, r = spec.M, spec.K, spec.N, svdq.RANK
     X_bits = None
     if args.layer == "fc2":
@@ -155,11 +160,20 @@ def main():
             h=torch.empty((M, r), dtype=torch.float32, device="cuda"),
             Y=torch.empty((M, N), dtype=torch.bfloat16, device="cuda")))
     ws_mb = sum(t.numel() * t.element_size() for t in sets[0].values() if t is not None) / 1e6
+    if qkvnorm:
+        rc, rs = synth.gen_rope(M)
+        qkn = dict(nq=svdq.bf16_tensor(synth.gen_qk_norm(spec.config_id, 10)),
+                   nk=svdq.bf16_tensor(synth.gen_qk_norm(spec.config_id, 11)),
+                   c=torch.from_numpy(rc).cuda(), s=torch.from_numpy(rs).cuda())
 
     def k1(b):
         svdq.quantize_act(b["X"], b["smooth"], b["down"], prec, xq=b["xq"], xscale=b["xscale"], h=b["h"])
 
     def k2(b):
+        if qkvnorm:
+            svdq.w4a4_linear_qkv_norm_rope(b["xq"], b["xscale"], b["h"], b["wq"], b["wscale"], b["up"], b["bias"],
+                                           qkn["nq"], qkn["nk"], 1e-6, qkn["c"], qkn["s"], Y=b["Y"])
+            return
         svdq.w4a4_linear(b["xq"], b["xscale"], b["h"], b["wq"], b["wscale"], b["up"], b["bias"], prec,
                          epi, Y=b["Y"])
 
@@ -224,7 +238,10 @@ def main():
         rows = int(min(M, max(8, rows * args.cpu_seconds / probe)))
         t0 = time.time()
         xq, xs, h = O.quant_act(L["X"][:rows], p["smooth"], p["down"], prec)
-        O.linear(xq, xs, h, p["wq"], p["wscale"], p["up"], L["bias"], prec, gelu=spec.gelu)
+        yl = O.linear(xq, xs, h, p["wq"], p["wscale"], p["up"], L["bias"], prec, gelu=spec.gelu)
+        if qkvnorm:
+            O.qkv_norm_rope(yl, synth.gen_qk_norm(spec.config_id, 10), synth.gen_qk_norm(spec.config_id, 11), 1e-6,
+                            rc[:rows], rs[:rows])
         t_cpu = time.time() - t0
         cpu = {"value": round(2.0 * rows * N * K / t_cpu / 1e12, 6), "unit": "TOPS", "cores": O.num_threads(),
                "kind": "oracle",
@@ -248,11 +265,13 @@ def main():
         "data": "synthetic (seeded Student-t activations with outlier channels, N(0,0.02^2) weights)",
         "config": {"workload": f"{spec.name}: {M} tokens x {K} -> {N}, rank {r}, "
                                f"{'INT4 g64' if prec == svdq.INT4 else 'MXFP4 g32'}, bias"
-                               f"{', GELU-tanh' if spec.gelu else ''}; "
-                               "step = svdq_quantize_act + svdq_w4a4_linear",
+                               f"{', GELU-tanh' if spec.gelu else ''}"
+                               f"{', Q/K RMS-norm + rotary embedding in the epilogue' if qkvnorm else ''}; "
+                               "step = svdq_quantize_act + "
+                               f"{'svdq_w4a4_linear_qkv_norm_rope' if qkvnorm else 'svdq_w4a4_linear'}",
                    "M": M, "K": K, "N": N, "rank": r, "buffer_sets": len(sets),
                    "working_set_MB_per_set": round(ws_mb, 1)},
-        "roofline": {"bound": "mfma", "kernel": "svdq_w4a4_linear",
+        "roofline": {"bound": "mfma", "kernel": "svdq_w4a4_linear_qkv_norm_rope" if qkvnorm else "svdq_w4a4_linear",
                      "achieved": round(k2_tops, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(k2_tops / peak, 4), "traffic": traffic,
                      "avg_ms": round(k2_ms, 5)},

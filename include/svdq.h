@@ -39,7 +39,8 @@
  *   - Ownership: the caller allocates and frees every buffer.  No call
  *     allocates device memory or keeps a pointer after it returns.
  *   - Device calls (svdq_quantize_act, svdq_w4a4_linear,
- *     svdq_w4a4_linear_requant, svdq_awq_w4a16_linear) take device
+ *     svdq_w4a4_linear_requant, svdq_w4a4_linear_qkv_norm_rope,
+ *     svdq_awq_w4a16_linear) take device
  *     pointers and a hipStream_t (as void*, NULL = the null stream); they
  *     validate everything first, enqueue kernels on `stream` and return
  *     without synchronizing.  On any error nothing has been enqueued or
@@ -229,6 +230,36 @@ svdq_status svdq_w4a4_linear_requant(const uint8_t *xq, const void *xscale, cons
                                      svdq_precision prec, svdq_epilogue epi, const float *smooth2,
                                      const uint16_t *down2, uint8_t *xq2, void *xscale2, float *h2,
                                      void *work, size_t work_bytes, void *stream);
+
+/*
+ * svdq_w4a4_linear_qkv_norm_rope -- svdq_w4a4_linear for a fused QKV
+ * projection whose epilogue also applies the Q/K RMS-norm and the rotary
+ * embedding ("Quantizing models with structural rewrites": the Nunchaku
+ * engine's fused operator consumes the QKV projection, the Q/K normalization
+ * and the rotary embeddings together).
+ *
+ *   xq ... bias  as for svdq_w4a4_linear; INT4 only (MXFP4:
+ *                SVDQ_ERR_UNSUPPORTED); no GELU
+ *   N            3 H 128 (SVDQ_ERR_SHAPE otherwise): channels [0, 128 H) are
+ *                the Q heads, then H K heads, then H V heads, 128 each
+ *   norm_q       [128] bf16 bits, device   RMS-norm weight of every Q head
+ *   norm_k       [128] bf16 bits, device   RMS-norm weight of every K head
+ *   eps          finite, >= 0 (SVDQ_ERR_INVALID_ARG otherwise)
+ *   rope_cos     [M][64] fp32, device      cos of token m's angle for pair p
+ *   rope_sin     [M][64] fp32, device      sin of the same angle
+ *   Y            [M][N] bf16 bits, device (out)
+ * With yb = the bf16 value svdq_w4a4_linear would store: V channels get yb;
+ * a Q or K head gets u_d = yb_d / sqrt(mean_d(yb_d^2) + eps) * w_d (fp32),
+ * then out_2p = u_2p cos_mp - u_2p+1 sin_mp, out_2p+1 = u_2p+1 cos_mp +
+ * u_2p sin_mp, rounded to bf16 (round-to-nearest-even).  One kernel launch.
+ * Errors as for svdq_w4a4_linear, plus the ones above.
+ */
+svdq_status svdq_w4a4_linear_qkv_norm_rope(const uint8_t *xq, const void *xscale, const float *h,
+                                           const uint8_t *wq, const void *wscale, const uint16_t *up,
+                                           const uint16_t *bias, int M, int N, int K, int rank,
+                                           svdq_precision prec, const uint16_t *norm_q, const uint16_t *norm_k,
+                                           float eps, const float *rope_cos, const float *rope_sin, uint16_t *Y,
+                                           void *stream);
 
 /*
  * svdq_awq_pack_weights -- host packing for the weight-only AWQ W4A16 layer

@@ -94,6 +94,35 @@ def test_requant_validation_and_workspace():
         assert call(prec=svdq.MXFP4, K=256) == -5
 
 
+def test_qkv_norm_rope_validation():
+    """The fused QKV + Q/K norm + rotary entry point: argument errors before
+    the device check."""
+    L = svdq.lib()
+    _, p = _host(1 << 16)
+    _, q = _host(1 << 16, offset=4)
+
+    def call(**kw):
+        a = dict(xq=p, xs=p, h=p, wq=p, ws=p, up=p, bias=None, M=16, N=384, K=128, r=32, prec=svdq.INT4,
+                 nq=p, nk=p, eps=1e-6, c=p, s=p, Y=p)
+        a.update(kw)
+        return L.svdq_w4a4_linear_qkv_norm_rope(a["xq"], a["xs"], a["h"], a["wq"], a["ws"], a["up"], a["bias"],
+                                                a["M"], a["N"], a["K"], a["r"], a["prec"], a["nq"], a["nk"],
+                                                ctypes.c_float(a["eps"]), a["c"], a["s"], a["Y"], None)
+    assert call(N=256) == -2                    # N = 3 H 128
+    assert call(prec=svdq.MXFP4) == -4         # INT4 only
+    assert call(eps=-1.0) == -1
+    assert call(eps=float("nan")) == -1
+    assert call(eps=float("inf")) == -1
+    assert call(r=16) == -4
+    assert call(nq=None) == -1
+    assert call(c=None) == -1
+    assert call(s=q) == -3
+    assert call(nk=q) == -3
+    assert call(K=96) == -2
+    if not _has_gpu():
+        assert call() == -5
+
+
 def test_awq_validation():
     """The weight-only AWQ W4A16 entry point: argument errors before the
     device check."""

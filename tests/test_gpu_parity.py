@@ -407,3 +407,62 @@ def test_awq_deterministic_and_empty():
     Y0 = svdq.awq_w4a16_linear(_t(X[:0]), _t(wq), _t(ws), _t(b))
     torch.cuda.synchronize()
     assert Y0.shape == (0, 64)
+
+
+# ------------------------------- QKV projection + Q/K RMS-norm + rotary (INT4)
+
+def _qkvnorm_case(M, K, N, bias=True, rows=None, eps=1e-6):
+    L, p = _layer("qkv", M, K, N, svdq.INT4, bias=bias)
+    nq, nk = synth.gen_qk_norm(2, 10), synth.gen_qk_norm(2, 11)
+    c, s = synth.gen_rope(M)
+    xq, xs, h, oh = _quant_act_check(L["X"], p["smooth"], p["down"], svdq.INT4)
+    Y = svdq.w4a4_linear_qkv_norm_rope(xq, xs, h, _t(p["wq"]), _t(p["wscale"]), _t(p["up"]), _t(L["bias"]),
+                                       _t(nq), _t(nk), eps, _t(c), _t(s))
+    Yp = svdq.w4a4_linear(xq, xs, h, _t(p["wq"]), _t(p["wscale"]), _t(p["up"]), _t(L["bias"]), svdq.INT4)
+    torch.cuda.synchronize()
+    ylin = O.linear(_np(xq), _np(xs), oh, p["wq"], p["wscale"], p["up"], L["bias"], svdq.INT4, rows=rows)
+    sel = slice(None) if rows is None else rows
+    pick = (lambda t: t) if rows is None else (lambda t: t[torch.from_numpy(rows).long().cuda()])
+    # the projection itself, as the plain kernel stores it, against the oracle
+    _y_check(pick(Yp), ylin, f"qkv projection {M}x{K}->{N}")
+    # the norm and rotation consume that bf16 projection on both sides (the
+    # bf16 rounding is a decision taken once, in fp32, by the GPU; a 1-ulp
+    # difference there can exceed the tolerance after a rotation cancels)
+    yb = bf16_bits_to_f32(_np(pick(Yp))).astype(np.float64)
+    y_ref = O.qkv_norm_rope(yb, nq, nk, eps, c[sel], s[sel])
+    _y_check(pick(Y), y_ref, f"qkv norm rope {M}x{K}->{N}")
+    # V heads are exactly what the plain linear stores
+    H = N // 384
+    yv = _np(Y)[:, 256 * H:]
+    assert np.array_equal(yv, _np(Yp)[:, 256 * H:])
+    return Y
+
+
+@pytest.mark.parametrize("M,K,N,bias", [(64, 256, 384, True), (130, 512, 768, False), (257, 320, 1152, True),
+                                        (1, 128, 384, True)])
+def test_qkv_norm_rope_synthetic(M, K, N, bias):
+    _say(f"qkv norm rope M={M} K={K} N={N} bias={bias}")
+    _qkvnorm_case(M, K, N, bias)
+
+
+def test_qkv_norm_rope_full_size():
+    """4608 tokens x 3072 -> 9216 (24 heads each of Q, K, V) with the
+    FLUX-like rotary table; outputs on sampled rows (text and image tokens)."""
+    _say("qkv norm rope full size")
+    M = 4608
+    _qkvnorm_case(M, 3072, 9216, rows=np.unique(np.concatenate([_rows(M, 40), [511, 512]])).astype(np.int32))
+
+
+def test_qkv_norm_rope_deterministic_and_empty():
+    L, p = _layer("qkv", 40, 256, 384, svdq.INT4)
+    nq, nk = synth.gen_qk_norm(2, 10), synth.gen_qk_norm(2, 11)
+    c, s = synth.gen_rope(40)
+    xq, xs, h, _ = _quant_act_check(L["X"], p["smooth"], p["down"], svdq.INT4)
+    args = (xq, xs, h, _t(p["wq"]), _t(p["wscale"]), _t(p["up"]), _t(L["bias"]), _t(nq), _t(nk), 1e-6, _t(c), _t(s))
+    Y1 = svdq.w4a4_linear_qkv_norm_rope(*args)
+    Y2 = svdq.w4a4_linear_qkv_norm_rope(*args)
+    torch.cuda.synchronize()
+    assert torch.equal(Y1.view(torch.int16), Y2.view(torch.int16))
+    Y0 = svdq.w4a4_linear_qkv_norm_rope(xq[:0], xs[:0], h[:0], *args[3:10], _t(c[:0]), _t(s[:0]))
+    torch.cuda.synchronize()
+    assert Y0.shape == (0, 384)

@@ -12,6 +12,7 @@ Functions mirror the C ABI in include/svdq.h:
     quantize_act(X, smooth, down, prec=INT4, ...)              device, torch tensors
     w4a4_linear(xq, xscale, h, wq, wscale, up, bias, ...)      device, torch tensors
     w4a4_linear_requant(...)                                    device, torch tensors
+    w4a4_linear_qkv_norm_rope(...)                              device, torch tensors
     awq_pack_weights(W)                                         host, numpy in/out
     awq_w4a16_linear(X, wq, wscale, bias, ...)                  device, torch tensors
 
@@ -44,7 +45,8 @@ STATUS = {
 }
 EXPORTS = ("svdq_status_string", "svdq_version", "svdq_check_device", "svdq_pack_weights",
            "svdq_pack_residual", "svdq_quantize_act", "svdq_w4a4_linear", "svdq_requant_workspace_bytes",
-           "svdq_w4a4_linear_requant", "svdq_awq_pack_weights", "svdq_awq_w4a16_linear")
+           "svdq_w4a4_linear_requant", "svdq_w4a4_linear_qkv_norm_rope", "svdq_awq_pack_weights",
+           "svdq_awq_w4a16_linear")
 
 
 class SvdqError(RuntimeError):
@@ -84,6 +86,9 @@ def lib():
         L.svdq_w4a4_linear_requant.restype = I
         L.svdq_w4a4_linear_requant.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, P, P, P, P, P, P,
                                                ctypes.c_size_t, P]
+        L.svdq_w4a4_linear_qkv_norm_rope.restype = I
+        L.svdq_w4a4_linear_qkv_norm_rope.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, P, P, ctypes.c_float, P, P,
+                                                     P, P]
         L.svdq_awq_pack_weights.restype = I
         L.svdq_awq_pack_weights.argtypes = [P, I, I, P, P]
         L.svdq_awq_w4a16_linear.restype = I
@@ -255,6 +260,30 @@ def w4a4_linear_requant(xq, xscale, h, wq, wscale, up, bias, smooth2, down2, pre
         _dev(work, (torch.uint8, torch.float32), "work"), work.numel() * work.element_size(), _stream(stream))
     _check(st, "svdq_w4a4_linear_requant")
     return xq2, xs2, h2
+
+
+def w4a4_linear_qkv_norm_rope(xq, xscale, h, wq, wscale, up, bias, norm_q, norm_k, eps: float, rope_cos,
+                              rope_sin, prec: int = INT4, Y=None, stream=None):
+    """w4a4_linear of a fused QKV projection (N = 3 H 128) with the Q/K
+    RMS-norm and rotary embedding applied in its epilogue (one kernel)."""
+    torch = _torch()
+    M = xq.shape[0]
+    K = xq.shape[1] * 2
+    N = wq.shape[0]
+    r = up.shape[1]
+    if Y is None:
+        Y = torch.empty((M, N), dtype=torch.bfloat16, device=xq.device)
+    pbias = None if bias is None else _dev(bias, (torch.bfloat16, torch.int16), "bias")
+    st = lib().svdq_w4a4_linear_qkv_norm_rope(
+        _dev(xq, (torch.uint8,), "xq"), _dev(xscale, (torch.float32, torch.uint8), "xscale"),
+        _dev(h, (torch.float32,), "h"), _dev(wq, (torch.uint8,), "wq"),
+        _dev(wscale, (torch.float32, torch.uint8), "wscale"), _dev(up, (torch.bfloat16, torch.int16), "up"),
+        pbias, M, N, K, r, prec, _dev(norm_q, (torch.bfloat16, torch.int16), "norm_q"),
+        _dev(norm_k, (torch.bfloat16, torch.int16), "norm_k"), float(eps),
+        _dev(rope_cos, (torch.float32,), "rope_cos"), _dev(rope_sin, (torch.float32,), "rope_sin"),
+        _dev(Y, (torch.bfloat16, torch.int16), "Y"), _stream(stream))
+    _check(st, "svdq_w4a4_linear_qkv_norm_rope")
+    return Y
 
 
 def awq_pack_weights(W: np.ndarray):

@@ -173,6 +173,35 @@ extern "C" svdq_status svdq_w4a4_linear_requant(const uint8_t *xq, const void *x
     return e == hipSuccess ? SVDQ_OK : SVDQ_ERR_HIP;
 }
 
+extern "C" svdq_status svdq_w4a4_linear_qkv_norm_rope(const uint8_t *xq, const void *xscale, const float *h,
+                                                      const uint8_t *wq, const void *wscale, const uint16_t *up,
+                                                      const uint16_t *bias, int M, int N, int K, int rank,
+                                                      svdq_precision prec, const uint16_t *norm_q,
+                                                      const uint16_t *norm_k, float eps, const float *rope_cos,
+                                                      const float *rope_sin, uint16_t *Y, void *stream)
+{
+    svdq_status st = check_common(M, K, rank, prec);
+    if (st != SVDQ_OK) return st;
+    if (N < 0) return SVDQ_ERR_INVALID_ARG;
+    if (!(eps >= 0.0f) || eps > 3.0e38f) return SVDQ_ERR_INVALID_ARG;      // finite, non-negative
+    if (N % 384 != 0) return SVDQ_ERR_SHAPE;
+    if (prec != SVDQ_INT4) return SVDQ_ERR_UNSUPPORTED;
+    // buffers of zero size may be NULL (empty tensors have no storage)
+    if ((M > 0 && (!xq || !xscale || !h || !rope_cos || !rope_sin)) ||
+        (N > 0 && (!wq || !wscale || !up || !norm_q || !norm_k)) || (M > 0 && N > 0 && !Y))
+        return SVDQ_ERR_INVALID_ARG;
+    if (!aligned16(xq) || !aligned16(xscale) || !aligned16(h) || !aligned16(wq) || !aligned16(wscale) ||
+        !aligned16(up) || !aligned16(Y) || (bias && !aligned16(bias)) || !aligned16(norm_q) || !aligned16(norm_k) ||
+        !aligned16(rope_cos) || !aligned16(rope_sin))
+        return SVDQ_ERR_MISALIGNED;
+    st = current_device_ok();
+    if (st != SVDQ_OK) return st;
+    if (M == 0 || N == 0) return SVDQ_OK;
+    hipError_t e = launch_w4a4_linear_qknorm(xq, (const float *)xscale, h, wq, (const float *)wscale, up, bias, M, N,
+                                             K, norm_q, norm_k, eps, rope_cos, rope_sin, Y, (hipStream_t)stream);
+    return e == hipSuccess ? SVDQ_OK : SVDQ_ERR_HIP;
+}
+
 extern "C" svdq_status svdq_awq_w4a16_linear(const uint16_t *X, const uint8_t *wq, const float *wscale,
                                              const uint16_t *bias, int M, int N, int K, uint16_t *Y,
                                              void *stream)

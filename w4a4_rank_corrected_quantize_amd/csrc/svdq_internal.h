@@ -36,6 +36,13 @@ hipError_t launch_w4a4_linear_requant(const uint8_t *xq, const void *xscale, con
                                       const uint16_t *down2, uint8_t *xq2, void *xscale2, float *h2, float *work,
                                       hipStream_t stream);
 
+// INT4 linear of a QKV projection (N = 3 H 128) whose epilogue RMS-normalizes
+// the Q and K heads and applies the rotary embedding.
+hipError_t launch_w4a4_linear_qknorm(const uint8_t *xq, const float *xscale, const float *h, const uint8_t *wq,
+                                     const float *wscale, const uint16_t *up, const uint16_t *bias, int M, int N,
+                                     int K, const uint16_t *norm_q, const uint16_t *norm_k, float eps,
+                                     const float *rope_cos, const float *rope_sin, uint16_t *Y, hipStream_t stream);
+
 // Weight-only AWQ W4A16 layer (K % 256 == 0).
 hipError_t launch_awq_linear(const uint16_t *X, const uint8_t *wq, const float *wscale, const uint16_t *bias,
                              int M, int N, int K, uint16_t *Y, hipStream_t stream);

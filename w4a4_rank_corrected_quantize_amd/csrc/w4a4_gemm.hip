@@ -238,6 +238,24 @@ struct RequantArgs {
     float *hpart;             // [ceil(N/256)][M][32]
 };
 
+// What the INT4 kernel's epilogue does with the wave tile.
+constexpr int EPI_STORE = 0;      // y -> bf16 Y
+constexpr int EPI_REQUANT = 1;    // the next layer's activation step (RequantArgs)
+constexpr int EPI_QKNORM = 2;     // Q/K RMS-norm + rotary embedding of a QKV projection (QKNormArgs)
+
+// The fused attention-input step: N = 3 H 128 output channels are H heads of
+// Q, then K, then V.  Q and K heads are RMS-normalized over their 128
+// channels with their bf16 norm weight and then rotated pairwise by the
+// token's angles; V heads are stored as the linear stores them.
+struct QKNormArgs {
+    const uint16_t *norm_q;   // [128] bf16 bits
+    const uint16_t *norm_k;   // [128] bf16 bits
+    const float *rope_cos;    // [M][64]
+    const float *rope_sin;    // [M][64]
+    int heads;                // H
+    float eps;
+};
+
 // Epilogue of the requantizing INT4 kernel for one wave tile (64 channels n
 // of one 64-group x 64 tokens m).  Lane (l32, hk) holds, per 32-token tile
 // tm, token m = mb + 32 tm + l32 and the channels nb + 32 tn + 8 j + 4 hk +
@@ -429,11 +447,141 @@ __device__ __forceinline__ void requant_epilogue(const f32x16 (&acc)[I4_TN][I4_T
     }
 }
 
-template <bool REQ>
+// Epilogue of the QKV kernel with Q/K RMS-norm and rotary embedding, for
+// one wave tile (64 channels n x 64 tokens m).  A 128-channel head is the
+// tile of this wave and of its neighbour (wn ^ 1): each lane sums the
+// squares of its 32 values per token, adds its partner half (lane ^ 32), and
+// the two waves exchange their sums through LDS.  Element i of tile (tn, tm)
+// is channel nb + 32 tn + 8 (i / 4) + 4 hk + i % 4 of token mb + 32 tm +
+// l32, so a rotation pair (2p, 2p + 1) sits in one lane.  `smem` is LDS that
+// no wave reads any more.
+__device__ __forceinline__ void qknorm_epilogue(const f32x16 (&acc)[I4_TN][I4_TM], const bf16x8 (&hhi)[I4_TM][2],
+                                                const bf16x8 (&hlo)[I4_TM][2], const uint16_t *__restrict__ up,
+                                                const uint16_t *__restrict__ bias, int M, int N,
+                                                const QKNormArgs &qk, int mb, int nb, int wave, int lane,
+                                                uint16_t *__restrict__ Y, uint8_t *smem)
+{
+    const int l32 = lane & 31, hk = lane >> 5;
+    // the linear's outputs, rounded to bf16 exactly as the plain epilogue
+    // stores them
+    uint2 yb[I4_TN][I4_TM][4];
+#pragma unroll
+    for (int tn = 0; tn < I4_TN; ++tn) {
+        const int nrow = nb + tn * 32 + l32;
+        bf16x8 ua[2];
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+            uint4 uv = {0u, 0u, 0u, 0u};
+            if (nrow < N) uv = *reinterpret_cast<const uint4 *>(up + (size_t)nrow * 32 + 16 * s2 + 8 * hk);
+            ua[s2] = __builtin_bit_cast(bf16x8, uv);
+        }
+        uint2 bv[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) bv[j] = bias4(bias, nb + tn * 32 + 8 * j + 4 * hk, N);
+#pragma unroll
+        for (int tm = 0; tm < I4_TM; ++tm) {
+            f32x16 lr = {};
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) {
+                lr = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ua[s2], hhi[tm][s2], lr, 0, 0, 0);
+                lr = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ua[s2], hlo[tm][s2], lr, 0, 0, 0);
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float a4[4] = {acc[tn][tm][4 * j], acc[tn][tm][4 * j + 1], acc[tn][tm][4 * j + 2],
+                                     acc[tn][tm][4 * j + 3]};
+                const float l4[4] = {lr[4 * j], lr[4 * j + 1], lr[4 * j + 2], lr[4 * j + 3]};
+                yb[tn][tm][j] = finish4(a4, l4, bv[j], 0);
+            }
+        }
+    }
+    const int head = nb / 128;                   // the same for this wave and its neighbour
+    const bool norm = head < 2 * qk.heads;       // a Q or a K head
+    float *red = reinterpret_cast<float *>(smem + 8 * OUT_TILE_BYTES);   // [8 waves][64 tokens]
+    // the norm weights and the rotation tables do not depend on the sums:
+    // their loads are in flight while the sums are formed and exchanged
+    const uint16_t *__restrict__ w = head < qk.heads ? qk.norm_q : qk.norm_k;
+    uint2 wv[I4_TN][4];
+    float2 cv[I4_TM][I4_TN][4], sv[I4_TM][I4_TN][4];
+    if (norm) {
+#pragma unroll
+        for (int tn = 0; tn < I4_TN; ++tn)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                wv[tn][j] = *reinterpret_cast<const uint2 *>(w + ((nb + tn * 32 + 8 * j + 4 * hk) & 127));
+#pragma unroll
+        for (int tm = 0; tm < I4_TM; ++tm) {
+            const int m = mb + tm * 32 + l32 < M ? mb + tm * 32 + l32 : M - 1;   // rows past M are never stored
+#pragma unroll
+            for (int tn = 0; tn < I4_TN; ++tn)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int d = (nb + tn * 32 + 8 * j + 4 * hk) & 127;        // channel in the head, % 4 == 0
+                    cv[tm][tn][j] = *reinterpret_cast<const float2 *>(qk.rope_cos + (size_t)m * 64 + d / 2);
+                    sv[tm][tn][j] = *reinterpret_cast<const float2 *>(qk.rope_sin + (size_t)m * 64 + d / 2);
+                }
+        }
+    }
+    if (norm) {
+#pragma unroll
+        for (int tm = 0; tm < I4_TM; ++tm) {
+            float ss = 0.0f;
+#pragma unroll
+            for (int tn = 0; tn < I4_TN; ++tn)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const float v0 = bf16_to_f32(yb[tn][tm][j].x & 0xFFFFu), v1 = bf16_to_f32(yb[tn][tm][j].x >> 16);
+                    const float v2 = bf16_to_f32(yb[tn][tm][j].y & 0xFFFFu), v3 = bf16_to_f32(yb[tn][tm][j].y >> 16);
+                    ss = __builtin_fmaf(v0, v0, ss);
+                    ss = __builtin_fmaf(v1, v1, ss);
+                    ss = __builtin_fmaf(v2, v2, ss);
+                    ss = __builtin_fmaf(v3, v3, ss);
+                }
+            ss += __shfl_xor(ss, 32);
+            if (hk == 0) red[wave * 64 + tm * 32 + l32] = ss;
+        }
+    }
+    __syncthreads();
+    uint8_t *tile = smem + wave * OUT_TILE_BYTES;
+    if (norm) {
+#pragma unroll
+        for (int tm = 0; tm < I4_TM; ++tm) {
+            const int ml = tm * 32 + l32;
+            const float tot = red[wave * 64 + ml] + red[(wave ^ 1) * 64 + ml];
+            const float rs = __builtin_amdgcn_rsqf(__builtin_fmaf(tot, 1.0f / 128.0f, qk.eps));
+#pragma unroll
+            for (int tn = 0; tn < I4_TN; ++tn)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const uint2 y2 = yb[tn][tm][j], w2 = wv[tn][j];
+                    const float2 c = cv[tm][tn][j], sn = sv[tm][tn][j];
+                    const float u0 = bf16_to_f32(y2.x & 0xFFFFu) * rs * bf16_to_f32(w2.x & 0xFFFFu);
+                    const float u1 = bf16_to_f32(y2.x >> 16) * rs * bf16_to_f32(w2.x >> 16);
+                    const float u2 = bf16_to_f32(y2.y & 0xFFFFu) * rs * bf16_to_f32(w2.y & 0xFFFFu);
+                    const float u3 = bf16_to_f32(y2.y >> 16) * rs * bf16_to_f32(w2.y >> 16);
+                    const float o0 = u0 * c.x - u1 * sn.x, o1 = u1 * c.x + u0 * sn.x;
+                    const float o2 = u2 * c.y - u3 * sn.y, o3 = u3 * c.y + u2 * sn.y;
+                    stage4(tile, ml, tn * 32 + 8 * j + 4 * hk, make_uint2(pack_bf16x2(o0, o1), pack_bf16x2(o2, o3)));
+                }
+        }
+    } else {
+#pragma unroll
+        for (int tn = 0; tn < I4_TN; ++tn)
+#pragma unroll
+            for (int tm = 0; tm < I4_TM; ++tm)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) stage4(tile, tm * 32 + l32, tn * 32 + 8 * j + 4 * hk, yb[tn][tm][j]);
+    }
+    __syncthreads();
+    flush_tile(tile, Y, mb, nb, M, N, lane);
+}
+
+template <int EPI>
 __global__ __launch_bounds__(I4_THREADS) void w4a4_int4_kernel(
     const uint8_t *__restrict__ xq, const float *__restrict__ xscale, const float *__restrict__ h,
     const uint8_t *__restrict__ wq, const float *__restrict__ wscale, const uint16_t *__restrict__ up,
-    const uint16_t *__restrict__ bias, int M, int N, int K, int gelu, uint16_t *__restrict__ Y, RequantArgs rq)
+    const uint16_t *__restrict__ bias, int M, int N, int K, int gelu, uint16_t *__restrict__ Y, RequantArgs rq,
+    QKNormArgs qk)
 {
     __shared__ I4Smem sm;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -602,9 +750,14 @@ __global__ __launch_bounds__(I4_THREADS) void w4a4_int4_kernel(
             load_h8(h, mb + tm * 32 + l32, M, 16 * s + 8 * hk, hv);
             split_h(hv, hhi[tm][s], hlo[tm][s]);
         }
-    if constexpr (REQ) {
+    if constexpr (EPI == EPI_REQUANT) {
         requant_epilogue(acc, hhi, hlo, up, bias, M, N, gelu, rq, mb, nb, tn_, m0, wn, wm, tid, lane,
                          reinterpret_cast<float *>(&sm));
+        return;
+    }
+    if constexpr (EPI == EPI_QKNORM) {
+        static_assert(8 * OUT_TILE_BYTES + 8 * 64 * sizeof(float) <= sizeof(I4Smem), "staging and head sums fit");
+        qknorm_epilogue(acc, hhi, hlo, up, bias, M, N, qk, mb, nb, wave, lane, Y, reinterpret_cast<uint8_t *>(&sm));
         return;
     }
     uint8_t *tile = reinterpret_cast<uint8_t *>(&sm) + wave * OUT_TILE_BYTES;
@@ -1266,9 +1419,9 @@ hipError_t launch_w4a4_linear(const uint8_t *xq, const void *xscale, const float
     const int64_t rows = M > N ? M : N;
     if (prec == SVDQ_INT4) {
         const int tiles = ((N + I4_BN - 1) / I4_BN) * ((M + I4_BM - 1) / I4_BM);
-        hipLaunchKernelGGL(w4a4_int4_kernel<false>, dim3((unsigned)tiles), dim3(I4_THREADS), 0, stream, xq,
+        hipLaunchKernelGGL(w4a4_int4_kernel<EPI_STORE>, dim3((unsigned)tiles), dim3(I4_THREADS), 0, stream, xq,
                            (const float *)xscale, h, wq, (const float *)wscale, up, bias, M, N, K, gelu, Y,
-                           RequantArgs{});
+                           RequantArgs{}, QKNormArgs{});
     } else {
         // the LDS-DMA kernel takes whole 256-channel steps and 32-bit offsets
         if (K % 256 == 0 && rows * (K / 2) < ((int64_t)1 << 31)) {
@@ -1308,9 +1461,9 @@ hipError_t launch_w4a4_linear_requant(const uint8_t *xq, const void *xscale, con
     const RequantArgs rq{smooth2, down2, xq2, xscale2, work};
     if (prec == SVDQ_INT4) {
         const int tiles = tiles_n * ((M + I4_BM - 1) / I4_BM);
-        hipLaunchKernelGGL(w4a4_int4_kernel<true>, dim3((unsigned)tiles), dim3(I4_THREADS), 0, stream, xq,
+        hipLaunchKernelGGL(w4a4_int4_kernel<EPI_REQUANT>, dim3((unsigned)tiles), dim3(I4_THREADS), 0, stream, xq,
                            (const float *)xscale, h, wq, (const float *)wscale, up, bias, M, N, K, gelu,
-                           (uint16_t *)nullptr, rq);
+                           (uint16_t *)nullptr, rq, QKNormArgs{});
     } else {
         const int tiles = tiles_n * ((M + MXD_BM - 1) / MXD_BM);
         const int ncu = device_cu_count();
@@ -1323,6 +1476,19 @@ hipError_t launch_w4a4_linear_requant(const uint8_t *xq, const void *xscale, con
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(requant_h_reduce, dim3((unsigned)((M * 8 + 255) / 256)), dim3(256), 0, stream,
                        (const float *)work, tiles_n, M, h2);
+    return hipGetLastError();
+}
+
+hipError_t launch_w4a4_linear_qknorm(const uint8_t *xq, const float *xscale, const float *h, const uint8_t *wq,
+                                     const float *wscale, const uint16_t *up, const uint16_t *bias, int M, int N,
+                                     int K, const uint16_t *norm_q, const uint16_t *norm_k, float eps,
+                                     const float *rope_cos, const float *rope_sin, uint16_t *Y, hipStream_t stream)
+{
+    const int tiles = ((N + I4_BN - 1) / I4_BN) * ((M + I4_BM - 1) / I4_BM);
+    static_assert(I4_WN * 2 == 128 && I4_BN % 128 == 0, "a head is the tile of two neighbouring waves");
+    const QKNormArgs qk{norm_q, norm_k, rope_cos, rope_sin, N / 384, eps};
+    hipLaunchKernelGGL(w4a4_int4_kernel<EPI_QKNORM>, dim3((unsigned)tiles), dim3(I4_THREADS), 0, stream, xq, xscale,
+                       h, wq, wscale, up, bias, M, N, K, 0, Y, RequantArgs{}, qk);
     return hipGetLastError();
 }
 

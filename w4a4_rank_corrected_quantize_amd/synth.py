@@ -160,3 +160,32 @@ def make_layer(spec: LayerSpec, M: Optional[int] = None, K: Optional[int] = None
     out["bias"] = gen_bias(spec.config_id, spec.bias_stream, N, spec.bias_std)
     out["act_absmax"] = calibration_absmax(out["X"])
     return out
+
+
+# ------------------------------------------- Q/K norm weights and rotary angles
+
+def gen_qk_norm(config_id: int, stream: int) -> np.ndarray:
+    """bf16 RMS-norm weight of a 128-channel head, N(1, 0.1^2)."""
+    return f64_to_bf16_bits(rng_for(config_id, stream).normal(1.0, 0.1, size=(128,)))
+
+
+def gen_rope(M: int, text_tokens: Optional[int] = None, grid_w: int = 64,
+             axes_dim=(16, 56, 56), theta: float = 10000.0) -> tuple[np.ndarray, np.ndarray]:
+    """cos and sin [M][64] (fp32) of a FLUX-like 3-axis rotary embedding: the
+    first `text_tokens` tokens sit at position (0, 0, 0), the rest on a
+    grid_w-wide patch grid at (0, row, col); pair j of an axis of d channels
+    turns by position * theta^(-2j/d)."""
+    if text_tokens is None:
+        text_tokens = 512 if M == 4608 else M // 9
+    ids = np.zeros((M, 3), np.float64)
+    i = np.arange(M) - text_tokens
+    img = i >= 0
+    ids[img, 1] = i[img] // grid_w
+    ids[img, 2] = i[img] % grid_w
+    ang = []
+    for a, d in enumerate(axes_dim):
+        w = theta ** (-np.arange(0, d, 2, dtype=np.float64) / d)
+        ang.append(ids[:, a:a + 1] * w[None, :])
+    th = np.concatenate(ang, axis=1)
+    assert th.shape == (M, 64)
+    return np.cos(th).astype(np.float32), np.sin(th).astype(np.float32)

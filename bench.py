@@ -38,10 +38,10 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, 8 TB/s
 # only reported while the kernel source still hashes to the value it was
 # measured on; otherwise traffic is null.
 TRAFFIC = {
-    # FETCH_SIZE 72636 KiB / 0.50003 + WRITE_SIZE 110593 KiB / 1.00000 (per dispatch)
-    ("int4", "fc1"): {"source_sha": "6abc002afff30598", "bytes": 261997435},
-    # FETCH_SIZE 70905 KiB / 0.50003 + WRITE_SIZE 111109 KiB / 1.00000
-    ("mxfp4", "fc1"): {"source_sha": "6abc002afff30598", "bytes": 258982047},
+    # FETCH_SIZE 72778 KiB / 0.50003 + WRITE_SIZE 110610 KiB / 1.00000 (per dispatch)
+    ("int4", "fc1"): {"source_sha": "2c4f4356924ca34e", "bytes": 262305323},
+    # FETCH_SIZE 70922 KiB / 0.50003 + WRITE_SIZE 111107 KiB / 1.00000
+    ("mxfp4", "fc1"): {"source_sha": "2c4f4356924ca34e", "bytes": 259014531},
 }
 
 

@@ -70,9 +70,9 @@ extern "C" {
 typedef enum svdq_status {
     SVDQ_OK = 0,
     SVDQ_ERR_INVALID_ARG = -1,        /* NULL pointer, bad enum value, negative size */
-    SVDQ_ERR_SHAPE = -2,              /* K not a multiple of the group, N not a multiple of 8, ... */
+    SVDQ_ERR_SHAPE = -2,              /* a size not the multiple the call requires (K of the group, N of 8, ...) */
     SVDQ_ERR_MISALIGNED = -3,         /* a device pointer not 16-byte aligned */
-    SVDQ_ERR_UNSUPPORTED = -4,        /* rank other than 32 */
+    SVDQ_ERR_UNSUPPORTED = -4,        /* rank other than 32, or a precision / K the call does not support */
     SVDQ_ERR_UNSUPPORTED_DEVICE = -5, /* no HIP device, or the current device is not gfx950 */
     SVDQ_ERR_NONFINITE = -6,          /* non-finite weight or calibration statistic (pack) */
     SVDQ_ERR_HIP = -7                 /* a HIP runtime or launch failure */

@@ -78,9 +78,11 @@ extern "C" const char *svdq_status_string(svdq_status status)
     switch (status) {
     case SVDQ_OK: return "ok";
     case SVDQ_ERR_INVALID_ARG: return "invalid argument (NULL pointer, bad enum or negative size)";
-    case SVDQ_ERR_SHAPE: return "unsupported shape (K must be a multiple of the group size, N of 8)";
+    case SVDQ_ERR_SHAPE:
+        return "unsupported shape (a size is not the multiple the call requires: K of the group size, N of 8, ...)";
     case SVDQ_ERR_MISALIGNED: return "device pointer not 16-byte aligned";
-    case SVDQ_ERR_UNSUPPORTED: return "unsupported configuration (rank must be 32)";
+    case SVDQ_ERR_UNSUPPORTED:
+        return "unsupported configuration (rank other than 32, or a precision or K the call does not support)";
     case SVDQ_ERR_UNSUPPORTED_DEVICE: return "no HIP device, or the current device is not a gfx950 (MI355X)";
     case SVDQ_ERR_NONFINITE: return "non-finite weight, calibration statistic or smoothing factor";
     case SVDQ_ERR_HIP: return "HIP runtime or kernel launch failure";

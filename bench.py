@@ -218,6 +218,7 @@ def main():
     ops = 2.0 * M * N * K
     value = ops / (ms_per_step * 1e-3) / 1e12
     k2_tops = ops / (k2_ms * 1e-3) / 1e12
+    ref = library_reference(torch, M, N, K)
     peak = PEAK_INT8_TOPS if prec == svdq.INT4 else PEAK_FP4_TFLOPS
     k1_gbs = k1_bytes(M, K, r, prec) / (k1_ms * 1e-3) / 1e9
     k2_gbs = k2_bytes(M, N, K, r, prec, bias=L["bias"] is not None) / (k2_ms * 1e-3) / 1e9
@@ -280,10 +281,44 @@ def main():
                               "frac": round(k1_gbs / PEAK_HBM_GBS, 4),
                               "algorithmic_bytes": k1_bytes(M, K, r, prec)},
         "linear_kernel_GBs": round(k2_gbs, 1),
+        "matrix_core_reference": ref,
         "host_pack_s": round(pack_s, 2),
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
+
+
+def library_reference(torch, M, N, K, reps=20):
+    """Dense GEMMs of the same shape through torch (hipBLASLt): fp8 e4m3 with
+    per-tensor scales and bf16.  They are what the matrix cores reach here on
+    a plain contraction: a measured ceiling for the same M, N, K, next to the
+    nominal peak.  None where torch lacks the op."""
+    out = {"kind": "torch._scaled_mm fp8 e4m3 (per-tensor scales) and torch.matmul bf16, "
+                   f"{M} x {K} -> {N}, no quantization groups, no epilogue"}
+    a = torch.randn(M, K, device="cuda")
+    b = torch.randn(N, K, device="cuda")
+
+    def rate(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return round(2.0 * M * N * K / (e0.elapsed_time(e1) / reps * 1e-3) / 1e12, 1)
+    try:
+        a8, b8 = a.to(torch.float8_e4m3fn), b.to(torch.float8_e4m3fn)
+        one = torch.tensor(1.0, device="cuda")
+        out["fp8_tflops"] = rate(lambda: torch._scaled_mm(a8, b8.t(), scale_a=one, scale_b=one,
+                                                          out_dtype=torch.bfloat16))
+    except Exception:
+        out["fp8_tflops"] = None
+    a16, b16 = a.to(torch.bfloat16), b.to(torch.bfloat16)
+    out["bf16_tflops"] = rate(lambda: a16 @ b16.t())
+    return out
 
 
 def awq_bytes(M, N, K, bias=True):

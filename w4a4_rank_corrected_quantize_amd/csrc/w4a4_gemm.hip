@@ -200,6 +200,27 @@ __device__ __forceinline__ void widen_fp8(uint4 p, uint4 &lo, uint4 &hi)
     hi = (uint4){o[4], o[5], o[6], o[7]};
 }
 
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+__device__ __forceinline__ uint32_t lds_offset(const void *p)
+{
+    return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const lds_u8 *)p);
+}
+
+// One LDS-DMA load per lane: 16 (or 4) bytes from sbase + voff to LDS
+// lds + 16 * lane (4 * lane).  M0 is saved and restored around it.
+__device__ __forceinline__ void dma_b128(uint32_t lds, uint32_t voff, const void *sbase)
+{
+    uint32_t keep;
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %2, %3\n\ts_mov_b32 m0, %0"
+                 : "=&s"(keep) : "s"(lds), "v"(voff), "s"(sbase) : "memory");
+}
+__device__ __forceinline__ void dma_b32(uint32_t lds, uint32_t voff, const void *sbase)
+{
+    uint32_t keep;
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %2, %3\n\ts_mov_b32 m0, %0"
+                 : "=&s"(keep) : "s"(lds), "v"(voff), "s"(sbase) : "memory");
+}
+
 // Scale operands of the outer-product instruction (A = weights, B = tokens):
 // row n of A holds (sw_hi, sw_lo, sw_hi) at k = 0..2 and again at k = 8..10,
 // column m of B holds (sx_hi, sx_hi, sx_lo) at the same k; every other k is
@@ -223,6 +244,7 @@ struct __attribute__((aligned(16))) I4Smem {
     uint8_t x[2][I4_BM * I4_ROWB];
     uint2 sw[2][2][I4_BN];     // [buf][group in step][n], scale_operand_w(sw * 2^17)
     uint2 sx[2][2][I4_BM];     // [buf][group in step][m], scale_operand_x(sx)
+    float sp[2][(I4_BN + I4_BM) * 8];   // scale panels: 8 groups (4 steps) of the W rows, then the X rows
 };
 
 // The next layer's activation step, computed from this layer's output in the
@@ -576,6 +598,11 @@ __device__ __forceinline__ void qknorm_epilogue(const f32x16 (&acc)[I4_TN][I4_TM
     flush_tile(tile, Y, mb, nb, M, N, lane);
 }
 
+// Scale panels hold 8 groups of every W and X row of the block tile, a row of
+// 8 floats per matrix row; group g of row r sits at position g ^ sp_swz(r), so
+// that the 8-byte reads of 32 consecutive rows fall in distinct banks.
+__device__ __forceinline__ int sp_swz(int r) { return 2 * ((r >> 3) & 3); }
+
 template <int EPI>
 __global__ __launch_bounds__(I4_THREADS) void w4a4_int4_kernel(
     const uint8_t *__restrict__ xq, const float *__restrict__ xscale, const float *__restrict__ h,
@@ -600,32 +627,57 @@ __global__ __launch_bounds__(I4_THREADS) void w4a4_int4_kernel(
     // chunk t (all with segment t & 3).  Loads are unconditional: rows past
     // N / M are clamped to the last row (their outputs are never stored), and
     // for an odd G the missing second group of the last step re-reads the
-    // row's first chunk (the compute loop never reads it), so every path has
-    // the same number of loads in flight.
+    // step's first group (the compute loop never reads it), so every path has
+    // the same number of loads in flight and none leaves the row.
     constexpr int WCH = I4_BN * 4, XCH = I4_BM * 4;
     static_assert(WCH == 2 * I4_THREADS && XCH == I4_THREADS, "loader shape");
     const int lseg = tid & 3, lr = tid >> 2;
     const uint8_t *__restrict__ pw0 = wq + (size_t)min(n0 + lr, N - 1) * KB + lseg * 16;
     const uint8_t *__restrict__ pw1 = wq + (size_t)min(n0 + lr + I4_BN / 2, N - 1) * KB + lseg * 16;
     const uint8_t *__restrict__ px0 = xq + (size_t)min(m0 + lr, M - 1) * KB + lseg * 16;
-    // scales: threads [0, BN) -> sw row, [BN, BN + BM) -> sx row, others idle
+    // Scales: threads [0, BN) turn the sw of W row t, threads [BN, BN + BM)
+    // the sx of X row t - BN into the step's scale operands; the others idle.
+    // The scales reach LDS as panels of 8 groups (4 steps) per row, moved by
+    // LDS-DMA: 48 dword loads of 64 lanes per panel (0..31 the W rows, 32..47
+    // the X rows), wave w issuing loads 6 w .. 6 w + 5.  Eight lanes cover one
+    // row's 32 contiguous bytes, so a load touches 8 rows instead of the 64
+    // that per-thread scale loads would.  Groups past G re-read group G - 1.
     const bool sc_w = tid < I4_BN, sc_x = tid >= I4_BN && tid < I4_BN + I4_BM;
-    const float *__restrict__ ps = sc_w ? wscale + (size_t)min(n0 + tid, N - 1) * G
-                                        : xscale + (size_t)min(m0 + (sc_x ? tid - I4_BN : 0), M - 1) * G;
-    const uint4 z4 = {0u, 0u, 0u, 0u};
+    const uint32_t sp_lds0 = lds_offset(&sm.sp[0][0]);
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);      // DMA bases and LDS offsets are uniform
+    const float *__restrict__ wsb = wscale + (size_t)n0 * G;      // the tile's first rows
+    const float *__restrict__ xsb = xscale + (size_t)m0 * G;
+    uint32_t sp_off[6];                                          // byte offset of the lane's (row, group 0..7)
+#pragma unroll
+    for (int j = 0; j < 6; ++j) {
+        const int i = 6 * wave + j, d = 64 * i + lane, r = d >> 3;
+        const int g = (d & 7) ^ sp_swz(r);
+        const int rr = r < I4_BN ? min(r, N - 1 - n0) : min(r - I4_BN, M - 1 - m0);
+        sp_off[j] = (uint32_t)(rr * G + g) * 4u;
+    }
+    auto sp_issue = [&](int p) {
+        const int g0 = 8 * p;
+#pragma unroll
+        for (int j = 0; j < 6; ++j) {
+            const int i = 6 * wave_u + j;
+            const int d = 64 * i + lane, r = d >> 3, g = (d & 7) ^ sp_swz(r);
+            // + 4 g0 bytes, or the row's last group when g0 + g is past G
+            const uint32_t add = g0 + g < G ? 4u * (uint32_t)g0 : 4u * (uint32_t)(G - 1 - g);
+            dma_b32(sp_lds0 + (uint32_t)(p & 1) * (uint32_t)sizeof(sm.sp[0]) + 256u * i, sp_off[j] + add,
+                    i < 32 ? wsb : xsb);
+        }
+    };
 
     // Two register sets: the global loads of step st + 2 are issued at the
     // start of step st and written to LDS at the end of step st + 1.
     uint4 rgA0, rgA1, rgA2, rgB0, rgB1, rgB2;
-    float rsA0, rsA1, rsB0, rsB1;
+
 #define I4_GLOAD(st, R)                                                                \
     do {                                                                               \
-        const int koff_ = ((st) * 64 + lseg * 16 < KB) ? (st) * 64 : 0;                \
+        const int koff_ = ((st) * 64 + lseg * 16 < KB) ? (st) * 64 : (st) * 64 - 32;   \
         rg##R##0 = *reinterpret_cast<const uint4 *>(pw0 + koff_);                      \
         rg##R##1 = *reinterpret_cast<const uint4 *>(pw1 + koff_);                      \
         rg##R##2 = *reinterpret_cast<const uint4 *>(px0 + koff_);                      \
-        rs##R##0 = ps[min(2 * (st), G - 1)];                                           \
-        rs##R##1 = ps[min(2 * (st) + 1, G - 1)];                                       \
     } while (0)
     // When G is odd, the second half of the last step holds codes that the
     // compute loop never reads.
@@ -644,12 +696,17 @@ __global__ __launch_bounds__(I4_THREADS) void w4a4_int4_kernel(
         d_ = sm.x[buf] + lr * I4_ROWB + lseg * 32;                                     \
         *reinterpret_cast<uint4 *>(d_) = a_;                                           \
         *reinterpret_cast<uint4 *>(d_ + 16) = b_;                                      \
-        if (sc_w) {                                                                    \
-            sm.sw[buf][0][tid] = scale_operand_w(rs##R##0 * kTwo17);                   \
-            sm.sw[buf][1][tid] = scale_operand_w(rs##R##1 * kTwo17);                   \
-        } else if (sc_x) {                                                             \
-            sm.sx[buf][0][tid - I4_BN] = scale_operand_x(rs##R##0);                    \
-            sm.sx[buf][1][tid - I4_BN] = scale_operand_x(rs##R##1);                    \
+        if (sc_w || sc_x) {                                                            \
+            const int r_ = tid, j_ = (st) & 3;                                         \
+            const float2 v_ = *reinterpret_cast<const float2 *>(                       \
+                &sm.sp[((st) >> 2) & 1][8 * r_ + ((2 * j_) ^ sp_swz(r_))]);            \
+            if (sc_w) {                                                                \
+                sm.sw[buf][0][tid] = scale_operand_w(v_.x * kTwo17);                   \
+                sm.sw[buf][1][tid] = scale_operand_w(v_.y * kTwo17);                   \
+            } else {                                                                   \
+                sm.sx[buf][0][tid - I4_BN] = scale_operand_x(v_.x);                    \
+                sm.sx[buf][1][tid - I4_BN] = scale_operand_x(v_.y);                    \
+            }                                                                          \
         }                                                                              \
     } while (0)
 
@@ -717,7 +774,10 @@ __global__ __launch_bounds__(I4_THREADS) void w4a4_int4_kernel(
     };
 
     if (steps > 0) {
+        sp_issue(0);
         I4_GLOAD(0, A);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
         I4_LSTORE(0, 0, A);
         I4_GLOAD(min(1, steps - 1), B);
     }
@@ -725,8 +785,14 @@ __global__ __launch_bounds__(I4_THREADS) void w4a4_int4_kernel(
     for (int st = 0; st < steps; st += 2) {
         // even step: LDS buffer 0, registers A are free for step st + 2
         I4_GLOAD(min(st + 2, steps - 1), A);     // unconditional: same load count on every path
+        // the panel of steps st + 4 .. st + 7 goes to the buffer whose last reader
+        // was the staging of step st - 1 (before the previous barrier)
+        if ((st & 3) == 0 && st + 4 < steps) sp_issue((st >> 2) + 1);
         compute_step(st, 0);
         if (st + 1 < steps) I4_LSTORE(st + 1, 1, B);
+        // a panel issued at step st - 2 is read by the staging of step st + 2:
+        // every load older than the last step's register loads is done
+        if ((st & 3) == 2) asm volatile("s_waitcnt vmcnt(3)" ::: "memory");
         __syncthreads();
         if (st + 1 >= steps) break;
         // odd step: LDS buffer 1, registers B are free for step st + 3
@@ -1069,27 +1135,6 @@ struct __attribute__((aligned(16))) MXDStage {
     uint32_t ex[2 * MXD_BM];
 };
 static_assert(8 * OUT_TILE_BYTES <= sizeof(MXDStage), "output staging fits in one stage");
-
-typedef __attribute__((address_space(3))) uint8_t lds_u8;
-__device__ __forceinline__ uint32_t lds_offset(const void *p)
-{
-    return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const lds_u8 *)p);
-}
-
-// One LDS-DMA load per lane: 16 (or 4) bytes from sbase + voff to LDS
-// lds + 16 * lane (4 * lane).  M0 is saved and restored around it.
-__device__ __forceinline__ void dma_b128(uint32_t lds, uint32_t voff, const void *sbase)
-{
-    uint32_t keep;
-    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %2, %3\n\ts_mov_b32 m0, %0"
-                 : "=&s"(keep) : "s"(lds), "v"(voff), "s"(sbase) : "memory");
-}
-__device__ __forceinline__ void dma_b32(uint32_t lds, uint32_t voff, const void *sbase)
-{
-    uint32_t keep;
-    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %2, %3\n\ts_mov_b32 m0, %0"
-                 : "=&s"(keep) : "s"(lds), "v"(voff), "s"(sbase) : "memory");
-}
 
 // Epilogue of the requantizing MXFP4 kernel for one wave tile (128 channels,
 // four 32-channel blocks, x 64 tokens): as requant_epilogue, with E8M0 block

@@ -39,9 +39,9 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, 8 TB/s
 # measured on; otherwise traffic is null.
 TRAFFIC = {
     # FETCH_SIZE 72778 KiB / 0.50003 + WRITE_SIZE 110610 KiB / 1.00000 (per dispatch)
-    ("int4", "fc1"): {"source_sha": "2c4f4356924ca34e", "bytes": 262305323},
+    ("int4", "fc1"): {"source_sha": "019e810849c9b972", "bytes": 262995968},
     # FETCH_SIZE 70922 KiB / 0.50003 + WRITE_SIZE 111107 KiB / 1.00000
-    ("mxfp4", "fc1"): {"source_sha": "2c4f4356924ca34e", "bytes": 259014531},
+    ("mxfp4", "fc1"): {"source_sha": "019e810849c9b972", "bytes": 259108864},
 }
 
 

@@ -303,12 +303,16 @@ def test_linear_many_tiles_ragged(prec, K):
     _y_check(Y[torch.from_numpy(rows).long().cuda()], y_ref, "many tiles")
 
 
-@pytest.mark.parametrize("prec", PRECS)
-def test_full_size_dit_block(prec):
-    """QKV and the fc1 -> fc2 MLP pair at 4608 tokens, hidden 3072: codes,
-    scales and h of every row bit-exact / bounded; outputs on sampled rows."""
-    _say(f"full-size DiT block prec={prec}")
-    names = ("qkv", "fc1", "fc2") if prec == svdq.INT4 else ("mx_qkv", "mx_fc1", "mx_fc2")
+@pytest.mark.parametrize("prec,tokens", [(svdq.INT4, 4608), (svdq.MXFP4, 4608), (svdq.MXFP4, 1024)])
+def test_full_size_dit_block(prec, tokens):
+    """QKV and the fc1 -> fc2 MLP pair at 4608 tokens (1024 for the MXFP4
+    512 x 512 image), hidden 3072: codes, scales and h of every row
+    bit-exact / bounded; outputs on sampled rows."""
+    _say(f"full-size DiT block prec={prec} tokens={tokens}")
+    if prec == svdq.INT4:
+        names = ("qkv", "fc1", "fc2")
+    else:
+        names = ("mx_qkv", "mx_fc1", "mx_fc2") if tokens == 4608 else ("mx1k_qkv", "mx1k_fc1", "mx1k_fc2")
     q = synth.make_layer(synth.SPECS[names[0]])
     pq = svdq.pack_weights(q["W"], q["act_absmax"], prec=prec)
     xq, xs, h, oh = _quant_act_check(q["X"], pq["smooth"], pq["down"], prec)

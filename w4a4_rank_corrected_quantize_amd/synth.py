@@ -90,6 +90,13 @@ SPECS = {
                         gelu=True, mx=True, w_stream=5, bias_stream=6),
     "mx_fc2": LayerSpec("mx_fc2", 4, 4608, 12288, 3072, "external", 0, 1.0,
                         mx=True, w_stream=7, bias_stream=8),
+    # the same three MXFP4 linears for a 512 x 512 image: 1024 image tokens,
+    # text tokens left out
+    "mx1k_qkv": LayerSpec("mx1k_qkv", 7, 1024, 3072, 9216, "student_t4", 16, 50.0, mx=True),
+    "mx1k_fc1": LayerSpec("mx1k_fc1", 7, 1024, 3072, 12288, "student_t4", 16, 50.0,
+                          gelu=True, mx=True, w_stream=5, bias_stream=6),
+    "mx1k_fc2": LayerSpec("mx1k_fc2", 7, 1024, 12288, 3072, "external", 0, 1.0,
+                          mx=True, w_stream=7, bias_stream=8),
     # weight-only AWQ W4A16 modulation layer: one conditioning vector per
     # image, 3072 -> 6 x 3072 (shift, scale and gate of two norms)
     "awq_mod": LayerSpec("awq_mod", 6, 1, 3072, 18432, "normal", 0, 1.0),

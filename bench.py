@@ -79,8 +79,11 @@ def k2_bytes(M, N, K, r, prec, bias=True):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    # the clock settles only after ~30 ms of back-to-back launches (the
+    # linear's time falls from ~410 to ~320 us over its first ~90 launches),
+    # so the default warm-up covers that ramp
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--prec", choices=["int4", "mxfp4"], default="int4")
     ap.add_argument("--layer", choices=["fc1", "qkv", "fc2", "mlp", "awq", "qkvnorm"], default="fc1",
                     help="fc1 is the headline workload; fc2 takes fc1's output (computed on the GPU); "
@@ -96,8 +99,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle sample time")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build runs the layer on a single MI355X "
-              "and has no multi-GPU path (see the sharding note in DESIGN.md).", file=sys.stderr)
+        print("bench.py measures one GPU only: the layer runs on a single MI355X and there is "
+              "no multi-GPU path; run it with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -231,7 +234,9 @@ def main():
     if not args.no_cpu_baseline:
         from oracle import oracle as O
         print("[bench] timing the CPU oracle on a row sample", file=sys.stderr, flush=True)
-        rows = 8
+        # a 64-row probe sizes the sample (a smaller one is dominated by the
+        # per-call cost and undersizes it)
+        rows = min(M, 64)
         t0 = time.time()
         xq, xs, h = O.quant_act(L["X"][:rows], p["smooth"], p["down"], prec)
         O.linear(xq, xs, h, p["wq"], p["wscale"], p["up"], L["bias"], prec, gelu=spec.gelu)

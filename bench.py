@@ -353,12 +353,43 @@ def awq_main(args, torch, svdq, synth):
     for i in range(args.warmup):
         step(sets[i % nsets])
     torch.cuda.synchronize()
-    print(f"[bench] warmup done ({args.warmup} steps); timing {args.steps} steps", file=sys.stderr, flush=True)
+    # A 12 us kernel outruns the host's launches (~25 us each through the
+    # binding), so the K timed steps are captured once in a HIP graph and
+    # replayed: the timed region then holds the GPU's work, not host gaps.
+    # Each replay's outputs are checked against an eager step first.
+    launch = "hip graph"
+    try:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(args.steps):
+                step(sets[i % nsets])
+        torch.cuda.synchronize()
+        ref = []
+        for b in sets[:min(nsets, args.steps)]:
+            step(b)
+            ref.append(b["Y"].clone())
+        torch.cuda.synchronize()
+        for _ in range(3):
+            for b in sets:
+                b["Y"].zero_()
+            graph.replay()
+            torch.cuda.synchronize()
+            for b, r in zip(sets, ref):
+                if not torch.equal(b["Y"], r):
+                    raise RuntimeError("graph replay differs from the eager launch")
+    except Exception as e:      # report, and time the launches eagerly instead
+        print(f"[bench] graph capture not used ({e}); timing eager launches", file=sys.stderr, flush=True)
+        graph, launch = None, "eager"
+    print(f"[bench] warmup done ({args.warmup} steps); timing {args.steps} steps ({launch})", file=sys.stderr,
+          flush=True)
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record()
-    for i in range(args.steps):
-        step(sets[i % nsets])
+    if graph is not None:
+        graph.replay()
+    else:
+        for i in range(args.steps):
+            step(sets[i % nsets])
     stop.record()
     torch.cuda.synchronize()
     ms = start.elapsed_time(stop) / args.steps
@@ -390,7 +421,7 @@ def awq_main(args, torch, svdq, synth):
         "config": {"workload": f"{spec.name}: {M} x {K} -> {N}, INT4 g64 weight-only, bias; "
                                "step = svdq_awq_w4a16_linear",
                    "M": M, "K": K, "N": N, "buffer_sets": nsets,
-                   "weights_MB_per_set": round((wq.nbytes + ws.nbytes) / 1e6, 1)},
+                   "weights_MB_per_set": round((wq.nbytes + ws.nbytes) / 1e6, 1), "launch": launch},
         "roofline": {"bound": "hbm", "kernel": "svdq_awq_w4a16_linear", "achieved": round(gbs, 1),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
                      "traffic": None, "avg_ms": round(ms, 5), "algorithmic_bytes": nbytes},

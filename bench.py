@@ -95,6 +95,8 @@ def main():
     ap.add_argument("--sets", type=int, default=0,
                     help="rotating buffer sets (default 3; 12 for awq, whose 32 MB of weights per set "
                          "would otherwise stay in the 256 MB last-level cache)")
+    ap.add_argument("--tokens", type=int, choices=[4608, 1024], default=4608,
+                    help="1024: the MXFP4 linears of a 512 x 512 image (--prec mxfp4, fc1 / qkv / fc2)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle sample time")
     args = ap.parse_args()
@@ -128,12 +130,16 @@ def main():
     if qkvnorm and prec != svdq.INT4:
         print("--layer qkvnorm is INT4 only", file=sys.stderr)
         sys.exit(2)
-    spec = synth.SPECS[("" if prec == svdq.INT4 else "mx_") + ("qkv" if qkvnorm else args.layer)]
+    if args.tokens != 4608 and (prec != svdq.MXFP4 or args.layer not in ("fc1", "qkv", "fc2")):
+        print("--tokens 1024 is the MXFP4 fc1 / qkv / fc2 workload", file=sys.stderr)
+        sys.exit(2)
+    pre = "" if prec == svdq.INT4 else ("mx_" if args.tokens == 4608 else "mx1k_")
+    spec = synth.SPECS[pre + ("qkv" if qkvnorm else args.layer)]
     M, K, N, r = spec.M, spec.K, spec.N, svdq.RANK
     X_bits = None
     if args.layer == "fc2":
         # fc2's input is fc1's bf16 output: run fc1 once on the GPU to make it
-        f1 = synth.SPECS[("" if prec == svdq.INT4 else "mx_") + "fc1"]
+        f1 = synth.SPECS[pre + "fc1"]
         print(f"[bench] making fc2's input with {f1.name} on the GPU", file=sys.stderr, flush=True)
         L1 = synth.make_layer(f1)
         d1 = svdq.to_device(svdq.pack_weights(L1["W"], L1["act_absmax"], prec=prec))

@@ -39,8 +39,8 @@
  *   - Ownership: the caller allocates and frees every buffer.  No call
  *     allocates device memory or keeps a pointer after it returns.
  *   - Device calls (svdq_quantize_act, svdq_w4a4_linear,
- *     svdq_w4a4_linear_requant, svdq_w4a4_linear_qkv_norm_rope,
- *     svdq_awq_w4a16_linear) take device
+ *     svdq_w4a4_linear_requant, svdq_w4a4_linear_splitk,
+ *     svdq_w4a4_linear_qkv_norm_rope, svdq_awq_w4a16_linear) take device
  *     pointers and a hipStream_t (as void*, NULL = the null stream); they
  *     validate everything first, enqueue kernels on `stream` and return
  *     without synchronizing.  On any error nothing has been enqueued or
@@ -187,6 +187,41 @@ svdq_status svdq_w4a4_linear(const uint8_t *xq, const void *xscale, const float 
                              const uint8_t *wq, const void *wscale, const uint16_t *up,
                              const uint16_t *bias, int M, int N, int K, int rank,
                              svdq_precision prec, svdq_epilogue epi, uint16_t *Y, void *stream);
+
+/*
+ * svdq_w4a4_linear_splitk_workspace_bytes -- device workspace that
+ * svdq_w4a4_linear_splitk needs on the current device: S * M * N fp32
+ * partial sums when the MXFP4 product is split into S slices of K, else 0
+ * (INT4, shapes whose tiles already fill half the chip, K % 256 != 0, M or
+ * N <= 0, invalid arguments, or no gfx950 device).  It depends on the
+ * device's compute-unit count.
+ */
+size_t svdq_w4a4_linear_splitk_workspace_bytes(int M, int N, int K, svdq_precision prec);
+
+/*
+ * svdq_w4a4_linear_splitk -- svdq_w4a4_linear for skinny shapes (few
+ * tokens, long K, such as the MLP's second linear of a 512 x 512 image:
+ * 1024 x 12288 -> 3072), where the product's tiles would leave most of the
+ * chip idle.  Same arguments, arithmetic and output as svdq_w4a4_linear,
+ * plus:
+ *   work, work_bytes  device scratch of at least
+ *                     svdq_w4a4_linear_splitk_workspace_bytes(M, N, K,
+ *                     prec) bytes, 16-byte aligned (may be NULL when that
+ *                     is 0); overwritten, caller-owned
+ * With a split, each of S work items per tile sums its K slice into the
+ * workspace in fp32, and a second kernel adds the S slices in slice order
+ * (so the result is deterministic) before the epilogue; its low-rank term
+ * is the fp32 dot product of h with the bf16 up row.  Sums in a different
+ * order than svdq_w4a4_linear's, so outputs may differ from it in the last
+ * bf16 place.  Without a split it is svdq_w4a4_linear.  Errors as for
+ * svdq_w4a4_linear, and SVDQ_ERR_INVALID_ARG for a NULL or too small work
+ * (checked after the device, whose compute units set the size).
+ */
+svdq_status svdq_w4a4_linear_splitk(const uint8_t *xq, const void *xscale, const float *h,
+                                    const uint8_t *wq, const void *wscale, const uint16_t *up,
+                                    const uint16_t *bias, int M, int N, int K, int rank,
+                                    svdq_precision prec, svdq_epilogue epi, uint16_t *Y, void *work,
+                                    size_t work_bytes, void *stream);
 
 /*
  * svdq_requant_workspace_bytes -- device workspace that

@@ -144,6 +144,35 @@ def test_awq_validation():
         assert L.svdq_awq_w4a16_linear(None, p, p, None, 0, N, K, None, None) == -5   # empty: still checks the device
 
 
+def test_splitk_validation():
+    """The split-K linear: argument errors before the device check; no
+    workspace is asked for without a device or for shapes it does not split."""
+    L = svdq.lib()
+    _, p = _host(1 << 16)
+    _, q = _host(1 << 16, offset=4)
+
+    def call(**kw):
+        a = dict(xq=p, xs=p, h=p, wq=p, ws=p, up=p, bias=None, M=16, N=64, K=2048, r=32, prec=svdq.MXFP4, epi=0,
+                 Y=p, work=p, wb=1 << 16)
+        a.update(kw)
+        return L.svdq_w4a4_linear_splitk(a["xq"], a["xs"], a["h"], a["wq"], a["ws"], a["up"], a["bias"], a["M"],
+                                         a["N"], a["K"], a["r"], a["prec"], a["epi"], a["Y"], a["work"], a["wb"],
+                                         None)
+    assert call(N=12) == -2
+    assert call(K=2040) == -2
+    assert call(r=16) == -4
+    assert call(epi=3) == -1
+    assert call(Y=None) == -1
+    assert call(work=q) == -3
+    assert call(Y=q) == -3
+    assert L.svdq_w4a4_linear_splitk_workspace_bytes(16, 64, 2048, svdq.INT4) == 0
+    assert L.svdq_w4a4_linear_splitk_workspace_bytes(0, 64, 2048, svdq.MXFP4) == 0
+    assert L.svdq_w4a4_linear_splitk_workspace_bytes(16, 64, 2040, svdq.MXFP4) == 0
+    if not _has_gpu():
+        assert call() == -5
+        assert L.svdq_w4a4_linear_splitk_workspace_bytes(16, 64, 2048, svdq.MXFP4) == 0
+
+
 def _has_gpu():
     try:
         import torch

@@ -192,6 +192,72 @@ def test_linear_synthetic(prec, M, K, N, bias, gelu):
     _y_check(Y, y_ref, f"M={M} K={K} N={N}")
 
 
+@pytest.mark.parametrize("M,K,N,gelu", [
+    (130, 2048, 264, True),      # 2 tiles, 8 steps: 2 slices
+    (300, 4096, 520, False),     # 6 tiles: 4 slices of 4 steps
+    (1, 3072, 64, True),         # one token: 3 slices of 4 steps
+    (257, 3328, 40, False),      # 13 steps: slices of 5, 5 and 3
+])
+def test_linear_splitk_synthetic(M, K, N, gelu):
+    """The split-K MXFP4 linear: every output against the oracle (the unsplit
+    call sums in another order, so the two may differ in low bf16 places);
+    the workspace is used (S > 1) and its stale contents do not matter."""
+    prec = svdq.MXFP4
+    _say(f"linear split-K M={M} K={K} N={N} gelu={gelu}")
+    need = svdq.linear_splitk_workspace_bytes(M, N, K, prec)
+    assert need > 0 and need % (4 * M * N) == 0 and need // (4 * M * N) >= 2
+    L, p = _layer("qkv", M, K, N, prec)
+    xq, xs, h, oh = _quant_act_check(L["X"], p["smooth"], p["down"], prec)
+    epi = svdq.EPI_GELU_TANH if gelu else svdq.EPI_NONE
+    args = (xq, xs, h, _t(p["wq"]), _t(p["wscale"]), _t(p["up"]), _t(L["bias"]), prec, epi)
+    work = torch.full((need // 4,), float("nan"), dtype=torch.float32, device="cuda")   # stale contents
+    Ys = svdq.w4a4_linear_splitk(*args, work=work)
+    Ys2 = svdq.w4a4_linear_splitk(*args, work=work)
+    Y = svdq.w4a4_linear(*args)
+    torch.cuda.synchronize()
+    assert torch.equal(Ys, Ys2), "split-K result not deterministic"
+    y_ref = O.linear(_np(xq), _np(xs), oh, p["wq"], p["wscale"], p["up"], L["bias"], prec, gelu=gelu)
+    _y_check(Ys, y_ref, f"split-K M={M} K={K} N={N}")
+    _y_check(Y, y_ref, f"unsplit M={M} K={K} N={N}")
+
+
+def test_linear_splitk_passthrough():
+    """Shapes that are not split (INT4; tiles that fill the chip; K % 256)
+    need no workspace and give exactly svdq_w4a4_linear's output."""
+    _say("linear split-K pass-through")
+    for prec, M, K, N in [(svdq.INT4, 130, 2048, 264), (svdq.MXFP4, 2000, 512, 9000), (svdq.MXFP4, 50, 2080, 40)]:
+        assert svdq.linear_splitk_workspace_bytes(M, N, K, prec) == 0
+        L, p = _layer("qkv", M, K, N, prec)
+        xq, xs, h = svdq.quantize_act(_t(L["X"]), _t(p["smooth"]), _t(p["down"]), prec)
+        args = (xq, xs, h, _t(p["wq"]), _t(p["wscale"]), _t(p["up"]), _t(L["bias"]), prec, svdq.EPI_GELU_TANH)
+        Ys = svdq.w4a4_linear_splitk(*args)
+        Y = svdq.w4a4_linear(*args)
+        torch.cuda.synchronize()
+        assert torch.equal(Ys, Y), (prec, M, K, N)
+
+
+def test_linear_splitk_full_size_fc2_1024():
+    """The MXFP4 fc2 of a 512 x 512 image (1024 x 12288 -> 3072, fc1's GELU
+    output re-quantized): sampled rows against the oracle."""
+    _say("linear split-K 1024 x 12288 -> 3072")
+    prec = svdq.MXFP4
+    f1 = synth.make_layer(synth.SPECS["mx1k_fc1"])
+    p1 = svdq.pack_weights(f1["W"], f1["act_absmax"], prec=prec)
+    xq, xs, h = svdq.quantize_act(_t(f1["X"]), _t(p1["smooth"]), _t(p1["down"]), prec)
+    Y1 = svdq.w4a4_linear(xq, xs, h, _t(p1["wq"]), _t(p1["wscale"]), _t(p1["up"]), _t(f1["bias"]), prec,
+                          svdq.EPI_GELU_TANH)
+    torch.cuda.synchronize()
+    f2 = synth.make_layer(synth.SPECS["mx1k_fc2"], X_bits=_np(Y1))
+    p2 = svdq.pack_weights(f2["W"], f2["act_absmax"], prec=prec)
+    xq, xs, h, oh = _quant_act_check(_np(Y1), p2["smooth"], p2["down"], prec)
+    assert svdq.linear_splitk_workspace_bytes(1024, 3072, 12288, prec) > 0
+    Y2 = svdq.w4a4_linear_splitk(xq, xs, h, _t(p2["wq"]), _t(p2["wscale"]), _t(p2["up"]), _t(f2["bias"]), prec)
+    torch.cuda.synchronize()
+    rows = _rows(1024, 32, seed=13)
+    y_ref = O.linear(_np(xq), _np(xs), oh, p2["wq"], p2["wscale"], p2["up"], f2["bias"], prec, rows=rows)
+    _y_check(Y2[torch.from_numpy(rows).long().cuda()], y_ref, "split-K fc2 1024")
+
+
 @pytest.mark.parametrize("prec", PRECS)
 def test_linear_invariants(prec):
     """up = 0 => the 4-bit product alone; residual codes 0 => the low-rank

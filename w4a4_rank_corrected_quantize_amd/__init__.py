@@ -46,7 +46,7 @@ STATUS = {
 EXPORTS = ("svdq_status_string", "svdq_version", "svdq_check_device", "svdq_pack_weights",
            "svdq_pack_residual", "svdq_quantize_act", "svdq_w4a4_linear", "svdq_requant_workspace_bytes",
            "svdq_w4a4_linear_requant", "svdq_w4a4_linear_qkv_norm_rope", "svdq_awq_pack_weights",
-           "svdq_awq_w4a16_linear")
+           "svdq_awq_w4a16_linear", "svdq_w4a4_linear_splitk_workspace_bytes", "svdq_w4a4_linear_splitk")
 
 
 class SvdqError(RuntimeError):
@@ -81,6 +81,10 @@ def lib():
         L.svdq_quantize_act.argtypes = [P, I, I, P, P, I, I, P, P, P, P]
         L.svdq_w4a4_linear.restype = I
         L.svdq_w4a4_linear.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, P, P]
+        L.svdq_w4a4_linear_splitk_workspace_bytes.restype = ctypes.c_size_t
+        L.svdq_w4a4_linear_splitk_workspace_bytes.argtypes = [I, I, I, I]
+        L.svdq_w4a4_linear_splitk.restype = I
+        L.svdq_w4a4_linear_splitk.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, P, P, ctypes.c_size_t, P]
         L.svdq_requant_workspace_bytes.restype = ctypes.c_size_t
         L.svdq_requant_workspace_bytes.argtypes = [I, I, I, I]
         L.svdq_w4a4_linear_requant.restype = I
@@ -221,6 +225,39 @@ def w4a4_linear(xq, xscale, h, wq, wscale, up, bias, prec: int = INT4, epi: int 
         _dev(wscale, (torch.float32, torch.uint8), "wscale"), _dev(up, (torch.bfloat16, torch.int16), "up"),
         pbias, M, N, K, r, prec, epi, _dev(Y, (torch.bfloat16, torch.int16), "Y"), _stream(stream))
     _check(st, "svdq_w4a4_linear")
+    return Y
+
+
+def linear_splitk_workspace_bytes(M: int, N: int, K: int, prec: int = MXFP4) -> int:
+    """Device scratch bytes that w4a4_linear_splitk needs on the current
+    device (0 when the shape is not split)."""
+    return int(lib().svdq_w4a4_linear_splitk_workspace_bytes(M, N, K, prec))
+
+
+def w4a4_linear_splitk(xq, xscale, h, wq, wscale, up, bias, prec: int = MXFP4, epi: int = EPI_NONE,
+                       Y=None, work=None, stream=None):
+    """w4a4_linear with K split across work items when the tiles cannot fill
+    the chip (fp32 partial sums in `work`, summed in slice order)."""
+    torch = _torch()
+    M = xq.shape[0]
+    K = xq.shape[1] * 2
+    N = wq.shape[0]
+    r = up.shape[1]
+    if Y is None:
+        Y = torch.empty((M, N), dtype=torch.bfloat16, device=xq.device)
+    need = linear_splitk_workspace_bytes(M, N, K, prec)
+    if work is None and need > 0:
+        work = torch.empty(need // 4, dtype=torch.float32, device=xq.device)
+    pwork = None if work is None else _dev(work, (torch.float32, torch.uint8), "work")
+    nbytes = 0 if work is None else work.numel() * work.element_size()
+    pbias = None if bias is None else _dev(bias, (torch.bfloat16, torch.int16), "bias")
+    st = lib().svdq_w4a4_linear_splitk(
+        _dev(xq, (torch.uint8,), "xq"), _dev(xscale, (torch.float32, torch.uint8), "xscale"),
+        _dev(h, (torch.float32,), "h"), _dev(wq, (torch.uint8,), "wq"),
+        _dev(wscale, (torch.float32, torch.uint8), "wscale"), _dev(up, (torch.bfloat16, torch.int16), "up"),
+        pbias, M, N, K, r, prec, epi, _dev(Y, (torch.bfloat16, torch.int16), "Y"), pwork, nbytes,
+        _stream(stream))
+    _check(st, "svdq_w4a4_linear_splitk")
     return Y
 
 

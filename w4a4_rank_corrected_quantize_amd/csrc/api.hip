@@ -137,6 +137,41 @@ extern "C" svdq_status svdq_w4a4_linear(const uint8_t *xq, const void *xscale, c
     return e == hipSuccess ? SVDQ_OK : SVDQ_ERR_HIP;
 }
 
+extern "C" size_t svdq_w4a4_linear_splitk_workspace_bytes(int M, int N, int K, svdq_precision prec)
+{
+    if (M <= 0 || N <= 0 || K <= 0 || (prec != SVDQ_INT4 && prec != SVDQ_MXFP4)) return 0;
+    if (K % group_size(prec) != 0) return 0;
+    if (current_device_ok() != SVDQ_OK) return 0;       // the split depends on the device's CU count
+    return splitk_work_bytes(M, N, K, prec);
+}
+
+extern "C" svdq_status svdq_w4a4_linear_splitk(const uint8_t *xq, const void *xscale, const float *h,
+                                               const uint8_t *wq, const void *wscale, const uint16_t *up,
+                                               const uint16_t *bias, int M, int N, int K, int rank,
+                                               svdq_precision prec, svdq_epilogue epi, uint16_t *Y, void *work,
+                                               size_t work_bytes, void *stream)
+{
+    svdq_status st = check_common(M, K, rank, prec);
+    if (st != SVDQ_OK) return st;
+    if (N < 0) return SVDQ_ERR_INVALID_ARG;
+    if (epi != SVDQ_EPI_NONE && epi != SVDQ_EPI_GELU_TANH) return SVDQ_ERR_INVALID_ARG;
+    if (N % 8 != 0) return SVDQ_ERR_SHAPE;
+    if ((M > 0 && (!xq || !xscale || !h)) || (N > 0 && (!wq || !wscale || !up)) ||
+        (M > 0 && N > 0 && !Y))
+        return SVDQ_ERR_INVALID_ARG;
+    if (!aligned16(xq) || !aligned16(xscale) || !aligned16(h) || !aligned16(wq) || !aligned16(wscale) ||
+        !aligned16(up) || !aligned16(Y) || (bias && !aligned16(bias)) || (work && !aligned16(work)))
+        return SVDQ_ERR_MISALIGNED;
+    st = current_device_ok();
+    if (st != SVDQ_OK) return st;
+    if (M == 0 || N == 0) return SVDQ_OK;
+    const size_t need = splitk_work_bytes(M, N, K, prec);
+    if (need > 0 && (!work || work_bytes < need)) return SVDQ_ERR_INVALID_ARG;
+    hipError_t e = launch_w4a4_linear_splitk(xq, xscale, h, wq, wscale, up, bias, M, N, K, prec, epi, Y,
+                                             (float *)work, (hipStream_t)stream);
+    return e == hipSuccess ? SVDQ_OK : SVDQ_ERR_HIP;
+}
+
 extern "C" size_t svdq_requant_workspace_bytes(int M, int N, int rank, svdq_precision prec)
 {
     (void)rank;

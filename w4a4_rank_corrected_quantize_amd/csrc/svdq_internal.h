@@ -36,6 +36,18 @@ hipError_t launch_w4a4_linear_requant(const uint8_t *xq, const void *xscale, con
                                       const uint16_t *down2, uint8_t *xq2, void *xscale2, float *h2, float *work,
                                       hipStream_t stream);
 
+// Split K for the MXFP4 linear when its 256 x 256 tiles fill less than half
+// of the chip: S slices of K (S = 1: no split; `sps` steps of 256 channels
+// per slice), fp32 partial sums in `work` (splitk_work_bytes, 0 without a
+// split), then a fixed-order sum with the epilogue.  Without a split the
+// launch is launch_w4a4_linear's.
+int splitk_slices(int M, int N, int K, svdq_precision prec, int &sps);
+size_t splitk_work_bytes(int M, int N, int K, svdq_precision prec);
+hipError_t launch_w4a4_linear_splitk(const uint8_t *xq, const void *xscale, const float *h, const uint8_t *wq,
+                                     const void *wscale, const uint16_t *up, const uint16_t *bias, int M, int N,
+                                     int K, svdq_precision prec, svdq_epilogue epi, uint16_t *Y, float *work,
+                                     hipStream_t stream);
+
 // INT4 linear of a QKV projection (N = 3 H 128) whose epilogue RMS-normalizes
 // the Q and K heads and applies the rotary embedding.
 hipError_t launch_w4a4_linear_qknorm(const uint8_t *xq, const float *xscale, const float *h, const uint8_t *wq,

@@ -1297,11 +1297,26 @@ __device__ __forceinline__ void requant_epilogue_mx(const f32x16 (&acc)[MX_TN][M
 // alternate over the global step count, and the first step of the next tile
 // is loaded into the free stage while the epilogue of the current tile runs
 // (its output staging uses the other stage).
-template <bool REQ>
+// What the LDS-DMA MXFP4 kernel does with a finished tile.
+constexpr int MXE_STORE = 0;      // y -> bf16 Y
+constexpr int MXE_REQUANT = 1;    // the next layer's activation step (RequantArgs)
+constexpr int MXE_PARTIAL = 2;    // fp32 partial sums of one K slice (split K)
+
+// Split K: work item t is tile t % tiles over K slice t / tiles, of S slices
+// of `sps` 256-channel steps each (the last one may be shorter); the slice's
+// fp32 sums go to part[slice][M][N].
+struct SplitArgs {
+    float *part;
+    int S;
+    int sps;
+};
+
+template <int MODE>
 __global__ __launch_bounds__(MXD_THREADS) void w4a4_mxfp4_dma_kernel(
     const uint8_t *__restrict__ xq, const uint8_t *__restrict__ xscale, const float *__restrict__ h,
     const uint8_t *__restrict__ wq, const uint8_t *__restrict__ wscale, const uint16_t *__restrict__ up,
-    const uint16_t *__restrict__ bias, int M, int N, int K, int gelu, uint16_t *__restrict__ Y, RequantArgs rq)
+    const uint16_t *__restrict__ bias, int M, int N, int K, int gelu, uint16_t *__restrict__ Y, RequantArgs rq,
+    SplitArgs sk)
 {
     __shared__ MXDStage stage[2];
     const int tid = threadIdx.x, lane = tid & 63;
@@ -1343,12 +1358,24 @@ __global__ __launch_bounds__(MXD_THREADS) void w4a4_mxfp4_dma_kernel(
         dma_b32(lds_offset(&S.ex[64 * wave]), exo, xscale + 8 * st);
     };
 
+    const int items = MODE == MXE_PARTIAL ? tiles * sk.S : tiles;
+    // item -> tile and its range of steps [st0, st0 + nst)
+    auto item_steps = [&](int it, int &st0, int &nst) {
+        if constexpr (MODE == MXE_PARTIAL) {
+            st0 = (it / tiles) * sk.sps;
+            nst = min(sk.sps, steps - st0);
+        } else {
+            st0 = 0;
+            nst = steps;
+        }
+    };
     int t = blockIdx.x;
-    if (t >= tiles) return;
-    int n0, m0;
-    set_tile(t, n0, m0);
-    int g = 0;                      // global step count: step st of the current tile uses stage (g + st) & 1
-    issue(0, 0);
+    if (t >= items) return;
+    int n0, m0, st0, nst;
+    set_tile(t % tiles, n0, m0);
+    item_steps(t, st0, nst);
+    int g = 0;                      // global step count: step st of the current item uses stage (g + st) & 1
+    issue(st0, 0);
     while (true) {
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         asm volatile("s_barrier" ::: "memory");
@@ -1359,9 +1386,9 @@ __global__ __launch_bounds__(MXD_THREADS) void w4a4_mxfp4_dma_kernel(
             for (int b = 0; b < MX_TM; ++b)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.0f;
-        for (int st = 0; st < steps; ++st) {
+        for (int st = 0; st < nst; ++st) {
             const int sg = (g + st) & 1;
-            if (st + 1 < steps) issue(st + 1, sg ^ 1);
+            if (st + 1 < nst) issue(st0 + st + 1, sg ^ 1);
             const MXDStage &S = stage[sg];
             // four 64-channel slices per step; the fragments of slice sl + 1
             // are read while the products of slice sl run
@@ -1427,17 +1454,39 @@ __global__ __launch_bounds__(MXD_THREADS) void w4a4_mxfp4_dma_kernel(
             asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
             asm volatile("s_barrier" ::: "memory");
         }
-        // the last step used stage (g + steps - 1) & 1: the other one takes
-        // the next tile's first step while this tile's epilogue runs
-        const int last = (g + steps - 1) & 1;
+        // the last step used stage (g + nst - 1) & 1: the other one takes
+        // the next item's first step while this item's epilogue runs
+        const int last = (g + nst - 1) & 1;
         const int mb = m0 + wm * MX_WM, nb = n0 + wn * MX_WN;
         const int tile_n = n0 / MXD_BN, tile_m0 = m0;
+        const int slice = t / tiles;
         const int tnext = t + (int)gridDim.x;
-        if (tnext < tiles) {
-            set_tile(tnext, n0, m0);
-            issue(0, last ^ 1);
+        const int nst_done = nst;
+        if (tnext < items) {
+            set_tile(tnext % tiles, n0, m0);
+            item_steps(tnext, st0, nst);
+            issue(st0, last ^ 1);
         }
-        if constexpr (REQ) {
+        if constexpr (MODE == MXE_PARTIAL) {
+            // lane (l32, hk) holds, per 32 x 32 tile, token mb + 32 tm + l32 and
+            // channels nb + 32 tn + 8 j + 4 hk + (0..3)
+            float *dst = sk.part + (size_t)slice * M * N;
+#pragma unroll
+            for (int tm = 0; tm < MX_TM; ++tm) {
+                const int m = mb + tm * 32 + l32;
+                if (m >= M) continue;
+#pragma unroll
+                for (int tn = 0; tn < MX_TN; ++tn)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int n = nb + tn * 32 + 8 * j + 4 * hk;
+                        if (n < N)
+                            *reinterpret_cast<float4 *>(dst + (size_t)m * N + n) =
+                                make_float4(acc[tn][tm][4 * j], acc[tn][tm][4 * j + 1], acc[tn][tm][4 * j + 2],
+                                            acc[tn][tm][4 * j + 3]);
+                    }
+            }
+        } else if constexpr (MODE == MXE_REQUANT) {
             static_assert(2 * MXD_BM * 32 * sizeof(float) <= sizeof(MXDStage), "partial sums fit in a stage");
             requant_epilogue_mx(acc, h, up, bias, M, N, gelu, rq, mb, nb, tile_n, tile_m0, wn, wm, tid, lane,
                                 reinterpret_cast<float *>(&stage[last]));
@@ -1445,8 +1494,8 @@ __global__ __launch_bounds__(MXD_THREADS) void w4a4_mxfp4_dma_kernel(
             wave_epilogue<MX_TN, MX_TM>(acc, h, up, bias, M, N, gelu, Y, mb, nb,
                                         reinterpret_cast<uint8_t *>(&stage[last]) + wave * OUT_TILE_BYTES, lane);
         }
-        if (tnext >= tiles) break;
-        g += steps;
+        if (tnext >= items) break;
+        g += nst_done;
         t = tnext;
         // the staging area becomes the second stage of the next tile
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -1473,9 +1522,9 @@ hipError_t launch_w4a4_linear(const uint8_t *xq, const void *xscale, const float
             const int tiles = ((N + MXD_BN - 1) / MXD_BN) * ((M + MXD_BM - 1) / MXD_BM);
             const int ncu = device_cu_count();
             const int blocks = tiles < ncu ? tiles : ncu;      // persistent: one block per CU
-            hipLaunchKernelGGL(w4a4_mxfp4_dma_kernel<false>, dim3((unsigned)blocks), dim3(MXD_THREADS), 0, stream, xq,
-                               (const uint8_t *)xscale, h, wq, (const uint8_t *)wscale, up, bias, M, N, K, gelu, Y,
-                               RequantArgs{});
+            hipLaunchKernelGGL(w4a4_mxfp4_dma_kernel<MXE_STORE>, dim3((unsigned)blocks), dim3(MXD_THREADS), 0, stream,
+                               xq, (const uint8_t *)xscale, h, wq, (const uint8_t *)wscale, up, bias, M, N, K, gelu,
+                               Y, RequantArgs{}, SplitArgs{nullptr, 1, K >> 8});
         } else {
             const int tiles = ((N + MX_BN - 1) / MX_BN) * ((M + MX_BM - 1) / MX_BM);
             hipLaunchKernelGGL(w4a4_mxfp4_kernel, dim3((unsigned)tiles), dim3(MX_THREADS), 0, stream, xq,
@@ -1513,14 +1562,95 @@ hipError_t launch_w4a4_linear_requant(const uint8_t *xq, const void *xscale, con
         const int tiles = tiles_n * ((M + MXD_BM - 1) / MXD_BM);
         const int ncu = device_cu_count();
         const int blocks = tiles < ncu ? tiles : ncu;
-        hipLaunchKernelGGL(w4a4_mxfp4_dma_kernel<true>, dim3((unsigned)blocks), dim3(MXD_THREADS), 0, stream, xq,
-                           (const uint8_t *)xscale, h, wq, (const uint8_t *)wscale, up, bias, M, N, K, gelu,
-                           (uint16_t *)nullptr, rq);
+        hipLaunchKernelGGL(w4a4_mxfp4_dma_kernel<MXE_REQUANT>, dim3((unsigned)blocks), dim3(MXD_THREADS), 0, stream,
+                           xq, (const uint8_t *)xscale, h, wq, (const uint8_t *)wscale, up, bias, M, N, K, gelu,
+                           (uint16_t *)nullptr, rq, SplitArgs{nullptr, 1, K >> 8});
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(requant_h_reduce, dim3((unsigned)((M * 8 + 255) / 256)), dim3(256), 0, stream,
                        (const float *)work, tiles_n, M, h2);
+    return hipGetLastError();
+}
+
+// Split-K epilogue: y = the slices' fp32 sums added in slice order
+// + h . up + b (+ GELU) -> bf16, for 4 consecutive channels per thread.  The
+// low-rank term is the fp32 dot product of h with the bf16 up row.
+__global__ __launch_bounds__(256) void splitk_finish_kernel(const float *__restrict__ part, int S,
+                                                            const float *__restrict__ h,
+                                                            const uint16_t *__restrict__ up,
+                                                            const uint16_t *__restrict__ bias, int M, int N,
+                                                            int gelu, uint16_t *__restrict__ Y)
+{
+    const int nq = N >> 2;
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;      // (m, n / 4)
+    if (i >= (int64_t)M * nq) return;
+    const int m = (int)(i / nq), n = 4 * (int)(i % nq);
+    float a[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int s = 0; s < S; ++s) {
+        const float4 v = *reinterpret_cast<const float4 *>(part + ((size_t)s * M + m) * N + n);
+        a[0] += v.x; a[1] += v.y; a[2] += v.z; a[3] += v.w;
+    }
+    float lr[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    const float4 *hr = reinterpret_cast<const float4 *>(h + (size_t)m * 32);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        const float4 hv = hr[q];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const uint2 u = *reinterpret_cast<const uint2 *>(up + (size_t)(n + e) * 32 + 4 * q);
+            lr[e] = __builtin_fmaf(hv.x, bf16_to_f32(u.x & 0xFFFFu), lr[e]);
+            lr[e] = __builtin_fmaf(hv.y, bf16_to_f32(u.x >> 16), lr[e]);
+            lr[e] = __builtin_fmaf(hv.z, bf16_to_f32(u.y & 0xFFFFu), lr[e]);
+            lr[e] = __builtin_fmaf(hv.w, bf16_to_f32(u.y >> 16), lr[e]);
+        }
+    }
+    *reinterpret_cast<uint2 *>(Y + (size_t)m * N + n) = finish4(a, lr, bias4(bias, n, N), gelu);
+}
+
+int splitk_slices(int M, int N, int K, svdq_precision prec, int &sps)
+{
+    const int steps = K >> 8;
+    sps = steps;
+    // the LDS-DMA MXFP4 kernel only (the same range as its requantizing form)
+    if (prec != SVDQ_MXFP4 || !requant_supported(M, N, K, prec) || M <= 0 || N <= 0) return 1;
+    const int tiles = ((N + MXD_BN - 1) / MXD_BN) * ((M + MXD_BM - 1) / MXD_BM);
+    const int ncu = device_cu_count();
+    if (2 * tiles > ncu) return 1;                      // the tiles alone fill at least half the chip
+    const int S = min(min(ncu / tiles, 4), steps / 4);  // at most 4 slices of at least 4 steps
+    if (S < 2) return 1;
+    sps = (steps + S - 1) / S;
+    return (steps + sps - 1) / sps;                     // no empty slice
+}
+
+size_t splitk_work_bytes(int M, int N, int K, svdq_precision prec)
+{
+    int sps;
+    const int S = splitk_slices(M, N, K, prec, sps);
+    return S < 2 ? 0 : (size_t)S * M * N * sizeof(float);
+}
+
+hipError_t launch_w4a4_linear_splitk(const uint8_t *xq, const void *xscale, const float *h, const uint8_t *wq,
+                                     const void *wscale, const uint16_t *up, const uint16_t *bias, int M, int N,
+                                     int K, svdq_precision prec, svdq_epilogue epi, uint16_t *Y, float *work,
+                                     hipStream_t stream)
+{
+    int sps;
+    const int S = splitk_slices(M, N, K, prec, sps);
+    if (S < 2) return launch_w4a4_linear(xq, xscale, h, wq, wscale, up, bias, M, N, K, prec, epi, Y, stream);
+    const int gelu = epi == SVDQ_EPI_GELU_TANH ? 1 : 0;
+    const int tiles = ((N + MXD_BN - 1) / MXD_BN) * ((M + MXD_BM - 1) / MXD_BM);
+    const int ncu = device_cu_count();
+    const int items = tiles * S;
+    const int blocks = items < ncu ? items : ncu;
+    hipLaunchKernelGGL(w4a4_mxfp4_dma_kernel<MXE_PARTIAL>, dim3((unsigned)blocks), dim3(MXD_THREADS), 0, stream, xq,
+                       (const uint8_t *)xscale, h, wq, (const uint8_t *)wscale, up, bias, M, N, K, gelu,
+                       (uint16_t *)nullptr, RequantArgs{}, SplitArgs{work, S, sps});
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t threads = (int64_t)M * (N / 4);
+    hipLaunchKernelGGL(splitk_finish_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream,
+                       (const float *)work, S, h, up, bias, M, N, gelu, Y);
     return hipGetLastError();
 }
 

@@ -97,6 +97,9 @@ def main():
                          "would otherwise stay in the 256 MB last-level cache)")
     ap.add_argument("--tokens", type=int, choices=[4608, 1024], default=4608,
                     help="1024: the MXFP4 linears of a 512 x 512 image (--prec mxfp4, fc1 / qkv / fc2)")
+    ap.add_argument("--splitk", action="store_true",
+                    help="time svdq_w4a4_linear_splitk (K split across work items when the tiles cannot fill "
+                         "the chip; the workspace is allocated before the timed region)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle sample time")
     args = ap.parse_args()
@@ -168,6 +171,14 @@ def main():
             xscale=torch.empty((M, K // g), dtype=sdt, device="cuda"),
             h=torch.empty((M, r), dtype=torch.float32, device="cuda"),
             Y=torch.empty((M, N), dtype=torch.bfloat16, device="cuda")))
+    work = None
+    if args.splitk:
+        if qkvnorm:
+            print("--splitk does not apply to --layer qkvnorm", file=sys.stderr)
+            sys.exit(2)
+        nb = svdq.linear_splitk_workspace_bytes(M, N, K, prec)
+        work = torch.empty(max(nb // 4, 1), dtype=torch.float32, device="cuda")
+        print(f"[bench] split-K workspace {nb / 1e6:.1f} MB", file=sys.stderr, flush=True)
     ws_mb = sum(t.numel() * t.element_size() for t in sets[0].values() if t is not None) / 1e6
     if qkvnorm:
         rc, rs = synth.gen_rope(M)
@@ -182,6 +193,10 @@ def main():
         if qkvnorm:
             svdq.w4a4_linear_qkv_norm_rope(b["xq"], b["xscale"], b["h"], b["wq"], b["wscale"], b["up"], b["bias"],
                                            qkn["nq"], qkn["nk"], 1e-6, qkn["c"], qkn["s"], Y=b["Y"])
+            return
+        if work is not None:
+            svdq.w4a4_linear_splitk(b["xq"], b["xscale"], b["h"], b["wq"], b["wscale"], b["up"], b["bias"], prec,
+                                    epi, Y=b["Y"], work=work)
             return
         svdq.w4a4_linear(b["xq"], b["xscale"], b["h"], b["wq"], b["wscale"], b["up"], b["bias"], prec,
                          epi, Y=b["Y"])
@@ -283,7 +298,9 @@ def main():
                                f"{'svdq_w4a4_linear_qkv_norm_rope' if qkvnorm else 'svdq_w4a4_linear'}",
                    "M": M, "K": K, "N": N, "rank": r, "buffer_sets": len(sets),
                    "working_set_MB_per_set": round(ws_mb, 1)},
-        "roofline": {"bound": "mfma", "kernel": "svdq_w4a4_linear_qkv_norm_rope" if qkvnorm else "svdq_w4a4_linear",
+        "roofline": {"bound": "mfma", "kernel": ("svdq_w4a4_linear_qkv_norm_rope" if qkvnorm else
+                                                  "svdq_w4a4_linear_splitk (both kernels)" if work is not None
+                                                  else "svdq_w4a4_linear"),
                      "achieved": round(k2_tops, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(k2_tops / peak, 4), "traffic": traffic,
                      "avg_ms": round(k2_ms, 5)},

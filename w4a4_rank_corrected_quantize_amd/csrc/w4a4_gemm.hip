@@ -1469,22 +1469,53 @@ __global__ __launch_bounds__(MXD_THREADS) void w4a4_mxfp4_dma_kernel(
         }
         if constexpr (MODE == MXE_PARTIAL) {
             // lane (l32, hk) holds, per 32 x 32 tile, token mb + 32 tm + l32 and
-            // channels nb + 32 tn + 8 j + 4 hk + (0..3)
+            // channels nb + 32 tn + 8 j + 4 hk + (0..3).  Slice 0 also adds the
+            // low-rank term, as the unsplit epilogue computes it.
             float *dst = sk.part + (size_t)slice * M * N;
+            bf16x8 hhi[MX_TM][2], hlo[MX_TM][2];
+            if (slice == 0) {
 #pragma unroll
-            for (int tm = 0; tm < MX_TM; ++tm) {
-                const int m = mb + tm * 32 + l32;
-                if (m >= M) continue;
+                for (int tm = 0; tm < MX_TM; ++tm)
 #pragma unroll
-                for (int tn = 0; tn < MX_TN; ++tn)
+                    for (int s2 = 0; s2 < 2; ++s2) {
+                        float hv[8];
+                        load_h8(h, mb + tm * 32 + l32, M, 16 * s2 + 8 * hk, hv);
+                        split_h(hv, hhi[tm][s2], hlo[tm][s2]);
+                    }
+            }
+#pragma unroll
+            for (int tn = 0; tn < MX_TN; ++tn) {
+                if (slice == 0) {
+                    const int nrow = nb + tn * 32 + l32;
+                    bf16x8 ua[2];
+#pragma unroll
+                    for (int s2 = 0; s2 < 2; ++s2) {
+                        uint4 uv = {0u, 0u, 0u, 0u};
+                        if (nrow < N) uv = *reinterpret_cast<const uint4 *>(up + (size_t)nrow * 32 + 16 * s2 + 8 * hk);
+                        ua[s2] = __builtin_bit_cast(bf16x8, uv);
+                    }
+#pragma unroll
+                    for (int tm = 0; tm < MX_TM; ++tm)
+#pragma unroll
+                        for (int s2 = 0; s2 < 2; ++s2) {
+                            acc[tn][tm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ua[s2], hhi[tm][s2], acc[tn][tm],
+                                                                                  0, 0, 0);
+                            acc[tn][tm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ua[s2], hlo[tm][s2], acc[tn][tm],
+                                                                                  0, 0, 0);
+                        }
+                }
+#pragma unroll
+                for (int tm = 0; tm < MX_TM; ++tm) {
+                    const int m = mb + tm * 32 + l32;
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
                         const int n = nb + tn * 32 + 8 * j + 4 * hk;
-                        if (n < N)
+                        if (m < M && n < N)
                             *reinterpret_cast<float4 *>(dst + (size_t)m * N + n) =
                                 make_float4(acc[tn][tm][4 * j], acc[tn][tm][4 * j + 1], acc[tn][tm][4 * j + 2],
                                             acc[tn][tm][4 * j + 3]);
                     }
+                }
             }
         } else if constexpr (MODE == MXE_REQUANT) {
             static_assert(2 * MXD_BM * 32 * sizeof(float) <= sizeof(MXDStage), "partial sums fit in a stage");
@@ -1573,12 +1604,10 @@ hipError_t launch_w4a4_linear_requant(const uint8_t *xq, const void *xscale, con
     return hipGetLastError();
 }
 
-// Split-K epilogue: y = the slices' fp32 sums added in slice order
-// + h . up + b (+ GELU) -> bf16, for 4 consecutive channels per thread.  The
-// low-rank term is the fp32 dot product of h with the bf16 up row.
+// Split-K epilogue: y = the slices' fp32 sums added in slice order (slice 0
+// carries the low-rank term) + b (+ GELU) -> bf16, 4 consecutive channels per
+// thread.
 __global__ __launch_bounds__(256) void splitk_finish_kernel(const float *__restrict__ part, int S,
-                                                            const float *__restrict__ h,
-                                                            const uint16_t *__restrict__ up,
                                                             const uint16_t *__restrict__ bias, int M, int N,
                                                             int gelu, uint16_t *__restrict__ Y)
 {
@@ -1588,24 +1617,12 @@ __global__ __launch_bounds__(256) void splitk_finish_kernel(const float *__restr
     const int m = (int)(i / nq), n = 4 * (int)(i % nq);
     float a[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     for (int s = 0; s < S; ++s) {
-        const float4 v = *reinterpret_cast<const float4 *>(part + ((size_t)s * M + m) * N + n);
+        typedef float f32x4 __attribute__((ext_vector_type(4)));
+        const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(part + ((size_t)s * M + m) * N + n));
         a[0] += v.x; a[1] += v.y; a[2] += v.z; a[3] += v.w;
     }
-    float lr[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    const float4 *hr = reinterpret_cast<const float4 *>(h + (size_t)m * 32);
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-        const float4 hv = hr[q];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const uint2 u = *reinterpret_cast<const uint2 *>(up + (size_t)(n + e) * 32 + 4 * q);
-            lr[e] = __builtin_fmaf(hv.x, bf16_to_f32(u.x & 0xFFFFu), lr[e]);
-            lr[e] = __builtin_fmaf(hv.y, bf16_to_f32(u.x >> 16), lr[e]);
-            lr[e] = __builtin_fmaf(hv.z, bf16_to_f32(u.y & 0xFFFFu), lr[e]);
-            lr[e] = __builtin_fmaf(hv.w, bf16_to_f32(u.y >> 16), lr[e]);
-        }
-    }
-    *reinterpret_cast<uint2 *>(Y + (size_t)m * N + n) = finish4(a, lr, bias4(bias, n, N), gelu);
+    const float zero[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    *reinterpret_cast<uint2 *>(Y + (size_t)m * N + n) = finish4(a, zero, bias4(bias, n, N), gelu);
 }
 
 int splitk_slices(int M, int N, int K, svdq_precision prec, int &sps)
@@ -1650,7 +1667,7 @@ hipError_t launch_w4a4_linear_splitk(const uint8_t *xq, const void *xscale, cons
     if (e != hipSuccess) return e;
     const int64_t threads = (int64_t)M * (N / 4);
     hipLaunchKernelGGL(splitk_finish_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream,
-                       (const float *)work, S, h, up, bias, M, N, gelu, Y);
+                       (const float *)work, S, bias, M, N, gelu, Y);
     return hipGetLastError();
 }
 

@@ -39,9 +39,9 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, 8 TB/s
 # measured on; otherwise traffic is null.
 TRAFFIC = {
     # FETCH_SIZE 72778 KiB / 0.50003 + WRITE_SIZE 110610 KiB / 1.00000 (per dispatch)
-    ("int4", "fc1"): {"source_sha": "019e810849c9b972", "bytes": 262995968},
+    ("int4", "fc1"): {"source_sha": "c8a8921c0134cc9f", "bytes": 263321600},
     # FETCH_SIZE 70922 KiB / 0.50003 + WRITE_SIZE 111107 KiB / 1.00000
-    ("mxfp4", "fc1"): {"source_sha": "019e810849c9b972", "bytes": 259108864},
+    ("mxfp4", "fc1"): {"source_sha": "c8a8921c0134cc9f", "bytes": 259399680},
 }
 
 

@@ -194,8 +194,8 @@ svdq_status svdq_w4a4_linear(const uint8_t *xq, const void *xscale, const float 
  * partial sums when the MXFP4 product is split into S slices of K (S of 2
  * to 4; every slice but the last at least 1024 channels), else 0 (INT4,
  * shapes whose 256 x 256 tiles already fill half the chip, K < 2048 or
- * K % 256 != 0, M or N <= 0, invalid arguments, or no gfx950 device).  It depends on the
- * device's compute-unit count.
+ * K % 256 != 0, M or N <= 0, invalid arguments, or no gfx950 device).
+ * It depends on the device's compute-unit count.
  */
 size_t svdq_w4a4_linear_splitk_workspace_bytes(int M, int N, int K, svdq_precision prec);
 

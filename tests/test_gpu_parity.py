@@ -259,6 +259,46 @@ def test_linear_splitk_full_size_fc2_1024():
 
 
 @pytest.mark.parametrize("prec", PRECS)
+def test_layer_graph_replay(prec):
+    """The activation step and the linear captured in a HIP graph (as a
+    serving loop would): every replay, with eager work and synchronizations
+    in between, equals the eager launches bit for bit."""
+    _say(f"graph replay prec={prec}")
+    M, K, N = 300, 1024, 520
+    L, p = _layer("qkv", M, K, N, prec)
+    X = _t(L["X"])
+    args = dict(smooth=_t(p["smooth"]), down=_t(p["down"]), wq=_t(p["wq"]), ws=_t(p["wscale"]), up=_t(p["up"]),
+                b=_t(L["bias"]))
+    g = svdq.group_of(prec)
+    sdt = torch.float32 if prec == svdq.INT4 else torch.uint8
+    xq = torch.empty((M, K // 2), dtype=torch.uint8, device="cuda")
+    xs = torch.empty((M, K // g), dtype=sdt, device="cuda")
+    h = torch.empty((M, svdq.RANK), dtype=torch.float32, device="cuda")
+    Y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+
+    def step():
+        svdq.quantize_act(X, args["smooth"], args["down"], prec, xq=xq, xscale=xs, h=h)
+        svdq.w4a4_linear(xq, xs, h, args["wq"], args["ws"], args["up"], args["b"], prec, svdq.EPI_GELU_TANH, Y=Y)
+
+    step()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (xq, xs, h, Y)]
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    for _ in range(3):
+        for t in (xq, h, Y):
+            t.zero_()
+        xs.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for a, b in zip((xq, xs, h, Y), ref):
+            assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("prec", PRECS)
 def test_linear_invariants(prec):
     """up = 0 => the 4-bit product alone; residual codes 0 => the low-rank
     product alone (+ bias)."""

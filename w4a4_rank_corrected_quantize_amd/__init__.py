@@ -237,7 +237,9 @@ def linear_splitk_workspace_bytes(M: int, N: int, K: int, prec: int = MXFP4) -> 
 def w4a4_linear_splitk(xq, xscale, h, wq, wscale, up, bias, prec: int = MXFP4, epi: int = EPI_NONE,
                        Y=None, work=None, stream=None):
     """w4a4_linear with K split across work items when the tiles cannot fill
-    the chip (fp32 partial sums in `work`, summed in slice order)."""
+    the chip (fp32 partial sums in `work`, summed in slice order).  When
+    `work` is None this binding allocates it with torch; pass a preallocated
+    tensor of linear_splitk_workspace_bytes(...) bytes in a serving loop."""
     torch = _torch()
     M = xq.shape[0]
     K = xq.shape[1] * 2

@@ -286,8 +286,9 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int4 codes (exact fp8 values) on the fp8 matrix cores, exact per-group partials, "
-                 "fp32 rescale" if prec == svdq.INT4
+        "dtype": "int4 codes as exact fp8 E4M3 subnormals on the fp8 matrix cores (exact per-group partials); "
+                 "group scale sx*sw from a bf16 hi/lo matrix product (~2^-16 relative), one fp32 fma per group"
+        if prec == svdq.INT4
         else "mxfp4 (e2m1 x e2m1, e8m0 scales) on the scaled fp4 matrix cores, fp32 accumulation",
         "data": "synthetic (seeded Student-t activations with outlier channels, N(0,0.02^2) weights)",
         "config": {"workload": f"{spec.name}: {M} tokens x {K} -> {N}, rank {r}, "
@@ -572,7 +573,8 @@ def mlp_main(args, torch, svdq, synth):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int4 codes (exact fp8 values) on the fp8 matrix cores, exact per-group partials, fp32 rescale"
+        "dtype": "int4 codes as exact fp8 E4M3 subnormals on the fp8 matrix cores (exact per-group partials); "
+                 "group scale sx*sw from a bf16 hi/lo matrix product (~2^-16 relative), one fp32 fma per group"
                  if prec == svdq.INT4
                  else "mxfp4 (e2m1 x e2m1, e8m0 scales) on the scaled fp4 matrix cores, fp32 accumulation",
         "data": "synthetic (seeded Student-t activations with outlier channels, N(0,0.02^2) weights); "

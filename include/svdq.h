@@ -35,6 +35,18 @@
  * formats are sign-magnitude with the sign of the input in bit 3 (kept for
  * zero): INT4 code = sign << 3 | |q|, E2M1 code = sign << 3 | grid index.
  *
+ * Layout choices (the pages fix none of them):
+ *   - down is stored [r][K] and up [N][r], i.e. both factors transposed
+ *     against the textbook L1 [K][r], L2 [r][N]: the activation kernel reads
+ *     16 consecutive channels of all 32 ranks as 32-byte runs, and the
+ *     product's epilogue reads one output channel's 32 ranks as one 64-byte
+ *     line.
+ *   - INT4 codes are sign-magnitude, not two's complement: a sign-magnitude
+ *     code becomes the exact fp8 (E4M3) byte of q 2^-9 with bit operations
+ *     only, which is how the product feeds the matrix cores.
+ *   - N % 8 == 0 for the linears: every row of Y, bias and up then starts on
+ *     a 16-byte boundary.
+ *
  * Conventions.
  *   - Ownership: the caller allocates and frees every buffer.  No call
  *     allocates device memory or keeps a pointer after it returns.
@@ -70,7 +82,8 @@ extern "C" {
 typedef enum svdq_status {
     SVDQ_OK = 0,
     SVDQ_ERR_INVALID_ARG = -1,        /* NULL pointer, bad enum value, negative size */
-    SVDQ_ERR_SHAPE = -2,              /* a size not the multiple the call requires (K of the group, N of 8, ...) */
+    SVDQ_ERR_SHAPE = -2,              /* a size not the multiple the call requires (K of the group, N of 8, ...),
+                                         or a matrix of SVDQ_MAX_ELEMENTS elements or more */
     SVDQ_ERR_MISALIGNED = -3,         /* a device pointer not 16-byte aligned */
     SVDQ_ERR_UNSUPPORTED = -4,        /* rank other than 32, or a precision / K the call does not support */
     SVDQ_ERR_UNSUPPORTED_DEVICE = -5, /* no HIP device, or the current device is not gfx950 */
@@ -89,6 +102,11 @@ typedef enum svdq_epilogue {
 } svdq_epilogue;
 
 #define SVDQ_RANK 32
+
+/* Every matrix a call touches (M x K, N x K, M x N) must hold fewer than
+ * this many elements (SVDQ_ERR_SHAPE otherwise), so that every byte offset
+ * inside one buffer fits in 31 bits. */
+#define SVDQ_MAX_ELEMENTS (1 << 30)
 
 /* Human-readable text of a status code (static storage, never NULL). */
 const char *svdq_status_string(svdq_status status);
@@ -178,10 +196,12 @@ svdq_status svdq_quantize_act(const uint16_t *X, int M, int K, const float *smoo
  *   Y               [M][N] bf16 bits (device, out), round-to-nearest-even
  * INT4: per 64-group exact integer partial products from the matrix
  * cores (each code enters the fp8 matrix instruction as an exact E4M3
- * value), rescaled by sx * sw in fp32; MXFP4: the scaled f8f6f4 matrix
- * instruction applies both E8M0 scales.  The low-rank term uses h split
- * into a bf16 high and low part.  One kernel launch.  Errors as for
- * svdq_quantize_act.
+ * value); the group scale sx * sw of each output comes from the bf16 matrix
+ * instruction on high/low bf16 splits of both scales (relative error about
+ * 2^-16) and multiplies the exact partial in one fp32 fma.  MXFP4: the
+ * scaled f8f6f4 matrix instruction applies both E8M0 scales.  The low-rank
+ * term uses h split into a bf16 high and low part.  One kernel launch.
+ * Errors as for svdq_quantize_act.
  */
 svdq_status svdq_w4a4_linear(const uint8_t *xq, const void *xscale, const float *h,
                              const uint8_t *wq, const void *wscale, const uint16_t *up,
@@ -211,8 +231,9 @@ size_t svdq_w4a4_linear_splitk_workspace_bytes(int M, int N, int K, svdq_precisi
  *                     is 0); overwritten, caller-owned
  * With a split, each of S work items per tile sums its K slice into the
  * workspace in fp32, and a second kernel adds the S slices in slice order
- * (so the result is deterministic) before the epilogue; its low-rank term
- * is the fp32 dot product of h with the bf16 up row.  Sums in a different
+ * (so the result is deterministic) before the epilogue; slice 0 adds the
+ * low-rank term with the same bf16 high/low matrix product as the unsplit
+ * epilogue.  Sums in a different
  * order than svdq_w4a4_linear's, so outputs may differ from it in the last
  * bf16 place.  Without a split it is svdq_w4a4_linear.  Errors as for
  * svdq_w4a4_linear, and SVDQ_ERR_INVALID_ARG for a NULL or too small work

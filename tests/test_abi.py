@@ -190,3 +190,31 @@ def test_no_gpu_means_unsupported_device():
     assert L.svdq_w4a4_linear(p, p, p, p, p, p, None, 16, 16, 128, 32, svdq.INT4, 0, p, None) == -5
     with pytest.raises(svdq.SvdqError):
         svdq.check_device()
+
+
+def test_matrices_of_2_30_elements_are_rejected():
+    """Every matrix a call touches must hold fewer than 2^30 elements, so the
+    kernels' 32-bit byte offsets (the LDS-DMA lane offsets among them) cannot
+    wrap: larger shapes return SVDQ_ERR_SHAPE before the device check, and the
+    split-K workspace query returns 0 for them."""
+    L = svdq.lib()
+    _, p = _host(1 << 16)
+    big = 1 << 21                      # 2^21 rows x 512 channels = 2^30 elements
+    I, MX = svdq.INT4, svdq.MXFP4
+    assert L.svdq_quantize_act(p, big, 512, p, p, 32, I, p, p, p, None) == -2
+    assert L.svdq_quantize_act(p, big - 1, 512, p, p, 32, I, p, p, p, None) != -2
+    # weights N x K, activations M x K, output M x N
+    assert L.svdq_w4a4_linear(p, p, p, p, p, p, None, 16, big, 512, 32, I, 0, p, None) == -2
+    assert L.svdq_w4a4_linear(p, p, p, p, p, p, None, big, 16, 512, 32, MX, 0, p, None) == -2
+    assert L.svdq_w4a4_linear(p, p, p, p, p, p, None, 1 << 15, 1 << 15, 64, 32, I, 0, p, None) == -2
+    assert L.svdq_w4a4_linear_splitk(p, p, p, p, p, p, None, 16, big, 512, 32, MX, 0, p, p, 1 << 16, None) == -2
+    assert L.svdq_w4a4_linear_splitk_workspace_bytes(16, big, 512, MX) == 0
+    assert L.svdq_w4a4_linear_requant(p, p, p, p, p, p, None, 16, big, 512, 32, I, 0, p, p, p, p, p, p,
+                                      1 << 16, None) == -2
+    assert L.svdq_w4a4_linear_qkv_norm_rope(p, p, p, p, p, p, None, 16, 3 * (1 << 21), 512, 32, I, p, p,
+                                            ctypes.c_float(0.0), p, p, p, None) == -2
+    assert L.svdq_awq_w4a16_linear(p, p, p, None, 16, big, 512, p, None) == -2
+    # host packing of an N x K weight
+    assert L.svdq_awq_pack_weights(p, big, 512, p, p) == -2
+    assert L.svdq_pack_residual(p, p, p, p, big, 512, 32, I, p, p) == -2
+    assert L.svdq_pack_weights(p, p, big, 512, 32, I, p, p, p, p, p) == -2

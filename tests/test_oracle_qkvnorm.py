@@ -97,3 +97,39 @@ def test_scale_invariance_without_eps_and_rounding_of_inputs():
     # a bf16 ulp of every value changes nothing
     tiny = y * (1 + 2.0 ** -12)
     assert np.array_equal(O.qkv_norm_rope(tiny, w, w, 1e-6, c, s), O.qkv_norm_rope(y, w, w, 1e-6, c, s))
+
+
+@pytest.mark.parametrize("value,eps,want", [
+    (2.0, 12.0, 0.5),        # mean square 4: 1 / sqrt(4 + 12) = 1/4
+    (3.0, 7.0, 0.75),        # mean square 9: 3 / sqrt(16)
+    (1.0, 3.0, 0.5),         # eps three times the mean square
+    (0.5, 0.0, 1.0),         # no eps: every value becomes 1
+])
+def test_eps_closed_forms(value, eps, want):
+    """Worked by hand: a head whose 128 values all have magnitude v has mean
+    square v^2, so with unit weights and no rotation each output is
+    +-v / sqrt(v^2 + eps).  eps outside the square root (v / (v + eps)),
+    added to the sum of squares instead of the mean (v / sqrt(v^2 + eps /
+    128)) or left out would give other values in every case with eps > 0."""
+    M, H = 2, 1
+    y = np.full((M, 384 * H), value, np.float64)
+    y[:, 1::2] *= -1.0                          # signs must pass through
+    w = np.full(128, ONE)
+    out = O.qkv_norm_rope(y, w, w, eps, np.ones((M, 64), np.float32), np.zeros((M, 64), np.float32))
+    sign = np.where(np.arange(128) % 2 == 0, 1.0, -1.0)
+    for hd in range(2):
+        assert np.array_equal(out[:, 128 * hd: 128 * hd + 128], np.tile(want * sign, (M, 1)))
+    assert np.array_equal(out[:, 256:], y[:, 256:])
+
+
+def test_eps_with_mixed_magnitudes():
+    """Half the channels 4, half 0: mean square 8; eps = 1 gives sqrt(9) = 3,
+    so the outputs are 4/3 and 0 (4/3 rounded once in fp64)."""
+    y = np.zeros((1, 384), np.float64)
+    y[0, 0:128:2] = 4.0
+    y[0, 128:256:2] = -4.0
+    w = np.full(128, ONE)
+    out = O.qkv_norm_rope(y, w, w, 1.0, np.ones((1, 64), np.float32), np.zeros((1, 64), np.float32))
+    assert np.all(np.abs(out[0, 0:128:2] - 4.0 / 3.0) <= 2.0 ** -51)
+    assert np.all(np.abs(out[0, 128:256:2] + 4.0 / 3.0) <= 2.0 ** -51)
+    assert np.all(out[0, 1:256:2] == 0.0)

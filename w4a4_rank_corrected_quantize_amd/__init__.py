@@ -131,9 +131,14 @@ def _np(a, dtype):
 
 def pack_weights(W: np.ndarray, act_absmax: np.ndarray, rank: int = RANK, prec: int = INT4) -> dict:
     """Smoothing, top-r SVD and residual packing of one layer (host)."""
+    prec = _prec(prec)
     W, pW = _np(W, np.uint16)
     a, pa = _np(act_absmax, np.float32)
+    if W.ndim != 2:
+        raise ValueError(f"W must have 2 dimensions, got shape {W.shape}")
     N, K = W.shape
+    if a.shape != (K,):
+        raise ValueError(f"act_absmax has shape {a.shape}, expected {(K,)}")
     g = group_of(prec)
     smooth = np.zeros(K, np.float32)
     down = np.zeros((rank, K), np.uint16)
@@ -151,7 +156,14 @@ def pack_residual(W, smooth, down, up, prec: int = INT4):
     s, ps = _np(smooth, np.float32)
     d, pd = _np(down, np.uint16)
     u, pu = _np(up, np.uint16)
+    prec = _prec(prec)
+    if W.ndim != 2 or d.ndim != 2:
+        raise ValueError("W and down must have 2 dimensions")
     N, K = W.shape
+    r = d.shape[0]
+    for arr, want, name in ((s, (K,), "smooth"), (d, (r, K), "down"), (u, (N, r), "up")):
+        if arr.shape != want:
+            raise ValueError(f"{name} has shape {arr.shape}, expected {want}")
     g = group_of(prec)
     wq = np.zeros((N, K // 2), np.uint8)
     wscale = np.zeros((N, max(K // g, 0)), np.float32 if prec == INT4 else np.uint8)
@@ -168,15 +180,54 @@ def _torch():
     return torch
 
 
-def _dev(t, dtypes, name):
+def _chk(t, dtypes, name, shape=None):
+    """Type, dtype, shape (when given) and contiguity of a tensor argument."""
     torch = _torch()
-    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
-        raise TypeError(f"{name} must be a device tensor")
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
     if t.dtype not in dtypes:
         raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
-    return ctypes.c_void_p(t.data_ptr())
+
+
+def _ptrs(*specs):
+    """Pointers of device tensors given as (tensor, dtypes, name[, shape])
+    (None for an absent optional tensor).  Every tensor's type, dtype, shape
+    and contiguity are checked before any device check, so a wrong shape is
+    reported the same way with or without a GPU."""
+    for sp in specs:
+        if sp is not None:
+            _chk(*sp)
+    out = []
+    for sp in specs:
+        if sp is None:
+            out.append(None)
+            continue
+        t, name = sp[0], sp[2]
+        if t.device.type != "cuda":
+            raise TypeError(f"{name} must be a device tensor")
+        out.append(ctypes.c_void_p(t.data_ptr()))
+    return out
+
+
+def _prec(prec: int) -> int:
+    if prec not in (INT4, MXFP4):
+        raise ValueError(f"prec must be INT4 ({INT4}) or MXFP4 ({MXFP4}), got {prec}")
+    return prec
+
+
+def _scale_dtypes(prec: int):
+    """The one scale dtype each precision takes: fp32 (INT4), E8M0 bytes (MXFP4)."""
+    torch = _torch()
+    return (torch.float32,) if prec == INT4 else (torch.uint8,)
+
+
+def _ndim(t, n, name):
+    if getattr(t, "ndim", None) != n:
+        raise ValueError(f"{name} must have {n} dimensions, got shape {tuple(getattr(t, 'shape', ()))}")
 
 
 def _stream(stream):
@@ -189,6 +240,9 @@ def _stream(stream):
 def quantize_act(X, smooth, down, prec: int = INT4, xq=None, xscale=None, h=None, stream=None):
     """Fused smoothing + 4-bit quantization + down projection (one kernel)."""
     torch = _torch()
+    prec = _prec(prec)
+    _ndim(X, 2, "X")
+    _ndim(down, 2, "down")
     M, K = X.shape
     r = down.shape[0]
     g = group_of(prec)
@@ -199,31 +253,43 @@ def quantize_act(X, smooth, down, prec: int = INT4, xq=None, xscale=None, h=None
         xscale = torch.empty((M, K // g), dtype=torch.float32 if prec == INT4 else torch.uint8, device=dev)
     if h is None:
         h = torch.empty((M, r), dtype=torch.float32, device=dev)
-    st = lib().svdq_quantize_act(
-        _dev(X, (torch.bfloat16, torch.int16), "X"), M, K,
-        _dev(smooth, (torch.float32,), "smooth"), _dev(down, (torch.bfloat16, torch.int16), "down"), r,
-        prec, _dev(xq, (torch.uint8,), "xq"), _dev(xscale, (torch.float32, torch.uint8), "xscale"),
-        _dev(h, (torch.float32,), "h"), _stream(stream))
+    bf = (torch.bfloat16, torch.int16)
+    pX, ps, pd, pq, pxs, ph = _ptrs(
+        (X, bf, "X"), (smooth, (torch.float32,), "smooth", (K,)), (down, bf, "down", (r, K)),
+        (xq, (torch.uint8,), "xq", (M, K // 2)), (xscale, _scale_dtypes(prec), "xscale", (M, K // g)),
+        (h, (torch.float32,), "h", (M, r)))
+    st = lib().svdq_quantize_act(pX, M, K, ps, pd, r, prec, pq, pxs, ph, _stream(stream))
     _check(st, "svdq_quantize_act")
     return xq, xscale, h
+
+
+def _linear_specs(xq, xscale, h, wq, wscale, up, bias, prec):
+    """Shapes of the product's operands: M, K from xq, N from wq, r from up;
+    every other operand must agree with them."""
+    torch = _torch()
+    prec = _prec(prec)
+    for t, name in ((xq, "xq"), (xscale, "xscale"), (h, "h"), (wq, "wq"), (wscale, "wscale"), (up, "up")):
+        _ndim(t, 2, name)
+    M, K = xq.shape[0], xq.shape[1] * 2
+    N, r = wq.shape[0], up.shape[1]
+    g = group_of(prec)
+    bf = (torch.bfloat16, torch.int16)
+    specs = [(xq, (torch.uint8,), "xq"), (xscale, _scale_dtypes(prec), "xscale", (M, K // g)),
+             (h, (torch.float32,), "h", (M, r)), (wq, (torch.uint8,), "wq", (N, K // 2)),
+             (wscale, _scale_dtypes(prec), "wscale", (N, K // g)), (up, bf, "up", (N, r)),
+             None if bias is None else (bias, bf, "bias", (N,))]
+    return M, N, K, r, specs
 
 
 def w4a4_linear(xq, xscale, h, wq, wscale, up, bias, prec: int = INT4, epi: int = EPI_NONE,
                 Y=None, stream=None):
     """4-bit product + low-rank up projection + bias (+ GELU) -> bf16 (one kernel)."""
     torch = _torch()
-    M = xq.shape[0]
-    K = xq.shape[1] * 2
-    N = wq.shape[0]
-    r = up.shape[1]
+    M, N, K, r, specs = _linear_specs(xq, xscale, h, wq, wscale, up, bias, prec)
     if Y is None:
         Y = torch.empty((M, N), dtype=torch.bfloat16, device=xq.device)
-    pbias = None if bias is None else _dev(bias, (torch.bfloat16, torch.int16), "bias")
-    st = lib().svdq_w4a4_linear(
-        _dev(xq, (torch.uint8,), "xq"), _dev(xscale, (torch.float32, torch.uint8), "xscale"),
-        _dev(h, (torch.float32,), "h"), _dev(wq, (torch.uint8,), "wq"),
-        _dev(wscale, (torch.float32, torch.uint8), "wscale"), _dev(up, (torch.bfloat16, torch.int16), "up"),
-        pbias, M, N, K, r, prec, epi, _dev(Y, (torch.bfloat16, torch.int16), "Y"), _stream(stream))
+    *ptrs, pY = _ptrs(*specs, (Y, (torch.bfloat16, torch.int16), "Y", (M, N)))
+    st = lib().svdq_w4a4_linear(*ptrs, M, N, K, r, prec, epi, pY, _stream(stream))
     _check(st, "svdq_w4a4_linear")
     return Y
 
@@ -241,24 +307,16 @@ def w4a4_linear_splitk(xq, xscale, h, wq, wscale, up, bias, prec: int = MXFP4, e
     `work` is None this binding allocates it with torch; pass a preallocated
     tensor of linear_splitk_workspace_bytes(...) bytes in a serving loop."""
     torch = _torch()
-    M = xq.shape[0]
-    K = xq.shape[1] * 2
-    N = wq.shape[0]
-    r = up.shape[1]
+    M, N, K, r, specs = _linear_specs(xq, xscale, h, wq, wscale, up, bias, prec)
     if Y is None:
         Y = torch.empty((M, N), dtype=torch.bfloat16, device=xq.device)
     need = linear_splitk_workspace_bytes(M, N, K, prec)
     if work is None and need > 0:
         work = torch.empty(need // 4, dtype=torch.float32, device=xq.device)
-    pwork = None if work is None else _dev(work, (torch.float32, torch.uint8), "work")
+    wspec = None if work is None else (work, (torch.float32, torch.uint8), "work")
+    *ptrs, pY, pwork = _ptrs(*specs, (Y, (torch.bfloat16, torch.int16), "Y", (M, N)), wspec)
     nbytes = 0 if work is None else work.numel() * work.element_size()
-    pbias = None if bias is None else _dev(bias, (torch.bfloat16, torch.int16), "bias")
-    st = lib().svdq_w4a4_linear_splitk(
-        _dev(xq, (torch.uint8,), "xq"), _dev(xscale, (torch.float32, torch.uint8), "xscale"),
-        _dev(h, (torch.float32,), "h"), _dev(wq, (torch.uint8,), "wq"),
-        _dev(wscale, (torch.float32, torch.uint8), "wscale"), _dev(up, (torch.bfloat16, torch.int16), "up"),
-        pbias, M, N, K, r, prec, epi, _dev(Y, (torch.bfloat16, torch.int16), "Y"), pwork, nbytes,
-        _stream(stream))
+    st = lib().svdq_w4a4_linear_splitk(*ptrs, M, N, K, r, prec, epi, pY, pwork, nbytes, _stream(stream))
     _check(st, "svdq_w4a4_linear_splitk")
     return Y
 
@@ -274,29 +332,24 @@ def w4a4_linear_requant(xq, xscale, h, wq, wscale, up, bias, smooth2, down2, pre
     scales and h (smooth2, down2 of that layer) instead of Y.  Returns
     (xq2, xscale2, h2)."""
     torch = _torch()
-    M = xq.shape[0]
-    K = xq.shape[1] * 2
-    N = wq.shape[0]
-    r = up.shape[1]
+    M, N, K, r, specs = _linear_specs(xq, xscale, h, wq, wscale, up, bias, prec)
+    g = group_of(prec)
     dev = xq.device
     if out is None:
-        scales = (torch.empty((M, max(N // 64, 1)), dtype=torch.float32, device=dev) if prec == INT4
-                  else torch.empty((M, max(N // 32, 1)), dtype=torch.uint8, device=dev))
+        scales = (torch.empty((M, N // 64), dtype=torch.float32, device=dev) if prec == INT4
+                  else torch.empty((M, N // 32), dtype=torch.uint8, device=dev))
         out = (torch.empty((M, N // 2), dtype=torch.uint8, device=dev), scales,
                torch.empty((M, r), dtype=torch.float32, device=dev))
     xq2, xs2, h2 = out
     nbytes = requant_workspace_bytes(M, N, r, prec)
     if work is None:
         work = torch.empty((max(nbytes, 16),), dtype=torch.uint8, device=dev)
-    pbias = None if bias is None else _dev(bias, (torch.bfloat16, torch.int16), "bias")
-    st = lib().svdq_w4a4_linear_requant(
-        _dev(xq, (torch.uint8,), "xq"), _dev(xscale, (torch.float32, torch.uint8), "xscale"),
-        _dev(h, (torch.float32,), "h"), _dev(wq, (torch.uint8,), "wq"),
-        _dev(wscale, (torch.float32, torch.uint8), "wscale"), _dev(up, (torch.bfloat16, torch.int16), "up"),
-        pbias, M, N, K, r, prec, epi, _dev(smooth2, (torch.float32,), "smooth2"),
-        _dev(down2, (torch.bfloat16, torch.int16), "down2"), _dev(xq2, (torch.uint8,), "xq2"),
-        _dev(xs2, (torch.float32, torch.uint8), "xscale2"), _dev(h2, (torch.float32,), "h2"),
-        _dev(work, (torch.uint8, torch.float32), "work"), work.numel() * work.element_size(), _stream(stream))
+    bf = (torch.bfloat16, torch.int16)
+    ptrs = _ptrs(*specs, (smooth2, (torch.float32,), "smooth2", (N,)), (down2, bf, "down2", (r, N)),
+                 (xq2, (torch.uint8,), "xq2", (M, N // 2)), (xs2, _scale_dtypes(prec), "xscale2", (M, N // g)),
+                 (h2, (torch.float32,), "h2", (M, r)), (work, (torch.uint8, torch.float32), "work"))
+    st = lib().svdq_w4a4_linear_requant(*ptrs[:7], M, N, K, r, prec, epi, *ptrs[7:],
+                                        work.numel() * work.element_size(), _stream(stream))
     _check(st, "svdq_w4a4_linear_requant")
     return xq2, xs2, h2
 
@@ -306,21 +359,15 @@ def w4a4_linear_qkv_norm_rope(xq, xscale, h, wq, wscale, up, bias, norm_q, norm_
     """w4a4_linear of a fused QKV projection (N = 3 H 128) with the Q/K
     RMS-norm and rotary embedding applied in its epilogue (one kernel)."""
     torch = _torch()
-    M = xq.shape[0]
-    K = xq.shape[1] * 2
-    N = wq.shape[0]
-    r = up.shape[1]
+    M, N, K, r, specs = _linear_specs(xq, xscale, h, wq, wscale, up, bias, prec)
     if Y is None:
         Y = torch.empty((M, N), dtype=torch.bfloat16, device=xq.device)
-    pbias = None if bias is None else _dev(bias, (torch.bfloat16, torch.int16), "bias")
-    st = lib().svdq_w4a4_linear_qkv_norm_rope(
-        _dev(xq, (torch.uint8,), "xq"), _dev(xscale, (torch.float32, torch.uint8), "xscale"),
-        _dev(h, (torch.float32,), "h"), _dev(wq, (torch.uint8,), "wq"),
-        _dev(wscale, (torch.float32, torch.uint8), "wscale"), _dev(up, (torch.bfloat16, torch.int16), "up"),
-        pbias, M, N, K, r, prec, _dev(norm_q, (torch.bfloat16, torch.int16), "norm_q"),
-        _dev(norm_k, (torch.bfloat16, torch.int16), "norm_k"), float(eps),
-        _dev(rope_cos, (torch.float32,), "rope_cos"), _dev(rope_sin, (torch.float32,), "rope_sin"),
-        _dev(Y, (torch.bfloat16, torch.int16), "Y"), _stream(stream))
+    bf = (torch.bfloat16, torch.int16)
+    ptrs = _ptrs(*specs, (norm_q, bf, "norm_q", (128,)), (norm_k, bf, "norm_k", (128,)),
+                 (rope_cos, (torch.float32,), "rope_cos", (M, 64)), (rope_sin, (torch.float32,), "rope_sin", (M, 64)),
+                 (Y, bf, "Y", (M, N)))
+    st = lib().svdq_w4a4_linear_qkv_norm_rope(*ptrs[:7], M, N, K, r, prec, ptrs[7], ptrs[8], float(eps),
+                                              *ptrs[9:], _stream(stream))
     _check(st, "svdq_w4a4_linear_qkv_norm_rope")
     return Y
 
@@ -329,6 +376,8 @@ def awq_pack_weights(W: np.ndarray):
     """Weight-only AWQ W4A16 packing (host): bf16 bits [N][K] ->
     (wq uint8 [N][K/2], wscale fp32 [N][K/64])."""
     W, pW = _np(W, np.uint16)
+    if W.ndim != 2:
+        raise ValueError(f"W must have 2 dimensions, got shape {W.shape}")
     N, K = W.shape
     wq = np.zeros((N, K // 2), np.uint8)
     wscale = np.zeros((N, max(K // 64, 0)), np.float32)
@@ -340,15 +389,17 @@ def awq_pack_weights(W: np.ndarray):
 def awq_w4a16_linear(X, wq, wscale, bias=None, Y=None, stream=None):
     """Weight-only 4-bit linear with bf16 activations -> bf16 (one kernel)."""
     torch = _torch()
+    for t, name in ((X, "X"), (wq, "wq"), (wscale, "wscale")):
+        _ndim(t, 2, name)
     M, K = X.shape
     N = wq.shape[0]
     if Y is None:
         Y = torch.empty((M, N), dtype=torch.bfloat16, device=X.device)
-    pbias = None if bias is None else _dev(bias, (torch.bfloat16, torch.int16), "bias")
-    st = lib().svdq_awq_w4a16_linear(
-        _dev(X, (torch.bfloat16, torch.int16), "X"), _dev(wq, (torch.uint8,), "wq"),
-        _dev(wscale, (torch.float32,), "wscale"), pbias, M, N, K,
-        _dev(Y, (torch.bfloat16, torch.int16), "Y"), _stream(stream))
+    bf = (torch.bfloat16, torch.int16)
+    pX, pq, ps, pb, pY = _ptrs((X, bf, "X"), (wq, (torch.uint8,), "wq", (N, K // 2)),
+                               (wscale, (torch.float32,), "wscale", (N, K // 64)),
+                               None if bias is None else (bias, bf, "bias", (N,)), (Y, bf, "Y", (M, N)))
+    st = lib().svdq_awq_w4a16_linear(pX, pq, ps, pb, M, N, K, pY, _stream(stream))
     _check(st, "svdq_awq_w4a16_linear")
     return Y
 

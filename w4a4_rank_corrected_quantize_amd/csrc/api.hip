@@ -45,7 +45,14 @@ svdq_status check_common(int M, int K, int rank, svdq_precision prec)
     if (rank != SVDQ_RANK) return SVDQ_ERR_UNSUPPORTED;
     const int g = group_size(prec);
     if (K < g || K % g != 0) return SVDQ_ERR_SHAPE;
+    if (!elems_ok(M, K)) return SVDQ_ERR_SHAPE;
     return SVDQ_OK;
+}
+
+// the weight and output matrices of a linear
+svdq_status check_linear_sizes(int M, int N, int K)
+{
+    return elems_ok(N, K) && elems_ok(M, N) ? SVDQ_OK : SVDQ_ERR_SHAPE;
 }
 
 }  // namespace
@@ -122,6 +129,7 @@ extern "C" svdq_status svdq_w4a4_linear(const uint8_t *xq, const void *xscale, c
     if (N < 0) return SVDQ_ERR_INVALID_ARG;
     if (epi != SVDQ_EPI_NONE && epi != SVDQ_EPI_GELU_TANH) return SVDQ_ERR_INVALID_ARG;
     if (N % 8 != 0) return SVDQ_ERR_SHAPE;
+    if (check_linear_sizes(M, N, K) != SVDQ_OK) return SVDQ_ERR_SHAPE;
     // buffers of zero size may be NULL (empty tensors have no storage)
     if ((M > 0 && (!xq || !xscale || !h)) || (N > 0 && (!wq || !wscale || !up)) ||
         (M > 0 && N > 0 && !Y))
@@ -141,6 +149,7 @@ extern "C" size_t svdq_w4a4_linear_splitk_workspace_bytes(int M, int N, int K, s
 {
     if (M <= 0 || N <= 0 || K <= 0 || (prec != SVDQ_INT4 && prec != SVDQ_MXFP4)) return 0;
     if (K % group_size(prec) != 0) return 0;
+    if (!elems_ok(M, K) || check_linear_sizes(M, N, K) != SVDQ_OK) return 0;
     if (current_device_ok() != SVDQ_OK) return 0;       // the split depends on the device's CU count
     return splitk_work_bytes(M, N, K, prec);
 }
@@ -156,6 +165,7 @@ extern "C" svdq_status svdq_w4a4_linear_splitk(const uint8_t *xq, const void *xs
     if (N < 0) return SVDQ_ERR_INVALID_ARG;
     if (epi != SVDQ_EPI_NONE && epi != SVDQ_EPI_GELU_TANH) return SVDQ_ERR_INVALID_ARG;
     if (N % 8 != 0) return SVDQ_ERR_SHAPE;
+    if (check_linear_sizes(M, N, K) != SVDQ_OK) return SVDQ_ERR_SHAPE;
     if ((M > 0 && (!xq || !xscale || !h)) || (N > 0 && (!wq || !wscale || !up)) ||
         (M > 0 && N > 0 && !Y))
         return SVDQ_ERR_INVALID_ARG;
@@ -192,6 +202,7 @@ extern "C" svdq_status svdq_w4a4_linear_requant(const uint8_t *xq, const void *x
     if (N < 0) return SVDQ_ERR_INVALID_ARG;
     if (epi != SVDQ_EPI_NONE && epi != SVDQ_EPI_GELU_TANH) return SVDQ_ERR_INVALID_ARG;
     if (N % 64 != 0) return SVDQ_ERR_SHAPE;
+    if (check_linear_sizes(M, N, K) != SVDQ_OK) return SVDQ_ERR_SHAPE;
     if (!requant_supported(M, N, K, prec)) return SVDQ_ERR_UNSUPPORTED;
     // buffers of zero size may be NULL (empty tensors have no storage)
     if ((M > 0 && (!xq || !xscale || !h)) || (N > 0 && (!wq || !wscale || !up || !smooth2 || !down2)) ||
@@ -222,6 +233,7 @@ extern "C" svdq_status svdq_w4a4_linear_qkv_norm_rope(const uint8_t *xq, const v
     if (N < 0) return SVDQ_ERR_INVALID_ARG;
     if (!(eps >= 0.0f) || eps > 3.0e38f) return SVDQ_ERR_INVALID_ARG;      // finite, non-negative
     if (N % 384 != 0) return SVDQ_ERR_SHAPE;
+    if (check_linear_sizes(M, N, K) != SVDQ_OK) return SVDQ_ERR_SHAPE;
     if (prec != SVDQ_INT4) return SVDQ_ERR_UNSUPPORTED;
     // buffers of zero size may be NULL (empty tensors have no storage)
     if ((M > 0 && (!xq || !xscale || !h || !rope_cos || !rope_sin)) ||
@@ -245,6 +257,7 @@ extern "C" svdq_status svdq_awq_w4a16_linear(const uint16_t *X, const uint8_t *w
 {
     if (M < 0 || N < 0 || K < 0) return SVDQ_ERR_INVALID_ARG;
     if (K < 256 || K % 256 != 0) return SVDQ_ERR_SHAPE;
+    if (!elems_ok(M, K) || check_linear_sizes(M, N, K) != SVDQ_OK) return SVDQ_ERR_SHAPE;
     // buffers of zero size may be NULL (empty tensors have no storage)
     if ((M > 0 && !X) || (N > 0 && (!wq || !wscale)) || (M > 0 && N > 0 && !Y)) return SVDQ_ERR_INVALID_ARG;
     if (!aligned16(X) || !aligned16(wq) || !aligned16(wscale) || (bias && !aligned16(bias)) || !aligned16(Y))

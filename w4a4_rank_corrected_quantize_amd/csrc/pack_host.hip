@@ -317,6 +317,7 @@ static svdq_status check_pack_args(const void *W, int N, int K, int rank, svdq_p
     if (rank != SVDQ_RANK) return SVDQ_ERR_UNSUPPORTED;
     int g = group_size(prec);
     if (N < 1 || K < g || K % g != 0) return SVDQ_ERR_SHAPE;
+    if (!elems_ok(N, K)) return SVDQ_ERR_SHAPE;
     return SVDQ_OK;
 }
 
@@ -444,6 +445,7 @@ extern "C" svdq_status svdq_awq_pack_weights(const uint16_t *W, int N, int K, ui
     if (!W || !wq || !wscale) return SVDQ_ERR_INVALID_ARG;
     if (N < 0 || K < 0) return SVDQ_ERR_INVALID_ARG;
     if (N < 1 || K < 256 || K % 256 != 0) return SVDQ_ERR_SHAPE;
+    if (!elems_ok(N, K)) return SVDQ_ERR_SHAPE;
     for (int64_t i = 0; i < (int64_t)N * K; ++i)
         if (!bf16_finite(W[i])) return SVDQ_ERR_NONFINITE;
     const int G = K / 64;

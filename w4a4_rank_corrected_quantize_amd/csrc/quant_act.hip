@@ -186,11 +186,11 @@ __global__ __launch_bounds__(64 * K1_WAVES) void quant_act_kernel(
                 a = group_max<4>(a);
                 const uint32_t e8 = mx_block_e8m0(a);
                 const float inv = mx_inv_scale(e8);
-                // t = xhat 2^-X is exact; the hardware E2M1 conversion (unit
-                // scale) rounds to the grid with ties to the even index,
-                // saturates at 6 and keeps the sign of zero, i.e. it is
-                // e2m1_code (checked on the GPU against e2m1_code for every fp32
-                // t with |t| < 16, both signs)
+                // t = xhat 2^-X is exact and below 16; the hardware E2M1
+                // conversion (unit scale) rounds to the grid with ties to the
+                // even index, saturates at 6 and keeps the sign of zero
+                // (tests/native/e2m1_sweep.hip checks this on the GPU for every
+                // fp32 t with |t| < 16, both signs)
                 code = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, v[0] * inv, v[1] * inv, 1.0f, 0);
                 code = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(code, v[2] * inv, v[3] * inv, 1.0f, 1);
                 code = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(code, v[4] * inv, v[5] * inv, 1.0f, 2);

@@ -11,6 +11,12 @@ namespace svdq {
 
 int group_size(svdq_precision prec);
 
+// Every matrix a call touches (M x K, N x K, M x N) must hold fewer than
+// SVDQ_MAX_ELEMENTS elements, so every byte offset inside one buffer fits in
+// 31 bits: the LDS-DMA loads take 32-bit lane offsets and the host loops
+// index rows with int products.
+inline bool elems_ok(int64_t rows, int64_t cols) { return rows * cols < (int64_t)SVDQ_MAX_ELEMENTS; }
+
 // Compute units of the current device (cached per device; 256 if unknown).
 int device_cu_count();
 

@@ -71,6 +71,12 @@ def lib():
         L.oracle_awq_code.argtypes = [P, I]
         L.oracle_awq_pack.argtypes = [P, I, I, P, P]
         L.oracle_awq_linear.argtypes = [P, P, P, P, I, I, I, P]
+        L.oracle_nf4_codebook.argtypes = [P]
+        L.oracle_nf4_code.restype = I
+        L.oracle_nf4_code.argtypes = [ctypes.c_float, P]
+        L.oracle_nf4_pack.argtypes = [P, I, I, P, P, P]
+        L.oracle_nf4_dequant.argtypes = [P, P, P, I, I, P]
+        L.oracle_nf4_linear.argtypes = [P, P, P, P, P, I, I, I, P, I, P]
         _lib = L
     return _lib
 
@@ -336,4 +342,55 @@ def qkv_norm_rope(ylin, norm_q, norm_k, eps: float, rope_cos, rope_sin):
     c, s = _c(rope_cos, np.float32), _c(rope_sin, np.float32)
     out = np.zeros((M, N), np.float64)
     lib().oracle_qkv_norm_rope(_p(y), M, N, _p(wq_), _p(wk_), float(eps), _p(c), _p(s), _p(out))
+    return out
+
+
+# ------------------------------------------------------- NF4 W4A16 (weight-only)
+
+def nf4_codebook() -> np.ndarray:
+    """The 16 fp32 NF4 levels (ascending; level 7 is 0, levels 0 and 15 are -1, 1)."""
+    c = np.zeros(16, np.float32)
+    lib().oracle_nf4_codebook(_p(c))
+    return c
+
+
+def nf4_code(x: float) -> int:
+    """Code of one normalized weight x = fl32(w / absmax)."""
+    c = nf4_codebook()
+    return int(lib().oracle_nf4_code(ctypes.c_float(float(x)), _p(c)))
+
+
+def nf4_pack(W):
+    """bf16 bits [N][K] (K % 64 == 0) -> (codes uint8 [N][K/2], statistic
+    codes uint8 [N*K/64], chunk scales fp32 [ceil(N*K/64 / 256)])."""
+    W = _c(W, np.uint16)
+    N, K = W.shape
+    nb = N * (K // 64)
+    wq = np.zeros((N, K // 2), np.uint8)
+    qabs = np.zeros(nb, np.uint8)
+    chunk = np.zeros((nb + 255) // 256, np.float32)
+    lib().oracle_nf4_pack(_p(W), N, K, _p(wq), _p(qabs), _p(chunk))
+    return wq, qabs, chunk
+
+
+def nf4_dequant(wq, qabs, chunk, N: int, K: int) -> np.ndarray:
+    """Dequantized weights w' as bf16 bits [N][K]."""
+    wq, qabs, chunk = _c(wq, np.uint8), _c(qabs, np.uint8), _c(chunk, np.float32)
+    out = np.zeros((N, K), np.uint16)
+    lib().oracle_nf4_dequant(_p(wq), _p(qabs), _p(chunk), N, K, _p(out))
+    return out
+
+
+def nf4_linear(X, wq, qabs, chunk, bias, rows=None) -> np.ndarray:
+    """y = X W'^T + b in fp64 ([len(rows) or M][N])."""
+    X = _c(X, np.uint16)
+    wq, qabs, chunk = _c(wq, np.uint8), _c(qabs, np.uint8), _c(chunk, np.float32)
+    M, K = X.shape
+    N = wq.shape[0]
+    b = None if bias is None else _c(bias, np.uint16)
+    r = None if rows is None else _c(rows, np.int32)
+    R = M if r is None else r.size
+    out = np.zeros((R, N), np.float64)
+    lib().oracle_nf4_linear(_p(X), _p(wq), _p(qabs), _p(chunk), _p(b), M, N, K, _p(r), 0 if r is None else r.size,
+                            _p(out))
     return out

@@ -490,3 +490,169 @@ int oracle_num_threads(void)
 #endif
     return t;
 }
+
+/* ------------------------------------------------ NF4 W4A16 (weight-only) */
+
+/*
+ * Weight-only 4-bit comparison path of the pages ("BitsAndBytes W4
+ * Quantization", vLLM-Omni docs, sections "Overview" and "Parameters":
+ * BF16 weights quantized at load time to the "nf4" 4-bit data type,
+ * activations kept in bf16, and with compress_statistics the block scaling
+ * statistics double-quantized).  The pages name the data type only; the
+ * readings below follow the published NF4 construction (quantiles of the
+ * standard normal distribution normalized to [-1, 1], with an exact zero):
+ *
+ *   codebook   16 fp32 levels c_0 < ... < c_15: c_7 = 0; the 8 positive
+ *              levels are Phi^-1(1/2 + j (1/2 - d) / 8), j = 1..8, the 7
+ *              negative ones -Phi^-1(1/2 + j (1/2 - d) / 7), j = 1..7, all
+ *              divided by Phi^-1(1 - d) (so c_0 = -1, c_15 = 1), with the
+ *              tail probability d = (1/32 + 1/30) / 2 (halfway between the
+ *              half-bin probabilities of 16 and 15 equal bins); each level
+ *              rounded once to fp32
+ *   block      64 consecutive weights of a row; a = max |w| (fp32)
+ *   code       x = fl32(w / a); the nearest level, comparing x with the
+ *              midpoints (c_i + c_i+1) / 2 exactly, a tie going to the level
+ *              of smaller magnitude; a == 0 gives code 7 (zero)
+ *   statistics the block absmaxes in row-major (n, block) order, in chunks
+ *              of 256: s = max a over the chunk; q_b = round-half-even of
+ *              the exact 255 a_b / s (0 when s == 0); the chunk stores
+ *              d = fl32(s / 255)
+ *   dequant    ahat_b = fl32(q_b * d);  w'_nk = bf16(fl32(c_code * ahat_b))
+ *   linear     y_mn = sum_k X_mk w'_nk + b_n  (X bf16; fp64 here)
+ *
+ * Phi^-1 is found by bisection on Phi(x) = erfc(-x / sqrt 2) / 2 to the
+ * last fp64 bit: slow and plain.
+ */
+static double nf4_phi(double x) { return 0.5 * erfc(-x / sqrt(2.0)); }
+
+static double nf4_phi_inv(double p)
+{
+    double lo = -40.0, hi = 40.0;
+    for (int it = 0; it < 200; ++it) {
+        double mid = 0.5 * (lo + hi);
+        if (mid == lo || mid == hi) break;
+        if (nf4_phi(mid) < p) lo = mid;
+        else hi = mid;
+    }
+    return 0.5 * (lo + hi);
+}
+
+void oracle_nf4_codebook(float *c)
+{
+    const double d = (1.0 / 32.0 + 1.0 / 30.0) / 2.0;
+    const double top = nf4_phi_inv(1.0 - d);
+    c[7] = 0.0f;
+    for (int j = 1; j <= 8; ++j) c[7 + j] = (float)(nf4_phi_inv(0.5 + j * (0.5 - d) / 8.0) / top);
+    for (int j = 1; j <= 7; ++j) c[7 - j] = (float)(-nf4_phi_inv(0.5 + j * (0.5 - d) / 7.0) / top);
+}
+
+/* Code of one normalized weight x (|x| <= 1). */
+int oracle_nf4_code(float x, const float *c)
+{
+    int code = 0;
+    for (int i = 0; i < 15; ++i) {
+        double mid = ((double)c[i] + (double)c[i + 1]) / 2.0;   /* exact in fp64 */
+        if ((double)x > mid || ((double)x == mid && mid < 0.0)) code = i + 1;
+    }
+    return code;
+}
+
+/* Round-half-even of the exact 255 a / s, for 0 <= a <= s, s > 0. */
+static int nf4_stat_code(float a, float s)
+{
+    double num = 255.0 * (double)a;                 /* exact */
+    int k = (int)floor(num / (double)s);
+    /* settle k exactly: k s <= 255 a < (k + 1) s, each product exact */
+    while (k > 0 && (double)k * (double)s > num) --k;
+    while ((double)(k + 1) * (double)s <= num) ++k;
+    double twice = 2.0 * num, mid = (2.0 * k + 1.0) * (double)s;   /* exact */
+    if (twice > mid || (twice == mid && (k & 1))) ++k;
+    return k > 255 ? 255 : k;
+}
+
+/* W bf16 [N][K], K % 64 == 0 -> codes [N][K/2] (element 2i low nibble),
+ * statistic codes [N*K/64], chunk scales [ceil(N*K/64 / 256)]. */
+void oracle_nf4_pack(const uint16_t *W, int N, int K, uint8_t *wq, uint8_t *qabs, float *chunk)
+{
+    float c[16];
+    oracle_nf4_codebook(c);
+    const int G = K / 64;
+    const int64_t nb = (int64_t)N * G;
+    float *amax = (float *)malloc(sizeof(float) * (size_t)(nb > 0 ? nb : 1));
+    for (int n = 0; n < N; ++n) {
+        for (int g = 0; g < G; ++g) {
+            const uint16_t *w = W + (size_t)n * K + 64 * g;
+            float a = 0.0f;
+            for (int i = 0; i < 64; ++i) {
+                float t = (float)fabs(bf16_val(w[i]));
+                if (t > a) a = t;
+            }
+            amax[(size_t)n * G + g] = a;
+            uint8_t *dst = wq + (size_t)n * (K / 2) + 32 * g;
+            for (int i = 0; i < 64; i += 2) {
+                int c0 = 7, c1 = 7;
+                if (a > 0.0f) {
+                    c0 = oracle_nf4_code((float)(bf16_val(w[i]) / (double)a), c);
+                    c1 = oracle_nf4_code((float)(bf16_val(w[i + 1]) / (double)a), c);
+                }
+                dst[i / 2] = (uint8_t)(c0 | (c1 << 4));
+            }
+        }
+    }
+    const int64_t nchunk = (nb + 255) / 256;
+    for (int64_t ch = 0; ch < nchunk; ++ch) {
+        const int64_t b0 = 256 * ch, b1 = b0 + 256 < nb ? b0 + 256 : nb;
+        float s = 0.0f;
+        for (int64_t b = b0; b < b1; ++b)
+            if (amax[b] > s) s = amax[b];
+        chunk[ch] = (float)((double)s / 255.0);
+        for (int64_t b = b0; b < b1; ++b) qabs[b] = (uint8_t)(s > 0.0f ? nf4_stat_code(amax[b], s) : 0);
+    }
+    free(amax);
+}
+
+static uint16_t bf16_bits_rne(float f)
+{
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    if ((u & 0x7F800000u) == 0x7F800000u) return (uint16_t)(u >> 16);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+/* Dequantized weights w' (bf16 bits) [N][K]. */
+void oracle_nf4_dequant(const uint8_t *wq, const uint8_t *qabs, const float *chunk, int N, int K, uint16_t *Wd)
+{
+    float c[16];
+    oracle_nf4_codebook(c);
+    const int G = K / 64;
+    for (int n = 0; n < N; ++n)
+        for (int k = 0; k < K; ++k) {
+            const int64_t b = (int64_t)n * G + k / 64;
+            const float ahat = (float)((double)qabs[b] * (double)chunk[b / 256]);
+            const uint8_t byte = wq[(size_t)n * (K / 2) + k / 2];
+            const int code = (k & 1) ? byte >> 4 : byte & 15;
+            Wd[(size_t)n * K + k] = bf16_bits_rne((float)((double)c[code] * (double)ahat));
+        }
+}
+
+/* y = X W'^T + b in fp64 for the listed rows (rows == NULL: all M). */
+void oracle_nf4_linear(const uint16_t *X, const uint8_t *wq, const uint8_t *qabs, const float *chunk,
+                       const uint16_t *bias, int M, int N, int K, const int *rows, int nrows, double *out)
+{
+    uint16_t *Wd = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)N * (size_t)K + 2);
+    oracle_nf4_dequant(wq, qabs, chunk, N, K, Wd);
+    const int R = rows ? nrows : M;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int i = 0; i < R; ++i) {
+        const int m = rows ? rows[i] : i;
+        const uint16_t *x = X + (size_t)m * K;
+        for (int n = 0; n < N; ++n) {
+            const uint16_t *w = Wd + (size_t)n * K;
+            double acc = 0.0;
+            for (int k = 0; k < K; ++k) acc += bf16_val(x[k]) * bf16_val(w[k]);
+            out[(size_t)i * N + n] = acc + (bias ? bf16_val(bias[n]) : 0.0);
+        }
+    }
+    free(Wd);
+}

@@ -182,6 +182,13 @@ static int int4_of_nibble(int nib) { return (nib & 8) ? -(nib & 7) : (nib & 7); 
 
 int oracle_int4_value(uint8_t code) { return int4_of_nibble(code & 15); }
 
+/* Twice the E2M1 value of a code (an integer in [-12, 12]). */
+static int e2m1_twice(int code)
+{
+    const int m = (int)(2.0 * E2M1_GRID[code & 7]);
+    return (code & 8) ? -m : m;
+}
+
 static int nibble_at(const uint8_t *row, int k)
 {
     uint8_t b = row[k >> 1];
@@ -324,10 +331,13 @@ void oracle_linear(const uint8_t *xq, const void *xscale, const double *h,
                 const uint8_t *ex = (const uint8_t *)xscale + (size_t)m * (K / 32);
                 const uint8_t *ew = (const uint8_t *)wscale + (size_t)n * (K / 32);
                 for (int b = 0; b < K / 32; ++b) {
-                    double P = 0.0;
+                    /* Every E2M1 value is a multiple of 1/2 below 6 in magnitude,
+                     * so the block's dot product is the integer sum of the
+                     * doubled values' products, divided by 4 (exact). */
+                    long long S = 0;
                     for (int k = 32 * b; k < 32 * b + 32; ++k)
-                        P += oracle_e2m1_value((uint8_t)nibble_at(xr, k)) *
-                             oracle_e2m1_value((uint8_t)nibble_at(wr, k));
+                        S += (long long)e2m1_twice(nibble_at(xr, k)) * (long long)e2m1_twice(nibble_at(wr, k));
+                    const double P = (double)S / 4.0;
                     q4 += oracle_e8m0_value(ex[b]) * oracle_e8m0_value(ew[b]) * P;
                 }
             }

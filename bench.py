@@ -30,6 +30,7 @@ import numpy as np  # noqa: E402
 
 PEAK_INT8_TOPS = 5000.0     # MI355X dense int8 matrix peak, 5.0 POP/s
 PEAK_FP4_TFLOPS = 10100.0   # MI355X dense MXFP4 matrix peak, 10.1 PFLOP/s
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak, 2.5 PFLOP/s
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, 8 TB/s
 
 # HBM traffic of svdq_w4a4_linear per launch, from two rocprofv3 --pmc runs
@@ -85,11 +86,13 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--prec", choices=["int4", "mxfp4"], default="int4")
-    ap.add_argument("--layer", choices=["fc1", "qkv", "fc2", "mlp", "awq", "qkvnorm"], default="fc1",
+    ap.add_argument("--layer", choices=["fc1", "qkv", "fc2", "mlp", "awq", "qkvnorm", "nf4_fc1", "nf4_qkv"],
+                    default="fc1",
                     help="fc1 is the headline workload; fc2 takes fc1's output (computed on the GPU); "
                          "mlp times fc1 -> fc2 with fc2's activation step fused into fc1's epilogue, "
                          "next to the unfused pair; awq times the weight-only AWQ W4A16 modulation layer; "
-                         "qkvnorm is qkv with the Q/K RMS-norm and rotary embedding fused into the epilogue")
+                         "qkvnorm is qkv with the Q/K RMS-norm and rotary embedding fused into the epilogue; "
+                         "nf4_fc1 / nf4_qkv time the weight-only NF4 W4A16 comparison path on those shapes")
     ap.add_argument("--copy-calibration", type=int, metavar="MIB", default=0,
                     help="only run a plain copy of MIB MiB (to scale the HBM byte counters)")
     ap.add_argument("--sets", type=int, default=0,
@@ -125,6 +128,9 @@ def main():
         return
     if args.layer == "awq":
         awq_main(args, torch, svdq, synth)
+        return
+    if args.layer.startswith("nf4_"):
+        nf4_main(args, torch, svdq, synth)
         return
     if not args.sets:
         args.sets = 3
@@ -449,6 +455,87 @@ def awq_main(args, torch, svdq, synth):
         "roofline": {"bound": "hbm", "kernel": "svdq_awq_w4a16_linear", "achieved": round(gbs, 1),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
                      "traffic": None, "avg_ms": round(ms, 5), "algorithmic_bytes": nbytes},
+        "host_pack_s": round(pack_s, 2),
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def nf4_bytes(M, N, K):
+    nb = N * (K // 64)
+    return 2 * M * K + N * K // 2 + nb + 4 * ((nb + 255) // 256) + 2 * M * N
+
+
+def nf4_main(args, torch, svdq, synth):
+    """The weight-only NF4 W4A16 comparison path (bf16 activations, NF4
+    weights with double-quantized statistics, dequantized inside the bf16
+    matrix-core GEMM) on the QKV or fc1 shape at 4608 tokens."""
+    spec = synth.SPECS[args.layer]
+    M, K, N = spec.M, spec.K, spec.N
+    nsets = args.sets or 3
+    print(f"[bench] generating {spec.name} {M}x{K}->{N} and packing on the host", file=sys.stderr, flush=True)
+    L = synth.make_layer(spec)
+    t0 = time.time()
+    wq, qabs, chunk = svdq.nf4_pack_weights(L["W"])
+    pack_s = time.time() - t0
+    sets = [dict(X=svdq.bf16_tensor(L["X"]), wq=torch.from_numpy(wq).cuda(), qa=torch.from_numpy(qabs).cuda(),
+                 ch=torch.from_numpy(chunk).cuda(), Y=torch.empty((M, N), dtype=torch.bfloat16, device="cuda"))
+            for _ in range(nsets)]
+
+    def step(b):
+        svdq.nf4_w4a16_linear(b["X"], b["wq"], b["qa"], b["ch"], None, Y=b["Y"])
+
+    for i in range(args.warmup):
+        step(sets[i % nsets])
+    torch.cuda.synchronize()
+    print(f"[bench] warmup done ({args.warmup} steps); timing {args.steps} steps", file=sys.stderr, flush=True)
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(args.steps):
+        step(sets[i % nsets])
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / args.steps
+    flops = 2.0 * M * N * K
+    tflops = flops / (ms * 1e-3) / 1e12
+    ref = library_reference(torch, M, N, K)
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle import oracle as O
+        print("[bench] timing the CPU oracle on a row sample", file=sys.stderr, flush=True)
+        oq, oa, oc = O.nf4_pack(L["W"])
+        rows = 64
+        t0 = time.time()
+        O.nf4_linear(L["X"], oq, oa, oc, None, rows=np.arange(rows, dtype=np.int32))
+        probe = max(time.time() - t0, 1e-3)
+        rows = int(min(M, max(8, rows * args.cpu_seconds / probe)))
+        t0 = time.time()
+        O.nf4_linear(L["X"], oq, oa, oc, None, rows=np.arange(rows, dtype=np.int32))
+        t_cpu = time.time() - t0
+        cpu = {"value": round(2.0 * rows * N * K / t_cpu / 1e12, 6), "unit": "TFLOP/s", "cores": O.num_threads(),
+               "kind": "oracle", "sample": f"{rows} of {M} token rows of the same layer, {t_cpu:.1f} s"}
+    line = {
+        "metric": "NF4 W4A16 linear TFLOP/s & % bf16-MFMA peak (weight-only comparison path)",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "nf4 weights (64-blocks, 8-bit double-quantized statistics per 256 blocks) dequantized to bf16 "
+                 "in the kernel x bf16 activations on the bf16 matrix cores, fp32 accumulation",
+        "data": "synthetic (seeded N(0,1) activations, N(0,0.02^2) weights)",
+        "config": {"workload": f"{spec.name}: {M} tokens x {K} -> {N}, NF4 weight-only, no bias; "
+                               "step = svdq_nf4_w4a16_linear",
+                   "M": M, "K": K, "N": N, "buffer_sets": nsets},
+        "roofline": {"bound": "mfma", "kernel": "svdq_nf4_w4a16_linear", "achieved": round(tflops, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None, "avg_ms": round(ms, 5), "algorithmic_bytes": nf4_bytes(M, N, K)},
+        "matrix_core_reference": ref,
         "host_pack_s": round(pack_s, 2),
         "cpu_baseline": cpu,
     }

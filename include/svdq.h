@@ -358,6 +358,67 @@ svdq_status svdq_awq_pack_weights(const uint16_t *W, int N, int K, uint8_t *wq, 
 svdq_status svdq_awq_w4a16_linear(const uint16_t *X, const uint8_t *wq, const float *wscale,
                                   const uint16_t *bias, int M, int N, int K, uint16_t *Y, void *stream);
 
+/*
+ * NF4 weight-only W4A16 layer -- the pages' comparison system
+ * ("BitsAndBytes W4 Quantization", sections "Overview" and "Parameters":
+ * BF16 weights quantized at load time to the 4-bit "nf4" data type,
+ * activations kept in bf16; compress_statistics double-quantizes the block
+ * scaling statistics).
+ *
+ * Format.  Levels: 16 fp32 quantiles of the standard normal distribution
+ * normalized to [-1, 1] with an exact zero (svdq_nf4_codebook).  A block is
+ * 64 consecutive weights of a row, with absmax a (fp32); a weight's code is
+ * the level nearest to fl32(w / a) (a tie goes to the level of smaller
+ * magnitude; a == 0 gives the zero level, code 7).  The block absmaxes, in
+ * row-major (n, block) order, are double-quantized in chunks of 256: s =
+ * max a over the chunk, the chunk stores d = fl32(s / 255) and block b stores
+ * q_b = round-half-even of 255 a_b / s.  Dequantized weight:
+ *   ahat_b = fl32(q_b * d),   w' = bf16(fl32(level[code] * ahat_b)).
+ */
+
+/* The 16 NF4 levels, ascending (level 7 is 0, levels 0 and 15 are -1 and 1);
+ * host, writes 16 floats.  Error: SVDQ_ERR_INVALID_ARG for NULL. */
+svdq_status svdq_nf4_codebook(float *levels);
+
+/*
+ * svdq_nf4_pack_weights -- host packing of one weight for the NF4 layer.
+ *   W            [N][K] bf16 bits, host            N >= 1, K >= 64, K % 64 == 0
+ *   wq           [N][K/2] uint8, host (out)        codes; in each group of 8
+ *                consecutive weights of a row, byte i holds weight i (low
+ *                nibble) and weight i + 4 (high nibble)
+ *   qabs         [N K / 64] uint8, host (out)      statistic codes, (n, block) order
+ *   chunk_scale  [ceil(N K / 64 / 256)] fp32, host (out)   d of each chunk
+ * Synchronous, all host cores.  Errors: SVDQ_ERR_INVALID_ARG,
+ * SVDQ_ERR_SHAPE, SVDQ_ERR_NONFINITE (any non-finite W).
+ */
+svdq_status svdq_nf4_pack_weights(const uint16_t *W, int N, int K, uint8_t *wq, uint8_t *qabs,
+                                  float *chunk_scale);
+
+/*
+ * svdq_nf4_dequantize -- the dequantized weights w' as bf16 [N][K] (device),
+ * from device copies of svdq_nf4_pack_weights' outputs.  One kernel launch
+ * on `stream`.  Errors: SVDQ_ERR_INVALID_ARG, SVDQ_ERR_SHAPE (K),
+ * SVDQ_ERR_MISALIGNED, SVDQ_ERR_UNSUPPORTED_DEVICE, SVDQ_ERR_HIP.
+ */
+svdq_status svdq_nf4_dequantize(const uint8_t *wq, const uint8_t *qabs, const float *chunk_scale, int N, int K,
+                                uint16_t *Wd, void *stream);
+
+/*
+ * svdq_nf4_w4a16_linear -- y = X W'^T + b, W' dequantized inside the kernel
+ * (the same w' as svdq_nf4_dequantize), sums in fp32 on the bf16 matrix
+ * cores, rounded once to bf16 (round-to-nearest-even).
+ *   X            [M][K] bf16 bits, device          M >= 0 (0: no-op)
+ *   wq, qabs, chunk_scale   device copies of svdq_nf4_pack_weights' outputs
+ *   bias         [N] bf16 bits, device, or NULL
+ *   N, K         N >= 0 (0: no-op), N % 8 == 0; K >= 64, K % 64 == 0
+ *   Y            [M][N] bf16 bits, device (out)
+ * One kernel launch.  Errors: SVDQ_ERR_INVALID_ARG, SVDQ_ERR_SHAPE,
+ * SVDQ_ERR_MISALIGNED, SVDQ_ERR_UNSUPPORTED_DEVICE, SVDQ_ERR_HIP.
+ */
+svdq_status svdq_nf4_w4a16_linear(const uint16_t *X, const uint8_t *wq, const uint8_t *qabs,
+                                  const float *chunk_scale, const uint16_t *bias, int M, int N, int K, uint16_t *Y,
+                                  void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -599,3 +599,72 @@ def test_qkv_norm_rope_deterministic_and_empty():
     Y0 = svdq.w4a4_linear_qkv_norm_rope(xq[:0], xs[:0], h[:0], *args[3:10], _t(c[:0]), _t(s[:0]))
     torch.cuda.synchronize()
     assert Y0.shape == (0, 384)
+
+
+# -------------------------------------------- NF4 W4A16 (weight-only, bf16 X)
+
+def _nf4_case(M, K, N, bias=True, seed=0):
+    rng = np.random.default_rng(seed + 31 * M + K + N)
+    X = synth.f64_to_bf16_bits(rng.standard_normal((M, K)))
+    W = synth.f64_to_bf16_bits(rng.normal(0, 0.02, (N, K)))
+    b = synth.f64_to_bf16_bits(rng.normal(0, 0.01, N)) if bias else None
+    return X, W, b
+
+
+def _nf4_run(X, W, b, rows=None):
+    """The library packs (its own storage order) and runs on the GPU; the
+    oracle packs W itself (codes checked bit-exact against the library's in
+    the CPU tests) and computes the fp64 reference."""
+    lq, la, lc = svdq.nf4_pack_weights(W)
+    oq, oa, oc = O.nf4_pack(W)
+    Y = svdq.nf4_w4a16_linear(_t(X), _t(lq), _t(la), _t(lc), _t(b))
+    torch.cuda.synchronize()
+    return Y, O.nf4_linear(X, oq, oa, oc, b, rows=rows), (lq, la, lc), (oq, oa, oc)
+
+
+@pytest.mark.parametrize("N,K", [(8, 64), (40, 128), (264, 3072), (1000, 640), (136, 12288)])
+def test_nf4_dequantize_bit_exact(N, K):
+    """The GPU's decoded weights (the values the linear multiplies) equal the
+    oracle's w' = bf16(fl32(level * fl32(q d))) bit for bit."""
+    _say(f"nf4 dequantize N={N} K={K}")
+    _, W, _ = _nf4_case(4, K, N)
+    W[0, :64] = 0                                     # a zero block
+    lq, la, lc = svdq.nf4_pack_weights(W)
+    oq, oa, oc = O.nf4_pack(W)
+    Wd = svdq.nf4_dequantize(_t(lq), _t(la), _t(lc))
+    torch.cuda.synchronize()
+    want = O.nf4_dequant(oq, oa, oc, N, K)
+    got = _np(Wd)
+    assert np.array_equal(got, want), f"dequantized weights differ at {np.argwhere(got != want)[:5]}"
+
+
+@pytest.mark.parametrize("M,K,N,bias", [(1, 64, 8, True), (37, 192, 24, False), (256, 256, 256, True),
+                                        (300, 1024, 520, True), (257, 3072, 264, False), (513, 640, 1000, True),
+                                        (64, 12288, 136, True)])
+def test_nf4_linear_synthetic(M, K, N, bias):
+    _say(f"nf4 linear M={M} K={K} N={N} bias={bias}")
+    X, W, b = _nf4_case(M, K, N, bias)
+    Y, y_ref, _, _ = _nf4_run(X, W, b)
+    _y_check(Y, y_ref, f"nf4 {M}x{K}->{N}")
+
+
+@pytest.mark.parametrize("name", ["nf4_qkv", "nf4_fc1"])
+def test_nf4_full_size(name):
+    """The comparison path's two workloads (4608 tokens, 3072 -> 9216 and
+    3072 -> 12288, activations N(0, 1)): every output against the oracle."""
+    lay = synth.make_layer(synth.SPECS[name])
+    _say(f"nf4 full size {name}")
+    Y, y_ref, _, _ = _nf4_run(lay["X"], lay["W"], lay["bias"])
+    _y_check(Y, y_ref, name)
+
+
+def test_nf4_deterministic_and_empty():
+    X, W, b = _nf4_case(300, 512, 264)
+    lq, la, lc = (_t(a) for a in svdq.nf4_pack_weights(W))
+    Y1 = svdq.nf4_w4a16_linear(_t(X), lq, la, lc, _t(b))
+    Y2 = svdq.nf4_w4a16_linear(_t(X), lq, la, lc, _t(b))
+    torch.cuda.synchronize()
+    assert torch.equal(Y1.view(torch.int16), Y2.view(torch.int16))
+    Y0 = svdq.nf4_w4a16_linear(_t(X[:0]), lq, la, lc, _t(b))
+    torch.cuda.synchronize()
+    assert Y0.shape == (0, 264)

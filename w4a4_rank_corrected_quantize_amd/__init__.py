@@ -46,7 +46,8 @@ STATUS = {
 EXPORTS = ("svdq_status_string", "svdq_version", "svdq_check_device", "svdq_pack_weights",
            "svdq_pack_residual", "svdq_quantize_act", "svdq_w4a4_linear", "svdq_requant_workspace_bytes",
            "svdq_w4a4_linear_requant", "svdq_w4a4_linear_qkv_norm_rope", "svdq_awq_pack_weights",
-           "svdq_awq_w4a16_linear", "svdq_w4a4_linear_splitk_workspace_bytes", "svdq_w4a4_linear_splitk")
+           "svdq_awq_w4a16_linear", "svdq_w4a4_linear_splitk_workspace_bytes", "svdq_w4a4_linear_splitk",
+           "svdq_nf4_codebook", "svdq_nf4_pack_weights", "svdq_nf4_dequantize", "svdq_nf4_w4a16_linear")
 
 
 class SvdqError(RuntimeError):
@@ -97,6 +98,14 @@ def lib():
         L.svdq_awq_pack_weights.argtypes = [P, I, I, P, P]
         L.svdq_awq_w4a16_linear.restype = I
         L.svdq_awq_w4a16_linear.argtypes = [P, P, P, P, I, I, I, P, P]
+        L.svdq_nf4_codebook.restype = I
+        L.svdq_nf4_codebook.argtypes = [P]
+        L.svdq_nf4_pack_weights.restype = I
+        L.svdq_nf4_pack_weights.argtypes = [P, I, I, P, P, P]
+        L.svdq_nf4_dequantize.restype = I
+        L.svdq_nf4_dequantize.argtypes = [P, P, P, I, I, P, P]
+        L.svdq_nf4_w4a16_linear.restype = I
+        L.svdq_nf4_w4a16_linear.argtypes = [P, P, P, P, P, I, I, I, P, P]
         _lib = L
     return _lib
 
@@ -401,6 +410,65 @@ def awq_w4a16_linear(X, wq, wscale, bias=None, Y=None, stream=None):
                                None if bias is None else (bias, bf, "bias", (N,)), (Y, bf, "Y", (M, N)))
     st = lib().svdq_awq_w4a16_linear(pX, pq, ps, pb, M, N, K, pY, _stream(stream))
     _check(st, "svdq_awq_w4a16_linear")
+    return Y
+
+
+def nf4_codebook() -> np.ndarray:
+    """The 16 NF4 levels (fp32, ascending)."""
+    c = np.zeros(16, np.float32)
+    _check(lib().svdq_nf4_codebook(c.ctypes.data), "svdq_nf4_codebook")
+    return c
+
+
+def nf4_pack_weights(W: np.ndarray):
+    """NF4 weight-only packing (host): bf16 bits [N][K] -> (wq uint8 [N][K/2],
+    qabs uint8 [N*K/64], chunk_scale fp32 [ceil(N*K/64/256)])."""
+    W, pW = _np(W, np.uint16)
+    if W.ndim != 2:
+        raise ValueError(f"W must have 2 dimensions, got shape {W.shape}")
+    N, K = W.shape
+    nb = N * (K // 64)
+    wq = np.zeros((N, K // 2), np.uint8)
+    qabs = np.zeros(max(nb, 1), np.uint8)[:nb]
+    chunk = np.zeros(max((nb + 255) // 256, 1), np.float32)[:(nb + 255) // 256]
+    st = lib().svdq_nf4_pack_weights(pW, N, K, wq.ctypes.data, qabs.ctypes.data, chunk.ctypes.data)
+    _check(st, "svdq_nf4_pack_weights")
+    return wq, qabs, chunk
+
+
+def _nf4_specs(wq, qabs, chunk):
+    torch = _torch()
+    _ndim(wq, 2, "wq")
+    N, K = wq.shape[0], wq.shape[1] * 2
+    nb = N * (K // 64)
+    return N, K, [(wq, (torch.uint8,), "wq"), (qabs, (torch.uint8,), "qabs", (nb,)),
+                  (chunk, (torch.float32,), "chunk_scale", ((nb + 255) // 256,))]
+
+
+def nf4_dequantize(wq, qabs, chunk, Wd=None, stream=None):
+    """The dequantized NF4 weights as a bf16 tensor [N][K] (one kernel)."""
+    torch = _torch()
+    N, K, specs = _nf4_specs(wq, qabs, chunk)
+    if Wd is None:
+        Wd = torch.empty((N, K), dtype=torch.bfloat16, device=wq.device)
+    pq, pa, pc, pW = _ptrs(*specs, (Wd, (torch.bfloat16, torch.int16), "Wd", (N, K)))
+    _check(lib().svdq_nf4_dequantize(pq, pa, pc, N, K, pW, _stream(stream)), "svdq_nf4_dequantize")
+    return Wd
+
+
+def nf4_w4a16_linear(X, wq, qabs, chunk, bias=None, Y=None, stream=None):
+    """Weight-only NF4 linear with bf16 activations -> bf16 (one kernel)."""
+    torch = _torch()
+    N, K, specs = _nf4_specs(wq, qabs, chunk)
+    _ndim(X, 2, "X")
+    M = X.shape[0]
+    if Y is None:
+        Y = torch.empty((M, N), dtype=torch.bfloat16, device=X.device)
+    bf = (torch.bfloat16, torch.int16)
+    pX, pq, pa, pc, pb, pY = _ptrs((X, bf, "X", (M, K)), *specs, None if bias is None else (bias, bf, "bias", (N,)),
+                                   (Y, bf, "Y", (M, N)))
+    st = lib().svdq_nf4_w4a16_linear(pX, pq, pa, pc, pb, M, N, K, pY, _stream(stream))
+    _check(st, "svdq_nf4_w4a16_linear")
     return Y
 
 

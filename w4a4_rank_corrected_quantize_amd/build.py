@@ -32,6 +32,7 @@ SOURCES = {
     "quant_act.hip": ["-ffp-contract=off"],
     "w4a4_gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     "awq_gemv.hip": [],
+    "nf4_gemm.hip": [],
 }
 
 

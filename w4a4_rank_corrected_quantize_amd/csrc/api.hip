@@ -268,3 +268,45 @@ extern "C" svdq_status svdq_awq_w4a16_linear(const uint16_t *X, const uint8_t *w
     hipError_t e = launch_awq_linear(X, wq, wscale, bias, M, N, K, Y, (hipStream_t)stream);
     return e == hipSuccess ? SVDQ_OK : SVDQ_ERR_HIP;
 }
+
+static Nf4Levels nf4_levels_arg()
+{
+    Nf4Levels lv;
+    std::memcpy(lv.c, nf4_codebook_cached(), sizeof(lv.c));
+    return lv;
+}
+
+extern "C" svdq_status svdq_nf4_dequantize(const uint8_t *wq, const uint8_t *qabs, const float *chunk_scale, int N,
+                                           int K, uint16_t *Wd, void *stream)
+{
+    if (N < 0 || K < 0) return SVDQ_ERR_INVALID_ARG;
+    if (K < 64 || K % 64 != 0) return SVDQ_ERR_SHAPE;
+    if (!elems_ok(N, K)) return SVDQ_ERR_SHAPE;
+    if (N > 0 && (!wq || !qabs || !chunk_scale || !Wd)) return SVDQ_ERR_INVALID_ARG;
+    if (!aligned16(wq) || !aligned16(qabs) || !aligned16(chunk_scale) || !aligned16(Wd)) return SVDQ_ERR_MISALIGNED;
+    svdq_status st = current_device_ok();
+    if (st != SVDQ_OK) return st;
+    if (N == 0) return SVDQ_OK;
+    hipError_t e = launch_nf4_dequant(wq, qabs, chunk_scale, N, K, nf4_levels_arg(), Wd, (hipStream_t)stream);
+    return e == hipSuccess ? SVDQ_OK : SVDQ_ERR_HIP;
+}
+
+extern "C" svdq_status svdq_nf4_w4a16_linear(const uint16_t *X, const uint8_t *wq, const uint8_t *qabs,
+                                             const float *chunk_scale, const uint16_t *bias, int M, int N, int K,
+                                             uint16_t *Y, void *stream)
+{
+    if (M < 0 || N < 0 || K < 0) return SVDQ_ERR_INVALID_ARG;
+    if (K < 64 || K % 64 != 0 || N % 8 != 0) return SVDQ_ERR_SHAPE;
+    if (!elems_ok(M, K) || check_linear_sizes(M, N, K) != SVDQ_OK) return SVDQ_ERR_SHAPE;
+    // buffers of zero size may be NULL (empty tensors have no storage)
+    if ((M > 0 && !X) || (N > 0 && (!wq || !qabs || !chunk_scale)) || (M > 0 && N > 0 && !Y))
+        return SVDQ_ERR_INVALID_ARG;
+    if (!aligned16(X) || !aligned16(wq) || !aligned16(qabs) || !aligned16(chunk_scale) || (bias && !aligned16(bias)) ||
+        !aligned16(Y))
+        return SVDQ_ERR_MISALIGNED;
+    svdq_status st = current_device_ok();
+    if (st != SVDQ_OK) return st;
+    if (M == 0 || N == 0) return SVDQ_OK;
+    hipError_t e = launch_nf4_linear(X, wq, qabs, chunk_scale, bias, M, N, K, nf4_levels_arg(), Y, (hipStream_t)stream);
+    return e == hipSuccess ? SVDQ_OK : SVDQ_ERR_HIP;
+}

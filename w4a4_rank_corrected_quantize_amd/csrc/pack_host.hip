@@ -21,6 +21,7 @@
 #include <cstdint>
 #include <cstring>
 #include <functional>
+#include <mutex>
 #include <thread>
 #include <vector>
 
@@ -479,5 +480,135 @@ extern "C" svdq_status svdq_awq_pack_weights(const uint16_t *W, int N, int K, ui
                     }
         }
     });
+    return SVDQ_OK;
+}
+
+// ------------------------------------------------------------------- NF4
+//
+// Weight-only NF4 packing ("BitsAndBytes W4 Quantization", sections
+// "Overview" and "Parameters": weights quantized at load time to the 4-bit
+// "nf4" data type, activations kept in bf16; compress_statistics
+// double-quantizes the block statistics).  NF4 levels are quantiles of the
+// standard normal distribution normalized to [-1, 1] with an exact zero: 8
+// positive levels at probabilities 1/2 + j (1/2 - d) / 8 and 7 negative ones
+// at 1/2 - j (1/2 - d) / 7, divided by Phi^-1(1 - d), d = (1/32 + 1/30) / 2.
+// Phi^-1 comes from Newton's method on Phi(x) = erfc(-x / sqrt 2) / 2 started
+// at 0 (Phi is concave for x > 0, so after the first step the iterates
+// decrease monotonically to the root); each level is rounded once to fp32.
+namespace svdq {
+namespace {
+
+double normal_quantile_upper(double p)     // p in [1/2, 1)
+{
+    const double inv_sqrt_2pi = 0.39894228040143267794;
+    double x = 0.0;
+    for (int it = 0; it < 100; ++it) {
+        const double f = 0.5 * std::erfc(-x * 0.70710678118654752440) - p;
+        const double step = f / (inv_sqrt_2pi * std::exp(-0.5 * x * x));
+        const double nx = x - step;
+        if (nx == x) break;
+        if (it > 3 && std::fabs(step) <= 1e-17 * std::fabs(x)) { x = nx; break; }
+        x = nx;
+    }
+    return x;
+}
+
+void nf4_levels(float *c)
+{
+    const double d = (1.0 / 32.0 + 1.0 / 30.0) / 2.0;
+    const double top = normal_quantile_upper(1.0 - d);
+    c[7] = 0.0f;
+    for (int j = 1; j <= 8; ++j) c[7 + j] = (float)(normal_quantile_upper(0.5 + j * (0.5 - d) / 8.0) / top);
+    for (int j = 1; j <= 7; ++j) c[7 - j] = (float)(-normal_quantile_upper(0.5 + j * (0.5 - d) / 7.0) / top);
+    c[15] = 1.0f;      // the top quantile divided by itself
+    c[0] = -1.0f;
+}
+
+}  // namespace
+
+// The 16 levels, cached after the first call (computed once per process).
+const float *nf4_codebook_cached()
+{
+    static float levels[16];
+    static std::once_flag once;
+    std::call_once(once, [] { nf4_levels(levels); });
+    return levels;
+}
+
+}  // namespace svdq
+
+extern "C" svdq_status svdq_nf4_codebook(float *levels)
+{
+    if (!levels) return SVDQ_ERR_INVALID_ARG;
+    std::memcpy(levels, svdq::nf4_codebook_cached(), 16 * sizeof(float));
+    return SVDQ_OK;
+}
+
+extern "C" svdq_status svdq_nf4_pack_weights(const uint16_t *W, int N, int K, uint8_t *wq, uint8_t *qabs,
+                                             float *chunk_scale)
+{
+    using namespace svdq;
+    if (!W || !wq || !qabs || !chunk_scale) return SVDQ_ERR_INVALID_ARG;
+    if (N < 0 || K < 0) return SVDQ_ERR_INVALID_ARG;
+    if (N < 1 || K < 64 || K % 64 != 0) return SVDQ_ERR_SHAPE;
+    if (!elems_ok(N, K)) return SVDQ_ERR_SHAPE;
+    for (int64_t i = 0; i < (int64_t)N * K; ++i)
+        if (!bf16_finite(W[i])) return SVDQ_ERR_NONFINITE;
+    const float *c = nf4_codebook_cached();
+    double mid[15];                          // exact midpoints of neighbouring levels
+    for (int i = 0; i < 15; ++i) mid[i] = 0.5 * ((double)c[i] + (double)c[i + 1]);
+    const int G = K / 64;
+    const int64_t nb = (int64_t)N * G;
+    std::vector<float> amax((size_t)nb);
+    parallel_for(N, [&](int64_t n0, int64_t n1) {
+        for (int64_t n = n0; n < n1; ++n) {
+            const uint16_t *w = W + n * K;
+            uint8_t *row = wq + n * (int64_t)(K / 2);
+            for (int g = 0; g < G; ++g) {
+                float a = 0.0f;
+                for (int i = 0; i < 64; ++i) a = std::max(a, std::fabs(bits_f32((uint32_t)w[64 * g + i] << 16)));
+                amax[(size_t)(n * G + g)] = a;
+                uint8_t code[64];
+                for (int i = 0; i < 64; ++i) {
+                    int q = 7;
+                    if (a > 0.0f) {
+                        // x = fl32(w / a): the fp64 quotient of two fp32 values rounded
+                        // to fp32 is the correctly rounded fp32 quotient
+                        const double x = (double)(float)((double)bits_f32((uint32_t)w[64 * g + i] << 16) / (double)a);
+                        // binary search over the midpoints; a tie goes toward zero
+                        int lo = 0, hi = 15;       // answer in [lo, hi]
+                        while (lo < hi) {
+                            const int m = (lo + hi) >> 1;       // compare with mid[m]
+                            const bool above = mid[m] < 0.0 ? x >= mid[m] : x > mid[m];
+                            if (above) lo = m + 1;
+                            else hi = m;
+                        }
+                        q = lo;
+                    }
+                    code[i] = (uint8_t)q;
+                }
+                // in each group of 8 consecutive weights, byte i holds weight i
+                // (low nibble) and weight i + 4 (high nibble)
+                for (int e = 0; e < 8; ++e)
+                    for (int i = 0; i < 4; ++i)
+                        row[32 * g + 4 * e + i] = (uint8_t)(code[8 * e + i] | code[8 * e + 4 + i] << 4);
+            }
+        }
+    });
+    // statistics: chunks of 256 block absmaxes in row-major (n, block) order
+    const int64_t nchunk = (nb + 255) / 256;
+    for (int64_t ch = 0; ch < nchunk; ++ch) {
+        const int64_t b0 = 256 * ch, b1 = std::min<int64_t>(nb, b0 + 256);
+        float s = 0.0f;
+        for (int64_t b = b0; b < b1; ++b) s = std::max(s, amax[(size_t)b]);
+        chunk_scale[ch] = (float)((double)s / 255.0);
+        for (int64_t b = b0; b < b1; ++b) {
+            // round-half-even of 255 a / s: 255 a is exact in fp64; a quotient of
+            // 1/2 or more that is not exactly k + 1/2 lies at least 2^-34 from it
+            // (a >= s / 510, and 2 * 255 a - (2k + 1) s is a multiple of ulp(a)),
+            // far beyond the fp64 rounding error of the division (< 2^-45)
+            qabs[b] = (uint8_t)(s > 0.0f ? std::nearbyint(255.0 * (double)amax[(size_t)b] / (double)s) : 0.0);
+        }
+    }
     return SVDQ_OK;
 }

@@ -65,4 +65,16 @@ hipError_t launch_w4a4_linear_qknorm(const uint8_t *xq, const float *xscale, con
 hipError_t launch_awq_linear(const uint16_t *X, const uint8_t *wq, const float *wscale, const uint16_t *bias,
                              int M, int N, int K, uint16_t *Y, hipStream_t stream);
 
+// Weight-only NF4 W4A16 layer: the 16 fp32 levels (computed once on the
+// host), the dequantization kernel and the linear.
+struct Nf4Levels {
+    float c[16];
+};
+const float *nf4_codebook_cached();
+hipError_t launch_nf4_dequant(const uint8_t *wq, const uint8_t *qabs, const float *chunk, int N, int K,
+                              const Nf4Levels &lv, uint16_t *Wd, hipStream_t stream);
+hipError_t launch_nf4_linear(const uint16_t *X, const uint8_t *wq, const uint8_t *qabs, const float *chunk,
+                             const uint16_t *bias, int M, int N, int K, const Nf4Levels &lv, uint16_t *Y,
+                             hipStream_t stream);
+
 }  // namespace svdq

@@ -23,6 +23,8 @@ float64 -> float32 -> bf16, each step round-to-nearest-even):
               W ~ N(0, 0.02^2), no bias.
   * DiT layers: X ~ Student-t(nu=4) with 16 outlier channels scaled x50,
               W ~ N(0, 0.02^2), bias ~ N(0, 0.01^2).
+  * NF4 weight-only layers (config 5, QKV and fc1 shapes): X ~ N(0, 1), no
+              outlier channels, W ~ N(0, 0.02^2), no bias.
 The calibration statistic that the packing step consumes (per-channel max
 |X|) is taken over the very X of the run: the pages' calibration pass needs
 a dataset, and this stands in for it.
@@ -100,6 +102,10 @@ SPECS = {
     # weight-only AWQ W4A16 modulation layer: one conditioning vector per
     # image, 3072 -> 6 x 3072 (shift, scale and gate of two norms)
     "awq_mod": LayerSpec("awq_mod", 6, 1, 3072, 18432, "normal", 0, 1.0),
+    # weight-only NF4 W4A16 comparison path on the QKV and fc1 shapes:
+    # activations N(0, 1) without outlier channels, no bias
+    "nf4_qkv": LayerSpec("nf4_qkv", 5, 4608, 3072, 9216, "normal", 0, 1.0, bias_std=None),
+    "nf4_fc1": LayerSpec("nf4_fc1", 5, 4608, 3072, 12288, "normal", 0, 1.0, bias_std=None, w_stream=3),
 }
 
 

@@ -102,11 +102,10 @@ def test_quantize_act_synthetic(prec, M, K):
     _quant_act_check(L["X"], p["smooth"], p["down"], prec)
 
 
-@pytest.mark.parametrize("prec", PRECS)
-def test_quantize_act_mx_half_step(prec):
-    """K = 32 * odd: the MXFP4 kernel ends on half a 64-channel step."""
-    if prec == svdq.INT4:
-        pytest.skip("INT4 needs K % 64 == 0")
+def test_quantize_act_mx_half_step():
+    """K = 32 * odd (MXFP4 only; INT4 groups are 64 wide): the MXFP4 kernel
+    ends on half a 64-channel step."""
+    prec = svdq.MXFP4
     _say("quantize_act mx K=96/160")
     for M, K in [(20, 96), (3, 160)]:
         L, p = _layer("qkv", M, K, 16, prec)
@@ -177,15 +176,24 @@ def test_quantize_act_deterministic_and_empty():
     (130, 320, 136, True, False),
     (257, 512, 264, False, True),
     (300, 1024, 512, True, True),
-    # MXFP4 only: an odd number of 32-channel blocks per row, so the
-    # register-staged kernel's last 64-channel slice is half zero-filled
+])
+def test_linear_synthetic(prec, M, K, N, bias, gelu):
+    _linear_case(prec, M, K, N, bias, gelu)
+
+
+@pytest.mark.parametrize("M,K,N,bias,gelu", [
     (45, 96, 40, True, True),
     (130, 160, 264, True, False),
     (77, 2080, 136, False, True),
 ])
-def test_linear_synthetic(prec, M, K, N, bias, gelu):
-    if prec == svdq.INT4 and K % 64:
-        pytest.skip("INT4 needs K % 64 == 0")
+def test_linear_mx_odd_blocks(M, K, N, bias, gelu):
+    """MXFP4 only (INT4 groups are 64 wide): an odd number of 32-channel blocks
+    per row, so the register-staged kernel's last 64-channel slice is half
+    zero-filled."""
+    _linear_case(svdq.MXFP4, M, K, N, bias, gelu)
+
+
+def _linear_case(prec, M, K, N, bias, gelu):
     _say(f"linear prec={prec} M={M} K={K} N={N} bias={bias} gelu={gelu}")
     spec = "small" if (M, K, N) == (128, 256, 256) else "qkv"
     L, p = _layer(spec, M, K, N, prec, bias=bias)

@@ -181,3 +181,26 @@ def test_awq_pack_errors():
         svdq.awq_pack_weights(Wn)
     wq, ws = svdq.awq_pack_weights(W)
     assert np.all(wq == 0x88) and np.all(ws == 0)
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("K,N", [(3072, 12288), (12288, 3072)])
+def test_pack_weights_full_layer_shapes(K, N):
+    """The DiT MLP shapes, where the randomized SVD's convergence is at
+    stake (fc1: 3072 -> 12288, fc2: 12288 -> 3072, Student-t calibration
+    activations with outlier channels): Eckart-Young within 1e-3 of numpy's
+    LAPACK factors (both rounded to bf16 the same way), never below the
+    optimum, and the residual codes and scales bit-exact against the oracle
+    given the library's factors."""
+    X, W, absmax = _layer(256, K, N, seed=K + 7)
+    p = svdq.pack_weights(W, absmax, prec=svdq.INT4)
+    assert np.array_equal(p["smooth"].view(np.uint32), O.smooth(W, absmax).view(np.uint32))
+    e_lib, What = _energy(W, p["smooth"], p["down"], p["up"])
+    d_np, u_np, S, _, _ = O.lowrank(W, p["smooth"], 32)
+    e_np, _ = _energy(W, p["smooth"], d_np, u_np)
+    e_opt = np.sum(S[32:] ** 2)
+    assert e_lib >= e_opt * (1 - 1e-9)
+    assert e_lib <= e_np * (1 + 1e-3)
+    wq, ws = O.residual(W, p["smooth"], p["down"], p["up"], svdq.INT4)
+    assert np.array_equal(p["wq"], wq)
+    assert np.array_equal(p["wscale"].view(np.uint32), ws.view(np.uint32))

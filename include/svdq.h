@@ -88,7 +88,8 @@ typedef enum svdq_status {
     SVDQ_ERR_UNSUPPORTED = -4,        /* rank other than 32, or a precision / K the call does not support */
     SVDQ_ERR_UNSUPPORTED_DEVICE = -5, /* no HIP device, or the current device is not gfx950 */
     SVDQ_ERR_NONFINITE = -6,          /* non-finite weight or calibration statistic (pack) */
-    SVDQ_ERR_HIP = -7                 /* a HIP runtime or launch failure */
+    SVDQ_ERR_HIP = -7,                /* a HIP runtime or launch failure */
+    SVDQ_ERR_SCRATCH = -8             /* the allocation-free call needs more than SVDQ_NOALLOC_SCRATCH_BYTES */
 } svdq_status;
 
 typedef enum svdq_precision {
@@ -244,6 +245,34 @@ svdq_status svdq_w4a4_linear_splitk(const uint8_t *xq, const void *xscale, const
                                     const uint16_t *bias, int M, int N, int K, int rank,
                                     svdq_precision prec, svdq_epilogue epi, uint16_t *Y, void *work,
                                     size_t work_bytes, void *stream);
+
+/* Size of the library's static device scratch buffer (one per GPU, held
+ * until the process ends), used by svdq_w4a4_linear_splitk_noalloc. */
+#define SVDQ_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/*
+ * svdq_w4a4_linear_splitk_noalloc -- svdq_w4a4_linear_splitk for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): the same arguments,
+ * kernels and results, without `work`: the split-K slice sums go to a
+ * static device buffer of SVDQ_NOALLOC_SCRATCH_BYTES that the library holds
+ * on each GPU it runs on.  The call itself allocates nothing (its first call
+ * on a device looks up that device's buffer address once).
+ *   - Shapes whose split needs more than SVDQ_NOALLOC_SCRATCH_BYTES
+ *     (svdq_w4a4_linear_splitk_workspace_bytes) return SVDQ_ERR_SCRATCH and
+ *     enqueue nothing.
+ *   - Every call on one GPU shares that GPU's buffer: calls that overlap in
+ *     time on one GPU (different streams, or different threads without
+ *     ordering) race and give undefined results; calls on one stream are
+ *     ordered and safe.  The buffer keeps the last call's contents; every
+ *     call writes what it reads, so nothing needs clearing.
+ * Errors as for svdq_w4a4_linear_splitk (without the workspace ones), plus
+ * SVDQ_ERR_SCRATCH.
+ */
+svdq_status svdq_w4a4_linear_splitk_noalloc(const uint8_t *xq, const void *xscale, const float *h,
+                                            const uint8_t *wq, const void *wscale, const uint16_t *up,
+                                            const uint16_t *bias, int M, int N, int K, int rank,
+                                            svdq_precision prec, svdq_epilogue epi, uint16_t *Y, void *stream);
 
 /*
  * svdq_requant_workspace_bytes -- device workspace that

@@ -41,13 +41,14 @@ RANK = 32
 STATUS = {
     0: "SVDQ_OK", -1: "SVDQ_ERR_INVALID_ARG", -2: "SVDQ_ERR_SHAPE", -3: "SVDQ_ERR_MISALIGNED",
     -4: "SVDQ_ERR_UNSUPPORTED", -5: "SVDQ_ERR_UNSUPPORTED_DEVICE", -6: "SVDQ_ERR_NONFINITE",
-    -7: "SVDQ_ERR_HIP",
+    -7: "SVDQ_ERR_HIP", -8: "SVDQ_ERR_SCRATCH",
 }
 EXPORTS = ("svdq_status_string", "svdq_version", "svdq_check_device", "svdq_pack_weights",
            "svdq_pack_residual", "svdq_quantize_act", "svdq_w4a4_linear", "svdq_requant_workspace_bytes",
            "svdq_w4a4_linear_requant", "svdq_w4a4_linear_qkv_norm_rope", "svdq_awq_pack_weights",
            "svdq_awq_w4a16_linear", "svdq_w4a4_linear_splitk_workspace_bytes", "svdq_w4a4_linear_splitk",
-           "svdq_nf4_codebook", "svdq_nf4_pack_weights", "svdq_nf4_dequantize", "svdq_nf4_w4a16_linear")
+           "svdq_nf4_codebook", "svdq_nf4_pack_weights", "svdq_nf4_dequantize", "svdq_nf4_w4a16_linear",
+           "svdq_w4a4_linear_splitk_noalloc")
 
 
 class SvdqError(RuntimeError):
@@ -86,6 +87,8 @@ def lib():
         L.svdq_w4a4_linear_splitk_workspace_bytes.argtypes = [I, I, I, I]
         L.svdq_w4a4_linear_splitk.restype = I
         L.svdq_w4a4_linear_splitk.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, P, P, ctypes.c_size_t, P]
+        L.svdq_w4a4_linear_splitk_noalloc.restype = I
+        L.svdq_w4a4_linear_splitk_noalloc.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, P, P]
         L.svdq_requant_workspace_bytes.restype = ctypes.c_size_t
         L.svdq_requant_workspace_bytes.argtypes = [I, I, I, I]
         L.svdq_w4a4_linear_requant.restype = I
@@ -327,6 +330,25 @@ def w4a4_linear_splitk(xq, xscale, h, wq, wscale, up, bias, prec: int = MXFP4, e
     nbytes = 0 if work is None else work.numel() * work.element_size()
     st = lib().svdq_w4a4_linear_splitk(*ptrs, M, N, K, r, prec, epi, pY, pwork, nbytes, _stream(stream))
     _check(st, "svdq_w4a4_linear_splitk")
+    return Y
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def w4a4_linear_splitk_noalloc(xq, xscale, h, wq, wscale, up, bias, prec: int = MXFP4, epi: int = EPI_NONE,
+                               Y=None, stream=None):
+    """w4a4_linear_splitk without a workspace: the slice sums go to the
+    library's static per-GPU scratch buffer (NOALLOC_SCRATCH_BYTES), so the
+    library allocates nothing.  Calls that overlap in time on one GPU race.
+    With Y given, this binding allocates nothing either."""
+    torch = _torch()
+    M, N, K, r, specs = _linear_specs(xq, xscale, h, wq, wscale, up, bias, prec)
+    if Y is None:
+        Y = torch.empty((M, N), dtype=torch.bfloat16, device=xq.device)
+    *ptrs, pY = _ptrs(*specs, (Y, (torch.bfloat16, torch.int16), "Y", (M, N)))
+    st = lib().svdq_w4a4_linear_splitk_noalloc(*ptrs, M, N, K, r, prec, epi, pY, _stream(stream))
+    _check(st, "svdq_w4a4_linear_splitk_noalloc")
     return Y
 
 

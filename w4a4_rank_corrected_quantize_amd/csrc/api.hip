@@ -5,6 +5,7 @@
 // and a clear error is raised instead of producing incorrect outputs).
 #include <atomic>
 #include <cstring>
+#include <mutex>
 
 #include "svdq.h"
 #include "svdq_internal.h"
@@ -93,6 +94,8 @@ extern "C" const char *svdq_status_string(svdq_status status)
     case SVDQ_ERR_UNSUPPORTED_DEVICE: return "no HIP device, or the current device is not a gfx950 (MI355X)";
     case SVDQ_ERR_NONFINITE: return "non-finite weight, calibration statistic or smoothing factor";
     case SVDQ_ERR_HIP: return "HIP runtime or kernel launch failure";
+    case SVDQ_ERR_SCRATCH:
+        return "the call needs more scratch memory than the library's static buffer holds (SVDQ_NOALLOC_SCRATCH_BYTES)";
     }
     return "unknown status";
 }
@@ -308,5 +311,75 @@ extern "C" svdq_status svdq_nf4_w4a16_linear(const uint16_t *X, const uint8_t *w
     if (st != SVDQ_OK) return st;
     if (M == 0 || N == 0) return SVDQ_OK;
     hipError_t e = launch_nf4_linear(X, wq, qabs, chunk_scale, bias, M, N, K, nf4_levels_arg(), Y, (hipStream_t)stream);
+    return e == hipSuccess ? SVDQ_OK : SVDQ_ERR_HIP;
+}
+
+// ------------------------------------------------ allocation-free split K
+//
+// svdq_w4a4_linear_splitk_noalloc keeps the split-K slice sums in this
+// file-scope device array instead of a caller workspace.  Each device holds
+// its own copy at its own address; host code must use that address (from
+// hipGetSymbolAddress), never the array's name.
+static __device__ __align__(256) float scratch[SVDQ_NOALLOC_SCRATCH_BYTES / sizeof(float)];
+
+namespace {
+
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];     // device address of `scratch`, per device (null until looked up)
+
+// Device address of this device's `scratch`, looked up once per device with
+// that device current; null if the lookup fails.
+void *scratch_address(int dev)
+{
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess) {
+            (void)hipGetLastError();
+            return nullptr;
+        }
+        g_scratch_ptr[dev] = ptr;
+    }
+    return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" svdq_status svdq_w4a4_linear_splitk_noalloc(const uint8_t *xq, const void *xscale, const float *h,
+                                                       const uint8_t *wq, const void *wscale, const uint16_t *up,
+                                                       const uint16_t *bias, int M, int N, int K, int rank,
+                                                       svdq_precision prec, svdq_epilogue epi, uint16_t *Y,
+                                                       void *stream)
+{
+    svdq_status st = check_common(M, K, rank, prec);
+    if (st != SVDQ_OK) return st;
+    if (N < 0) return SVDQ_ERR_INVALID_ARG;
+    if (epi != SVDQ_EPI_NONE && epi != SVDQ_EPI_GELU_TANH) return SVDQ_ERR_INVALID_ARG;
+    if (N % 8 != 0) return SVDQ_ERR_SHAPE;
+    if (check_linear_sizes(M, N, K) != SVDQ_OK) return SVDQ_ERR_SHAPE;
+    if ((M > 0 && (!xq || !xscale || !h)) || (N > 0 && (!wq || !wscale || !up)) || (M > 0 && N > 0 && !Y))
+        return SVDQ_ERR_INVALID_ARG;
+    if (!aligned16(xq) || !aligned16(xscale) || !aligned16(h) || !aligned16(wq) || !aligned16(wscale) ||
+        !aligned16(up) || !aligned16(Y) || (bias && !aligned16(bias)))
+        return SVDQ_ERR_MISALIGNED;
+    st = current_device_ok();
+    if (st != SVDQ_OK) return st;
+    if (M == 0 || N == 0) return SVDQ_OK;
+    const size_t need = splitk_work_bytes(M, N, K, prec);
+    if (need > SVDQ_NOALLOC_SCRATCH_BYTES) return SVDQ_ERR_SCRATCH;
+    float *work = nullptr;
+    if (need > 0) {
+        int dev = -1;
+        if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+            (void)hipGetLastError();
+            return SVDQ_ERR_HIP;
+        }
+        work = static_cast<float *>(scratch_address(dev));
+        if (!work) return SVDQ_ERR_HIP;
+    }
+    // every slice of every tile is written in full before the finishing
+    // kernel reads it, so the scratch needs no clearing
+    hipError_t e = launch_w4a4_linear_splitk(xq, xscale, h, wq, wscale, up, bias, M, N, K, prec, epi, Y, work,
+                                             (hipStream_t)stream);
     return e == hipSuccess ? SVDQ_OK : SVDQ_ERR_HIP;
 }

@@ -136,9 +136,6 @@ def main():
         args.sets = 3
     prec = svdq.INT4 if args.prec == "int4" else svdq.MXFP4
     qkvnorm = args.layer == "qkvnorm"
-    if qkvnorm and prec != svdq.INT4:
-        print("--layer qkvnorm is INT4 only", file=sys.stderr)
-        sys.exit(2)
     if args.tokens != 4608 and (prec != svdq.MXFP4 or args.layer not in ("fc1", "qkv", "fc2")):
         print("--tokens 1024 is the MXFP4 fc1 / qkv / fc2 workload", file=sys.stderr)
         sys.exit(2)
@@ -198,7 +195,7 @@ def main():
     def k2(b):
         if qkvnorm:
             svdq.w4a4_linear_qkv_norm_rope(b["xq"], b["xscale"], b["h"], b["wq"], b["wscale"], b["up"], b["bias"],
-                                           qkn["nq"], qkn["nk"], 1e-6, qkn["c"], qkn["s"], Y=b["Y"])
+                                           qkn["nq"], qkn["nk"], 1e-6, qkn["c"], qkn["s"], prec, Y=b["Y"])
             return
         if work is not None:
             svdq.w4a4_linear_splitk(b["xq"], b["xscale"], b["h"], b["wq"], b["wscale"], b["up"], b["bias"], prec,

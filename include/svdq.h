@@ -89,17 +89,20 @@ typedef enum svdq_status {
     SVDQ_ERR_UNSUPPORTED_DEVICE = -5, /* no HIP device, or the current device is not gfx950 */
     SVDQ_ERR_NONFINITE = -6,          /* non-finite weight or calibration statistic (pack) */
     SVDQ_ERR_HIP = -7,                /* a HIP runtime or launch failure */
-    SVDQ_ERR_SCRATCH = -8             /* the allocation-free call needs more than SVDQ_NOALLOC_SCRATCH_BYTES */
+    SVDQ_ERR_SCRATCH = -8,            /* the allocation-free call needs more than SVDQ_NOALLOC_SCRATCH_BYTES */
+    SVDQ_STATUS_INT_RANGE_ = 0x7FFFFFFF   /* not a status: makes every int a valid value of the type */
 } svdq_status;
 
 typedef enum svdq_precision {
     SVDQ_INT4 = 0,   /* symmetric INT4, 64-wide groups, fp32 scales  [rows][K/64] */
-    SVDQ_MXFP4 = 1   /* E2M1, 32-wide blocks, E8M0 scales (uint8)    [rows][K/32] */
+    SVDQ_MXFP4 = 1,  /* E2M1, 32-wide blocks, E8M0 scales (uint8)    [rows][K/32] */
+    SVDQ_PRECISION_INT_RANGE_ = 0x7FFFFFFF   /* not a precision: every int is a valid value (calls reject it) */
 } svdq_precision;
 
 typedef enum svdq_epilogue {
     SVDQ_EPI_NONE = 0,
-    SVDQ_EPI_GELU_TANH = 1  /* 0.5 y (1 + tanh(sqrt(2/pi) (y + 0.044715 y^3))) after the bias */
+    SVDQ_EPI_GELU_TANH = 1, /* 0.5 y (1 + tanh(sqrt(2/pi) (y + 0.044715 y^3))) after the bias */
+    SVDQ_EPILOGUE_INT_RANGE_ = 0x7FFFFFFF    /* not an epilogue: every int is a valid value (calls reject it) */
 } svdq_epilogue;
 
 #define SVDQ_RANK 32
@@ -324,8 +327,8 @@ svdq_status svdq_w4a4_linear_requant(const uint8_t *xq, const void *xscale, cons
  * engine's fused operator consumes the QKV projection, the Q/K normalization
  * and the rotary embeddings together).
  *
- *   xq ... bias  as for svdq_w4a4_linear; INT4 only (MXFP4:
- *                SVDQ_ERR_UNSUPPORTED); no GELU
+ *   xq ... bias  as for svdq_w4a4_linear; no GELU.  MXFP4 needs
+ *                K % 256 == 0 (SVDQ_ERR_UNSUPPORTED otherwise)
  *   N            3 H 128 (SVDQ_ERR_SHAPE otherwise): channels [0, 128 H) are
  *                the Q heads, then H K heads, then H V heads, 128 each
  *   norm_q       [128] bf16 bits, device   RMS-norm weight of every Q head

@@ -31,7 +31,9 @@ from typing import Optional
 import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(HERE, "liboracle.so")
+# SVDQ_ORACLE_LIBRARY names another build of the oracle (the sanitizer tests
+# load a sanitized build this way)
+_LIB_PATH = os.environ.get("SVDQ_ORACLE_LIBRARY") or os.path.join(HERE, "liboracle.so")
 
 INT4 = 0
 MXFP4 = 1

@@ -528,16 +528,16 @@ def test_awq_deterministic_and_empty():
 
 # ------------------------------- QKV projection + Q/K RMS-norm + rotary (INT4)
 
-def _qkvnorm_case(M, K, N, bias=True, rows=None, eps=1e-6):
-    L, p = _layer("qkv", M, K, N, svdq.INT4, bias=bias)
+def _qkvnorm_case(M, K, N, bias=True, rows=None, eps=1e-6, prec=svdq.INT4):
+    L, p = _layer("qkv", M, K, N, prec, bias=bias)
     nq, nk = synth.gen_qk_norm(2, 10), synth.gen_qk_norm(2, 11)
     c, s = synth.gen_rope(M)
-    xq, xs, h, oh = _quant_act_check(L["X"], p["smooth"], p["down"], svdq.INT4)
+    xq, xs, h, oh = _quant_act_check(L["X"], p["smooth"], p["down"], prec)
     Y = svdq.w4a4_linear_qkv_norm_rope(xq, xs, h, _t(p["wq"]), _t(p["wscale"]), _t(p["up"]), _t(L["bias"]),
-                                       _t(nq), _t(nk), eps, _t(c), _t(s))
-    Yp = svdq.w4a4_linear(xq, xs, h, _t(p["wq"]), _t(p["wscale"]), _t(p["up"]), _t(L["bias"]), svdq.INT4)
+                                       _t(nq), _t(nk), eps, _t(c), _t(s), prec)
+    Yp = svdq.w4a4_linear(xq, xs, h, _t(p["wq"]), _t(p["wscale"]), _t(p["up"]), _t(L["bias"]), prec)
     torch.cuda.synchronize()
-    ylin = O.linear(_np(xq), _np(xs), oh, p["wq"], p["wscale"], p["up"], L["bias"], svdq.INT4, rows=rows)
+    ylin = O.linear(_np(xq), _np(xs), oh, p["wq"], p["wscale"], p["up"], L["bias"], prec, rows=rows)
     sel = slice(None) if rows is None else rows
     pick = (lambda t: t) if rows is None else (lambda t: t[torch.from_numpy(rows).long().cuda()])
     # the projection itself, as the plain kernel stores it, against the oracle
@@ -560,6 +560,27 @@ def _qkvnorm_case(M, K, N, bias=True, rows=None, eps=1e-6):
 def test_qkv_norm_rope_synthetic(M, K, N, bias):
     _say(f"qkv norm rope M={M} K={K} N={N} bias={bias}")
     _qkvnorm_case(M, K, N, bias)
+
+
+@pytest.mark.parametrize("M,K,N,bias", [(64, 256, 384, True), (130, 512, 768, False), (300, 1024, 1152, True),
+                                        (1, 256, 384, True), (600, 768, 3072, True)])
+def test_qkv_norm_rope_mx_synthetic(M, K, N, bias):
+    """The MXFP4 form (the persistent LDS-DMA kernel, K % 256 == 0): a head is
+    one wave's 128 channels; odd head counts leave half of the last 256-wide
+    channel tile empty."""
+    _say(f"qkv norm rope mx M={M} K={K} N={N} bias={bias}")
+    _qkvnorm_case(M, K, N, bias, prec=svdq.MXFP4)
+
+
+def test_qkv_norm_rope_mx_needs_whole_steps():
+    L, p = _layer("qkv", 16, 320, 384, svdq.MXFP4)
+    xq, xs, h = svdq.quantize_act(_t(L["X"]), _t(p["smooth"]), _t(p["down"]), svdq.MXFP4)
+    c, s = synth.gen_rope(16)
+    with pytest.raises(svdq.SvdqError) as e:
+        svdq.w4a4_linear_qkv_norm_rope(xq, xs, h, _t(p["wq"]), _t(p["wscale"]), _t(p["up"]), None,
+                                       _t(synth.gen_qk_norm(2, 10)), _t(synth.gen_qk_norm(2, 11)), 1e-6, _t(c), _t(s),
+                                       svdq.MXFP4)
+    assert e.value.status == -4
 
 
 @pytest.mark.parametrize("eps_factor", [1.0, 4.0])
@@ -587,11 +608,12 @@ def test_qkv_norm_rope_eps_comparable_to_mean_square(eps_factor):
         _y_check(Y, O.qkv_norm_rope(yb, nq, nk, 0.0, c, s), "eps left out")
 
 
-def test_qkv_norm_rope_full_size():
+@pytest.mark.parametrize("prec", PRECS)
+def test_qkv_norm_rope_full_size(prec):
     """4608 tokens x 3072 -> 9216 (24 heads each of Q, K, V) with the
     FLUX-like rotary table; every output of every token (text and image)."""
-    _say("qkv norm rope full size")
-    _qkvnorm_case(4608, 3072, 9216)
+    _say(f"qkv norm rope full size prec={prec}")
+    _qkvnorm_case(4608, 3072, 9216, prec=prec)
 
 
 def test_qkv_norm_rope_deterministic_and_empty():

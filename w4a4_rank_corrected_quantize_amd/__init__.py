@@ -30,7 +30,9 @@ from typing import Optional
 import numpy as np
 
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG_DIR, "libsvdq.so")
+# SVDQ_LIBRARY names another build of the same library (the sanitizer
+# tests load an address/undefined-behaviour-sanitized build this way)
+LIB_PATH = os.environ.get("SVDQ_LIBRARY") or os.path.join(PKG_DIR, "libsvdq.so")
 
 INT4 = 0
 MXFP4 = 1

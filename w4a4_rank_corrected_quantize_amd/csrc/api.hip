@@ -237,7 +237,7 @@ extern "C" svdq_status svdq_w4a4_linear_qkv_norm_rope(const uint8_t *xq, const v
     if (!(eps >= 0.0f) || eps > 3.0e38f) return SVDQ_ERR_INVALID_ARG;      // finite, non-negative
     if (N % 384 != 0) return SVDQ_ERR_SHAPE;
     if (check_linear_sizes(M, N, K) != SVDQ_OK) return SVDQ_ERR_SHAPE;
-    if (prec != SVDQ_INT4) return SVDQ_ERR_UNSUPPORTED;
+    if (!requant_supported(M, N, K, prec)) return SVDQ_ERR_UNSUPPORTED;      // MXFP4: the LDS-DMA kernel's range
     // buffers of zero size may be NULL (empty tensors have no storage)
     if ((M > 0 && (!xq || !xscale || !h || !rope_cos || !rope_sin)) ||
         (N > 0 && (!wq || !wscale || !up || !norm_q || !norm_k)) || (M > 0 && N > 0 && !Y))
@@ -249,8 +249,8 @@ extern "C" svdq_status svdq_w4a4_linear_qkv_norm_rope(const uint8_t *xq, const v
     st = current_device_ok();
     if (st != SVDQ_OK) return st;
     if (M == 0 || N == 0) return SVDQ_OK;
-    hipError_t e = launch_w4a4_linear_qknorm(xq, (const float *)xscale, h, wq, (const float *)wscale, up, bias, M, N,
-                                             K, norm_q, norm_k, eps, rope_cos, rope_sin, Y, (hipStream_t)stream);
+    hipError_t e = launch_w4a4_linear_qknorm(xq, xscale, h, wq, wscale, up, bias, M, N, K, prec, norm_q, norm_k, eps,
+                                             rope_cos, rope_sin, Y, (hipStream_t)stream);
     return e == hipSuccess ? SVDQ_OK : SVDQ_ERR_HIP;
 }
 

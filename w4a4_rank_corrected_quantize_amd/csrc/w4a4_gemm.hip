@@ -1293,6 +1293,126 @@ __device__ __forceinline__ void requant_epilogue_mx(const f32x16 (&acc)[MX_TN][M
     }
 }
 
+// Epilogue of the MXFP4 QKV kernel with Q/K RMS-norm and rotary embedding,
+// for one wave tile: 4 x 2 tiles of 32 x 32 = 128 channels (one whole head,
+// since nb is a multiple of 128) x 64 tokens.  Lane (l32, hk) holds, per
+// token mb + 32 tm + l32, the channels 32 tn + 8 j + 4 hk + (0..3) of the head
+// (64 of its 128); its partner lane (l32, hk ^ 1) holds the other 64, so the
+// head's sum of squares takes one cross-half exchange, and a rotation pair
+// (2p, 2p + 1) sits in one lane.  The bf16 outputs are parked in the wave's
+// own LDS area (64 tokens x 128 channels, rows of 256 + 8 bytes) while the
+// sums are formed, normalized and rotated in place by the lanes that wrote
+// them, and stored as whole 256-byte rows.  `area` holds
+// QK_AREA_BYTES bytes per wave, used by no other wave.
+constexpr int QK_ROW = 264;
+constexpr int QK_AREA_BYTES = 64 * QK_ROW;
+
+__device__ __forceinline__ void qknorm_wave_epilogue_mx(const f32x16 (&acc)[MX_TN][MX_TM], const float *__restrict__ h,
+                                                        const uint16_t *__restrict__ up,
+                                                        const uint16_t *__restrict__ bias, int M, int N,
+                                                        const QKNormArgs &qk, uint16_t *__restrict__ Y, int mb, int nb,
+                                                        uint8_t *area, int lane)
+{
+    const int l32 = lane & 31, hk = lane >> 5;
+    bf16x8 hhi[MX_TM][2], hlo[MX_TM][2];
+#pragma unroll
+    for (int tm = 0; tm < MX_TM; ++tm)
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+            float hv[8];
+            load_h8(h, mb + tm * 32 + l32, M, 16 * s2 + 8 * hk, hv);
+            split_h(hv, hhi[tm][s2], hlo[tm][s2]);
+        }
+    const int head = nb / 128;
+    const bool norm = nb < N && head < 2 * qk.heads;      // a Q or a K head
+    // pass 1: the bf16 outputs, exactly as wave_epilogue stores them, into
+    // the area; the sum of their squares per token
+    float ss[MX_TM] = {0.0f, 0.0f};
+#pragma unroll
+    for (int tn = 0; tn < MX_TN; ++tn) {
+        const int nrow = nb + tn * 32 + l32;
+        bf16x8 ua[2];
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+            uint4 uv = {0u, 0u, 0u, 0u};
+            if (nrow < N) uv = *reinterpret_cast<const uint4 *>(up + (size_t)nrow * 32 + 16 * s2 + 8 * hk);
+            ua[s2] = __builtin_bit_cast(bf16x8, uv);
+        }
+        uint2 bv[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) bv[j] = bias4(bias, nb + tn * 32 + 8 * j + 4 * hk, N);
+#pragma unroll
+        for (int tm = 0; tm < MX_TM; ++tm) {
+            f32x16 lr = {};
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) {
+                lr = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ua[s2], hhi[tm][s2], lr, 0, 0, 0);
+                lr = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ua[s2], hlo[tm][s2], lr, 0, 0, 0);
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float a4[4] = {acc[tn][tm][4 * j], acc[tn][tm][4 * j + 1], acc[tn][tm][4 * j + 2],
+                                     acc[tn][tm][4 * j + 3]};
+                const float l4[4] = {lr[4 * j], lr[4 * j + 1], lr[4 * j + 2], lr[4 * j + 3]};
+                const uint2 y = finish4(a4, l4, bv[j], 0);
+                *reinterpret_cast<uint2 *>(area + (tm * 32 + l32) * QK_ROW + (tn * 32 + 8 * j + 4 * hk) * 2) = y;
+                const float v0 = bf16_to_f32(y.x & 0xFFFFu), v1 = bf16_to_f32(y.x >> 16);
+                const float v2 = bf16_to_f32(y.y & 0xFFFFu), v3 = bf16_to_f32(y.y >> 16);
+                ss[tm] = __builtin_fmaf(v0, v0, ss[tm]);
+                ss[tm] = __builtin_fmaf(v1, v1, ss[tm]);
+                ss[tm] = __builtin_fmaf(v2, v2, ss[tm]);
+                ss[tm] = __builtin_fmaf(v3, v3, ss[tm]);
+            }
+        }
+    }
+    // pass 2 (Q and K heads): normalize and rotate in place; each lane rereads
+    // only what it wrote
+    if (norm) {
+        const uint16_t *__restrict__ w = (head < qk.heads ? qk.norm_q : qk.norm_k) + 4 * hk;
+#pragma unroll
+        for (int tm = 0; tm < MX_TM; ++tm) {
+            const float tot = ss[tm] + __shfl_xor(ss[tm], 32);
+            const float rs = __builtin_amdgcn_rsqf(__builtin_fmaf(tot, 1.0f / 128.0f, qk.eps));
+            const int ml = tm * 32 + l32;
+            const int m = mb + ml < M ? mb + ml : M - 1;          // rows past M are never stored
+            // the lane's pairs start at channel 4 hk: pair 2 hk of the token's angles
+            const float *__restrict__ rc = qk.rope_cos + (size_t)m * 64 + 2 * hk;
+            const float *__restrict__ rsn = qk.rope_sin + (size_t)m * 64 + 2 * hk;
+#pragma unroll
+            for (int tn = 0; tn < MX_TN; ++tn)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int dq = 16 * tn + 4 * j;                  // (channel - 4 hk) / 2 of the lane's first pair
+                    uint2 *slot = reinterpret_cast<uint2 *>(area + ml * QK_ROW + (tn * 32 + 8 * j + 4 * hk) * 2);
+                    const uint2 y2 = *slot;
+                    const float2 c = *reinterpret_cast<const float2 *>(rc + dq);
+                    const float2 sn = *reinterpret_cast<const float2 *>(rsn + dq);
+                    const uint2 w2 = *reinterpret_cast<const uint2 *>(w + 2 * dq);
+                    const float u0 = bf16_to_f32(y2.x & 0xFFFFu) * rs * bf16_to_f32(w2.x & 0xFFFFu);
+                    const float u1 = bf16_to_f32(y2.x >> 16) * rs * bf16_to_f32(w2.x >> 16);
+                    const float u2 = bf16_to_f32(y2.y & 0xFFFFu) * rs * bf16_to_f32(w2.y & 0xFFFFu);
+                    const float u3 = bf16_to_f32(y2.y >> 16) * rs * bf16_to_f32(w2.y >> 16);
+                    const float o0 = u0 * c.x - u1 * sn.x, o1 = u1 * c.x + u0 * sn.x;
+                    const float o2 = u2 * c.y - u3 * sn.y, o3 = u3 * c.y + u2 * sn.y;
+                    *slot = make_uint2(pack_bf16x2(o0, o1), pack_bf16x2(o2, o3));
+                }
+        }
+    }
+    // the area is read back by other lanes of this wave: whole 256-byte rows,
+    // 16 lanes per row
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const int seg = lane & 15;
+#pragma unroll
+    for (int it = 0; it < 16; ++it) {
+        const int r = (lane >> 4) + 4 * it;
+        const uint4 v = *reinterpret_cast<const uint4 *>(area + r * QK_ROW + seg * 16);
+        const int m = mb + r, n = nb + seg * 8;
+        if (m < M && n < N) store_nt(Y + (size_t)m * N + n, v);
+    }
+}
+
 // Persistent: block b takes the tiles b, b + gridDim.x, ...  The two stages
 // alternate over the global step count, and the first step of the next tile
 // is loaded into the free stage while the epilogue of the current tile runs
@@ -1301,6 +1421,7 @@ __device__ __forceinline__ void requant_epilogue_mx(const f32x16 (&acc)[MX_TN][M
 constexpr int MXE_STORE = 0;      // y -> bf16 Y
 constexpr int MXE_REQUANT = 1;    // the next layer's activation step (RequantArgs)
 constexpr int MXE_PARTIAL = 2;    // fp32 partial sums of one K slice (split K)
+constexpr int MXE_QKNORM = 3;     // Q/K RMS-norm + rotary embedding of a QKV projection (QKNormArgs)
 
 // Split K: work item t is tile t % tiles over K slice t / tiles, of S slices
 // of `sps` 256-channel steps each (the last one may be shorter); the slice's
@@ -1316,7 +1437,7 @@ __global__ __launch_bounds__(MXD_THREADS) void w4a4_mxfp4_dma_kernel(
     const uint8_t *__restrict__ xq, const uint8_t *__restrict__ xscale, const float *__restrict__ h,
     const uint8_t *__restrict__ wq, const uint8_t *__restrict__ wscale, const uint16_t *__restrict__ up,
     const uint16_t *__restrict__ bias, int M, int N, int K, int gelu, uint16_t *__restrict__ Y, RequantArgs rq,
-    SplitArgs sk)
+    SplitArgs sk, QKNormArgs qk)
 {
     __shared__ MXDStage stage[2];
     const int tid = threadIdx.x, lane = tid & 63;
@@ -1460,9 +1581,12 @@ __global__ __launch_bounds__(MXD_THREADS) void w4a4_mxfp4_dma_kernel(
         const int mb = m0 + wm * MX_WM, nb = n0 + wn * MX_WN;
         const int tile_n = n0 / MXD_BN, tile_m0 = m0;
         const int slice = t / tiles;
-        const int tnext = t + (int)gridDim.x;
+        // the QKV-norm epilogue needs the registers that the next tile's
+        // prefetch would hold: that mode runs one tile per block
+        constexpr bool persistent = MODE != MXE_QKNORM;
+        const int tnext = persistent ? t + (int)gridDim.x : items;
         const int nst_done = nst;
-        if (tnext < items) {
+        if (persistent && tnext < items) {
             set_tile(tnext % tiles, n0, m0);
             item_steps(tnext, st0, nst);
             issue(st0, last ^ 1);
@@ -1517,6 +1641,11 @@ __global__ __launch_bounds__(MXD_THREADS) void w4a4_mxfp4_dma_kernel(
                     }
                 }
             }
+        } else if constexpr (MODE == MXE_QKNORM) {
+            // one tile per block: both stages are free for the output areas
+            static_assert(8 * QK_AREA_BYTES <= 2 * sizeof(MXDStage), "the output areas fit in the two stages");
+            qknorm_wave_epilogue_mx(acc, h, up, bias, M, N, qk, Y, mb, nb,
+                                    reinterpret_cast<uint8_t *>(&stage[0]) + wave * QK_AREA_BYTES, lane);
         } else if constexpr (MODE == MXE_REQUANT) {
             static_assert(2 * MXD_BM * 32 * sizeof(float) <= sizeof(MXDStage), "partial sums fit in a stage");
             requant_epilogue_mx(acc, h, up, bias, M, N, gelu, rq, mb, nb, tile_n, tile_m0, wn, wm, tid, lane,
@@ -1525,7 +1654,7 @@ __global__ __launch_bounds__(MXD_THREADS) void w4a4_mxfp4_dma_kernel(
             wave_epilogue<MX_TN, MX_TM>(acc, h, up, bias, M, N, gelu, Y, mb, nb,
                                         reinterpret_cast<uint8_t *>(&stage[last]) + wave * OUT_TILE_BYTES, lane);
         }
-        if (tnext >= items) break;
+        if (!persistent || tnext >= items) break;
         g += nst_done;
         t = tnext;
         // the staging area becomes the second stage of the next tile
@@ -1555,7 +1684,7 @@ hipError_t launch_w4a4_linear(const uint8_t *xq, const void *xscale, const float
             const int blocks = tiles < ncu ? tiles : ncu;      // persistent: one block per CU
             hipLaunchKernelGGL(w4a4_mxfp4_dma_kernel<MXE_STORE>, dim3((unsigned)blocks), dim3(MXD_THREADS), 0, stream,
                                xq, (const uint8_t *)xscale, h, wq, (const uint8_t *)wscale, up, bias, M, N, K, gelu,
-                               Y, RequantArgs{}, SplitArgs{nullptr, 1, K >> 8});
+                               Y, RequantArgs{}, SplitArgs{nullptr, 1, K >> 8}, QKNormArgs{});
         } else {
             const int tiles = ((N + MX_BN - 1) / MX_BN) * ((M + MX_BM - 1) / MX_BM);
             hipLaunchKernelGGL(w4a4_mxfp4_kernel, dim3((unsigned)tiles), dim3(MX_THREADS), 0, stream, xq,
@@ -1595,7 +1724,7 @@ hipError_t launch_w4a4_linear_requant(const uint8_t *xq, const void *xscale, con
         const int blocks = tiles < ncu ? tiles : ncu;
         hipLaunchKernelGGL(w4a4_mxfp4_dma_kernel<MXE_REQUANT>, dim3((unsigned)blocks), dim3(MXD_THREADS), 0, stream,
                            xq, (const uint8_t *)xscale, h, wq, (const uint8_t *)wscale, up, bias, M, N, K, gelu,
-                           (uint16_t *)nullptr, rq, SplitArgs{nullptr, 1, K >> 8});
+                           (uint16_t *)nullptr, rq, SplitArgs{nullptr, 1, K >> 8}, QKNormArgs{});
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -1662,7 +1791,7 @@ hipError_t launch_w4a4_linear_splitk(const uint8_t *xq, const void *xscale, cons
     const int blocks = items < ncu ? items : ncu;
     hipLaunchKernelGGL(w4a4_mxfp4_dma_kernel<MXE_PARTIAL>, dim3((unsigned)blocks), dim3(MXD_THREADS), 0, stream, xq,
                        (const uint8_t *)xscale, h, wq, (const uint8_t *)wscale, up, bias, M, N, K, gelu,
-                       (uint16_t *)nullptr, RequantArgs{}, SplitArgs{work, S, sps});
+                       (uint16_t *)nullptr, RequantArgs{}, SplitArgs{work, S, sps}, QKNormArgs{});
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t threads = (int64_t)M * (N / 4);
@@ -1671,16 +1800,28 @@ hipError_t launch_w4a4_linear_splitk(const uint8_t *xq, const void *xscale, cons
     return hipGetLastError();
 }
 
-hipError_t launch_w4a4_linear_qknorm(const uint8_t *xq, const float *xscale, const float *h, const uint8_t *wq,
-                                     const float *wscale, const uint16_t *up, const uint16_t *bias, int M, int N,
-                                     int K, const uint16_t *norm_q, const uint16_t *norm_k, float eps,
-                                     const float *rope_cos, const float *rope_sin, uint16_t *Y, hipStream_t stream)
+hipError_t launch_w4a4_linear_qknorm(const uint8_t *xq, const void *xscale, const float *h, const uint8_t *wq,
+                                     const void *wscale, const uint16_t *up, const uint16_t *bias, int M, int N,
+                                     int K, svdq_precision prec, const uint16_t *norm_q, const uint16_t *norm_k,
+                                     float eps, const float *rope_cos, const float *rope_sin, uint16_t *Y,
+                                     hipStream_t stream)
 {
+    if (prec == SVDQ_MXFP4) {
+        // the LDS-DMA kernel (K % 256 == 0, checked by qknorm_supported): a
+        // 128-channel head is one wave's channel range
+        static_assert(MX_WN == 128 && MXD_BN % 128 == 0, "a head is one wave tile");
+        const QKNormArgs qk{norm_q, norm_k, rope_cos, rope_sin, N / 384, eps};
+        const int tiles = ((N + MXD_BN - 1) / MXD_BN) * ((M + MXD_BM - 1) / MXD_BM);
+        hipLaunchKernelGGL(w4a4_mxfp4_dma_kernel<MXE_QKNORM>, dim3((unsigned)tiles), dim3(MXD_THREADS), 0, stream, xq,
+                           (const uint8_t *)xscale, h, wq, (const uint8_t *)wscale, up, bias, M, N, K, 0, Y,
+                           RequantArgs{}, SplitArgs{nullptr, 1, K >> 8}, qk);
+        return hipGetLastError();
+    }
     const int tiles = ((N + I4_BN - 1) / I4_BN) * ((M + I4_BM - 1) / I4_BM);
     static_assert(I4_WN * 2 == 128 && I4_BN % 128 == 0, "a head is the tile of two neighbouring waves");
     const QKNormArgs qk{norm_q, norm_k, rope_cos, rope_sin, N / 384, eps};
-    hipLaunchKernelGGL(w4a4_int4_kernel<EPI_QKNORM>, dim3((unsigned)tiles), dim3(I4_THREADS), 0, stream, xq, xscale,
-                       h, wq, wscale, up, bias, M, N, K, 0, Y, RequantArgs{}, qk);
+    hipLaunchKernelGGL(w4a4_int4_kernel<EPI_QKNORM>, dim3((unsigned)tiles), dim3(I4_THREADS), 0, stream, xq,
+                       (const float *)xscale, h, wq, (const float *)wscale, up, bias, M, N, K, 0, Y, RequantArgs{}, qk);
     return hipGetLastError();
 }
 

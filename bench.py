@@ -32,6 +32,7 @@ PEAK_INT8_TOPS = 5000.0     # MI355X dense int8 matrix peak, 5.0 POP/s
 PEAK_FP4_TFLOPS = 10100.0   # MI355X dense MXFP4 matrix peak, 10.1 PFLOP/s
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak, 2.5 PFLOP/s
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, 8 TB/s
+NO_CLOCK = False
 
 # HBM traffic of svdq_w4a4_linear per launch, from two rocprofv3 --pmc runs
 # (FETCH_SIZE, then WRITE_SIZE) of this script, each divided by what the same
@@ -64,6 +65,65 @@ def copy_calibration(mib):
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"copy_calibration_bytes_read": n, "bytes_written": n, "launches": 3}), flush=True)
+
+
+def host_info():
+    """The CPU model and the hardware threads this process may use (the CPU
+    baseline's `cores` is what the oracle actually ran on)."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu_model": model, "cpu_threads": len(os.sched_getaffinity(0))}
+
+
+def gpu_clock(torch, step, ms_per_step, seconds=1.0, period=0.05):
+    """The GFX clock while the step runs back to back: after the timed region
+    the step is enqueued for about `seconds` while a second thread reads the
+    clock that amd-smi reports (torch.cuda.clock_rate) every `period` s.  The
+    samples of the first 0.2 s are dropped (the reading averages over a window
+    that can reach back into the gap before the run).  None where amd-smi is
+    unavailable."""
+    import threading
+    if NO_CLOCK:
+        return None
+    try:
+        torch.cuda.clock_rate(0)
+    except Exception:
+        return None
+    samples, stop = [], threading.Event()
+
+    def sample():
+        t0 = time.time()
+        while not stop.is_set():
+            try:
+                mhz = float(torch.cuda.clock_rate(0))
+            except Exception:
+                return
+            if time.time() - t0 > 0.2 and mhz > 0:
+                samples.append(mhz)
+            stop.wait(period)
+
+    n = min(20000, max(1, int(seconds * 1e3 / max(ms_per_step, 1e-3))))
+    torch.cuda.synchronize()
+    th = threading.Thread(target=sample, daemon=True)
+    th.start()
+    for i in range(n):
+        step(i)
+    torch.cuda.synchronize()
+    stop.set()
+    th.join()
+    if not samples:
+        return None
+    return {"source": f"amd-smi GFX clock, sampled every {int(period * 1e3)} ms while {n} more steps ran "
+                      "back to back after the timed region",
+            "median_MHz": float(np.median(samples)), "min_MHz": min(samples), "max_MHz": max(samples),
+            "samples": len(samples)}
 
 
 def k1_bytes(M, K, r, prec):
@@ -104,8 +164,12 @@ def main():
                     help="time svdq_w4a4_linear_splitk (K split across work items when the tiles cannot fill "
                          "the chip; the workspace is allocated before the timed region)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-clock", action="store_true",
+                    help="skip the clock sampling after the timed region (under a counter profiler)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle sample time")
     args = ap.parse_args()
+    global NO_CLOCK
+    NO_CLOCK = args.no_clock
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the layer runs on a single MI355X and there is "
               "no multi-GPU path; run it with --gpus 1.", file=sys.stderr)
@@ -254,6 +318,7 @@ def main():
     if t is not None and t["source_sha"] == _source_sha("w4a4_gemm.hip"):
         traffic = t["bytes"]
 
+    clock = gpu_clock(torch, lambda i: (k1(sets[i % len(sets)]), k2(sets[i % len(sets)])), ms_per_step)
     cpu = None
     if not args.no_cpu_baseline:
         from oracle import oracle as O
@@ -315,6 +380,8 @@ def main():
         "linear_kernel_GBs": round(k2_gbs, 1),
         "matrix_core_reference": ref,
         "host_pack_s": round(pack_s, 2),
+        "gpu_clock": clock,
+        "host": host_info(),
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
@@ -421,6 +488,7 @@ def awq_main(args, torch, svdq, synth):
     torch.cuda.synchronize()
     ms = start.elapsed_time(stop) / args.steps
     nbytes = awq_bytes(M, N, K)
+    clock = gpu_clock(torch, lambda i: step(sets[i % nsets]), ms)
     gbs = nbytes / (ms * 1e-3) / 1e9
     cpu = None
     if not args.no_cpu_baseline:
@@ -453,6 +521,8 @@ def awq_main(args, torch, svdq, synth):
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
                      "traffic": None, "avg_ms": round(ms, 5), "algorithmic_bytes": nbytes},
         "host_pack_s": round(pack_s, 2),
+        "gpu_clock": clock,
+        "host": host_info(),
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
@@ -495,6 +565,7 @@ def nf4_main(args, torch, svdq, synth):
     torch.cuda.synchronize()
     ms = start.elapsed_time(stop) / args.steps
     flops = 2.0 * M * N * K
+    clock = gpu_clock(torch, lambda i: step(sets[i % nsets]), ms)
     tflops = flops / (ms * 1e-3) / 1e12
     ref = library_reference(torch, M, N, K)
     cpu = None
@@ -534,6 +605,8 @@ def nf4_main(args, torch, svdq, synth):
                      "traffic": None, "avg_ms": round(ms, 5), "algorithmic_bytes": nf4_bytes(M, N, K)},
         "matrix_core_reference": ref,
         "host_pack_s": round(pack_s, 2),
+        "gpu_clock": clock,
+        "host": host_info(),
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
@@ -641,6 +714,7 @@ def mlp_main(args, torch, svdq, synth):
         torch.cuda.synchronize()
         out[name + "_launch_ms"] = [round(float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs])), 5)
                                     for j in range(len(seq))]
+    clock = gpu_clock(torch, lambda i: [f(sets[i % len(sets)]) for f in fused], out["fused"])
     ops = 2.0 * M * N1 * K1 + 2.0 * M * N2 * N1
     req_ms = out["fused_launch_ms"][1]
     req_tops = 2.0 * M * N1 * K1 / (req_ms * 1e-3) / 1e12
@@ -673,6 +747,8 @@ def mlp_main(args, torch, svdq, synth):
         "roofline": {"bound": "mfma", "kernel": "svdq_w4a4_linear_requant (fc1, with the h2 sum)",
                      "achieved": round(req_tops, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(req_tops / peak, 4), "traffic": None, "avg_ms": req_ms},
+        "gpu_clock": clock,
+        "host": host_info(),
         "cpu_baseline": None,
     }
     print(json.dumps(line), flush=True)

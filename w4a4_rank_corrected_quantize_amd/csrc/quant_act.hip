@@ -25,6 +25,10 @@
 //     per lane), so each wave copies its chunk into its own LDS tile and reads
 //     it back transposed for v_mfma_f32_32x32x16_bf16 (A = down rows j,
 //     B = X^T columns m: one 32-row tile covers the block);
+//   * the chunk's slice of down (32 rows x 256 bytes) takes the same route:
+//     loaded as 8 runs of 4 rows x 256 contiguous bytes (8 full lines per
+//     load, where the operand layout would touch 32 lines per load) into a
+//     second LDS tile of the wave, and read back as the A operands;
 //   * the per-wave partial h tiles are summed in a fixed order through LDS at
 //     the end (deterministic).
 //
@@ -94,8 +98,12 @@ __global__ __launch_bounds__(64 * K1_WAVES) void quant_act_kernel(
     const uint16_t *__restrict__ down, uint8_t *__restrict__ xq, void *__restrict__ xscale,
     float *__restrict__ h)
 {
-    __shared__ __attribute__((aligned(16))) uint8_t tile[K1_WAVES][K1_RMAX * K1_TILE_STRIDE];
-    __shared__ float red[K1_WAVES][32][33];
+    // per wave: the X tile, then the down tile; the final reduction reuses
+    // the space once every wave has left its loop
+    constexpr int kTile = K1_RMAX * K1_TILE_STRIDE;
+    __shared__ __attribute__((aligned(16))) uint8_t smem[K1_WAVES * 2 * kTile];
+    static_assert(sizeof(float) * K1_WAVES * 32 * 33 <= sizeof(smem), "reduction fits in the tiles");
+    float(*red)[32][33] = reinterpret_cast<float(*)[32][33]>(smem);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int row0 = blockIdx.x * R;
     const int nrow = min(R, M - row0);      // 1 <= nrow <= 4 NL (the grid is sized by the host)
@@ -104,7 +112,8 @@ __global__ __launch_bounds__(64 * K1_WAVES) void quant_act_kernel(
     const int kl = 8 * (lane % K1_LPR);     // first channel of the lane within a chunk
     const int hk = lane >> 5;               // half of the product operand (channels 8 hk .. + 7)
     const int KB = K >> 1;                  // code bytes per row
-    uint8_t *mytile = tile[wave];
+    uint8_t *mytile = smem + wave * 2 * kTile;
+    uint8_t *mydown = mytile + kTile;
 
     // Loads are unconditional (addresses clamped into the buffers), so the
     // number of loads in flight is the same on every path: a row past the
@@ -129,14 +138,12 @@ __global__ __launch_bounds__(64 * K1_WAVES) void quant_act_kernel(
     auto process = [&](int c, const K1Chunk<NL> &L, int cn, K1Chunk<NL> &Ln) {
         const int kc = c * K1_CH + kl;
         const bool kv = kc < K;
-        // down operand of the chunk's 8 products (A: row j = lane % 32,
-        // channels 16 t + 8 (lane / 32) .. + 7), clamped into the buffer
-        uint4 dn[K1_CH / 16];
+        // the chunk's slice of down, row 4 t + lane / 16, channels
+        // kc .. kc + 7 (clamped into the buffer; zeroed past K below)
+        uint4 dn[32 / K1_RPL];
 #pragma unroll
-        for (int t = 0; t < K1_CH / 16; ++t) {
-            const int kk = min(c * K1_CH + 16 * t + 8 * hk, K - 8);
-            dn[t] = *reinterpret_cast<const uint4 *>(down + (size_t)(lane & 31) * K + kk);
-        }
+        for (int t = 0; t < 32 / K1_RPL; ++t)
+            dn[t] = *reinterpret_cast<const uint4 *>(down + (size_t)(K1_RPL * t + rq) * K + min(kc, K - 8));
         fetch(cn, Ln);
         const float sv[8] = {L.s0.x, L.s0.y, L.s0.z, L.s0.w, L.s1.x, L.s1.y, L.s1.z, L.s1.w};
 #pragma unroll
@@ -199,22 +206,27 @@ __global__ __launch_bounds__(64 * K1_WAVES) void quant_act_kernel(
             }
             if (st) *reinterpret_cast<uint32_t *>(xq + row * KB + (kc >> 1)) = code;
         }
+        // down rows into the wave's down tile; channels past K (last, partial
+        // chunk) add nothing
+#pragma unroll
+        for (int t = 0; t < 32 / K1_RPL; ++t)
+            *reinterpret_cast<uint4 *>(mydown + (K1_RPL * t + rq) * K1_TILE_STRIDE + 2 * kl) =
+                kv ? dn[t] : (uint4){0u, 0u, 0u, 0u};
         // the tile rows written above are read back by other lanes of this wave
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        // h^T[j][m] += sum_k down[j][k] X[m][k] over the chunk; rows m >= nrow
-        // read the last row (their outputs are dropped)
-        if ((c + 1) * K1_CH > K) {              // last, partial chunk: channels past K add nothing
-#pragma unroll
-            for (int t = 0; t < K1_CH / 16; ++t)
-                if (c * K1_CH + 16 * t + 8 * hk >= K) dn[t] = (uint4){0u, 0u, 0u, 0u};
-        }
+        // h^T[j][m] += sum_k down[j][k] X[m][k] over the chunk (A: row j =
+        // lane % 32, channels 16 t + 8 (lane / 32) .. + 7; B the same channels
+        // of row m = lane % 32); rows m >= nrow read the last row (their
+        // outputs are dropped)
         const uint8_t *src = mytile + min(lane & 31, nrow - 1) * K1_TILE_STRIDE + 16 * hk;
+        const uint8_t *dsrc = mydown + (lane & 31) * K1_TILE_STRIDE + 16 * hk;
 #pragma unroll
         for (int t = 0; t < K1_CH / 16; ++t) {
+            const uint4 a = *reinterpret_cast<const uint4 *>(dsrc + 32 * t);
             const uint4 b = *reinterpret_cast<const uint4 *>(src + 32 * t);
-            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(dn[t]), as_bf16x8(b), acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(b), acc, 0, 0, 0);
         }
         // the next chunk overwrites the tile only after every lane has read it
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -236,7 +248,9 @@ __global__ __launch_bounds__(64 * K1_WAVES) void quant_act_kernel(
     }
 
     // fixed-order reduction of the per-wave partial h^T tiles; lane l holds
-    // column m = l % 32 and rows j = 8 (i / 4) + 4 (l / 32) + i % 4
+    // column m = l % 32 and rows j = 8 (i / 4) + 4 (l / 32) + i % 4.  The
+    // partials overwrite the tiles, so every wave must be done with its own.
+    __syncthreads();
 #pragma unroll
     for (int i = 0; i < 16; ++i) red[wave][lane & 31][8 * (i >> 2) + 4 * hk + (i & 3)] = acc[i];
     __syncthreads();

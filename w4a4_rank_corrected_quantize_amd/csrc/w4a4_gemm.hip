@@ -1581,9 +1581,10 @@ __global__ __launch_bounds__(MXD_THREADS) void w4a4_mxfp4_dma_kernel(
         const int mb = m0 + wm * MX_WM, nb = n0 + wn * MX_WN;
         const int tile_n = n0 / MXD_BN, tile_m0 = m0;
         const int slice = t / tiles;
-        // the QKV-norm epilogue needs the registers that the next tile's
-        // prefetch would hold: that mode runs one tile per block
-        constexpr bool persistent = MODE != MXE_QKNORM;
+        // the QKV-norm and requantizing epilogues need the registers that the
+        // next tile's prefetch would hold (the requantizing one spilled 35
+        // VGPRs with it): those modes run one tile per block
+        constexpr bool persistent = MODE != MXE_QKNORM && MODE != MXE_REQUANT;
         const int tnext = persistent ? t + (int)gridDim.x : items;
         const int nst_done = nst;
         if (persistent && tnext < items) {
@@ -1720,9 +1721,7 @@ hipError_t launch_w4a4_linear_requant(const uint8_t *xq, const void *xscale, con
                            (uint16_t *)nullptr, rq, QKNormArgs{});
     } else {
         const int tiles = tiles_n * ((M + MXD_BM - 1) / MXD_BM);
-        const int ncu = device_cu_count();
-        const int blocks = tiles < ncu ? tiles : ncu;
-        hipLaunchKernelGGL(w4a4_mxfp4_dma_kernel<MXE_REQUANT>, dim3((unsigned)blocks), dim3(MXD_THREADS), 0, stream,
+        hipLaunchKernelGGL(w4a4_mxfp4_dma_kernel<MXE_REQUANT>, dim3((unsigned)tiles), dim3(MXD_THREADS), 0, stream,
                            xq, (const uint8_t *)xscale, h, wq, (const uint8_t *)wscale, up, bias, M, N, K, gelu,
                            (uint16_t *)nullptr, rq, SplitArgs{nullptr, 1, K >> 8}, QKNormArgs{});
     }

@@ -96,6 +96,7 @@ extern "C" const char *svdq_status_string(svdq_status status)
     case SVDQ_ERR_HIP: return "HIP runtime or kernel launch failure";
     case SVDQ_ERR_SCRATCH:
         return "the call needs more scratch memory than the library's static buffer holds (SVDQ_NOALLOC_SCRATCH_BYTES)";
+    case SVDQ_STATUS_INT_RANGE_: break;    // not a status: it only sizes the enum
     }
     return "unknown status";
 }

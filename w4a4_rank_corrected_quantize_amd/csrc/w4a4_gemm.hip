@@ -1583,8 +1583,9 @@ __global__ __launch_bounds__(MXD_THREADS) void w4a4_mxfp4_dma_kernel(
         const int slice = t / tiles;
         // the QKV-norm and requantizing epilogues need the registers that the
         // next tile's prefetch would hold (the requantizing one spilled 35
-        // VGPRs with it): those modes run one tile per block
-        constexpr bool persistent = MODE != MXE_QKNORM && MODE != MXE_REQUANT;
+        // VGPRs with it): those modes run one tile per block, and so do the
+        // split-K partial sums, whose items never outnumber the CUs
+        constexpr bool persistent = MODE == MXE_STORE;
         const int tnext = persistent ? t + (int)gridDim.x : items;
         const int nst_done = nst;
         if (persistent && tnext < items) {
@@ -1785,10 +1786,8 @@ hipError_t launch_w4a4_linear_splitk(const uint8_t *xq, const void *xscale, cons
     if (S < 2) return launch_w4a4_linear(xq, xscale, h, wq, wscale, up, bias, M, N, K, prec, epi, Y, stream);
     const int gelu = epi == SVDQ_EPI_GELU_TANH ? 1 : 0;
     const int tiles = ((N + MXD_BN - 1) / MXD_BN) * ((M + MXD_BM - 1) / MXD_BM);
-    const int ncu = device_cu_count();
-    const int items = tiles * S;
-    const int blocks = items < ncu ? items : ncu;
-    hipLaunchKernelGGL(w4a4_mxfp4_dma_kernel<MXE_PARTIAL>, dim3((unsigned)blocks), dim3(MXD_THREADS), 0, stream, xq,
+    const int items = tiles * S;                        // at most the CU count
+    hipLaunchKernelGGL(w4a4_mxfp4_dma_kernel<MXE_PARTIAL>, dim3((unsigned)items), dim3(MXD_THREADS), 0, stream, xq,
                        (const uint8_t *)xscale, h, wq, (const uint8_t *)wscale, up, bias, M, N, K, gelu,
                        (uint16_t *)nullptr, RequantArgs{}, SplitArgs{work, S, sps}, QKNormArgs{});
     hipError_t e = hipGetLastError();

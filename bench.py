@@ -40,10 +40,10 @@ NO_CLOCK = False
 # only reported while the kernel source still hashes to the value it was
 # measured on; otherwise traffic is null.
 TRAFFIC = {
-    # FETCH_SIZE 72778 KiB / 0.50003 + WRITE_SIZE 110610 KiB / 1.00000 (per dispatch)
-    ("int4", "fc1"): {"source_sha": "c8a8921c0134cc9f", "bytes": 263321600},
-    # FETCH_SIZE 70922 KiB / 0.50003 + WRITE_SIZE 111107 KiB / 1.00000
-    ("mxfp4", "fc1"): {"source_sha": "c8a8921c0134cc9f", "bytes": 259399680},
+    # FETCH_SIZE 73515 KiB / 0.50002 + WRITE_SIZE 110621 KiB / 1.00000 (per dispatch)
+    ("int4", "fc1"): {"source_sha": "1a4d8ae40cbcd877", "bytes": 263828403},
+    # FETCH_SIZE 70953 KiB / 0.50002 + WRITE_SIZE 111104 KiB / 1.00000
+    ("mxfp4", "fc1"): {"source_sha": "1a4d8ae40cbcd877", "bytes": 259076506},
 }
 
 

@@ -82,7 +82,7 @@ def host_info():
     return {"cpu_model": model, "cpu_threads": len(os.sched_getaffinity(0))}
 
 
-def gpu_clock(torch, step, ms_per_step, seconds=1.0, period=0.05):
+def gpu_clock(torch, step, ms_per_step, seconds=1.0, period=0.05, what="steps"):
     """The GFX clock while the step runs back to back: after the timed region
     the step is enqueued for about `seconds` while a second thread reads the
     clock that amd-smi reports (torch.cuda.clock_rate) every `period` s.  The
@@ -120,7 +120,7 @@ def gpu_clock(torch, step, ms_per_step, seconds=1.0, period=0.05):
     th.join()
     if not samples:
         return None
-    return {"source": f"amd-smi GFX clock, sampled every {int(period * 1e3)} ms while {n} more steps ran "
+    return {"source": f"amd-smi GFX clock, sampled every {int(period * 1e3)} ms while {n} more {what} ran "
                       "back to back after the timed region",
             "median_MHz": float(np.median(samples)), "min_MHz": min(samples), "max_MHz": max(samples),
             "samples": len(samples)}
@@ -160,6 +160,10 @@ def main():
                          "would otherwise stay in the 256 MB last-level cache)")
     ap.add_argument("--tokens", type=int, choices=[4608, 1024], default=4608,
                     help="1024: the MXFP4 linears of a 512 x 512 image (--prec mxfp4, fc1 / qkv / fc2)")
+    ap.add_argument("--launch", choices=["eager", "graph"], default=None,
+                    help="graph: capture the timed steps (and each kernel's launches) in HIP graphs and time their "
+                         "replays, so host launch gaps do not count; default graph for --tokens 1024 (kernels of "
+                         "10-40 us that the host cannot keep fed), eager otherwise")
     ap.add_argument("--splitk", action="store_true",
                     help="time svdq_w4a4_linear_splitk (K split across work items when the tiles cannot fill "
                          "the chip; the workspace is allocated before the timed region)")
@@ -278,33 +282,37 @@ def main():
     def ev():
         return torch.cuda.Event(enable_timing=True)
 
-    # 1) the timed region: K whole steps, events only at its ends
-    start, stop = ev(), ev()
-    torch.cuda.synchronize()
-    start.record()
-    for i in range(args.steps):
-        k1(sets[i % len(sets)])
-        k2(sets[i % len(sets)])
-    stop.record()
-    torch.cuda.synchronize()
-    total_ms = start.elapsed_time(stop)
-    ms_per_step = total_ms / args.steps
+    launch = args.launch or ("graph" if args.tokens == 1024 else "eager")
+    if launch == "graph":
+        ms_per_step, k1_ms, k2_ms, g_step = graph_times(torch, sets, k1, k2, args.steps)
+    else:
+        # 1) the timed region: K whole steps, events only at its ends
+        start, stop = ev(), ev()
+        torch.cuda.synchronize()
+        start.record()
+        for i in range(args.steps):
+            k1(sets[i % len(sets)])
+            k2(sets[i % len(sets)])
+        stop.record()
+        torch.cuda.synchronize()
+        total_ms = start.elapsed_time(stop)
+        ms_per_step = total_ms / args.steps
 
-    # 2) the same K steps again, with event pairs around each launch (on
-    #    torch's current stream, where both calls enqueue).  The linear's
-    #    times agree with rocprofv3's kernel trace; the activation kernel is
-    #    short enough (~20 us) that an event pair adds a few us to it.
-    evs = [(ev(), ev(), ev()) for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    for i in range(args.steps):
-        evs[i][0].record()
-        k1(sets[i % len(sets)])
-        evs[i][1].record()
-        k2(sets[i % len(sets)])
-        evs[i][2].record()
-    torch.cuda.synchronize()
-    k1_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
-    k2_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+        # 2) the same K steps again, with event pairs around each launch (on
+        #    torch's current stream, where both calls enqueue).  The linear's
+        #    times agree with rocprofv3's kernel trace; the activation kernel
+        #    is short enough (~20 us) that an event pair adds a few us to it.
+        evs = [(ev(), ev(), ev()) for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for i in range(args.steps):
+            evs[i][0].record()
+            k1(sets[i % len(sets)])
+            evs[i][1].record()
+            k2(sets[i % len(sets)])
+            evs[i][2].record()
+        torch.cuda.synchronize()
+        k1_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+        k2_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
 
     ops = 2.0 * M * N * K
     value = ops / (ms_per_step * 1e-3) / 1e12
@@ -318,7 +326,11 @@ def main():
     if t is not None and t["source_sha"] == _source_sha("w4a4_gemm.hip"):
         traffic = t["bytes"]
 
-    clock = gpu_clock(torch, lambda i: (k1(sets[i % len(sets)]), k2(sets[i % len(sets)])), ms_per_step)
+    if launch == "graph":
+        clock = gpu_clock(torch, lambda i: g_step.replay(), ms_per_step * args.steps,
+                          what=f"replays of the {args.steps}-step graph")
+    else:
+        clock = gpu_clock(torch, lambda i: (k1(sets[i % len(sets)]), k2(sets[i % len(sets)])), ms_per_step)
     cpu = None
     if not args.no_cpu_baseline:
         from oracle import oracle as O
@@ -366,7 +378,7 @@ def main():
                                "step = svdq_quantize_act + "
                                f"{'svdq_w4a4_linear_qkv_norm_rope' if qkvnorm else 'svdq_w4a4_linear'}",
                    "M": M, "K": K, "N": N, "rank": r, "buffer_sets": len(sets),
-                   "working_set_MB_per_set": round(ws_mb, 1)},
+                   "working_set_MB_per_set": round(ws_mb, 1), "launch": launch},
         "roofline": {"bound": "mfma", "kernel": ("svdq_w4a4_linear_qkv_norm_rope" if qkvnorm else
                                                   "svdq_w4a4_linear_splitk (both kernels)" if work is not None
                                                   else "svdq_w4a4_linear"),
@@ -385,6 +397,53 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
+
+
+def graph_times(torch, sets, k1, k2, steps):
+    """Per-step, activation-kernel and linear times from HIP-graph replays:
+    one graph of `steps` whole steps, one of `steps` activation launches and
+    one of `steps` linear launches, each replayed once between two events.
+    The step graph's outputs are checked against eager launches (three
+    replays, the outputs cleared in between) before anything is timed."""
+    n = len(sets)
+
+    def capture(body):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(steps):
+                body(sets[i % n])
+        torch.cuda.synchronize()
+        return g
+
+    g_step = capture(lambda b: (k1(b), k2(b)))
+    g_k1 = capture(k1)
+    g_k2 = capture(k2)
+    ref = []
+    for b in sets[:min(n, steps)]:
+        k1(b)
+        k2(b)
+        ref.append(b["Y"].clone())
+    torch.cuda.synchronize()
+    for _ in range(3):
+        for b in sets:
+            b["Y"].zero_()
+        g_step.replay()
+        torch.cuda.synchronize()
+        for b, y in zip(sets, ref):
+            if not torch.equal(b["Y"], y):
+                raise RuntimeError("graph replay differs from the eager launches")
+
+    def timed(g):
+        g.replay()                       # once untimed
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    return timed(g_step), timed(g_k1), timed(g_k2), g_step
 
 
 def library_reference(torch, M, N, K, reps=20):

@@ -168,6 +168,9 @@ def main():
                     help="time svdq_w4a4_linear_splitk (K split across work items when the tiles cannot fill "
                          "the chip; the workspace is allocated before the timed region)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--settle-ms", type=float, default=100.0,
+                    help="untimed steps for at least this long before the warm-up, so that the GPU clock has "
+                         "left its idle level whatever --warmup is (0: none)")
     ap.add_argument("--no-clock", action="store_true",
                     help="skip the clock sampling after the timed region (under a counter profiler)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle sample time")
@@ -272,12 +275,13 @@ def main():
         svdq.w4a4_linear(b["xq"], b["xscale"], b["h"], b["wq"], b["wscale"], b["up"], b["bias"], prec,
                          epi, Y=b["Y"])
 
+    settled = settle(torch, lambda i: (k1(sets[i % len(sets)]), k2(sets[i % len(sets)])), args.settle_ms)
     for i in range(args.warmup):
         k1(sets[i % len(sets)])
         k2(sets[i % len(sets)])
     torch.cuda.synchronize()
-    print(f"[bench] warmup done ({args.warmup} steps); timing {args.steps} steps", file=sys.stderr,
-          flush=True)
+    print(f"[bench] settled ({settled} steps), warmup done ({args.warmup} steps); timing {args.steps} steps",
+          file=sys.stderr, flush=True)
 
     def ev():
         return torch.cuda.Event(enable_timing=True)
@@ -362,6 +366,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle": {"ms": args.settle_ms, "steps": settled},
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -397,6 +402,25 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
+
+
+def settle(torch, step, ms):
+    """Runs the step back to back, untimed, for at least `ms` of wall time
+    before the warm-up steps.  The GFX clock of an idle MI355X takes ~30 ms
+    of back-to-back work to reach its sustained level (the linear's time
+    falls from ~410 to ~320 us over its first ~90 launches), so a short
+    warm-up would otherwise time part of the ramp.  Returns the number of
+    steps run."""
+    if ms <= 0:
+        return 0
+    n = 0
+    t0 = time.time()
+    while (time.time() - t0) * 1e3 < ms:
+        for _ in range(4):
+            step(n)
+            n += 1
+        torch.cuda.synchronize()
+    return n
 
 
 def graph_times(torch, sets, k1, k2, steps):
@@ -611,10 +635,12 @@ def nf4_main(args, torch, svdq, synth):
     def step(b):
         svdq.nf4_w4a16_linear(b["X"], b["wq"], b["qa"], b["ch"], None, Y=b["Y"])
 
+    settled = settle(torch, lambda i: step(sets[i % nsets]), args.settle_ms)
     for i in range(args.warmup):
         step(sets[i % nsets])
     torch.cuda.synchronize()
-    print(f"[bench] warmup done ({args.warmup} steps); timing {args.steps} steps", file=sys.stderr, flush=True)
+    print(f"[bench] settled ({settled} steps), warmup done ({args.warmup} steps); timing {args.steps} steps",
+          file=sys.stderr, flush=True)
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record()
@@ -649,6 +675,7 @@ def nf4_main(args, torch, svdq, synth):
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle": {"ms": args.settle_ms, "steps": settled},
         "ms_per_step": round(ms, 5),
         "higher_is_better": True,
         "scaling": "weak",

@@ -415,6 +415,42 @@ def test_linear_many_tiles_ragged(prec, K):
     _y_check(Y, y_ref, "many tiles")
 
 
+@pytest.mark.parametrize("prec", PRECS)
+def test_largest_accepted_activation(prec):
+    """The largest activation the calls accept: 65535 x 16384, one row short
+    of SVDQ_MAX_ELEMENTS (2^30) elements, so the last token tile is ragged
+    too.  The activation step's codes and scales bit-exact and h within the
+    bound, and the linear's output within tolerance, on 48 rows: the first
+    and last rows of the matrix and of several tiles, and random ones."""
+    M, K, N = 65535, 16384, 256
+    assert M * K < (1 << 30) <= (M + 1) * K
+    _say(f"largest activation prec={prec} M={M} K={K} N={N}")
+    rng = np.random.default_rng(2026)
+    X = np.empty((M, K), np.uint16)
+    for r0 in range(0, M, 4096):
+        b = min(4096, M - r0)
+        X[r0:r0 + b] = synth.f32_to_bf16_bits(rng.standard_normal((b, K), dtype=np.float32))
+    X[:, 7] = synth.f32_to_bf16_bits(np.full(M, 40.0, np.float32) * rng.standard_normal(M, dtype=np.float32))
+    W = synth.f32_to_bf16_bits(rng.normal(0.0, 0.02, (N, K)).astype(np.float32))
+    bias = synth.f32_to_bf16_bits(rng.normal(0.0, 0.01, N).astype(np.float32))
+    Xt = _t(X)
+    act = Xt.abs().amax(dim=0).float().cpu().numpy()
+    p = svdq.pack_weights(W, act, prec=prec)
+    xq, xs, h = svdq.quantize_act(Xt, _t(p["smooth"]), _t(p["down"]), prec)
+    Y = svdq.w4a4_linear(xq, xs, h, _t(p["wq"]), _t(p["wscale"]), _t(p["up"]), _t(bias), prec, svdq.EPI_NONE)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([[0, 1, 127, 128, 255, 256, 4607, 4608, M - 257, M - 256, M - 129, M - 128,
+                                      M - 2, M - 1], rng.choice(M, 34, replace=False)]))
+    ridx = torch.from_numpy(rows).cuda()
+    gq, gs, gh = _np(xq[ridx]), _np(xs[ridx]), _np(h[ridx])
+    oq, os_, oh = O.quant_act(X[rows], p["smooth"], p["down"], prec)
+    assert np.array_equal(gq, oq), f"codes differ at {np.argwhere(gq != oq)[:5]}"
+    assert np.array_equal(gs.view(np.uint8), os_.view(np.uint8))
+    assert np.all(np.abs(gh.astype(np.float64) - oh) <= _h_bound(X[rows], p["down"]))
+    y_ref = O.linear(gq, gs, oh, p["wq"], p["wscale"], p["up"], bias, prec)
+    _y_check(Y[ridx], y_ref, "largest activation")
+
+
 @pytest.mark.parametrize("prec,tokens", [(svdq.INT4, 4608), (svdq.MXFP4, 4608), (svdq.MXFP4, 1024)])
 def test_full_size_dit_block(prec, tokens):
     """QKV and the fc1 -> fc2 MLP pair at 4608 tokens (1024 for the MXFP4

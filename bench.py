@@ -571,7 +571,11 @@ def awq_main(args, torch, svdq, synth):
     torch.cuda.synchronize()
     ms = start.elapsed_time(stop) / args.steps
     nbytes = awq_bytes(M, N, K)
-    clock = gpu_clock(torch, lambda i: step(sets[i % nsets]), ms)
+    if graph is not None:   # eager launches leave the GPU idle between them (host-bound)
+        clock = gpu_clock(torch, lambda i: graph.replay(), ms * args.steps,
+                          what=f"replays of the {args.steps}-launch graph")
+    else:
+        clock = gpu_clock(torch, lambda i: step(sets[i % nsets]), ms)
     gbs = nbytes / (ms * 1e-3) / 1e9
     cpu = None
     if not args.no_cpu_baseline:

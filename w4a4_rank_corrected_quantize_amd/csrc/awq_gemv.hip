@@ -15,9 +15,13 @@
 //     16 bytes of X instead of one per lane and product), and the next slab's
 //     weights are in flight while the current one is computed; the 4 waves'
 //     partial results are summed in LDS in a fixed order (deterministic);
-//   * per chunk a lane (channel n = lane % 16, k-block b = lane / 16) reads
-//     the 32 code bytes that the storage order puts together for it (one
-//     coalesced 128-byte line per channel and chunk) with non-temporal loads;
+//   * a chunk of the 16 channels' codes is 16 lines of 128 bytes; each of
+//     the wave's two non-temporal loads takes 8 whole lines (8 lanes per
+//     line), and the lines go through a small per-wave LDS tile, from which
+//     a lane (channel n = lane % 16, k-block b = lane / 16) reads the 32 code
+//     bytes that the storage order puts together for it (half-line loads
+//     straight into that layout, 64 bytes of 16 lines per load, took 11-14 %
+//     longer);
 //   * a code c = q + 8 becomes the bf16 number 128 + c by OR-ing it into the
 //     bits of 128.0 (0x4300 | c), two codes per dword in one v_and_or: the
 //     storage order makes dword d of the lane's 32 bytes the B operand of
@@ -63,6 +67,7 @@ __device__ __forceinline__ bf16x8 awq_operand(uint32_t w)
 
 constexpr int AWQ_SLAB = 256 * AWQ_WAVES;            // channels of X staged per slab (one chunk per wave)
 constexpr int AWQ_XSTRIDE = AWQ_SLAB + 8;            // bf16 per staged row (16 B pad: conflict-free rows)
+constexpr int AWQ_WSTRIDE = 128 + 16;                // bytes per channel row of a wave's weight tile
 
 __global__ __launch_bounds__(64 * AWQ_WAVES) void awq_w4a16_kernel(const uint16_t *__restrict__ X,
                                                                    const uint8_t *__restrict__ wq,
@@ -72,6 +77,7 @@ __global__ __launch_bounds__(64 * AWQ_WAVES) void awq_w4a16_kernel(const uint16_
 {
     extern __shared__ __attribute__((aligned(16))) uint16_t xs[];   // min(M, 16) rows x AWQ_XSTRIDE
     __shared__ f32x4 part[AWQ_WAVES][64];
+    __shared__ __attribute__((aligned(16))) uint8_t wt[AWQ_WAVES][AWQ_COLS * AWQ_WSTRIDE];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int col = lane & 15, kb = lane >> 4;
     const int n = blockIdx.x * AWQ_COLS + col;
@@ -79,7 +85,13 @@ __global__ __launch_bounds__(64 * AWQ_WAVES) void awq_w4a16_kernel(const uint16_
     const int chunks = K >> 8;
     const int slabs = (chunks + AWQ_WAVES - 1) / AWQ_WAVES;
     const int KB = K >> 1, G = K >> 6;
-    const uint8_t *wrow = wq + (size_t)nrow * KB + 32 * kb;
+    // weight loads take whole 128-byte lines: 8 lanes per channel line, so
+    // one load covers channels (lane / 8) and the other 8 + lane / 8
+    const int l8 = lane >> 3, lp = 16 * (lane & 7);
+    const int n0 = blockIdx.x * AWQ_COLS;
+    const uint8_t *lrow0 = wq + (size_t)min(n0 + l8, N - 1) * KB + lp;
+    const uint8_t *lrow1 = wq + (size_t)min(n0 + 8 + l8, N - 1) * KB + lp;
+    uint8_t *mywt = wt[wave];
     const float *srow = wscale + (size_t)nrow * G;
     const bf16x8 neg136 = __builtin_bit_cast(bf16x8, (u32x4){kBf16_m136, kBf16_m136, kBf16_m136, kBf16_m136});
 
@@ -91,8 +103,8 @@ __global__ __launch_bounds__(64 * AWQ_WAVES) void awq_w4a16_kernel(const uint16_
         u32x4 w0 = {0u, 0u, 0u, 0u}, w1 = {0u, 0u, 0u, 0u};
         float4 sw = make_float4(0.f, 0.f, 0.f, 0.f);
         if (wave < chunks) {
-            w0 = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(wrow + 128 * wave));
-            w1 = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(wrow + 128 * wave + 16));
+            w0 = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(lrow0 + 128 * wave));
+            w1 = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(lrow1 + 128 * wave));
             sw = *reinterpret_cast<const float4 *>(srow + 4 * wave);
         }
         for (int s = 0; s < slabs; ++s) {
@@ -111,12 +123,21 @@ __global__ __launch_bounds__(64 * AWQ_WAVES) void awq_w4a16_kernel(const uint16_
             // next slab's weights are in flight while this one is computed
             const int cn = c + AWQ_WAVES;
             if (cn < chunks) {
-                w0 = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(wrow + 128 * cn));
-                w1 = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(wrow + 128 * cn + 16));
+                w0 = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(lrow0 + 128 * cn));
+                w1 = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(lrow1 + 128 * cn));
                 sw = *reinterpret_cast<const float4 *>(srow + 4 * cn);
             }
             if (c < chunks) {
-                const uint32_t wd[8] = {cw0.x, cw0.y, cw0.z, cw0.w, cw1.x, cw1.y, cw1.z, cw1.w};
+                // the lines into the wave's tile, read back as the lane's 32
+                // operand bytes (channel col, bytes 32 kb .. + 31)
+                *reinterpret_cast<u32x4 *>(mywt + l8 * AWQ_WSTRIDE + lp) = cw0;
+                *reinterpret_cast<u32x4 *>(mywt + (8 + l8) * AWQ_WSTRIDE + lp) = cw1;
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+                const u32x4 ow0 = *reinterpret_cast<const u32x4 *>(mywt + col * AWQ_WSTRIDE + 32 * kb);
+                const u32x4 ow1 = *reinterpret_cast<const u32x4 *>(mywt + col * AWQ_WSTRIDE + 32 * kb + 16);
+                const uint32_t wd[8] = {ow0.x, ow0.y, ow0.z, ow0.w, ow1.x, ow1.y, ow1.z, ow1.w};
                 const float swv[4] = {csw.x, csw.y, csw.z, csw.w};
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {

@@ -120,8 +120,8 @@ def gpu_clock(torch, step, ms_per_step, seconds=1.0, period=0.05, what="steps"):
     th.join()
     if not samples:
         return None
-    return {"source": f"amd-smi GFX clock, sampled every {int(period * 1e3)} ms while {n} more {what} ran "
-                      "back to back after the timed region",
+    return {"source": f"amd-smi GFX clock (the SMU's reported value, not a shader-cycle count), sampled every "
+                      f"{int(period * 1e3)} ms while {n} more {what} ran back to back after the timed region",
             "median_MHz": float(np.median(samples)), "min_MHz": min(samples), "max_MHz": max(samples),
             "samples": len(samples)}
 

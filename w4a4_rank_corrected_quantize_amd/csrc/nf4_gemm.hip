@@ -281,16 +281,24 @@ __global__ __launch_bounds__(NF_THREADS) void nf4_linear_kernel(
     load_codes(1, R);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    // step st: the other stage takes X and the decoded weights of step st + 1
-    // (R, loaded during step st - 1), R takes the codes of step st + 2, then
-    // the products of step st run from stage st & 1
+    // step st: the other stage takes the decoded weights of step st + 1 (R,
+    // loaded during step st - 1) and X of step st + 1, R takes the codes of
+    // step st + 2, then the products of step st run from stage st & 1.
+    // vmcnt completes in order and the compiler does not see the DMA, so
+    // its waits for R must come before the DMA is issued: the decode goes
+    // first, and nothing is conditional (the last step reloads its own data
+    // into the free stage, which nothing reads) -- with a skipped branch the
+    // compiler waited for every load where the paths merge, the DMA just
+    // issued included, ahead of the products.
     for (int st = 0; st < steps; ++st) {
         const int sg = st & 1;
-        if (st + 1 < steps) {
-            issue_x(st + 1, sg ^ 1);
-            decode_to(R, sg ^ 1);
-        }
-        load_codes(st + 2, R);          // unconditional (clamped): same load count on every path
+        decode_to(R, sg ^ 1);
+        issue_x(min(st + 1, steps - 1), sg ^ 1);
+        load_codes(st + 2, R);          // clamped: same load count on every path
+        // the code loads stay ahead of the products (left to the scheduler,
+        // they sank to the end of the step, where the wait below took their
+        // whole latency)
+        __builtin_amdgcn_sched_barrier(0);
         compute(sg);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();

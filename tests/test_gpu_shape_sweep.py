@@ -1,0 +1,128 @@
+"""Seeded random shapes through every device call, against the fp64 oracle.
+
+The other GPU tests pick their shapes by hand (tile edges, single steps, full
+size).  Here a fixed seed draws ragged M, N and K within each call's shape
+rules, so that a tiling or tail mistake that no hand-picked shape happens to
+hit still meets a case.  Same bar as test_gpu_parity: codes and scales
+bit-exact, h within the blocked-summation bound, bf16 outputs within
+8e-3 |y_ref| + 1e-3 rms(y_ref).
+"""
+import numpy as np
+import pytest
+
+import w4a4_rank_corrected_quantize_amd as svdq
+from oracle import oracle as O
+from tests.test_gpu_parity import (_awq_case, _awq_run, _layer, _nf4_case, _nf4_run, _np, _qkvnorm_case,
+                                   _quant_act_check, _requant_case, _say, _t, _y_check)
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+_rng = np.random.default_rng(20261203)
+
+
+def _draw(n, fn):
+    return [fn() for _ in range(n)]
+
+
+def _b():
+    return bool(_rng.integers(0, 2))
+
+
+# (prec, M, K, N, bias, gelu): INT4 K in steps of 64, MXFP4 in steps of 32
+# (odd numbers of E8M0 blocks and K % 256 != 0 included), N in steps of 8
+LINEAR = (_draw(16, lambda: (svdq.INT4, int(_rng.integers(1, 521)), 64 * int(_rng.integers(1, 25)),
+                            8 * int(_rng.integers(1, 101)), _b(), _b()))
+          + _draw(16, lambda: (svdq.MXFP4, int(_rng.integers(1, 521)), 32 * int(_rng.integers(1, 49)),
+                              8 * int(_rng.integers(1, 101)), _b(), _b())))
+# split K: skinny MXFP4 shapes with whole 256-channel steps
+SPLITK = _draw(6, lambda: (int(_rng.integers(1, 301)), 256 * int(_rng.integers(4, 17)),
+                           8 * int(_rng.integers(1, 71)), _b()))
+# fused next-layer step: N % 64 == 0 (the next layer's K); MXFP4 K % 256 == 0
+REQUANT = (_draw(4, lambda: (svdq.INT4, int(_rng.integers(1, 401)), 64 * int(_rng.integers(1, 13)),
+                             64 * int(_rng.integers(1, 11)), _b(), _b()))
+           + _draw(4, lambda: (svdq.MXFP4, int(_rng.integers(1, 401)), 256 * int(_rng.integers(1, 4)),
+                               64 * int(_rng.integers(1, 11)), _b(), _b())))
+# Q/K norm + rotary: N = 3 H 128
+QKNORM = (_draw(3, lambda: (svdq.INT4, int(_rng.integers(1, 301)), 64 * int(_rng.integers(1, 9)),
+                            384 * int(_rng.integers(1, 3)), _b()))
+          + _draw(3, lambda: (svdq.MXFP4, int(_rng.integers(1, 301)), 256 * int(_rng.integers(1, 3)),
+                              384 * int(_rng.integers(1, 3)), _b())))
+# weight-only paths
+AWQ = _draw(8, lambda: (int(_rng.integers(1, 41)), 256 * int(_rng.integers(1, 13)), int(_rng.integers(1, 401)),
+                        _b()))
+NF4 = _draw(8, lambda: (int(_rng.integers(1, 301)), 64 * int(_rng.integers(1, 49)), 8 * int(_rng.integers(1, 101)),
+                        _b()))
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    svdq.check_device()
+
+
+def _id(case):
+    return "-".join(str(int(v)) for v in case)
+
+
+@pytest.mark.parametrize("case", LINEAR, ids=_id)
+def test_sweep_linear(case):
+    prec, M, K, N, bias, gelu = case
+    _say(f"sweep linear prec={prec} M={M} K={K} N={N} bias={bias} gelu={gelu}")
+    L, p = _layer("qkv", M, K, N, prec, bias=bias)
+    xq, xs, h, oh = _quant_act_check(L["X"], p["smooth"], p["down"], prec)
+    Y = svdq.w4a4_linear(xq, xs, h, _t(p["wq"]), _t(p["wscale"]), _t(p["up"]), _t(L["bias"]), prec,
+                         svdq.EPI_GELU_TANH if gelu else svdq.EPI_NONE)
+    torch.cuda.synchronize()
+    y_ref = O.linear(_np(xq), _np(xs), oh, p["wq"], p["wscale"], p["up"], L["bias"], prec, gelu=gelu)
+    _y_check(Y, y_ref, f"sweep linear {case}")
+
+
+@pytest.mark.parametrize("case", SPLITK, ids=_id)
+def test_sweep_splitk(case):
+    M, K, N, gelu = case
+    prec = svdq.MXFP4
+    _say(f"sweep split-K M={M} K={K} N={N} gelu={gelu}")
+    L, p = _layer("qkv", M, K, N, prec)
+    xq, xs, h, oh = _quant_act_check(L["X"], p["smooth"], p["down"], prec)
+    epi = svdq.EPI_GELU_TANH if gelu else svdq.EPI_NONE
+    args = (xq, xs, h, _t(p["wq"]), _t(p["wscale"]), _t(p["up"]), _t(L["bias"]), prec, epi)
+    need = svdq.linear_splitk_workspace_bytes(M, N, K, prec)
+    work = torch.full((max(need, 4) // 4,), float("nan"), dtype=torch.float32, device="cuda")
+    Ys = svdq.w4a4_linear_splitk(*args, work=work)
+    torch.cuda.synchronize()
+    y_ref = O.linear(_np(xq), _np(xs), oh, p["wq"], p["wscale"], p["up"], L["bias"], prec, gelu=gelu)
+    _y_check(Ys, y_ref, f"sweep split-K {case} (workspace {need} bytes)")
+
+
+@pytest.mark.parametrize("case", REQUANT, ids=_id)
+def test_sweep_requant(case):
+    prec, M, K, N, bias, gelu = case
+    _say(f"sweep requant prec={prec} M={M} K={K} N={N} bias={bias} gelu={gelu}")
+    _requant_case(M, K, N, bias, gelu, prec)
+
+
+@pytest.mark.parametrize("case", QKNORM, ids=_id)
+def test_sweep_qkv_norm_rope(case):
+    prec, M, K, N, bias = case
+    _say(f"sweep qkv norm rope prec={prec} M={M} K={K} N={N} bias={bias}")
+    _qkvnorm_case(M, K, N, bias, prec=prec)
+
+
+@pytest.mark.parametrize("case", AWQ, ids=_id)
+def test_sweep_awq(case):
+    M, K, N, bias = case
+    _say(f"sweep awq M={M} K={K} N={N} bias={bias}")
+    X, W, b = _awq_case(M, K, N, bias)
+    Y, wq, ws = _awq_run(X, W, b)
+    _y_check(Y, O.awq_linear(X, wq, ws, b), f"sweep awq {case}")
+
+
+@pytest.mark.parametrize("case", NF4, ids=_id)
+def test_sweep_nf4(case):
+    M, K, N, bias = case
+    _say(f"sweep nf4 M={M} K={K} N={N} bias={bias}")
+    X, W, b = _nf4_case(M, K, N, bias)
+    Y, y_ref, _, _ = _nf4_run(X, W, b)
+    _y_check(Y, y_ref, f"sweep nf4 {case}")

@@ -34,27 +34,29 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak, 2.5 PFLOP/s
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, 8 TB/s
 NO_CLOCK = False
 
-# HBM traffic of svdq_w4a4_linear per launch, from two rocprofv3 --pmc runs
+# HBM traffic per launch of a workload's kernel, from two rocprofv3 --pmc runs
 # (FETCH_SIZE, then WRITE_SIZE) of this script, each divided by what the same
 # counter reads for a plain 512 MiB copy (--copy-calibration).  An entry is
 # only reported while the kernel source still hashes to the value it was
 # measured on; otherwise traffic is null.
 TRAFFIC = {
     # FETCH_SIZE 73515 KiB / 0.50002 + WRITE_SIZE 110621 KiB / 1.00000 (per dispatch)
-    ("int4", "fc1"): {"source": "w4a4_gemm.hip", "source_sha": "1a4d8ae40cbcd877", "bytes": 263828403},
+    "fc1": {"source": "w4a4_gemm.hip", "source_sha": "1a4d8ae40cbcd877", "bytes": 263828403},
     # FETCH_SIZE 70953 KiB / 0.50002 + WRITE_SIZE 111104 KiB / 1.00000
-    ("mxfp4", "fc1"): {"source": "w4a4_gemm.hip", "source_sha": "1a4d8ae40cbcd877", "bytes": 259076506},
+    "mx_fc1": {"source": "w4a4_gemm.hip", "source_sha": "1a4d8ae40cbcd877", "bytes": 259076506},
     # FETCH_SIZE 15680 KiB / 0.50002 + WRITE_SIZE 36 KiB / 1.00000
-    ("awq", "awq_mod"): {"source": "awq_gemv.hip", "source_sha": "fda4dd7b5f7b1013", "bytes": 32148220},
+    "awq_mod": {"source": "awq_gemv.hip", "source_sha": "fda4dd7b5f7b1013", "bytes": 32148220},
     # FETCH_SIZE 197078 KiB / 0.50002 + WRITE_SIZE 110594 KiB / 1.00000
-    ("nf4", "nf4_fc1"): {"source": "nf4_gemm.hip", "source_sha": "84b8f49923726640", "bytes": 516848112},
+    "nf4_fc1": {"source": "nf4_gemm.hip", "source_sha": "84b8f49923726640", "bytes": 516848112},
 }
 
 
-def measured_traffic(kind, layer):
-    """HBM bytes per launch from the table above, or None once the kernel
-    source no longer hashes to the value the counters were taken on."""
-    t = TRAFFIC.get((kind, layer))
+def measured_traffic(workload):
+    """HBM bytes per launch of the named workload's kernel (the synth spec
+    name: a table entry covers that shape only) from the table above, or None
+    once the kernel source no longer hashes to the value the counters were
+    taken on."""
+    t = TRAFFIC.get(workload)
     if t is None or t["source_sha"] != _source_sha(t["source"]):
         return None
     return t["bytes"]
@@ -338,7 +340,7 @@ def main():
     peak = PEAK_INT8_TOPS if prec == svdq.INT4 else PEAK_FP4_TFLOPS
     k1_gbs = k1_bytes(M, K, r, prec) / (k1_ms * 1e-3) / 1e9
     k2_gbs = k2_bytes(M, N, K, r, prec, bias=L["bias"] is not None) / (k2_ms * 1e-3) / 1e9
-    traffic = measured_traffic(args.prec, args.layer)
+    traffic = None if qkvnorm else measured_traffic(spec.name)
 
     if launch == "graph":
         clock = gpu_clock(torch, lambda i: g_step.replay(), ms_per_step * args.steps,
@@ -616,7 +618,7 @@ def awq_main(args, torch, svdq, synth):
                    "weights_MB_per_set": round((wq.nbytes + ws.nbytes) / 1e6, 1), "launch": launch},
         "roofline": {"bound": "hbm", "kernel": "svdq_awq_w4a16_linear", "achieved": round(gbs, 1),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
-                     "traffic": measured_traffic("awq", spec.name), "avg_ms": round(ms, 5),
+                     "traffic": measured_traffic(spec.name), "avg_ms": round(ms, 5),
                      "algorithmic_bytes": nbytes},
         "host_pack_s": round(pack_s, 2),
         "gpu_clock": clock,
@@ -703,7 +705,7 @@ def nf4_main(args, torch, svdq, synth):
                    "M": M, "K": K, "N": N, "buffer_sets": nsets},
         "roofline": {"bound": "mfma", "kernel": "svdq_nf4_w4a16_linear", "achieved": round(tflops, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": measured_traffic("nf4", spec.name), "avg_ms": round(ms, 5),
+                     "traffic": measured_traffic(spec.name), "avg_ms": round(ms, 5),
                      "algorithmic_bytes": nf4_bytes(M, N, K)},
         "matrix_core_reference": ref,
         "host_pack_s": round(pack_s, 2),

@@ -32,3 +32,16 @@ def test_help_lists_the_workloads():
     assert r.returncode == 0
     for word in ("--layer", "fc1", "nf4_fc1", "--launch", "--settle-ms", "--tokens"):
         assert word in r.stdout
+
+
+def test_traffic_entries_cover_their_own_workload_only():
+    """The HBM traffic a bench line reports belongs to one workload shape:
+    other shapes of the same kernel (1024 tokens, QKV) report none, and every
+    entry names a kernel source that exists."""
+    sys.path.insert(0, ROOT)
+    import bench
+    for name, t in bench.TRAFFIC.items():
+        assert os.path.exists(os.path.join(ROOT, "w4a4_rank_corrected_quantize_amd", "csrc", t["source"])), name
+        assert t["bytes"] > 0
+    for other in ("mx1k_fc1", "mx1k_qkv", "qkv", "mx_qkv", "fc2", "nf4_qkv"):
+        assert bench.measured_traffic(other) is None

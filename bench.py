@@ -371,10 +371,15 @@ def main():
                "sample": f"{rows} of {M} token rows of the same layer (activation step + linear), "
                          f"{t_cpu:.1f} s"}
 
+    headline = prec == svdq.INT4 and spec.name == "fc1" and not qkvnorm and work is None
+    metric = ("W4A4 linear TOPS & % int8-MFMA peak at M=4608,K=3072,N=12288 (r=32)" if headline else
+              f"W4A4 linear {'TOPS' if prec == svdq.INT4 else 'TFLOP/s'} & % "
+              f"{'int8' if prec == svdq.INT4 else 'fp4'}-MFMA peak at M={M},K={K},N={N} (r={r})"
+              f"{', Q/K norm + rotary epilogue' if qkvnorm else ''}{', split K' if work is not None else ''}")
     line = {
-        "metric": "W4A4 linear TOPS & % int8-MFMA peak at M=4608,K=3072,N=12288 (r=32)",
+        "metric": metric,
         "value": round(value, 2),
-        "unit": "TOPS",
+        "unit": "TOPS" if prec == svdq.INT4 else "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,

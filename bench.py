@@ -825,6 +825,31 @@ def mlp_main(args, torch, svdq, synth):
                                     for j in range(len(seq))]
     clock = gpu_clock(torch, lambda i: [f(sets[i % len(sets)]) for f in fused], out["fused"])
     ops = 2.0 * M * N1 * K1 + 2.0 * M * N2 * N1
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle import oracle as O
+        print("[bench] timing the CPU oracle on a row sample of the pair", file=sys.stderr, flush=True)
+
+        def oracle_rows(n):
+            # fc1's activation step and product, its fp64 output rounded to
+            # bf16 as fc2's input, fc2's activation step and product
+            q, s_, hh = O.quant_act(L1["X"][:n], p1["smooth"], p1["down"], prec)
+            y1 = O.linear(q, s_, hh, p1["wq"], p1["wscale"], p1["up"], L1["bias"], prec, gelu=True)
+            q, s_, hh = O.quant_act(synth.f64_to_bf16_bits(y1), p2["smooth"], p2["down"], prec)
+            O.linear(q, s_, hh, p2["wq"], p2["wscale"], p2["up"], L2["bias"], prec)
+
+        rows = min(M, 32)
+        t0 = time.time()
+        oracle_rows(rows)
+        probe = max(time.time() - t0, 1e-3)
+        rows = int(min(M, max(8, rows * args.cpu_seconds / probe)))
+        t0 = time.time()
+        oracle_rows(rows)
+        t_cpu = time.time() - t0
+        cpu = {"value": round(ops * rows / M / t_cpu / 1e12, 6), "unit": "TOPS", "cores": O.num_threads(),
+               "kind": "oracle",
+               "sample": f"{rows} of {M} token rows through both layers (activation steps + products), "
+                         f"{t_cpu:.1f} s"}
     req_ms = out["fused_launch_ms"][1]
     req_tops = 2.0 * M * N1 * K1 / (req_ms * 1e-3) / 1e12
     peak = PEAK_INT8_TOPS if prec == svdq.INT4 else PEAK_FP4_TFLOPS
@@ -858,7 +883,7 @@ def mlp_main(args, torch, svdq, synth):
                      "frac": round(req_tops / peak, 4), "traffic": None, "avg_ms": req_ms},
         "gpu_clock": clock,
         "host": host_info(),
-        "cpu_baseline": None,
+        "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
 

@@ -7,6 +7,8 @@ hit still meets a case.  Same bar as test_gpu_parity: codes and scales
 bit-exact, h within the blocked-summation bound, bf16 outputs within
 8e-3 |y_ref| + 1e-3 rms(y_ref).
 """
+import os
+
 import numpy as np
 import pytest
 
@@ -18,11 +20,14 @@ from tests.test_gpu_parity import (_awq_case, _awq_run, _layer, _nf4_case, _nf4_
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
-_rng = np.random.default_rng(20261203)
+# SVDQ_SWEEP_SEED / SVDQ_SWEEP_SCALE draw another or a larger set (the
+# committed run uses the defaults)
+_rng = np.random.default_rng(int(os.environ.get("SVDQ_SWEEP_SEED", "20261203")))
+_SCALE = max(1, int(os.environ.get("SVDQ_SWEEP_SCALE", "1")))
 
 
 def _draw(n, fn):
-    return [fn() for _ in range(n)]
+    return [fn() for _ in range(n * _SCALE)]
 
 
 def _b():

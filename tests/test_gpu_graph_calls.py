@@ -3,7 +3,8 @@ runtime would): each replay, with eager work, output clearing and
 synchronizations in between, equals the eager launch bit for bit.  None of
 the calls records a memset (outputs are cleared here by fill kernels,
 outside the graph), and workspaces and the allocation-free call's static
-buffer keep their addresses across replays."""
+buffer keep their addresses across replays.  Last, the calls from several
+host threads at once, each on its own stream (default priority)."""
 import numpy as np
 import pytest
 
@@ -123,3 +124,45 @@ def test_graph_nf4():
     Wd = torch.empty((N, K), dtype=torch.bfloat16, device="cuda")
     _replays_match(lambda: svdq.nf4_w4a16_linear(Xt, qt, qat, cht, bt, Y=Y), [Y])
     _replays_match(lambda: svdq.nf4_dequantize(qt, qat, cht, Wd=Wd), [Wd])
+
+
+@pytest.mark.parametrize("prec", PRECS)
+def test_concurrent_host_threads(prec):
+    """The calls are thread-safe: four host threads, each on its own stream
+    with its own buffers, run the activation step and the linear together
+    (ctypes releases the GIL during the calls); every result equals the
+    single-threaded one bit for bit."""
+    import threading
+    _say(f"host threads prec={prec}")
+    M, K, N = 200, 768, 264
+    L, p = _layer("qkv", M, K, N, prec)
+    X, s, d = _t(L["X"]), _t(p["smooth"]), _t(p["down"])
+    w = (_t(p["wq"]), _t(p["wscale"]), _t(p["up"]), _t(L["bias"]))
+    xq, xs, h = svdq.quantize_act(X, s, d, prec)
+    ref = svdq.w4a4_linear(xq, xs, h, *w, prec, svdq.EPI_GELU_TANH)
+    torch.cuda.synchronize()
+    results, errors = {}, []
+
+    def worker(t):
+        try:
+            st = torch.cuda.Stream()
+            with torch.cuda.stream(st):
+                for i in range(5):
+                    q, sc, hh = svdq.quantize_act(X, s, d, prec)
+                    y = svdq.w4a4_linear(q, sc, hh, *w, prec, svdq.EPI_GELU_TANH)
+                    results[(t, i)] = (q, y)
+            st.synchronize()
+        except Exception as e:      # reported below
+            errors.append(e)
+
+    threads = [threading.Thread(target=worker, args=(t,)) for t in range(4)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    assert len(results) == 20
+    for (q, y) in results.values():
+        assert torch.equal(q, xq)
+        assert torch.equal(y.view(torch.uint8), ref.view(torch.uint8))

@@ -204,7 +204,12 @@ svdq_status svdq_quantize_act(const uint16_t *X, int M, int K, const float *smoo
  * instruction on high/low bf16 splits of both scales (relative error about
  * 2^-16) and multiplies the exact partial in one fp32 fma.  MXFP4: the
  * scaled f8f6f4 matrix instruction applies both E8M0 scales.  The low-rank
- * term uses h split into a bf16 high and low part.  One kernel launch.
+ * term uses h split into a bf16 high and low part.  One kernel launch;
+ * for INT4, two when the tiles left after whole rounds of one block per CU
+ * are few: those tiles are then computed in 64 x 64 pieces with K split
+ * across a block's waves and the partial sums added in a fixed order (so
+ * their outputs may differ in low bf16 places from what the one-launch form
+ * gives for the same rows; results are deterministic for a given shape).
  * Errors as for svdq_quantize_act.
  */
 svdq_status svdq_w4a4_linear(const uint8_t *xq, const void *xscale, const float *h,

@@ -415,6 +415,29 @@ def test_linear_many_tiles_ragged(prec, K):
     _y_check(Y, y_ref, "many tiles")
 
 
+@pytest.mark.parametrize("K", [192, 704, 3072])
+def test_linear_int4_tail_pieces(K):
+    """INT4 shapes whose tiles fill whole rounds of one block per CU plus a
+    few (2100 x 4000: 17 x 16 = 272 tiles on 256 CUs, 16 left over): the
+    leftover tiles run in 64 x 64 pieces with K split over the block's waves
+    (three groups, so some waves have none; eleven, uneven; 48).  Every
+    output against the oracle, and a second call gives the same bits."""
+    if torch.cuda.get_device_properties(0).multi_processor_count != 256:
+        pytest.skip("the split into whole rounds below assumes 256 CUs")
+    M, N = 2100, 4000
+    prec = svdq.INT4
+    _say(f"linear INT4 tail pieces M={M} K={K} N={N}")
+    L, p = _layer("qkv", M, K, N, prec)
+    xq, xs, h, oh = _quant_act_check(L["X"], p["smooth"], p["down"], prec)
+    w = (_t(p["wq"]), _t(p["wscale"]), _t(p["up"]), _t(L["bias"]))
+    Y = svdq.w4a4_linear(xq, xs, h, *w, prec, svdq.EPI_GELU_TANH)
+    Y2 = svdq.w4a4_linear(xq, xs, h, *w, prec, svdq.EPI_GELU_TANH)
+    torch.cuda.synchronize()
+    assert torch.equal(Y.view(torch.int16), Y2.view(torch.int16))
+    y_ref = O.linear(_np(xq), _np(xs), oh, p["wq"], p["wscale"], p["up"], L["bias"], prec, gelu=True)
+    _y_check(Y, y_ref, "tail pieces")
+
+
 @pytest.mark.parametrize("prec", PRECS)
 def test_largest_accepted_activation(prec):
     """The largest activation the calls accept: 65535 x 16384, one row short

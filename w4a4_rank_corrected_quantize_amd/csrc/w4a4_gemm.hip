@@ -862,6 +862,183 @@ __global__ __launch_bounds__(I4_THREADS) void w4a4_int4_kernel(
     flush_tile(tile, Y, mb, nb, M, N, lane);
 }
 
+// The last, nearly empty round of INT4 tiles.  When the tiles that remain
+// after whole rounds of one block per CU are few (at 4608 x 3072 -> 9216:
+// 1296 tiles, five rounds and 16 tiles), each of them is computed by 8
+// blocks instead of one: block b takes the 64 x 64 piece b % 8 of the b / 8-th
+// remaining tile, and its 8 waves split that piece's K, wave w taking groups
+// [w G / 8, (w + 1) G / 8).  A wave's operands come straight from global
+// memory (the nibbles widened in registers, exactly as the staging of the
+// full-size kernel writes them), with the same products, scale products and
+// fma per group as there.  The 8 partial sums are added in wave order through
+// LDS, and wave 0 runs the full-size kernel's epilogue on the sum.  Only the
+// order of the 4-bit term's sum differs from the full-size kernel (partial
+// sums over K ranges instead of one running sum), so outputs may differ from
+// it in low bf16 places.
+constexpr int I4T_PIECES = (I4_BM / 64) * (I4_BN / 64);    // 64 x 64 pieces per tile
+
+__global__ __launch_bounds__(I4_THREADS) void w4a4_int4_tail_kernel(
+    const uint8_t *__restrict__ xq, const float *__restrict__ xscale, const float *__restrict__ h,
+    const uint8_t *__restrict__ wq, const float *__restrict__ wscale, const uint16_t *__restrict__ up,
+    const uint16_t *__restrict__ bias, int M, int N, int K, int gelu, uint16_t *__restrict__ Y, int first)
+{
+    static_assert(I4_THREADS == 512 && I4T_PIECES == 8, "8 waves, 8 pieces per tile");
+    __shared__ __attribute__((aligned(16))) float red[7][16 * I4_TN * I4_TM][64];   // waves 1-7's sums
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l32 = lane & 31, hk = lane >> 5;
+    const int tiles_n = (N + I4_BN - 1) / I4_BN, tiles_m = (M + I4_BM - 1) / I4_BM;
+    int tn_, tm_;
+    tile_coords(first + (int)blockIdx.x / I4T_PIECES, tiles_n, tiles_m, tn_, tm_);
+    const int piece = (int)blockIdx.x % I4T_PIECES;
+    const int mb = tm_ * I4_BM + 64 * (piece / (I4_BN / 64)), nb = tn_ * I4_BN + 64 * (piece % (I4_BN / 64));
+    const int G = K >> 6, KB = K >> 1;
+    const int g0 = wave * G / 8, g1 = (wave + 1) * G / 8;
+
+    // the lane's rows: weight rows nb + 32 tn + l32, token rows mb + 32 tm + l32
+    // (clamped; outputs of rows past N / M are never stored)
+    const uint8_t *wrow[I4_TN], *xrow[I4_TM];
+    const float *wsr[I4_TN], *xsr[I4_TM];
+#pragma unroll
+    for (int t = 0; t < I4_TN; ++t) {
+        const int n = min(nb + 32 * t + l32, N - 1);
+        wrow[t] = wq + (size_t)n * KB + 16 * hk;
+        wsr[t] = wscale + (size_t)n * G;
+    }
+#pragma unroll
+    for (int t = 0; t < I4_TM; ++t) {
+        const int m = min(mb + 32 * t + l32, M - 1);
+        xrow[t] = xq + (size_t)m * KB + 16 * hk;
+        xsr[t] = xscale + (size_t)m * G;
+    }
+
+    f32x16 acc[I4_TN][I4_TM];
+#pragma unroll
+    for (int a = 0; a < I4_TN; ++a)
+#pragma unroll
+        for (int b = 0; b < I4_TM; ++b)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.0f;
+    // the lane's 32 codes of group g (bytes 32 g + 16 hk of each row) and
+    // the rows' scales, loaded one group ahead
+    uint4 nw[I4_TN], nx[I4_TM];
+    float sw[I4_TN], sx[I4_TM];
+    auto load = [&](int g) {
+#pragma unroll
+        for (int t = 0; t < I4_TN; ++t) {
+            nw[t] = *reinterpret_cast<const uint4 *>(wrow[t] + 32 * g);
+            sw[t] = wsr[t][g];
+        }
+#pragma unroll
+        for (int t = 0; t < I4_TM; ++t) {
+            nx[t] = *reinterpret_cast<const uint4 *>(xrow[t] + 32 * g);
+            sx[t] = xsr[t][g];
+        }
+    };
+    const f32x16 zero16 = {};
+    if (g0 < g1) load(g0);
+#pragma unroll 1
+    for (int g = g0; g < g1; ++g) {
+        // widened as the full-size kernel's staging does
+        i32x8 aw[I4_TN], bx[I4_TM];
+        bf16x8 cw[I4_TN], cx[I4_TM];
+#pragma unroll
+        for (int t = 0; t < I4_TN; ++t) {
+            uint4 lo, hi;
+            widen_fp8(nw[t], lo, hi);
+            aw[t] = (i32x8){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+            const uint2 v = scale_operand_w(sw[t] * kTwo17);
+            cw[t] = __builtin_bit_cast(bf16x8, (uint4){v.x, v.y, 0u, 0u});
+        }
+#pragma unroll
+        for (int t = 0; t < I4_TM; ++t) {
+            uint4 lo, hi;
+            widen_fp8(nx[t], lo, hi);
+            bx[t] = (i32x8){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+            const uint2 v = scale_operand_x(sx[t]);
+            cx[t] = __builtin_bit_cast(bf16x8, (uint4){v.x, v.y, 0u, 0u});
+        }
+        if (g + 1 < g1) load(g + 1);
+#pragma unroll
+        for (int tn = 0; tn < I4_TN; ++tn)
+#pragma unroll
+            for (int tm = 0; tm < I4_TM; ++tm) {
+                const f32x16 pr = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(aw[tn], bx[tm], zero16, 0, 0, 0,
+                                                                                  127, 0, 127);
+                const f32x16 c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cw[tn], cx[tm], zero16, 0, 0, 0);
+#pragma unroll
+                for (int i = 0; i < 16; ++i) acc[tn][tm][i] = __builtin_fmaf(pr[i], c[i], acc[tn][tm][i]);
+            }
+    }
+
+    // waves 1-7 hand their sums to wave 0, which adds them in wave order
+    if (wave > 0) {
+#pragma unroll
+        for (int tn = 0; tn < I4_TN; ++tn)
+#pragma unroll
+            for (int tm = 0; tm < I4_TM; ++tm)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) red[wave - 1][16 * (I4_TM * tn + tm) + i][lane] = acc[tn][tm][i];
+    }
+    __syncthreads();
+    if (wave > 0) return;
+#pragma unroll 1
+    for (int w = 0; w < 7; ++w)
+#pragma unroll
+        for (int tn = 0; tn < I4_TN; ++tn)
+#pragma unroll
+            for (int tm = 0; tm < I4_TM; ++tm)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) acc[tn][tm][i] += red[w][16 * (I4_TM * tn + tm) + i][lane];
+
+    // the full-size kernel's epilogue for one wave tile (staged in the first
+    // partial-sum area, which wave 0 has finished reading)
+    bf16x8 hhi[I4_TM][2], hlo[I4_TM][2];
+#pragma unroll
+    for (int tm = 0; tm < I4_TM; ++tm)
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+            float hv[8];
+            load_h8(h, mb + tm * 32 + l32, M, 16 * s2 + 8 * hk, hv);
+            split_h(hv, hhi[tm][s2], hlo[tm][s2]);
+        }
+    uint8_t *tile = reinterpret_cast<uint8_t *>(&red[0][0][0]);
+    static_assert(OUT_TILE_BYTES <= sizeof(red), "output staging fits");
+#pragma unroll
+    for (int tn = 0; tn < I4_TN; ++tn) {
+        const int nrow = nb + tn * 32 + l32;
+        bf16x8 ua[2];
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+            uint4 uv = {0u, 0u, 0u, 0u};
+            if (nrow < N) uv = *reinterpret_cast<const uint4 *>(up + (size_t)nrow * 32 + 16 * s2 + 8 * hk);
+            ua[s2] = __builtin_bit_cast(bf16x8, uv);
+        }
+        uint2 bv[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) bv[j] = bias4(bias, nb + tn * 32 + 8 * j + 4 * hk, N);
+#pragma unroll
+        for (int tm = 0; tm < I4_TM; ++tm) {
+            f32x16 lr = {};
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) {
+                lr = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ua[s2], hhi[tm][s2], lr, 0, 0, 0);
+                lr = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ua[s2], hlo[tm][s2], lr, 0, 0, 0);
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                float a4[4] = {acc[tn][tm][4 * j], acc[tn][tm][4 * j + 1], acc[tn][tm][4 * j + 2],
+                               acc[tn][tm][4 * j + 3]};
+                float l4[4] = {lr[4 * j], lr[4 * j + 1], lr[4 * j + 2], lr[4 * j + 3]};
+                stage4(tile, tm * 32 + l32, tn * 32 + 8 * j + 4 * hk, finish4(a4, l4, bv[j], gelu));
+            }
+        }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    flush_tile(tile, Y, mb, nb, M, N, lane);
+}
+
 // Fixed-order sum of the per-tile partial h2: h2[m][j] = sum_t hpart[t][m][j],
 // t ascending.
 __global__ __launch_bounds__(256) void requant_h_reduce(const float *__restrict__ hpart, int T, int M,
@@ -1675,9 +1852,23 @@ hipError_t launch_w4a4_linear(const uint8_t *xq, const void *xscale, const float
     const int64_t rows = M > N ? M : N;
     if (prec == SVDQ_INT4) {
         const int tiles = ((N + I4_BN - 1) / I4_BN) * ((M + I4_BM - 1) / I4_BM);
-        hipLaunchKernelGGL(w4a4_int4_kernel<EPI_STORE>, dim3((unsigned)tiles), dim3(I4_THREADS), 0, stream, xq,
+        // whole rounds of one block per CU, then, when the remaining tiles are
+        // few enough that their pieces fill at most one round, those tiles in
+        // pieces (w4a4_int4_tail_kernel)
+        const int ncu = device_cu_count();
+        const int full = (tiles / ncu) * ncu, rest = tiles - full;
+        const bool pieces = full > 0 && rest > 0 && rest * I4T_PIECES <= ncu;
+        const int main_tiles = pieces ? full : tiles;
+        hipLaunchKernelGGL(w4a4_int4_kernel<EPI_STORE>, dim3((unsigned)main_tiles), dim3(I4_THREADS), 0, stream, xq,
                            (const float *)xscale, h, wq, (const float *)wscale, up, bias, M, N, K, gelu, Y,
                            RequantArgs{}, QKNormArgs{});
+        if (pieces) {
+            hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+            hipLaunchKernelGGL(w4a4_int4_tail_kernel, dim3((unsigned)(rest * I4T_PIECES)), dim3(I4_THREADS), 0,
+                               stream, xq, (const float *)xscale, h, wq, (const float *)wscale, up, bias, M, N, K,
+                               gelu, Y, full);
+        }
     } else {
         // the LDS-DMA kernel takes whole 256-channel steps and 32-bit offsets
         if (K % 256 == 0 && rows * (K / 2) < ((int64_t)1 << 31)) {

@@ -864,9 +864,10 @@ __global__ __launch_bounds__(I4_THREADS) void w4a4_int4_kernel(
 
 // The last, nearly empty round of INT4 tiles.  When the tiles that remain
 // after whole rounds of one block per CU are few (at 4608 x 3072 -> 9216:
-// 1296 tiles, five rounds and 16 tiles), each of them is computed by 8
-// blocks instead of one: block b takes the 64 x 64 piece b % 8 of the b / 8-th
-// remaining tile, and its 8 waves split that piece's K, wave w taking groups
+// 1296 tiles, five rounds and 16 tiles), each of them is computed by 8 or 16
+// blocks instead of one: block b takes piece b % P (64 tokens x 32 PTN
+// channels, P = 16 / PTN pieces per tile) of the b / P-th remaining tile, and
+// its 8 waves split that piece's K, wave w taking groups
 // [w G / 8, (w + 1) G / 8).  A wave's operands come straight from global
 // memory (the nibbles widened in registers, exactly as the staging of the
 // full-size kernel writes them), with the same products, scale products and
@@ -875,31 +876,37 @@ __global__ __launch_bounds__(I4_THREADS) void w4a4_int4_kernel(
 // order of the 4-bit term's sum differs from the full-size kernel (partial
 // sums over K ranges instead of one running sum), so outputs may differ from
 // it in low bf16 places.
-constexpr int I4T_PIECES = (I4_BM / 64) * (I4_BN / 64);    // 64 x 64 pieces per tile
+template <int PTN>
+struct I4Tail {
+    static constexpr int kPieces = (I4_BM / 64) * (I4_BN / (32 * PTN));   // pieces per tile
+    static constexpr int kAcc = 16 * PTN * I4_TM;                          // accumulators per lane
+};
 
+template <int PTN>
 __global__ __launch_bounds__(I4_THREADS) void w4a4_int4_tail_kernel(
     const uint8_t *__restrict__ xq, const float *__restrict__ xscale, const float *__restrict__ h,
     const uint8_t *__restrict__ wq, const float *__restrict__ wscale, const uint16_t *__restrict__ up,
     const uint16_t *__restrict__ bias, int M, int N, int K, int gelu, uint16_t *__restrict__ Y, int first)
 {
-    static_assert(I4_THREADS == 512 && I4T_PIECES == 8, "8 waves, 8 pieces per tile");
-    __shared__ __attribute__((aligned(16))) float red[7][16 * I4_TN * I4_TM][64];   // waves 1-7's sums
+    static_assert(I4_THREADS == 512, "8 waves");
+    constexpr int P = I4Tail<PTN>::kPieces, PW = 32 * PTN;    // pieces per tile, piece width (channels)
+    __shared__ __attribute__((aligned(16))) float red[7][I4Tail<PTN>::kAcc][64];   // waves 1-7's sums
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, hk = lane >> 5;
     const int tiles_n = (N + I4_BN - 1) / I4_BN, tiles_m = (M + I4_BM - 1) / I4_BM;
     int tn_, tm_;
-    tile_coords(first + (int)blockIdx.x / I4T_PIECES, tiles_n, tiles_m, tn_, tm_);
-    const int piece = (int)blockIdx.x % I4T_PIECES;
-    const int mb = tm_ * I4_BM + 64 * (piece / (I4_BN / 64)), nb = tn_ * I4_BN + 64 * (piece % (I4_BN / 64));
+    tile_coords(first + (int)blockIdx.x / P, tiles_n, tiles_m, tn_, tm_);
+    const int piece = (int)blockIdx.x % P;
+    const int mb = tm_ * I4_BM + 64 * (piece / (I4_BN / PW)), nb = tn_ * I4_BN + PW * (piece % (I4_BN / PW));
     const int G = K >> 6, KB = K >> 1;
     const int g0 = wave * G / 8, g1 = (wave + 1) * G / 8;
 
     // the lane's rows: weight rows nb + 32 tn + l32, token rows mb + 32 tm + l32
     // (clamped; outputs of rows past N / M are never stored)
-    const uint8_t *wrow[I4_TN], *xrow[I4_TM];
-    const float *wsr[I4_TN], *xsr[I4_TM];
+    const uint8_t *wrow[PTN], *xrow[I4_TM];
+    const float *wsr[PTN], *xsr[I4_TM];
 #pragma unroll
-    for (int t = 0; t < I4_TN; ++t) {
+    for (int t = 0; t < PTN; ++t) {
         const int n = min(nb + 32 * t + l32, N - 1);
         wrow[t] = wq + (size_t)n * KB + 16 * hk;
         wsr[t] = wscale + (size_t)n * G;
@@ -911,20 +918,20 @@ __global__ __launch_bounds__(I4_THREADS) void w4a4_int4_tail_kernel(
         xsr[t] = xscale + (size_t)m * G;
     }
 
-    f32x16 acc[I4_TN][I4_TM];
+    f32x16 acc[PTN][I4_TM];
 #pragma unroll
-    for (int a = 0; a < I4_TN; ++a)
+    for (int a = 0; a < PTN; ++a)
 #pragma unroll
         for (int b = 0; b < I4_TM; ++b)
 #pragma unroll
             for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.0f;
     // the lane's 32 codes of group g (bytes 32 g + 16 hk of each row) and
     // the rows' scales, loaded one group ahead
-    uint4 nw[I4_TN], nx[I4_TM];
-    float sw[I4_TN], sx[I4_TM];
+    uint4 nw[PTN], nx[I4_TM];
+    float sw[PTN], sx[I4_TM];
     auto load = [&](int g) {
 #pragma unroll
-        for (int t = 0; t < I4_TN; ++t) {
+        for (int t = 0; t < PTN; ++t) {
             nw[t] = *reinterpret_cast<const uint4 *>(wrow[t] + 32 * g);
             sw[t] = wsr[t][g];
         }
@@ -939,10 +946,10 @@ __global__ __launch_bounds__(I4_THREADS) void w4a4_int4_tail_kernel(
 #pragma unroll 1
     for (int g = g0; g < g1; ++g) {
         // widened as the full-size kernel's staging does
-        i32x8 aw[I4_TN], bx[I4_TM];
-        bf16x8 cw[I4_TN], cx[I4_TM];
+        i32x8 aw[PTN], bx[I4_TM];
+        bf16x8 cw[PTN], cx[I4_TM];
 #pragma unroll
-        for (int t = 0; t < I4_TN; ++t) {
+        for (int t = 0; t < PTN; ++t) {
             uint4 lo, hi;
             widen_fp8(nw[t], lo, hi);
             aw[t] = (i32x8){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
@@ -959,7 +966,7 @@ __global__ __launch_bounds__(I4_THREADS) void w4a4_int4_tail_kernel(
         }
         if (g + 1 < g1) load(g + 1);
 #pragma unroll
-        for (int tn = 0; tn < I4_TN; ++tn)
+        for (int tn = 0; tn < PTN; ++tn)
 #pragma unroll
             for (int tm = 0; tm < I4_TM; ++tm) {
                 const f32x16 pr = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(aw[tn], bx[tm], zero16, 0, 0, 0,
@@ -973,7 +980,7 @@ __global__ __launch_bounds__(I4_THREADS) void w4a4_int4_tail_kernel(
     // waves 1-7 hand their sums to wave 0, which adds them in wave order
     if (wave > 0) {
 #pragma unroll
-        for (int tn = 0; tn < I4_TN; ++tn)
+        for (int tn = 0; tn < PTN; ++tn)
 #pragma unroll
             for (int tm = 0; tm < I4_TM; ++tm)
 #pragma unroll
@@ -984,13 +991,13 @@ __global__ __launch_bounds__(I4_THREADS) void w4a4_int4_tail_kernel(
 #pragma unroll 1
     for (int w = 0; w < 7; ++w)
 #pragma unroll
-        for (int tn = 0; tn < I4_TN; ++tn)
+        for (int tn = 0; tn < PTN; ++tn)
 #pragma unroll
             for (int tm = 0; tm < I4_TM; ++tm)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) acc[tn][tm][i] += red[w][16 * (I4_TM * tn + tm) + i][lane];
 
-    // the full-size kernel's epilogue for one wave tile (staged in the first
+    // the full-size kernel's epilogue for a 64 x PW tile (staged in the first
     // partial-sum area, which wave 0 has finished reading)
     bf16x8 hhi[I4_TM][2], hlo[I4_TM][2];
 #pragma unroll
@@ -1004,7 +1011,7 @@ __global__ __launch_bounds__(I4_THREADS) void w4a4_int4_tail_kernel(
     uint8_t *tile = reinterpret_cast<uint8_t *>(&red[0][0][0]);
     static_assert(OUT_TILE_BYTES <= sizeof(red), "output staging fits");
 #pragma unroll
-    for (int tn = 0; tn < I4_TN; ++tn) {
+    for (int tn = 0; tn < PTN; ++tn) {
         const int nrow = nb + tn * 32 + l32;
         bf16x8 ua[2];
 #pragma unroll
@@ -1036,7 +1043,15 @@ __global__ __launch_bounds__(I4_THREADS) void w4a4_int4_tail_kernel(
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    flush_tile(tile, Y, mb, nb, M, N, lane);
+    // 64 rows x PW channels: 64 rows of 4 PTN segments of 16 bytes
+    constexpr int SEGS = 4 * PTN;
+#pragma unroll
+    for (int it = 0; it < SEGS; ++it) {
+        const int idx = lane + 64 * it, r = idx / SEGS, seg = idx % SEGS;
+        const uint4 v = *reinterpret_cast<const uint4 *>(tile + r * OUT_STRIDE + seg * 16);
+        const int m = mb + r, n = nb + seg * 8;
+        if (m < M && n < N) store_nt(Y + (size_t)m * N + n, v);
+    }
 }
 
 // Fixed-order sum of the per-tile partial h2: h2[m][j] = sum_t hpart[t][m][j],
@@ -1857,7 +1872,7 @@ hipError_t launch_w4a4_linear(const uint8_t *xq, const void *xscale, const float
         // pieces (w4a4_int4_tail_kernel)
         const int ncu = device_cu_count();
         const int full = (tiles / ncu) * ncu, rest = tiles - full;
-        const bool pieces = full > 0 && rest > 0 && rest * I4T_PIECES <= ncu;
+        const bool pieces = full > 0 && rest > 0 && rest * I4Tail<2>::kPieces <= ncu;
         const int main_tiles = pieces ? full : tiles;
         hipLaunchKernelGGL(w4a4_int4_kernel<EPI_STORE>, dim3((unsigned)main_tiles), dim3(I4_THREADS), 0, stream, xq,
                            (const float *)xscale, h, wq, (const float *)wscale, up, bias, M, N, K, gelu, Y,
@@ -1865,9 +1880,15 @@ hipError_t launch_w4a4_linear(const uint8_t *xq, const void *xscale, const float
         if (pieces) {
             hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
-            hipLaunchKernelGGL(w4a4_int4_tail_kernel, dim3((unsigned)(rest * I4T_PIECES)), dim3(I4_THREADS), 0,
-                               stream, xq, (const float *)xscale, h, wq, (const float *)wscale, up, bias, M, N, K,
-                               gelu, Y, full);
+            // the narrower pieces when they still fit in one round
+            if (rest * I4Tail<1>::kPieces <= ncu)
+                hipLaunchKernelGGL(w4a4_int4_tail_kernel<1>, dim3((unsigned)(rest * I4Tail<1>::kPieces)),
+                                   dim3(I4_THREADS), 0, stream, xq, (const float *)xscale, h, wq,
+                                   (const float *)wscale, up, bias, M, N, K, gelu, Y, full);
+            else
+                hipLaunchKernelGGL(w4a4_int4_tail_kernel<2>, dim3((unsigned)(rest * I4Tail<2>::kPieces)),
+                                   dim3(I4_THREADS), 0, stream, xq, (const float *)xscale, h, wq,
+                                   (const float *)wscale, up, bias, M, N, K, gelu, Y, full);
         }
     } else {
         // the LDS-DMA kernel takes whole 256-channel steps and 32-bit offsets

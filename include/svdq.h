@@ -345,7 +345,9 @@ svdq_status svdq_w4a4_linear_requant(const uint8_t *xq, const void *xscale, cons
  * With yb = the bf16 value svdq_w4a4_linear would store: V channels get yb;
  * a Q or K head gets u_d = yb_d / sqrt(mean_d(yb_d^2) + eps) * w_d (fp32),
  * then out_2p = u_2p cos_mp - u_2p+1 sin_mp, out_2p+1 = u_2p+1 cos_mp +
- * u_2p sin_mp, rounded to bf16 (round-to-nearest-even).  One kernel launch.
+ * u_2p sin_mp, rounded to bf16 (round-to-nearest-even).  One kernel launch
+ * (for INT4 two, with the leftover tiles in pieces, exactly when
+ * svdq_w4a4_linear takes two at the same shape; yb is then that call's).
  * Errors as for svdq_w4a4_linear, plus the ones above.
  */
 svdq_status svdq_w4a4_linear_qkv_norm_rope(const uint8_t *xq, const void *xscale, const float *h,

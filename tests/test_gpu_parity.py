@@ -667,6 +667,19 @@ def test_qkv_norm_rope_eps_comparable_to_mean_square(eps_factor):
         _y_check(Y, O.qkv_norm_rope(yb, nq, nk, 0.0, c, s), "eps left out")
 
 
+@pytest.mark.parametrize("K", [256, 704])
+def test_qkv_norm_rope_int4_tail_pieces(K):
+    """2800 tokens x 3072 channels (8 heads each of Q, K, V): 22 x 12 = 264
+    INT4 tiles on 256 CUs, the 8 left over computed in pieces of 32 tokens x
+    one head with K split over a block's waves.  Every output against the
+    oracle, V heads bit-equal to the plain linear's (whose leftover tiles
+    take the same pieces' sums)."""
+    if torch.cuda.get_device_properties(0).multi_processor_count != 256:
+        pytest.skip("the split into whole rounds below assumes 256 CUs")
+    _say(f"qkv norm rope INT4 tail pieces K={K}")
+    _qkvnorm_case(2800, K, 3072)
+
+
 @pytest.mark.parametrize("prec", PRECS)
 def test_qkv_norm_rope_full_size(prec):
     """4608 tokens x 3072 -> 9216 (24 heads each of Q, K, V) with the

@@ -864,47 +864,53 @@ __global__ __launch_bounds__(I4_THREADS) void w4a4_int4_kernel(
 
 // The last, nearly empty round of INT4 tiles.  When the tiles that remain
 // after whole rounds of one block per CU are few (at 4608 x 3072 -> 9216:
-// 1296 tiles, five rounds and 16 tiles), each of them is computed by 8 or 16
-// blocks instead of one: block b takes piece b % P (64 tokens x 32 PTN
-// channels, P = 16 / PTN pieces per tile) of the b / P-th remaining tile, and
-// its 8 waves split that piece's K, wave w taking groups
-// [w G / 8, (w + 1) G / 8).  A wave's operands come straight from global
-// memory (the nibbles widened in registers, exactly as the staging of the
-// full-size kernel writes them), with the same products, scale products and
-// fma per group as there.  The 8 partial sums are added in wave order through
-// LDS, and wave 0 runs the full-size kernel's epilogue on the sum.  Only the
-// order of the 4-bit term's sum differs from the full-size kernel (partial
-// sums over K ranges instead of one running sum), so outputs may differ from
-// it in low bf16 places.
-template <int PTN>
+// 1296 tiles, five rounds and 16 tiles), each of them is computed by several
+// blocks instead of one: block b takes piece b % P (32 PTM tokens x 32 PTN
+// channels) of the b / P-th remaining tile, and its 8 waves split that
+// piece's K, wave w taking groups [w G / 8, (w + 1) G / 8).  A wave's
+// operands come straight from global memory (the nibbles widened in
+// registers, exactly as the staging of the full-size kernel writes them),
+// with the same products, scale products and fma per group as there.  The 8
+// partial sums are added in wave order through LDS, and wave 0 runs the
+// epilogue on the sum: the plain one (pieces of 64 x 32 or 64 x 64), or the
+// Q/K RMS-norm + rotary one on pieces of 32 tokens x one 128-channel head.
+// Only the order of the 4-bit term's sum differs from the full-size kernel
+// (partial sums over K ranges instead of one running sum), so outputs may
+// differ from it in low bf16 places.
+template <int PTN, int PTM>
 struct I4Tail {
-    static constexpr int kPieces = (I4_BM / 64) * (I4_BN / (32 * PTN));   // pieces per tile
-    static constexpr int kAcc = 16 * PTN * I4_TM;                          // accumulators per lane
+    static constexpr int kPieces = (I4_BM / (32 * PTM)) * (I4_BN / (32 * PTN));   // pieces per tile
+    static constexpr int kAcc = 16 * PTN * PTM;                                   // accumulators per lane
 };
 
-template <int PTN>
+constexpr int QKP_ROW = 264;                 // staging row of a head piece: 128 bf16 + 8 bytes
+
+template <int PTN, int PTM, int EPI>
 __global__ __launch_bounds__(I4_THREADS) void w4a4_int4_tail_kernel(
     const uint8_t *__restrict__ xq, const float *__restrict__ xscale, const float *__restrict__ h,
     const uint8_t *__restrict__ wq, const float *__restrict__ wscale, const uint16_t *__restrict__ up,
-    const uint16_t *__restrict__ bias, int M, int N, int K, int gelu, uint16_t *__restrict__ Y, int first)
+    const uint16_t *__restrict__ bias, int M, int N, int K, int gelu, uint16_t *__restrict__ Y, int first,
+    QKNormArgs qk)
 {
     static_assert(I4_THREADS == 512, "8 waves");
-    constexpr int P = I4Tail<PTN>::kPieces, PW = 32 * PTN;    // pieces per tile, piece width (channels)
-    __shared__ __attribute__((aligned(16))) float red[7][I4Tail<PTN>::kAcc][64];   // waves 1-7's sums
+    static_assert(EPI == EPI_STORE ? (PTM == 2 && PTN <= 2) : (EPI == EPI_QKNORM && PTM == 1 && PTN == 4),
+                  "plain pieces of 64 x 32 / 64 x 64, head pieces of 32 x 128");
+    constexpr int P = I4Tail<PTN, PTM>::kPieces, PW = 32 * PTN, PH = 32 * PTM;   // pieces per tile, width, height
+    __shared__ __attribute__((aligned(16))) float red[7][I4Tail<PTN, PTM>::kAcc][64];   // waves 1-7's sums
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, hk = lane >> 5;
     const int tiles_n = (N + I4_BN - 1) / I4_BN, tiles_m = (M + I4_BM - 1) / I4_BM;
     int tn_, tm_;
     tile_coords(first + (int)blockIdx.x / P, tiles_n, tiles_m, tn_, tm_);
     const int piece = (int)blockIdx.x % P;
-    const int mb = tm_ * I4_BM + 64 * (piece / (I4_BN / PW)), nb = tn_ * I4_BN + PW * (piece % (I4_BN / PW));
+    const int mb = tm_ * I4_BM + PH * (piece / (I4_BN / PW)), nb = tn_ * I4_BN + PW * (piece % (I4_BN / PW));
     const int G = K >> 6, KB = K >> 1;
     const int g0 = wave * G / 8, g1 = (wave + 1) * G / 8;
 
     // the lane's rows: weight rows nb + 32 tn + l32, token rows mb + 32 tm + l32
     // (clamped; outputs of rows past N / M are never stored)
-    const uint8_t *wrow[PTN], *xrow[I4_TM];
-    const float *wsr[PTN], *xsr[I4_TM];
+    const uint8_t *wrow[PTN], *xrow[PTM];
+    const float *wsr[PTN], *xsr[PTM];
 #pragma unroll
     for (int t = 0; t < PTN; ++t) {
         const int n = min(nb + 32 * t + l32, N - 1);
@@ -912,23 +918,23 @@ __global__ __launch_bounds__(I4_THREADS) void w4a4_int4_tail_kernel(
         wsr[t] = wscale + (size_t)n * G;
     }
 #pragma unroll
-    for (int t = 0; t < I4_TM; ++t) {
+    for (int t = 0; t < PTM; ++t) {
         const int m = min(mb + 32 * t + l32, M - 1);
         xrow[t] = xq + (size_t)m * KB + 16 * hk;
         xsr[t] = xscale + (size_t)m * G;
     }
 
-    f32x16 acc[PTN][I4_TM];
+    f32x16 acc[PTN][PTM];
 #pragma unroll
     for (int a = 0; a < PTN; ++a)
 #pragma unroll
-        for (int b = 0; b < I4_TM; ++b)
+        for (int b = 0; b < PTM; ++b)
 #pragma unroll
             for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.0f;
     // the lane's 32 codes of group g (bytes 32 g + 16 hk of each row) and
     // the rows' scales, loaded one group ahead
-    uint4 nw[PTN], nx[I4_TM];
-    float sw[PTN], sx[I4_TM];
+    uint4 nw[PTN], nx[PTM];
+    float sw[PTN], sx[PTM];
     auto load = [&](int g) {
 #pragma unroll
         for (int t = 0; t < PTN; ++t) {
@@ -936,7 +942,7 @@ __global__ __launch_bounds__(I4_THREADS) void w4a4_int4_tail_kernel(
             sw[t] = wsr[t][g];
         }
 #pragma unroll
-        for (int t = 0; t < I4_TM; ++t) {
+        for (int t = 0; t < PTM; ++t) {
             nx[t] = *reinterpret_cast<const uint4 *>(xrow[t] + 32 * g);
             sx[t] = xsr[t][g];
         }
@@ -946,8 +952,8 @@ __global__ __launch_bounds__(I4_THREADS) void w4a4_int4_tail_kernel(
 #pragma unroll 1
     for (int g = g0; g < g1; ++g) {
         // widened as the full-size kernel's staging does
-        i32x8 aw[PTN], bx[I4_TM];
-        bf16x8 cw[PTN], cx[I4_TM];
+        i32x8 aw[PTN], bx[PTM];
+        bf16x8 cw[PTN], cx[PTM];
 #pragma unroll
         for (int t = 0; t < PTN; ++t) {
             uint4 lo, hi;
@@ -957,7 +963,7 @@ __global__ __launch_bounds__(I4_THREADS) void w4a4_int4_tail_kernel(
             cw[t] = __builtin_bit_cast(bf16x8, (uint4){v.x, v.y, 0u, 0u});
         }
 #pragma unroll
-        for (int t = 0; t < I4_TM; ++t) {
+        for (int t = 0; t < PTM; ++t) {
             uint4 lo, hi;
             widen_fp8(nx[t], lo, hi);
             bx[t] = (i32x8){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
@@ -968,7 +974,7 @@ __global__ __launch_bounds__(I4_THREADS) void w4a4_int4_tail_kernel(
 #pragma unroll
         for (int tn = 0; tn < PTN; ++tn)
 #pragma unroll
-            for (int tm = 0; tm < I4_TM; ++tm) {
+            for (int tm = 0; tm < PTM; ++tm) {
                 const f32x16 pr = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(aw[tn], bx[tm], zero16, 0, 0, 0,
                                                                                   127, 0, 127);
                 const f32x16 c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cw[tn], cx[tm], zero16, 0, 0, 0);
@@ -982,9 +988,9 @@ __global__ __launch_bounds__(I4_THREADS) void w4a4_int4_tail_kernel(
 #pragma unroll
         for (int tn = 0; tn < PTN; ++tn)
 #pragma unroll
-            for (int tm = 0; tm < I4_TM; ++tm)
+            for (int tm = 0; tm < PTM; ++tm)
 #pragma unroll
-                for (int i = 0; i < 16; ++i) red[wave - 1][16 * (I4_TM * tn + tm) + i][lane] = acc[tn][tm][i];
+                for (int i = 0; i < 16; ++i) red[wave - 1][16 * (PTM * tn + tm) + i][lane] = acc[tn][tm][i];
     }
     __syncthreads();
     if (wave > 0) return;
@@ -993,23 +999,24 @@ __global__ __launch_bounds__(I4_THREADS) void w4a4_int4_tail_kernel(
 #pragma unroll
         for (int tn = 0; tn < PTN; ++tn)
 #pragma unroll
-            for (int tm = 0; tm < I4_TM; ++tm)
+            for (int tm = 0; tm < PTM; ++tm)
 #pragma unroll
-                for (int i = 0; i < 16; ++i) acc[tn][tm][i] += red[w][16 * (I4_TM * tn + tm) + i][lane];
+                for (int i = 0; i < 16; ++i) acc[tn][tm][i] += red[w][16 * (PTM * tn + tm) + i][lane];
 
-    // the full-size kernel's epilogue for a 64 x PW tile (staged in the first
-    // partial-sum area, which wave 0 has finished reading)
-    bf16x8 hhi[I4_TM][2], hlo[I4_TM][2];
+    // the full-size kernel's epilogue arithmetic for the piece (staged in the
+    // first partial-sum area, which wave 0 has finished reading)
+    bf16x8 hhi[PTM][2], hlo[PTM][2];
 #pragma unroll
-    for (int tm = 0; tm < I4_TM; ++tm)
+    for (int tm = 0; tm < PTM; ++tm)
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
             float hv[8];
             load_h8(h, mb + tm * 32 + l32, M, 16 * s2 + 8 * hk, hv);
             split_h(hv, hhi[tm][s2], hlo[tm][s2]);
         }
-    uint8_t *tile = reinterpret_cast<uint8_t *>(&red[0][0][0]);
-    static_assert(OUT_TILE_BYTES <= sizeof(red), "output staging fits");
+    // y = acc + low-rank + bias (+ GELU), rounded to bf16 as the plain
+    // epilogue stores it
+    uint2 yb[PTN][PTM][4];
 #pragma unroll
     for (int tn = 0; tn < PTN; ++tn) {
         const int nrow = nb + tn * 32 + l32;
@@ -1024,7 +1031,7 @@ __global__ __launch_bounds__(I4_THREADS) void w4a4_int4_tail_kernel(
 #pragma unroll
         for (int j = 0; j < 4; ++j) bv[j] = bias4(bias, nb + tn * 32 + 8 * j + 4 * hk, N);
 #pragma unroll
-        for (int tm = 0; tm < I4_TM; ++tm) {
+        for (int tm = 0; tm < PTM; ++tm) {
             f32x16 lr = {};
 #pragma unroll
             for (int s2 = 0; s2 < 2; ++s2) {
@@ -1033,25 +1040,120 @@ __global__ __launch_bounds__(I4_THREADS) void w4a4_int4_tail_kernel(
             }
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                float a4[4] = {acc[tn][tm][4 * j], acc[tn][tm][4 * j + 1], acc[tn][tm][4 * j + 2],
-                               acc[tn][tm][4 * j + 3]};
-                float l4[4] = {lr[4 * j], lr[4 * j + 1], lr[4 * j + 2], lr[4 * j + 3]};
-                stage4(tile, tm * 32 + l32, tn * 32 + 8 * j + 4 * hk, finish4(a4, l4, bv[j], gelu));
+                const float a4[4] = {acc[tn][tm][4 * j], acc[tn][tm][4 * j + 1], acc[tn][tm][4 * j + 2],
+                                     acc[tn][tm][4 * j + 3]};
+                const float l4[4] = {lr[4 * j], lr[4 * j + 1], lr[4 * j + 2], lr[4 * j + 3]};
+                yb[tn][tm][j] = finish4(a4, l4, bv[j], EPI == EPI_STORE ? gelu : 0);
             }
         }
     }
+    uint8_t *tile = reinterpret_cast<uint8_t *>(&red[0][0][0]);
+    constexpr int STRIDE = EPI == EPI_STORE ? OUT_STRIDE : QKP_ROW;
+    static_assert(PH * STRIDE <= sizeof(red) && 2 * PW <= STRIDE, "the piece's staging fits");
+    if constexpr (EPI == EPI_QKNORM) {
+        // one head, all of it in this wave: lane (l32, hk) holds 64 of token
+        // mb + l32's channels, the other 64 are in lane l32 + 32 - 64 hk
+        const int head = nb / 128;
+        if (head < 2 * qk.heads) {       // a Q or a K head: RMS-norm, then rotary
+            const uint16_t *__restrict__ wn = head < qk.heads ? qk.norm_q : qk.norm_k;
+            const int m = mb + l32 < M ? mb + l32 : M - 1;       // rows past M are never stored
+            // the sum of squares in the full-size kernel's order: each
+            // 64-channel half (a wave tile there) by fma over its channels
+            // and the two lanes, then the two halves added
+            float ss[2] = {0.0f, 0.0f};
+#pragma unroll
+            for (int tn = 0; tn < PTN; ++tn)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const uint2 y2 = yb[tn][0][j];
+                    const float v0 = bf16_to_f32(y2.x & 0xFFFFu), v1 = bf16_to_f32(y2.x >> 16);
+                    const float v2 = bf16_to_f32(y2.y & 0xFFFFu), v3 = bf16_to_f32(y2.y >> 16);
+                    float &a = ss[tn >> 1];
+                    a = __builtin_fmaf(v0, v0, a);
+                    a = __builtin_fmaf(v1, v1, a);
+                    a = __builtin_fmaf(v2, v2, a);
+                    a = __builtin_fmaf(v3, v3, a);
+                }
+            ss[0] += __shfl_xor(ss[0], 32);
+            ss[1] += __shfl_xor(ss[1], 32);
+            const float rs = __builtin_amdgcn_rsqf(__builtin_fmaf(ss[0] + ss[1], 1.0f / 128.0f, qk.eps));
+#pragma unroll
+            for (int tn = 0; tn < PTN; ++tn)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int d = tn * 32 + 8 * j + 4 * hk;     // channel in the head, % 4 == 0
+                    const uint2 y2 = yb[tn][0][j];
+                    const uint2 w2 = *reinterpret_cast<const uint2 *>(wn + d);
+                    const float2 c = *reinterpret_cast<const float2 *>(qk.rope_cos + (size_t)m * 64 + d / 2);
+                    const float2 sn = *reinterpret_cast<const float2 *>(qk.rope_sin + (size_t)m * 64 + d / 2);
+                    const float u0 = bf16_to_f32(y2.x & 0xFFFFu) * rs * bf16_to_f32(w2.x & 0xFFFFu);
+                    const float u1 = bf16_to_f32(y2.x >> 16) * rs * bf16_to_f32(w2.x >> 16);
+                    const float u2 = bf16_to_f32(y2.y & 0xFFFFu) * rs * bf16_to_f32(w2.y & 0xFFFFu);
+                    const float u3 = bf16_to_f32(y2.y >> 16) * rs * bf16_to_f32(w2.y >> 16);
+                    const float o0 = u0 * c.x - u1 * sn.x, o1 = u1 * c.x + u0 * sn.x;
+                    const float o2 = u2 * c.y - u3 * sn.y, o3 = u3 * c.y + u2 * sn.y;
+                    yb[tn][0][j] = make_uint2(pack_bf16x2(o0, o1), pack_bf16x2(o2, o3));
+                }
+        }
+    }
+#pragma unroll
+    for (int tn = 0; tn < PTN; ++tn)
+#pragma unroll
+        for (int tm = 0; tm < PTM; ++tm)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                *reinterpret_cast<uint2 *>(tile + (tm * 32 + l32) * STRIDE + (tn * 32 + 8 * j + 4 * hk) * 2) =
+                    yb[tn][tm][j];
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    // 64 rows x PW channels: 64 rows of 4 PTN segments of 16 bytes
-    constexpr int SEGS = 4 * PTN;
+    // PH rows x PW channels: rows of PW / 8 segments of 16 bytes
+    constexpr int SEGS = PW / 8;
 #pragma unroll
-    for (int it = 0; it < SEGS; ++it) {
+    for (int it = 0; it < PH * SEGS / 64; ++it) {
         const int idx = lane + 64 * it, r = idx / SEGS, seg = idx % SEGS;
-        const uint4 v = *reinterpret_cast<const uint4 *>(tile + r * OUT_STRIDE + seg * 16);
+        const uint4 v = *reinterpret_cast<const uint4 *>(tile + r * STRIDE + seg * 16);
         const int m = mb + r, n = nb + seg * 8;
         if (m < M && n < N) store_nt(Y + (size_t)m * N + n, v);
     }
+}
+
+// Launches the pieces of the tiles left after `full` tiles, when they fit in
+// one round: plain pieces of 64 x 32 (16 per tile) or 64 x 64 (8), head
+// pieces of 32 x 128 (8).
+template <int EPI>
+hipError_t launch_int4_tail(const uint8_t *xq, const float *xscale, const float *h, const uint8_t *wq,
+                            const float *wscale, const uint16_t *up, const uint16_t *bias, int M, int N, int K,
+                            int gelu, uint16_t *Y, int full, int rest, int ncu, const QKNormArgs &qk,
+                            hipStream_t stream)
+{
+    if constexpr (EPI == EPI_QKNORM) {
+        hipLaunchKernelGGL((w4a4_int4_tail_kernel<4, 1, EPI_QKNORM>), dim3((unsigned)(rest * I4Tail<4, 1>::kPieces)),
+                           dim3(I4_THREADS), 0, stream, xq, xscale, h, wq, wscale, up, bias, M, N, K, 0, Y, full, qk);
+    } else if (rest * I4Tail<1, 2>::kPieces <= ncu) {
+        hipLaunchKernelGGL((w4a4_int4_tail_kernel<1, 2, EPI_STORE>), dim3((unsigned)(rest * I4Tail<1, 2>::kPieces)),
+                           dim3(I4_THREADS), 0, stream, xq, xscale, h, wq, wscale, up, bias, M, N, K, gelu, Y, full,
+                           qk);
+    } else {
+        hipLaunchKernelGGL((w4a4_int4_tail_kernel<2, 2, EPI_STORE>), dim3((unsigned)(rest * I4Tail<2, 2>::kPieces)),
+                           dim3(I4_THREADS), 0, stream, xq, xscale, h, wq, wscale, up, bias, M, N, K, gelu, Y, full,
+                           qk);
+    }
+    return hipGetLastError();
+}
+
+// Whole rounds of one block per CU, then the leftover tiles: the number of
+// tiles the full-size kernel takes (all of them when the leftover's pieces
+// would not fit in one round, which `rest` then reports as 0).
+int int4_main_tiles(int tiles, int pieces_per_tile, int ncu, int &rest)
+{
+    const int full = (tiles / ncu) * ncu;
+    rest = tiles - full;
+    if (full == 0 || rest == 0 || rest * pieces_per_tile > ncu) {
+        rest = 0;
+        return tiles;
+    }
+    return full;
 }
 
 // Fixed-order sum of the per-tile partial h2: h2[m][j] = sum_t hpart[t][m][j],
@@ -1871,24 +1973,16 @@ hipError_t launch_w4a4_linear(const uint8_t *xq, const void *xscale, const float
         // few enough that their pieces fill at most one round, those tiles in
         // pieces (w4a4_int4_tail_kernel)
         const int ncu = device_cu_count();
-        const int full = (tiles / ncu) * ncu, rest = tiles - full;
-        const bool pieces = full > 0 && rest > 0 && rest * I4Tail<2>::kPieces <= ncu;
-        const int main_tiles = pieces ? full : tiles;
+        int rest;
+        const int main_tiles = int4_main_tiles(tiles, I4Tail<2, 2>::kPieces, ncu, rest);
         hipLaunchKernelGGL(w4a4_int4_kernel<EPI_STORE>, dim3((unsigned)main_tiles), dim3(I4_THREADS), 0, stream, xq,
                            (const float *)xscale, h, wq, (const float *)wscale, up, bias, M, N, K, gelu, Y,
                            RequantArgs{}, QKNormArgs{});
-        if (pieces) {
+        if (rest > 0) {
             hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
-            // the narrower pieces when they still fit in one round
-            if (rest * I4Tail<1>::kPieces <= ncu)
-                hipLaunchKernelGGL(w4a4_int4_tail_kernel<1>, dim3((unsigned)(rest * I4Tail<1>::kPieces)),
-                                   dim3(I4_THREADS), 0, stream, xq, (const float *)xscale, h, wq,
-                                   (const float *)wscale, up, bias, M, N, K, gelu, Y, full);
-            else
-                hipLaunchKernelGGL(w4a4_int4_tail_kernel<2>, dim3((unsigned)(rest * I4Tail<2>::kPieces)),
-                                   dim3(I4_THREADS), 0, stream, xq, (const float *)xscale, h, wq,
-                                   (const float *)wscale, up, bias, M, N, K, gelu, Y, full);
+            return launch_int4_tail<EPI_STORE>(xq, (const float *)xscale, h, wq, (const float *)wscale, up, bias, M,
+                                               N, K, gelu, Y, main_tiles, rest, ncu, QKNormArgs{}, stream);
         }
     } else {
         // the LDS-DMA kernel takes whole 256-channel steps and 32-bit offsets
@@ -2030,9 +2124,16 @@ hipError_t launch_w4a4_linear_qknorm(const uint8_t *xq, const void *xscale, cons
     const int tiles = ((N + I4_BN - 1) / I4_BN) * ((M + I4_BM - 1) / I4_BM);
     static_assert(I4_WN * 2 == 128 && I4_BN % 128 == 0, "a head is the tile of two neighbouring waves");
     const QKNormArgs qk{norm_q, norm_k, rope_cos, rope_sin, N / 384, eps};
-    hipLaunchKernelGGL(w4a4_int4_kernel<EPI_QKNORM>, dim3((unsigned)tiles), dim3(I4_THREADS), 0, stream, xq,
+    // whole rounds, then the leftover tiles in head pieces (as the plain linear)
+    const int ncu = device_cu_count();
+    int rest;
+    const int main_tiles = int4_main_tiles(tiles, I4Tail<4, 1>::kPieces, ncu, rest);
+    hipLaunchKernelGGL(w4a4_int4_kernel<EPI_QKNORM>, dim3((unsigned)main_tiles), dim3(I4_THREADS), 0, stream, xq,
                        (const float *)xscale, h, wq, (const float *)wscale, up, bias, M, N, K, 0, Y, RequantArgs{}, qk);
-    return hipGetLastError();
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || rest == 0) return e;
+    return launch_int4_tail<EPI_QKNORM>(xq, (const float *)xscale, h, wq, (const float *)wscale, up, bias, M, N, K,
+                                        0, Y, main_tiles, rest, ncu, qk, stream);
 }
 
 }  // namespace svdq

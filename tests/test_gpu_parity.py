@@ -415,14 +415,16 @@ def test_linear_many_tiles_ragged(prec, K):
     _y_check(Y, y_ref, "many tiles")
 
 
-@pytest.mark.parametrize("M,K,N", [(2100, 192, 4000), (2100, 704, 4000), (2100, 3072, 4000), (1500, 704, 5880)])
+@pytest.mark.parametrize("M,K,N", [(2100, 64, 4000), (2100, 192, 4000), (2100, 704, 4000), (2100, 3072, 4000),
+                                   (1500, 704, 5880)])
 def test_linear_int4_tail_pieces(M, K, N):
     """INT4 shapes whose tiles fill whole rounds of one block per CU plus a
     few: 2100 x 4000 has 17 x 16 = 272 tiles on 256 CUs, 16 left over, which
     run as 16 pieces of 64 x 32 each; 1500 x 5880 has 12 x 23 = 276, 20 left
     over, as 8 pieces of 64 x 64 each.  K is split over the block's waves
-    (three groups, so some waves have none; eleven, uneven; 48).  Every
-    output against the oracle, and a second call gives the same bits."""
+    (one group: only the last wave has any; three, so some waves have none;
+    eleven, uneven; 48).  Every output against the oracle, and a second call
+    gives the same bits."""
     if torch.cuda.get_device_properties(0).multi_processor_count != 256:
         pytest.skip("the split into whole rounds below assumes 256 CUs")
     prec = svdq.INT4

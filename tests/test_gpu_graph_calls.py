@@ -104,6 +104,26 @@ def test_graph_qkv_norm_rope(prec):
     _replays_match(lambda: svdq.w4a4_linear_qkv_norm_rope(*a, *w, nq, nk, 1e-6, c, s, prec, Y=Y), [Y])
 
 
+def test_graph_int4_tail_pieces():
+    """The INT4 linear and its Q/K-norm form at shapes whose leftover tiles
+    run in pieces (two launches per call): both captured and replayed."""
+    if torch.cuda.get_device_properties(0).multi_processor_count != 256:
+        pytest.skip("the split into whole rounds assumes 256 CUs")
+    _say("graph INT4 tail pieces")
+    prec = svdq.INT4
+    M, K, N = 2100, 192, 4000           # 272 tiles: 16 left over
+    _, _, a, w = _acts(prec, M, K, N)
+    Y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    _replays_match(lambda: svdq.w4a4_linear(*a, *w, prec, svdq.EPI_GELU_TANH, Y=Y), [Y])
+    M, K, N = 2800, 256, 3072           # 264 tiles: 8 left over, 8 heads each of Q, K, V
+    _, _, a, w = _acts(prec, M, K, N)
+    nq, nk = _t(synth.gen_qk_norm(2, 10)), _t(synth.gen_qk_norm(2, 11))
+    c, s = synth.gen_rope(M)
+    c, s = _t(c), _t(s)
+    Y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    _replays_match(lambda: svdq.w4a4_linear_qkv_norm_rope(*a, *w, nq, nk, 1e-6, c, s, prec, Y=Y), [Y])
+
+
 def test_graph_awq():
     _say("graph awq")
     M, K, N = 3, 1024, 264

@@ -278,6 +278,25 @@ struct QKNormArgs {
     float eps;
 };
 
+// Q/K RMS-norm + rotary on 8 consecutive channels d0 .. d0 + 7 (d0 % 8 == 0)
+// of one token's head, given as 8 bf16 in `v`: u = y rs w (the token's 1 / rms,
+// the head's norm weights `wv` of those channels), then the 4 pairs rotated by
+// the token's angles (`c`, `sn`: cos and sin of pairs d0 / 2 .. d0 / 2 + 3),
+// rounded to bf16.
+__device__ __forceinline__ uint4 qk_norm_rope8(uint4 v, float rs, uint4 wv, float4 c, float4 sn)
+{
+    const uint32_t wd[4] = {wv.x, wv.y, wv.z, wv.w};
+    const float cc[4] = {c.x, c.y, c.z, c.w}, ssn[4] = {sn.x, sn.y, sn.z, sn.w};
+    uint32_t yd[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {          // pair q: channels d0 + 2 q, + 1
+        const float u0 = bf16_to_f32(yd[q] & 0xFFFFu) * rs * bf16_to_f32(wd[q] & 0xFFFFu);
+        const float u1 = bf16_to_f32(yd[q] >> 16) * rs * bf16_to_f32(wd[q] >> 16);
+        yd[q] = pack_bf16x2(u0 * cc[q] - u1 * ssn[q], u1 * cc[q] + u0 * ssn[q]);
+    }
+    return make_uint4(yd[0], yd[1], yd[2], yd[3]);
+}
+
 // Epilogue of the requantizing INT4 kernel for one wave tile (64 channels n
 // of one 64-group x 64 tokens m).  Lane (l32, hk) holds, per 32-token tile
 // tm, token m = mb + 32 tm + l32 and the channels nb + 32 tn + 8 j + 4 hk +
@@ -520,30 +539,6 @@ __device__ __forceinline__ void qknorm_epilogue(const f32x16 (&acc)[I4_TN][I4_TM
     const int head = nb / 128;                   // the same for this wave and its neighbour
     const bool norm = head < 2 * qk.heads;       // a Q or a K head
     float *red = reinterpret_cast<float *>(smem + 8 * OUT_TILE_BYTES);   // [8 waves][64 tokens]
-    // the norm weights and the rotation tables do not depend on the sums:
-    // their loads are in flight while the sums are formed and exchanged
-    const uint16_t *__restrict__ w = head < qk.heads ? qk.norm_q : qk.norm_k;
-    uint2 wv[I4_TN][4];
-    float2 cv[I4_TM][I4_TN][4], sv[I4_TM][I4_TN][4];
-    if (norm) {
-#pragma unroll
-        for (int tn = 0; tn < I4_TN; ++tn)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                wv[tn][j] = *reinterpret_cast<const uint2 *>(w + ((nb + tn * 32 + 8 * j + 4 * hk) & 127));
-#pragma unroll
-        for (int tm = 0; tm < I4_TM; ++tm) {
-            const int m = mb + tm * 32 + l32 < M ? mb + tm * 32 + l32 : M - 1;   // rows past M are never stored
-#pragma unroll
-            for (int tn = 0; tn < I4_TN; ++tn)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int d = (nb + tn * 32 + 8 * j + 4 * hk) & 127;        // channel in the head, % 4 == 0
-                    cv[tm][tn][j] = *reinterpret_cast<const float2 *>(qk.rope_cos + (size_t)m * 64 + d / 2);
-                    sv[tm][tn][j] = *reinterpret_cast<const float2 *>(qk.rope_sin + (size_t)m * 64 + d / 2);
-                }
-        }
-    }
     if (norm) {
 #pragma unroll
         for (int tm = 0; tm < I4_TM; ++tm) {
@@ -563,39 +558,48 @@ __device__ __forceinline__ void qknorm_epilogue(const f32x16 (&acc)[I4_TN][I4_TM
             if (hk == 0) red[wave * 64 + tm * 32 + l32] = ss;
         }
     }
-    __syncthreads();
+    // the bf16 outputs staged as they are, the token's 1 / rms in the spare
+    // bytes of its row
     uint8_t *tile = smem + wave * OUT_TILE_BYTES;
-    if (norm) {
+#pragma unroll
+    for (int tn = 0; tn < I4_TN; ++tn)
+#pragma unroll
+        for (int tm = 0; tm < I4_TM; ++tm)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) stage4(tile, tm * 32 + l32, tn * 32 + 8 * j + 4 * hk, yb[tn][tm][j]);
+    __syncthreads();
+    if (norm && hk == 0) {
 #pragma unroll
         for (int tm = 0; tm < I4_TM; ++tm) {
             const int ml = tm * 32 + l32;
             const float tot = red[wave * 64 + ml] + red[(wave ^ 1) * 64 + ml];
-            const float rs = __builtin_amdgcn_rsqf(__builtin_fmaf(tot, 1.0f / 128.0f, qk.eps));
-#pragma unroll
-            for (int tn = 0; tn < I4_TN; ++tn)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const uint2 y2 = yb[tn][tm][j], w2 = wv[tn][j];
-                    const float2 c = cv[tm][tn][j], sn = sv[tm][tn][j];
-                    const float u0 = bf16_to_f32(y2.x & 0xFFFFu) * rs * bf16_to_f32(w2.x & 0xFFFFu);
-                    const float u1 = bf16_to_f32(y2.x >> 16) * rs * bf16_to_f32(w2.x >> 16);
-                    const float u2 = bf16_to_f32(y2.y & 0xFFFFu) * rs * bf16_to_f32(w2.y & 0xFFFFu);
-                    const float u3 = bf16_to_f32(y2.y >> 16) * rs * bf16_to_f32(w2.y >> 16);
-                    const float o0 = u0 * c.x - u1 * sn.x, o1 = u1 * c.x + u0 * sn.x;
-                    const float o2 = u2 * c.y - u3 * sn.y, o3 = u3 * c.y + u2 * sn.y;
-                    stage4(tile, ml, tn * 32 + 8 * j + 4 * hk, make_uint2(pack_bf16x2(o0, o1), pack_bf16x2(o2, o3)));
-                }
+            *reinterpret_cast<float *>(tile + ml * OUT_STRIDE + 128) =
+                __builtin_amdgcn_rsqf(__builtin_fmaf(tot, 1.0f / 128.0f, qk.eps));
         }
-    } else {
-#pragma unroll
-        for (int tn = 0; tn < I4_TN; ++tn)
-#pragma unroll
-            for (int tm = 0; tm < I4_TM; ++tm)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) stage4(tile, tm * 32 + l32, tn * 32 + 8 * j + 4 * hk, yb[tn][tm][j]);
     }
-    __syncthreads();
-    flush_tile(tile, Y, mb, nb, M, N, lane);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // 8 lanes per token row, 8 channels (4 rotation pairs) each: Q and K heads
+    // are normalized and rotated on the way out, with the norm weights read
+    // once and the rotation tables as whole 128-byte runs per token
+    const int seg = lane & 7;
+    const int d0 = (nb & 127) + 8 * seg;         // the lane's first channel in the head
+    uint4 wv = {0u, 0u, 0u, 0u};
+    if (norm) wv = *reinterpret_cast<const uint4 *>((head < qk.heads ? qk.norm_q : qk.norm_k) + d0);
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+        const int r = (lane >> 3) + 8 * it;
+        uint4 v = *reinterpret_cast<const uint4 *>(tile + r * OUT_STRIDE + seg * 16);
+        const int m = mb + r, n = nb + seg * 8;
+        if (norm) {
+            const float rs = *reinterpret_cast<const float *>(tile + r * OUT_STRIDE + 128);
+            const int mc = m < M ? m : M - 1;                     // rows past M are never stored
+            v = qk_norm_rope8(v, rs, wv, *reinterpret_cast<const float4 *>(qk.rope_cos + (size_t)mc * 64 + d0 / 2),
+                              *reinterpret_cast<const float4 *>(qk.rope_sin + (size_t)mc * 64 + d0 / 2));
+        }
+        if (m < M && n < N) store_nt(Y + (size_t)m * N + n, v);
+    }
 }
 
 // Scale panels hold 8 groups of every W and X row of the block tile, a row of
@@ -1050,16 +1054,16 @@ __global__ __launch_bounds__(I4_THREADS) void w4a4_int4_tail_kernel(
     uint8_t *tile = reinterpret_cast<uint8_t *>(&red[0][0][0]);
     constexpr int STRIDE = EPI == EPI_STORE ? OUT_STRIDE : QKP_ROW;
     static_assert(PH * STRIDE <= sizeof(red) && 2 * PW <= STRIDE, "the piece's staging fits");
+    const int head = nb / 128;
+    const bool norm = EPI == EPI_QKNORM && head < 2 * qk.heads;    // a Q or a K head
     if constexpr (EPI == EPI_QKNORM) {
         // one head, all of it in this wave: lane (l32, hk) holds 64 of token
-        // mb + l32's channels, the other 64 are in lane l32 + 32 - 64 hk
-        const int head = nb / 128;
-        if (head < 2 * qk.heads) {       // a Q or a K head: RMS-norm, then rotary
-            const uint16_t *__restrict__ wn = head < qk.heads ? qk.norm_q : qk.norm_k;
-            const int m = mb + l32 < M ? mb + l32 : M - 1;       // rows past M are never stored
-            // the sum of squares in the full-size kernel's order: each
-            // 64-channel half (a wave tile there) by fma over its channels
-            // and the two lanes, then the two halves added
+        // mb + l32's channels, the other 64 are in lane l32 + 32 - 64 hk.  The
+        // sum of squares in the full-size kernel's order: each 64-channel
+        // half (a wave tile there) by fma over its channels and the two
+        // lanes, then the two halves added; the token's 1 / rms goes to the
+        // spare bytes of its staged row.
+        if (norm) {
             float ss[2] = {0.0f, 0.0f};
 #pragma unroll
             for (int tn = 0; tn < PTN; ++tn)
@@ -1076,24 +1080,9 @@ __global__ __launch_bounds__(I4_THREADS) void w4a4_int4_tail_kernel(
                 }
             ss[0] += __shfl_xor(ss[0], 32);
             ss[1] += __shfl_xor(ss[1], 32);
-            const float rs = __builtin_amdgcn_rsqf(__builtin_fmaf(ss[0] + ss[1], 1.0f / 128.0f, qk.eps));
-#pragma unroll
-            for (int tn = 0; tn < PTN; ++tn)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int d = tn * 32 + 8 * j + 4 * hk;     // channel in the head, % 4 == 0
-                    const uint2 y2 = yb[tn][0][j];
-                    const uint2 w2 = *reinterpret_cast<const uint2 *>(wn + d);
-                    const float2 c = *reinterpret_cast<const float2 *>(qk.rope_cos + (size_t)m * 64 + d / 2);
-                    const float2 sn = *reinterpret_cast<const float2 *>(qk.rope_sin + (size_t)m * 64 + d / 2);
-                    const float u0 = bf16_to_f32(y2.x & 0xFFFFu) * rs * bf16_to_f32(w2.x & 0xFFFFu);
-                    const float u1 = bf16_to_f32(y2.x >> 16) * rs * bf16_to_f32(w2.x >> 16);
-                    const float u2 = bf16_to_f32(y2.y & 0xFFFFu) * rs * bf16_to_f32(w2.y & 0xFFFFu);
-                    const float u3 = bf16_to_f32(y2.y >> 16) * rs * bf16_to_f32(w2.y >> 16);
-                    const float o0 = u0 * c.x - u1 * sn.x, o1 = u1 * c.x + u0 * sn.x;
-                    const float o2 = u2 * c.y - u3 * sn.y, o3 = u3 * c.y + u2 * sn.y;
-                    yb[tn][0][j] = make_uint2(pack_bf16x2(o0, o1), pack_bf16x2(o2, o3));
-                }
+            if (hk == 0)
+                *reinterpret_cast<float *>(tile + l32 * STRIDE + 256) =
+                    __builtin_amdgcn_rsqf(__builtin_fmaf(ss[0] + ss[1], 1.0f / 128.0f, qk.eps));
         }
     }
 #pragma unroll
@@ -1107,13 +1096,23 @@ __global__ __launch_bounds__(I4_THREADS) void w4a4_int4_tail_kernel(
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    // PH rows x PW channels: rows of PW / 8 segments of 16 bytes
+    // PH rows x PW channels: rows of PW / 8 segments of 16 bytes; head pieces
+    // are normalized and rotated on the way out (16 lanes per token, the
+    // rotation tables read as whole rows)
     constexpr int SEGS = PW / 8;
+    uint4 wv = {0u, 0u, 0u, 0u};
+    if (norm) wv = *reinterpret_cast<const uint4 *>((head < qk.heads ? qk.norm_q : qk.norm_k) + 8 * (lane % SEGS));
 #pragma unroll
     for (int it = 0; it < PH * SEGS / 64; ++it) {
         const int idx = lane + 64 * it, r = idx / SEGS, seg = idx % SEGS;
-        const uint4 v = *reinterpret_cast<const uint4 *>(tile + r * STRIDE + seg * 16);
+        uint4 v = *reinterpret_cast<const uint4 *>(tile + r * STRIDE + seg * 16);
         const int m = mb + r, n = nb + seg * 8;
+        if (norm) {
+            const float rs = *reinterpret_cast<const float *>(tile + r * STRIDE + 256);
+            const int mc = m < M ? m : M - 1;                     // rows past M are never stored
+            v = qk_norm_rope8(v, rs, wv, *reinterpret_cast<const float4 *>(qk.rope_cos + (size_t)mc * 64 + 4 * seg),
+                              *reinterpret_cast<const float4 *>(qk.rope_sin + (size_t)mc * 64 + 4 * seg));
+        }
         if (m < M && n < N) store_nt(Y + (size_t)m * N + n, v);
     }
 }
@@ -1592,11 +1591,12 @@ __device__ __forceinline__ void requant_epilogue_mx(const f32x16 (&acc)[MX_TN][M
 // since nb is a multiple of 128) x 64 tokens.  Lane (l32, hk) holds, per
 // token mb + 32 tm + l32, the channels 32 tn + 8 j + 4 hk + (0..3) of the head
 // (64 of its 128); its partner lane (l32, hk ^ 1) holds the other 64, so the
-// head's sum of squares takes one cross-half exchange, and a rotation pair
-// (2p, 2p + 1) sits in one lane.  The bf16 outputs are parked in the wave's
-// own LDS area (64 tokens x 128 channels, rows of 256 + 8 bytes) while the
-// sums are formed, normalized and rotated in place by the lanes that wrote
-// them, and stored as whole 256-byte rows.  `area` holds
+// head's sum of squares takes one cross-half exchange.  The bf16 outputs are
+// parked in the wave's own LDS area (64 tokens x 128 channels, rows of 256 +
+// 8 bytes, the spare 8 holding the token's 1 / rms) while the sums are
+// formed; then 16 lanes per token read the row back, 8 channels (4 rotation
+// pairs) each, normalize and rotate them with the token's angles read as
+// whole rows, and store the row as 256 contiguous bytes.  `area` holds
 // QK_AREA_BYTES bytes per wave, used by no other wave.
 constexpr int QK_ROW = 264;
 constexpr int QK_AREA_BYTES = 64 * QK_ROW;
@@ -1659,50 +1659,37 @@ __device__ __forceinline__ void qknorm_wave_epilogue_mx(const f32x16 (&acc)[MX_T
             }
         }
     }
-    // pass 2 (Q and K heads): normalize and rotate in place; each lane rereads
-    // only what it wrote
+    // the token's 1 / rms (Q and K heads) in the 8 spare bytes of its staged row
     if (norm) {
-        const uint16_t *__restrict__ w = (head < qk.heads ? qk.norm_q : qk.norm_k) + 4 * hk;
 #pragma unroll
         for (int tm = 0; tm < MX_TM; ++tm) {
             const float tot = ss[tm] + __shfl_xor(ss[tm], 32);
             const float rs = __builtin_amdgcn_rsqf(__builtin_fmaf(tot, 1.0f / 128.0f, qk.eps));
-            const int ml = tm * 32 + l32;
-            const int m = mb + ml < M ? mb + ml : M - 1;          // rows past M are never stored
-            // the lane's pairs start at channel 4 hk: pair 2 hk of the token's angles
-            const float *__restrict__ rc = qk.rope_cos + (size_t)m * 64 + 2 * hk;
-            const float *__restrict__ rsn = qk.rope_sin + (size_t)m * 64 + 2 * hk;
-#pragma unroll
-            for (int tn = 0; tn < MX_TN; ++tn)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int dq = 16 * tn + 4 * j;                  // (channel - 4 hk) / 2 of the lane's first pair
-                    uint2 *slot = reinterpret_cast<uint2 *>(area + ml * QK_ROW + (tn * 32 + 8 * j + 4 * hk) * 2);
-                    const uint2 y2 = *slot;
-                    const float2 c = *reinterpret_cast<const float2 *>(rc + dq);
-                    const float2 sn = *reinterpret_cast<const float2 *>(rsn + dq);
-                    const uint2 w2 = *reinterpret_cast<const uint2 *>(w + 2 * dq);
-                    const float u0 = bf16_to_f32(y2.x & 0xFFFFu) * rs * bf16_to_f32(w2.x & 0xFFFFu);
-                    const float u1 = bf16_to_f32(y2.x >> 16) * rs * bf16_to_f32(w2.x >> 16);
-                    const float u2 = bf16_to_f32(y2.y & 0xFFFFu) * rs * bf16_to_f32(w2.y & 0xFFFFu);
-                    const float u3 = bf16_to_f32(y2.y >> 16) * rs * bf16_to_f32(w2.y >> 16);
-                    const float o0 = u0 * c.x - u1 * sn.x, o1 = u1 * c.x + u0 * sn.x;
-                    const float o2 = u2 * c.y - u3 * sn.y, o3 = u3 * c.y + u2 * sn.y;
-                    *slot = make_uint2(pack_bf16x2(o0, o1), pack_bf16x2(o2, o3));
-                }
+            if (hk == 0) *reinterpret_cast<float *>(area + (tm * 32 + l32) * QK_ROW + 256) = rs;
         }
     }
     // the area is read back by other lanes of this wave: whole 256-byte rows,
-    // 16 lanes per row
+    // 16 lanes per row, each with 8 channels (4 rotation pairs) of its token.
+    // Q and K heads are normalized and rotated on the way out, so that the
+    // norm weights are read once and the rotation tables as whole rows
+    // (16 lanes x 16 bytes per token).
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     const int seg = lane & 15;
+    uint4 wv = {0u, 0u, 0u, 0u};
+    if (norm) wv = *reinterpret_cast<const uint4 *>((head < qk.heads ? qk.norm_q : qk.norm_k) + 8 * seg);
 #pragma unroll
     for (int it = 0; it < 16; ++it) {
         const int r = (lane >> 4) + 4 * it;
-        const uint4 v = *reinterpret_cast<const uint4 *>(area + r * QK_ROW + seg * 16);
+        uint4 v = *reinterpret_cast<const uint4 *>(area + r * QK_ROW + seg * 16);
         const int m = mb + r, n = nb + seg * 8;
+        if (norm) {
+            const float rs = *reinterpret_cast<const float *>(area + r * QK_ROW + 256);
+            const int mc = m < M ? m : M - 1;                     // rows past M are never stored
+            v = qk_norm_rope8(v, rs, wv, *reinterpret_cast<const float4 *>(qk.rope_cos + (size_t)mc * 64 + 4 * seg),
+                              *reinterpret_cast<const float4 *>(qk.rope_sin + (size_t)mc * 64 + 4 * seg));
+        }
         if (m < M && n < N) store_nt(Y + (size_t)m * N + n, v);
     }
 }

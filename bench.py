@@ -40,10 +40,10 @@ NO_CLOCK = False
 # only reported while the kernel source still hashes to the value it was
 # measured on; otherwise traffic is null.
 TRAFFIC = {
-    # FETCH_SIZE 73632 KiB / 0.50002 + WRITE_SIZE 110601 KiB / 1.00000 (per dispatch)
-    "fc1": {"source": "w4a4_gemm.hip", "source_sha": "3bc38fac52bad3a1", "bytes": 264047657},
-    # FETCH_SIZE 70954 KiB / 0.50002 + WRITE_SIZE 111105 KiB / 1.00000
-    "mx_fc1": {"source": "w4a4_gemm.hip", "source_sha": "3bc38fac52bad3a1", "bytes": 259078426},
+    # FETCH_SIZE 73645 KiB / 0.50002 + WRITE_SIZE 110603 KiB / 1.00000 (per dispatch)
+    "fc1": {"source": "w4a4_gemm.hip", "source_sha": "996de43298c60e1d", "bytes": 264075432},
+    # FETCH_SIZE 70942 KiB / 0.50002 + WRITE_SIZE 111106 KiB / 1.00000
+    "mx_fc1": {"source": "w4a4_gemm.hip", "source_sha": "996de43298c60e1d", "bytes": 259055643},
     # FETCH_SIZE 15680 KiB / 0.50002 + WRITE_SIZE 36 KiB / 1.00000
     "awq_mod": {"source": "awq_gemv.hip", "source_sha": "fda4dd7b5f7b1013", "bytes": 32148220},
     # FETCH_SIZE 197078 KiB / 0.50002 + WRITE_SIZE 110594 KiB / 1.00000

@@ -35,7 +35,10 @@
 //
 // Low-rank epilogue: h (fp32) is split into bf16 hi = bf16(h) and lo =
 // bf16(h - hi); the bf16 matrix instruction with `up` as the other operand
-// gives h . up to ~16 bits, well inside the output tolerance.
+// gives h . up to ~16 bits, well inside the output tolerance.  It takes the
+// 4-bit term as its accumulator input, and one more bf16 product (the bias
+// row against a column of ones) adds the bias exactly, so the VALU only
+// applies GELU and rounds.
 #include "svdq_internal.h"
 #include "svdq_quant.h"
 
@@ -104,15 +107,42 @@ __device__ __forceinline__ uint2 bias4(const uint16_t *__restrict__ bias, int n,
     return *reinterpret_cast<const uint2 *>(bias + n);
 }
 
-// y = acc + lr + b (+ GELU) for 4 consecutive channels, packed as 4 bf16.
-__device__ __forceinline__ uint2 finish4(const float *acc, const float *lr, uint2 b, int gelu)
+// y (+ GELU) for 4 consecutive channels, packed as 4 bf16.
+__device__ __forceinline__ uint2 finish4(const float *y, int gelu)
 {
-    float y0 = acc[0] + lr[0] + bf16_to_f32(b.x & 0xFFFFu), y1 = acc[1] + lr[1] + bf16_to_f32(b.x >> 16);
-    float y2 = acc[2] + lr[2] + bf16_to_f32(b.y & 0xFFFFu), y3 = acc[3] + lr[3] + bf16_to_f32(b.y >> 16);
+    float y0 = y[0], y1 = y[1], y2 = y[2], y3 = y[3];
     if (gelu) {
         y0 = gelu_tanh(y0); y1 = gelu_tanh(y1); y2 = gelu_tanh(y2); y3 = gelu_tanh(y3);
     }
     return make_uint2(pack_bf16x2(y0, y1), pack_bf16x2(y2, y3));
+}
+
+// Bias as a matrix-core operand: the A operand (rows n of a 32x32 tile) with
+// the bias of the lane's row at k = 0 of lane half 0 and zeros elsewhere.
+// Against kOnesB (1.0 at k = 0 of every column) the bf16 product adds b_n,
+// exactly, to every output of row n.  n is the tile's first channel + l32.
+__device__ __forceinline__ bf16x8 bias_operand(const uint16_t *__restrict__ bias, int n, int N, int hk)
+{
+    const uint32_t b = (bias && n < N && hk == 0) ? (uint32_t)bias[n] : 0u;
+    return __builtin_bit_cast(bf16x8, (uint4){b, 0u, 0u, 0u});
+}
+__device__ __forceinline__ bf16x8 ones_operand(int hk)
+{
+    return __builtin_bit_cast(bf16x8, (uint4){hk == 0 ? 0x3F80u : 0u, 0u, 0u, 0u});
+}
+
+// acc + h . up^T + b for one 32x32 tile on the matrix cores: the low-rank
+// term as two k steps of 16 with the hi and the lo part of h (A = up rows,
+// B = h rows), then the bias product.
+__device__ __forceinline__ f32x16 add_lowrank_bias(f32x16 acc, const bf16x8 (&ua)[2], const bf16x8 (&hhi)[2],
+                                                   const bf16x8 (&hlo)[2], bf16x8 bq, bf16x8 ones)
+{
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ua[s], hhi[s], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ua[s], hlo[s], acc, 0, 0, 0);
+    }
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(bq, ones, acc, 0, 0, 0);
 }
 
 // Output staging: each wave writes its 64 x 64 bf16 tile into its own LDS
@@ -322,23 +352,14 @@ __device__ __forceinline__ void requant_epilogue(const f32x16 (&acc)[I4_TN][I4_T
             if (nrow < N) uv = *reinterpret_cast<const uint4 *>(up + (size_t)nrow * 32 + 16 * s + 8 * hk);
             ua[s] = __builtin_bit_cast(bf16x8, uv);
         }
-        uint2 bv[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) bv[j] = bias4(bias, nb + tn * 32 + 8 * j + 4 * hk, N);
+        const bf16x8 bq = bias_operand(bias, nb + tn * 32 + l32, N, hk), ones = ones_operand(hk);
 #pragma unroll
         for (int tm = 0; tm < I4_TM; ++tm) {
-            f32x16 lr = {};
-#pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                lr = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ua[s], hhi[tm][s], lr, 0, 0, 0);
-                lr = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ua[s], hlo[tm][s], lr, 0, 0, 0);
-            }
+            const f32x16 lr = add_lowrank_bias(acc[tn][tm], ua, hhi[tm], hlo[tm], bq, ones);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                float a4[4] = {acc[tn][tm][4 * j], acc[tn][tm][4 * j + 1], acc[tn][tm][4 * j + 2],
-                               acc[tn][tm][4 * j + 3]};
-                float l4[4] = {lr[4 * j], lr[4 * j + 1], lr[4 * j + 2], lr[4 * j + 3]};
-                yb[tn][tm][j] = finish4(a4, l4, bv[j], gelu);
+                const float y4[4] = {lr[4 * j], lr[4 * j + 1], lr[4 * j + 2], lr[4 * j + 3]};
+                yb[tn][tm][j] = finish4(y4, gelu);
             }
         }
     }
@@ -516,23 +537,14 @@ __device__ __forceinline__ void qknorm_epilogue(const f32x16 (&acc)[I4_TN][I4_TM
             if (nrow < N) uv = *reinterpret_cast<const uint4 *>(up + (size_t)nrow * 32 + 16 * s2 + 8 * hk);
             ua[s2] = __builtin_bit_cast(bf16x8, uv);
         }
-        uint2 bv[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) bv[j] = bias4(bias, nb + tn * 32 + 8 * j + 4 * hk, N);
+        const bf16x8 bq = bias_operand(bias, nb + tn * 32 + l32, N, hk), ones = ones_operand(hk);
 #pragma unroll
         for (int tm = 0; tm < I4_TM; ++tm) {
-            f32x16 lr = {};
-#pragma unroll
-            for (int s2 = 0; s2 < 2; ++s2) {
-                lr = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ua[s2], hhi[tm][s2], lr, 0, 0, 0);
-                lr = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ua[s2], hlo[tm][s2], lr, 0, 0, 0);
-            }
+            const f32x16 lr = add_lowrank_bias(acc[tn][tm], ua, hhi[tm], hlo[tm], bq, ones);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const float a4[4] = {acc[tn][tm][4 * j], acc[tn][tm][4 * j + 1], acc[tn][tm][4 * j + 2],
-                                     acc[tn][tm][4 * j + 3]};
-                const float l4[4] = {lr[4 * j], lr[4 * j + 1], lr[4 * j + 2], lr[4 * j + 3]};
-                yb[tn][tm][j] = finish4(a4, l4, bv[j], 0);
+                const float y4[4] = {lr[4 * j], lr[4 * j + 1], lr[4 * j + 2], lr[4 * j + 3]};
+                yb[tn][tm][j] = finish4(y4, 0);
             }
         }
     }
@@ -842,23 +854,14 @@ __global__ __launch_bounds__(I4_THREADS) void w4a4_int4_kernel(
             if (nrow < N) uv = *reinterpret_cast<const uint4 *>(up + (size_t)nrow * 32 + 16 * s + 8 * hk);
             ua[s] = __builtin_bit_cast(bf16x8, uv);
         }
-        uint2 bv[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) bv[j] = bias4(bias, nb + tn * 32 + 8 * j + 4 * hk, N);
+        const bf16x8 bq = bias_operand(bias, nb + tn * 32 + l32, N, hk), ones = ones_operand(hk);
 #pragma unroll
         for (int tm = 0; tm < I4_TM; ++tm) {
-            f32x16 lr = {};
-#pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                lr = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ua[s], hhi[tm][s], lr, 0, 0, 0);
-                lr = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ua[s], hlo[tm][s], lr, 0, 0, 0);
-            }
+            const f32x16 lr = add_lowrank_bias(acc[tn][tm], ua, hhi[tm], hlo[tm], bq, ones);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                float a4[4] = {acc[tn][tm][4 * j], acc[tn][tm][4 * j + 1], acc[tn][tm][4 * j + 2],
-                               acc[tn][tm][4 * j + 3]};
-                float l4[4] = {lr[4 * j], lr[4 * j + 1], lr[4 * j + 2], lr[4 * j + 3]};
-                stage4(tile, tm * 32 + l32, tn * 32 + 8 * j + 4 * hk, finish4(a4, l4, bv[j], gelu));
+                const float y4[4] = {lr[4 * j], lr[4 * j + 1], lr[4 * j + 2], lr[4 * j + 3]};
+                stage4(tile, tm * 32 + l32, tn * 32 + 8 * j + 4 * hk, finish4(y4, gelu));
             }
         }
     }
@@ -1031,23 +1034,14 @@ __global__ __launch_bounds__(I4_THREADS) void w4a4_int4_tail_kernel(
             if (nrow < N) uv = *reinterpret_cast<const uint4 *>(up + (size_t)nrow * 32 + 16 * s2 + 8 * hk);
             ua[s2] = __builtin_bit_cast(bf16x8, uv);
         }
-        uint2 bv[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) bv[j] = bias4(bias, nb + tn * 32 + 8 * j + 4 * hk, N);
+        const bf16x8 bq = bias_operand(bias, nb + tn * 32 + l32, N, hk), ones = ones_operand(hk);
 #pragma unroll
         for (int tm = 0; tm < PTM; ++tm) {
-            f32x16 lr = {};
-#pragma unroll
-            for (int s2 = 0; s2 < 2; ++s2) {
-                lr = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ua[s2], hhi[tm][s2], lr, 0, 0, 0);
-                lr = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ua[s2], hlo[tm][s2], lr, 0, 0, 0);
-            }
+            const f32x16 lr = add_lowrank_bias(acc[tn][tm], ua, hhi[tm], hlo[tm], bq, ones);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const float a4[4] = {acc[tn][tm][4 * j], acc[tn][tm][4 * j + 1], acc[tn][tm][4 * j + 2],
-                                     acc[tn][tm][4 * j + 3]};
-                const float l4[4] = {lr[4 * j], lr[4 * j + 1], lr[4 * j + 2], lr[4 * j + 3]};
-                yb[tn][tm][j] = finish4(a4, l4, bv[j], EPI == EPI_STORE ? gelu : 0);
+                const float y4[4] = {lr[4 * j], lr[4 * j + 1], lr[4 * j + 2], lr[4 * j + 3]};
+                yb[tn][tm][j] = finish4(y4, EPI == EPI_STORE ? gelu : 0);
             }
         }
     }
@@ -1237,23 +1231,14 @@ __device__ __forceinline__ void wave_epilogue(const f32x16 (&acc)[TN][TM], const
                 if (nrow < N) uv = *reinterpret_cast<const uint4 *>(up + (size_t)nrow * 32 + 16 * s2 + 8 * hk);
                 ua[s2] = __builtin_bit_cast(bf16x8, uv);
             }
-            uint2 bv[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) bv[j] = bias4(bias, nb + tn * 32 + 8 * j + 4 * hk, N);
+            const bf16x8 bq = bias_operand(bias, nb + tn * 32 + l32, N, hk), ones = ones_operand(hk);
 #pragma unroll
             for (int tm = 0; tm < TM; ++tm) {
-                f32x16 lr = {};
-#pragma unroll
-                for (int s2 = 0; s2 < 2; ++s2) {
-                    lr = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ua[s2], hhi[tm][s2], lr, 0, 0, 0);
-                    lr = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ua[s2], hlo[tm][s2], lr, 0, 0, 0);
-                }
+                const f32x16 lr = add_lowrank_bias(acc[tn][tm], ua, hhi[tm], hlo[tm], bq, ones);
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    float a4[4] = {acc[tn][tm][4 * j], acc[tn][tm][4 * j + 1], acc[tn][tm][4 * j + 2],
-                                   acc[tn][tm][4 * j + 3]};
-                    float l4[4] = {lr[4 * j], lr[4 * j + 1], lr[4 * j + 2], lr[4 * j + 3]};
-                    stage4(tile, tm * 32 + l32, th * 32 + 8 * j + 4 * hk, finish4(a4, l4, bv[j], gelu));
+                    const float y4[4] = {lr[4 * j], lr[4 * j + 1], lr[4 * j + 2], lr[4 * j + 3]};
+                    stage4(tile, tm * 32 + l32, th * 32 + 8 * j + 4 * hk, finish4(y4, gelu));
                 }
             }
         }
@@ -1465,12 +1450,11 @@ __device__ __forceinline__ void requant_epilogue_mx(const f32x16 (&acc)[MX_TN][M
             if (nrow < N) uv = *reinterpret_cast<const uint4 *>(up + (size_t)nrow * 32 + 16 * s2 + 8 * hk);
             ua[s2] = __builtin_bit_cast(bf16x8, uv);
         }
-        uint2 bv[4];
+        const bf16x8 bq = bias_operand(bias, c0 + l32, N, hk), ones = ones_operand(hk);
         float4 s2v[4];
         bf16x8 dn[2];                    // A operands: down2 rows l32, k blocks 2 tn and 2 tn + 1
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            bv[j] = bias4(bias, c0 + 8 * j + 4 * hk, N);
             s2v[j] = live ? *reinterpret_cast<const float4 *>(rq.smooth2 + c0 + 8 * j + 4 * hk)
                           : make_float4(0.f, 0.f, 0.f, 0.f);
         }
@@ -1487,19 +1471,12 @@ __device__ __forceinline__ void requant_epilogue_mx(const f32x16 (&acc)[MX_TN][M
 #pragma unroll
         for (int tm = 0; tm < MX_TM; ++tm) {
             const int m = mb + tm * 32 + l32;
-            f32x16 lr = {};
-#pragma unroll
-            for (int s2 = 0; s2 < 2; ++s2) {
-                lr = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ua[s2], hhi[tm][s2], lr, 0, 0, 0);
-                lr = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ua[s2], hlo[tm][s2], lr, 0, 0, 0);
-            }
+            const f32x16 lr = add_lowrank_bias(acc[tn][tm], ua, hhi[tm], hlo[tm], bq, ones);
             uint2 yb[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                float a4[4] = {acc[tn][tm][4 * j], acc[tn][tm][4 * j + 1], acc[tn][tm][4 * j + 2],
-                               acc[tn][tm][4 * j + 3]};
-                float l4[4] = {lr[4 * j], lr[4 * j + 1], lr[4 * j + 2], lr[4 * j + 3]};
-                yb[j] = finish4(a4, l4, bv[j], gelu);
+                const float y4[4] = {lr[4 * j], lr[4 * j + 1], lr[4 * j + 2], lr[4 * j + 3]};
+                yb[j] = finish4(y4, gelu);
             }
             // smoothed values, block absmax over both lane halves, E8M0
             float v[4][4];
@@ -1632,23 +1609,14 @@ __device__ __forceinline__ void qknorm_wave_epilogue_mx(const f32x16 (&acc)[MX_T
             if (nrow < N) uv = *reinterpret_cast<const uint4 *>(up + (size_t)nrow * 32 + 16 * s2 + 8 * hk);
             ua[s2] = __builtin_bit_cast(bf16x8, uv);
         }
-        uint2 bv[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) bv[j] = bias4(bias, nb + tn * 32 + 8 * j + 4 * hk, N);
+        const bf16x8 bq = bias_operand(bias, nb + tn * 32 + l32, N, hk), ones = ones_operand(hk);
 #pragma unroll
         for (int tm = 0; tm < MX_TM; ++tm) {
-            f32x16 lr = {};
-#pragma unroll
-            for (int s2 = 0; s2 < 2; ++s2) {
-                lr = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ua[s2], hhi[tm][s2], lr, 0, 0, 0);
-                lr = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ua[s2], hlo[tm][s2], lr, 0, 0, 0);
-            }
+            const f32x16 lr = add_lowrank_bias(acc[tn][tm], ua, hhi[tm], hlo[tm], bq, ones);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const float a4[4] = {acc[tn][tm][4 * j], acc[tn][tm][4 * j + 1], acc[tn][tm][4 * j + 2],
-                                     acc[tn][tm][4 * j + 3]};
-                const float l4[4] = {lr[4 * j], lr[4 * j + 1], lr[4 * j + 2], lr[4 * j + 3]};
-                const uint2 y = finish4(a4, l4, bv[j], 0);
+                const float y4[4] = {lr[4 * j], lr[4 * j + 1], lr[4 * j + 2], lr[4 * j + 3]};
+                const uint2 y = finish4(y4, 0);
                 *reinterpret_cast<uint2 *>(area + (tm * 32 + l32) * QK_ROW + (tn * 32 + 8 * j + 4 * hk) * 2) = y;
                 const float v0 = bf16_to_f32(y.x & 0xFFFFu), v1 = bf16_to_f32(y.x >> 16);
                 const float v2 = bf16_to_f32(y.y & 0xFFFFu), v3 = bf16_to_f32(y.y >> 16);
@@ -2043,8 +2011,12 @@ __global__ __launch_bounds__(256) void splitk_finish_kernel(const float *__restr
         const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(part + ((size_t)s * M + m) * N + n));
         a[0] += v.x; a[1] += v.y; a[2] += v.z; a[3] += v.w;
     }
-    const float zero[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    *reinterpret_cast<uint2 *>(Y + (size_t)m * N + n) = finish4(a, zero, bias4(bias, n, N), gelu);
+    const uint2 b = bias4(bias, n, N);
+    a[0] += bf16_to_f32(b.x & 0xFFFFu);
+    a[1] += bf16_to_f32(b.x >> 16);
+    a[2] += bf16_to_f32(b.y & 0xFFFFu);
+    a[3] += bf16_to_f32(b.y >> 16);
+    *reinterpret_cast<uint2 *>(Y + (size_t)m * N + n) = finish4(a, gelu);
 }
 
 int splitk_slices(int M, int N, int K, svdq_precision prec, int &sps)

@@ -40,10 +40,10 @@ NO_CLOCK = False
 # only reported while the kernel source still hashes to the value it was
 # measured on; otherwise traffic is null.
 TRAFFIC = {
-    # FETCH_SIZE 73645 KiB / 0.50002 + WRITE_SIZE 110603 KiB / 1.00000 (per dispatch)
-    "fc1": {"source": "w4a4_gemm.hip", "source_sha": "996de43298c60e1d", "bytes": 264075432},
-    # FETCH_SIZE 70942 KiB / 0.50002 + WRITE_SIZE 111106 KiB / 1.00000
-    "mx_fc1": {"source": "w4a4_gemm.hip", "source_sha": "996de43298c60e1d", "bytes": 259055643},
+    # FETCH_SIZE 73470.6 KiB / 0.50002 + WRITE_SIZE 110599.9 KiB / 1.00000 (per dispatch)
+    "fc1": {"source": "w4a4_gemm.hip", "source_sha": "b5ce65339ac2b45f", "bytes": 263715511},
+    # FETCH_SIZE 70162.6 KiB / 0.50002 + WRITE_SIZE 110592.3 KiB / 1.00000
+    "mx_fc1": {"source": "w4a4_gemm.hip", "source_sha": "b5ce65339ac2b45f", "bytes": 256933089},
     # FETCH_SIZE 15680 KiB / 0.50002 + WRITE_SIZE 36 KiB / 1.00000
     "awq_mod": {"source": "awq_gemv.hip", "source_sha": "fda4dd7b5f7b1013", "bytes": 32148220},
     # FETCH_SIZE 197078 KiB / 0.50002 + WRITE_SIZE 110594 KiB / 1.00000

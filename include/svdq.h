@@ -204,7 +204,10 @@ svdq_status svdq_quantize_act(const uint16_t *X, int M, int K, const float *smoo
  * instruction on high/low bf16 splits of both scales (relative error about
  * 2^-16) and multiplies the exact partial in one fp32 fma.  MXFP4: the
  * scaled f8f6f4 matrix instruction applies both E8M0 scales.  The low-rank
- * term uses h split into a bf16 high and low part.  One kernel launch;
+ * term uses h split into a bf16 high and low part and accumulates onto the
+ * 4-bit term on the matrix cores; the bias enters there too, exactly, as
+ * one more bf16 product (the bias row against a column of ones).  One kernel
+ * launch;
  * for INT4, two when the tiles left after whole rounds of one block per CU
  * are few: those tiles are then computed in 64 x 64 pieces with K split
  * across a block's waves and the partial sums added in a fixed order (so
@@ -242,7 +245,7 @@ size_t svdq_w4a4_linear_splitk_workspace_bytes(int M, int N, int K, svdq_precisi
  * workspace in fp32, and a second kernel adds the S slices in slice order
  * (so the result is deterministic) before the epilogue; slice 0 adds the
  * low-rank term with the same bf16 high/low matrix product as the unsplit
- * epilogue.  Sums in a different
+ * epilogue, and the bias is added in fp32 after the slices.  Sums in a different
  * order than svdq_w4a4_linear's, so outputs may differ from it in the last
  * bf16 place.  Without a split it is svdq_w4a4_linear.  Errors as for
  * svdq_w4a4_linear, and SVDQ_ERR_INVALID_ARG for a NULL or too small work

@@ -329,6 +329,23 @@ def test_linear_invariants(prec):
     torch.cuda.synchronize()
 
 
+@pytest.mark.parametrize("prec", PRECS)
+@pytest.mark.parametrize("M,K,N", [(96, 512, 128), (133, 512, 200)])
+def test_linear_bias_alone_is_exact(prec, M, K, N):
+    """Zero residual codes and zero `up` leave y = b exactly: the 4-bit and
+    low-rank terms are exact zeros and the bias is a bf16 value, so every
+    output row must equal the bias (no GELU), whichever unit adds it."""
+    _say(f"bias alone prec={prec} M={M} K={K} N={N}")
+    L, p = _layer("qkv", M, K, N, prec)
+    xq, xs, h = svdq.quantize_act(_t(L["X"]), _t(p["smooth"]), _t(p["down"]), prec)
+    Y = svdq.w4a4_linear(xq, xs, h, _t(np.zeros_like(p["wq"])), _t(p["wscale"]), _t(np.zeros_like(p["up"])),
+                         _t(L["bias"]), prec)
+    got = bf16_bits_to_f32(_np(Y))
+    want = np.broadcast_to(bf16_bits_to_f32(L["bias"])[None, :], (M, N))
+    assert np.array_equal(got, want)
+    torch.cuda.synchronize()
+
+
 def test_linear_deterministic_and_empty():
     _say("linear determinism")
     L, p = _layer("qkv", 160, 512, 256, svdq.INT4)
